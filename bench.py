@@ -1,0 +1,311 @@
+#!/usr/bin/env python3
+"""Benchmark of the pre-norm SwiGLU FFN block on one MI355X.
+
+Headline (`value`): the decode-shape block, M=16 tokens, d=4096, f=11008,
+bf16, one whole C-ABI call per step, reported as algorithmic GB/s (weights
++ x + g + y bytes per call / time per call).  Weight sets are rotated over
+4 copies (1.08 GB) so the 256 MB last-level cache cannot serve repeats.
+
+The same JSON line also carries:
+  roofline      - the dominant kernel (decode gate/up projection) against the
+                  8 TB/s HBM peak, its average duration taken from HIP events
+                  the library records around each of its launches on the
+                  call's stream during the timed steps;
+  cpu_baseline  - the fp64 oracle on the host (1 BLAS thread) on the same
+                  decode workload;
+  extra         - the other workloads: prefill block (M=8192, d=4096,
+                  f=14336) fused and split gate/up, interleaved call by call,
+                  in TFLOP/s; the standalone RMSNorm (16384 x 4096 bf16);
+                  the Q8_0 decode block (M=8, d=5120, f=17408); decode at
+                  M=1 and 4; measured HBM read-only and copy ceilings.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra]
+Progress goes to stderr; stdout gets exactly one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+DECODE = dict(seed=3, M=16, d=4096, f=11008)
+PREFILL = dict(seed=4, M=8192, d=4096, f=14336)
+RMS = dict(seed=2, rows=16384, d=4096)
+Q8 = dict(seed=5, M=8, d=5120, f=17408)
+ROTATE = 4
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def to_dev(a, torch):
+    import numpy as np
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to("cuda")
+    return torch.from_numpy(a).to("cuda")
+
+
+def decode_bytes(M, d, f):
+    return 3 * f * d * 2 + 2 * M * d * 2 + d * 2
+
+
+def gateup_bytes(M, d, f):
+    return 2 * f * d * 2 + M * d * 2 + M * f * 2
+
+
+def time_calls(torch, fn, n):
+    """Average ms per call of fn() over n calls, HIP events on torch's current stream."""
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s.record()
+    for i in range(n):
+        fn(i)
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / n
+
+
+def cpu_baseline(b, target_s=10.0):
+    """The oracle as it stands on the decode workload, 1 BLAS thread, repeated
+    until ~target_s of CPU time has been spent (at least once)."""
+    from threadpoolctl import threadpool_limits
+    from oracle import ffn_oracle as O
+    reps, t0 = 0, time.perf_counter()
+    with threadpool_limits(limits=1):
+        while True:
+            O.block_from_stored("bf16", b.x, b.g, b.w_gate, b.w_up, b.w_down, b.eps)
+            reps += 1
+            if time.perf_counter() - t0 >= target_s:
+                break
+    dt = (time.perf_counter() - t0) / reps
+    gbs = decode_bytes(b.M, b.d, b.f) / dt / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"whole decode block M={b.M} d={b.d} f={b.f} (bf16 inputs decoded to fp64), "
+                      f"{reps} call(s), {dt:.2f} s per call"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--no-extra", action="store_true", help="skip the secondary workloads")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the FFN block here is a single-GPU library "
+              "(multi-GPU sharding is a design note, not built); run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    from transformer_ffn_block_amd import ffn, inputs as I
+
+    ffn.lib()
+    torch.cuda.init()
+    dev_name = torch.cuda.get_device_properties(0).name
+    log("device", dev_name)
+
+    # ------------------------------------------------------------------ decode
+    M, d, f = DECODE["M"], DECODE["d"], DECODE["f"]
+    log("generating decode inputs", DECODE)
+    b = I.make_block(DECODE["seed"], M, d, f, "bf16")
+    x, g = to_dev(b.x, torch), to_dev(b.g, torch)
+    w0 = [to_dev(a, torch) for a in (b.w_gate, b.w_up, b.w_down)]
+    sets = [w0] + [[t.clone() for t in w0] for _ in range(ROTATE - 1)]
+    ws = ffn.alloc_workspace(ffn.workspace_size(ffn.FFN_BF16, M, d, f, "auto"))
+    y = torch.empty_like(x)
+
+    def step(i):
+        wg, wu, wd = sets[i % ROTATE]
+        ffn.swiglu_block(x, g, wg, wu, wd, b.eps, "auto", out=y, workspace=ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ffn.timing_reset()
+    ffn.timing_enable(True, max_launches=4 * args.steps + 16)
+    ms = time_calls(torch, step, args.steps)
+    kt = ffn.timing_collect()
+    ffn.timing_enable(False)
+    value = decode_bytes(M, d, f) / (ms * 1e-3) / 1e9
+    log(f"decode M={M}: {ms * 1e3:.2f} us/call, {value:.1f} GB/s; kernels {kt}")
+    n_gu, t_gu = kt["decode_gateup"]
+    gu_us = t_gu / n_gu * 1e3
+    gu_gbs = gateup_bytes(M, d, f) / (gu_us * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "kernel": "decode_gateup", "achieved": round(gu_gbs, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gu_gbs / HBM_PEAK_GBS, 4),
+                "traffic": None, "avg_launch_us": round(gu_us, 2),
+                "bytes_per_launch": gateup_bytes(M, d, f)}
+    kernels = {k: {"launches": n, "avg_us": round(t / n * 1e3, 2)} for k, (n, t) in kt.items()}
+    # uninstrumented pass of the same steps, for the cost of the per-kernel events
+    ms_plain = time_calls(torch, step, args.steps)
+    log(f"decode uninstrumented: {ms_plain * 1e3:.2f} us/call")
+
+    extra = {"decode_M16_uninstrumented_GBps": round(decode_bytes(M, d, f) / (ms_plain * 1e-3) / 1e9, 1),
+             "decode_kernels": kernels}
+
+    if not args.no_extra:
+        # decode at M = 1 and 4 (first rows of the same draw)
+        for m in (1, 4):
+            xm = x[:m].contiguous()
+            ym = torch.empty_like(xm)
+
+            def stepm(i, xm=xm, ym=ym):
+                wg, wu, wd = sets[i % ROTATE]
+                ffn.swiglu_block(xm, g, wg, wu, wd, b.eps, "auto", out=ym, workspace=ws)
+            for i in range(20):
+                stepm(i)
+            msm = time_calls(torch, stepm, 100)
+            extra[f"decode_M{m}"] = {"us": round(msm * 1e3, 2),
+                                     "GBps": round(decode_bytes(m, d, f) / (msm * 1e-3) / 1e9, 1)}
+            log(f"decode M={m}: {msm * 1e3:.2f} us/call")
+        del sets, w0
+        torch.cuda.empty_cache()
+
+        # ------------------------------------------------------- HBM ceilings
+        nbytes = 4 << 30
+        buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        buf.fill_(1)
+        sink = torch.empty(16 * ffn.lib().ffn_probe_read_groups(32), dtype=torch.uint8, device="cuda")
+        best = 0.0
+        sweep = {}
+        for wpc in (4, 8, 16, 32):
+            for _ in range(2):
+                ffn.probe_read(buf, sink, wpc)
+            t = time_calls(torch, lambda i: ffn.probe_read(buf, sink, wpc), 5)
+            sweep[wpc] = round(nbytes / (t * 1e-3) / 1e9, 1)
+            best = max(best, sweep[wpc])
+        half = nbytes // 2
+        src, dst = buf[:half], buf[half:]
+        ffn.probe_copy(src, dst)
+        tc = time_calls(torch, lambda i: ffn.probe_copy(src, dst), 5)
+        copy_gbs = 2 * half / (tc * 1e-3) / 1e9
+        extra["hbm_read_ceiling_GBps"] = best
+        extra["hbm_read_sweep_waves_per_cu"] = sweep
+        extra["hbm_copy_ceiling_GBps"] = round(copy_gbs, 1)
+        log(f"HBM read ceiling {best:.0f} GB/s {sweep}, copy {copy_gbs:.0f} GB/s")
+        del buf, sink, src, dst
+        torch.cuda.empty_cache()
+
+        # ------------------------------------------------------------ RMSNorm
+        log("generating rmsnorm inputs", RMS)
+        xr, gr, eps, _ = I.make_rmsnorm(RMS["seed"], RMS["rows"], RMS["d"], "bf16")
+        xs = [to_dev(xr, torch)]
+        xs += [xs[0].clone() for _ in range(ROTATE - 1)]
+        ys = [torch.empty_like(xs[0]) for _ in range(ROTATE)]
+        gd = to_dev(gr, torch)
+        for i in range(8):
+            ffn.rmsnorm(xs[i % ROTATE], gd, eps, out=ys[i % ROTATE])
+        ffn.timing_reset()
+        ffn.timing_enable(True, 256)
+        tr = time_calls(torch, lambda i: ffn.rmsnorm(xs[i % ROTATE], gd, eps, out=ys[i % ROTATE]), 40)
+        kr = ffn.timing_collect()["rmsnorm"]
+        ffn.timing_enable(False)
+        rbytes = 2 * RMS["rows"] * RMS["d"] * 2 + RMS["d"] * 2
+        extra["rmsnorm"] = {"us": round(tr * 1e3, 2), "GBps": round(rbytes / (tr * 1e-3) / 1e9, 1),
+                            "kernel_avg_us": round(kr[1] / kr[0] * 1e3, 2),
+                            "frac_of_hbm_peak": round(rbytes / (tr * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                            "frac_of_read_ceiling": round(rbytes / (tr * 1e-3) / 1e9 / best, 4)}
+        log("rmsnorm", extra["rmsnorm"])
+        del xs, ys
+        torch.cuda.empty_cache()
+
+        # --------------------------------------------------------------- Q8_0
+        log("generating q8 inputs", Q8)
+        q = I.make_q8_block(Q8["seed"], Q8["M"], Q8["d"], Q8["f"])
+        qx, qg = to_dev(q.x, torch), to_dev(q.g, torch)
+
+        def qdev(m):
+            return (torch.from_numpy(m.qs).to("cuda"), torch.from_numpy(m.scales.view(np.int16)).to("cuda"))
+        q0 = [qdev(m) for m in (q.w_gate, q.w_up, q.w_down)]
+        qsets = [q0] + [[(a.clone(), s.clone()) for a, s in q0] for _ in range(ROTATE - 1)]
+        qws = ffn.alloc_workspace(ffn.lib().ffn_swiglu_block_q8_workspace_size(Q8["M"], Q8["d"], Q8["f"]))
+        qy = torch.empty_like(qx)
+
+        def qstep(i):
+            a, bq, c = qsets[i % ROTATE]
+            ffn.swiglu_block_q8(qx, qg, a, bq, c, q.eps, out=qy, workspace=qws)
+        for i in range(20):
+            qstep(i)
+        ffn.timing_reset()
+        ffn.timing_enable(True, 1024)
+        tq = time_calls(torch, qstep, 100)
+        kq = ffn.timing_collect()
+        ffn.timing_enable(False)
+        qbytes = 3 * (Q8["f"] * Q8["d"] + Q8["f"] * Q8["d"] // 32 * 2) + 2 * Q8["M"] * Q8["d"] * 2 + Q8["d"] * 2
+        extra["q8_decode"] = {"us": round(tq * 1e3, 2), "GBps": round(qbytes / (tq * 1e-3) / 1e9, 1),
+                              "kernels": {k: round(t / n * 1e3, 2) for k, (n, t) in kq.items()}}
+        log("q8", extra["q8_decode"])
+        del qsets, q0
+        torch.cuda.empty_cache()
+
+        # ------------------------------------------------------------ prefill
+        Mp, dp, fp = PREFILL["M"], PREFILL["d"], PREFILL["f"]
+        log("generating prefill inputs", PREFILL)
+        bp = I.make_block(PREFILL["seed"], Mp, dp, fp, "bf16")
+        px, pg = to_dev(bp.x, torch), to_dev(bp.g, torch)
+        pw = [[to_dev(a, torch) for a in (bp.w_gate, bp.w_up, bp.w_down)]]
+        pw.append([t.clone() for t in pw[0]])
+        pws = ffn.alloc_workspace(ffn.workspace_size(ffn.FFN_BF16, Mp, dp, fp, "split"))
+        py = torch.empty_like(px)
+        flops = 6.0 * Mp * dp * fp
+
+        def pstep(i, variant):
+            wg, wu, wd = pw[i % 2]
+            ffn.swiglu_block(px, pg, wg, wu, wd, bp.eps, variant, out=py, workspace=pws)
+        for i in range(3):
+            pstep(i, "fused")
+            pstep(i, "split")
+        ffn.timing_reset()
+        ffn.timing_enable(True, 1024)
+        tf, ts = [], []
+        for i in range(10):  # interleaved call by call
+            tf.append(time_calls(torch, lambda j: pstep(i, "fused"), 1))
+            ts.append(time_calls(torch, lambda j: pstep(i, "split"), 1))
+        kp = ffn.timing_collect()
+        ffn.timing_enable(False)
+        mf, msp = float(np.median(tf)), float(np.median(ts))
+        extra["prefill"] = {
+            "fused_ms": round(mf, 3), "split_ms": round(msp, 3),
+            "fused_TFLOPs": round(flops / (mf * 1e-3) / 1e12, 1),
+            "split_TFLOPs": round(flops / (msp * 1e-3) / 1e12, 1),
+            "fused_frac_of_bf16_peak": round(flops / (mf * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "split_over_fused_time": round(msp / mf, 3),
+            "kernels_avg_ms": {k: round(t / n, 4) for k, (n, t) in kp.items()}}
+        gu_ms = kp["gemm_gateup_fused"][1] / kp["gemm_gateup_fused"][0]
+        extra["prefill"]["gateup_fused_kernel_TFLOPs"] = round(4.0 * Mp * dp * fp / (gu_ms * 1e-3) / 1e12, 1)
+        log("prefill", extra["prefill"])
+        del pw
+        torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu:
+        log("timing the CPU oracle on the decode workload")
+        cpu = cpu_baseline(b)
+        log("cpu", cpu)
+
+    line = {
+        "metric": "FFN block: decode GB/s & prefill TFLOP/s on 1 GPU, % of HBM/MFMA peak",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights)",
+        "config": {"workload": "decode block M=16 d=4096 f=11008 bf16", "M": M, "d": d, "f": f,
+                   "rotated_weight_sets": ROTATE, "device": dev_name},
+        "roofline": roofline, "cpu_baseline": cpu, "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

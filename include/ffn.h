@@ -1,0 +1,172 @@
+/*
+ * ffn.h - C ABI of libffn.so, the MI355X (gfx950) pre-norm SwiGLU
+ * feed-forward block:
+ *
+ *     n = rmsnorm(x) * g                 r_m = 1 / sqrt(mean_k x[m,k]^2 + eps)
+ *     y = x + (silu(n W_gate^T) * (n W_up^T)) W_down^T,   silu(v) = v / (1 + e^-v)
+ *
+ * Sources of the operations (page title, section):
+ *   - RMSNorm, one reduction per row, eps inside the root:
+ *       "When to hand-write a GPU kernel on Apple Silicon", Rung 2 and Rung 4.
+ *   - SwiGLU silu(gate) * up, activation evaluated in fp32:
+ *       "When to hand-write a GPU kernel on Apple Silicon", Rung 1.
+ *   - gate and up projections of the SwiGLU MLP, fused in one kernel or
+ *     dispatched as two GEMMs plus the activation:
+ *       "Unfusing a Kernel Made It 1.63x Faster", Finding 1.
+ *   - the FFN-down projection:
+ *       "Megakernels on Mac", "Projection shape changes the achieved rate".
+ *   - Q8_0 weights (32 int8 quants share one fp16 scale):
+ *       "Unfusing a Kernel Made It 1.63x Faster", Finding 2 (format name).
+ *   - explicit supported shapes and failure behaviour, ownership of buffers
+ *     that submitted work still reads:
+ *       "Megakernels on Mac", "Choosing a fusion boundary" and
+ *       "Dependencies and synchronization".
+ * The pages do not place the norm or the residual; this library takes the
+ * pre-norm reading: the residual adds the un-normalised x.
+ *
+ * Conventions for every entry point:
+ *   - Tensors are DEVICE pointers to contiguous row-major arrays. Weights are
+ *     [out, in]: W_gate, W_up are [f, d], W_down is [d, f].
+ *   - The caller owns every buffer and keeps it alive until the work queued
+ *     on `stream` has completed. The library never allocates device memory,
+ *     never synchronises and never prints.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ *     stream). Intermediates live in the caller's workspace and are ordered
+ *     by the stream.
+ *   - Arguments are validated before anything is launched; a failing call
+ *     launches nothing and returns a status; ffn_last_error() then gives a
+ *     thread-local message.  Device faults surface at the caller's next
+ *     synchronisation.
+ *   - bf16 values are passed as raw 16-bit patterns (uint16_t storage).
+ *   - M == 0 (or rows == 0) returns FFN_OK and launches nothing.
+ *   - Output buffers must not overlap any input or the workspace.
+ *   - Results for a fixed variant are run-to-run bitwise deterministic (no
+ *     floating-point atomics); different variants may differ by rounding.
+ */
+#ifndef FFN_H
+#define FFN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FFN_OK = 0,
+  FFN_ERR_INVALID_ARGUMENT = 1, /* null pointer, negative size, bad enum, overlap */
+  FFN_ERR_UNSUPPORTED = 2,      /* shape/alignment outside what the kernels take   */
+  FFN_ERR_WORKSPACE = 3,        /* workspace missing or smaller than required      */
+  FFN_ERR_LAUNCH = 4            /* a kernel launch was rejected by the runtime     */
+} ffn_status;
+
+typedef enum { FFN_F32 = 0, FFN_BF16 = 1 } ffn_dtype;
+
+/* Gate/up schedule: FUSED computes both projections in one kernel whose
+ * epilogue applies silu(G)*U; SPLIT runs the gate GEMM, the up GEMM and a
+ * separate activation pass ("Unfusing a Kernel Made It 1.63x Faster",
+ * Finding 1).  AUTO picks by measured speed for the shape. */
+typedef enum { FFN_VARIANT_AUTO = 0, FFN_VARIANT_FUSED = 1, FFN_VARIANT_SPLIT = 2 } ffn_variant;
+
+/* One Q8_0 weight matrix [N, K] in split (structure-of-arrays) form:
+ *   qs     : int8  [N, K]      quants, 32 consecutive along K form a block
+ *   scales : fp16  [N, K/32]   IEEE binary16 bit patterns, one per block
+ * weight[j,k] = qs[j,k] * scales[j, k/32].  Subnormal scales are honoured.
+ * Both pointers are device pointers; qs 16-byte aligned, scales 2-byte. */
+typedef struct {
+  const int8_t *qs;
+  const uint16_t *scales;
+} ffn_q8_matrix;
+
+/* RMSNorm of `rows` rows of length d:
+ *   y[m,k] = x[m,k] * r_m * g[k],  r_m = 1/sqrt(sum_k x[m,k]^2 / d + eps)
+ * ("When to hand-write a GPU kernel on Apple Silicon", Rung 2; the 16-byte
+ * vector loads and the wavefront reduction follow Rung 4's lesson).
+ *   dt    : FFN_F32 or FFN_BF16; x, g, y all have this dtype; the sum of
+ *           squares and the scaling are computed in fp32, y rounded once.
+ *   x [rows, d], g [d], y [rows, d]: device pointers, 16-byte aligned.
+ *   d     : > 0; multiple of 8 (bf16) or 4 (fp32).
+ *   eps   : >= 0.
+ * Returns FFN_OK, INVALID_ARGUMENT (null, rows < 0, d <= 0, eps < 0 or NaN,
+ * y overlapping x or g), UNSUPPORTED (d multiple / alignment), LAUNCH. */
+ffn_status ffn_rmsnorm(ffn_dtype dt, const void *x, const void *g, void *y,
+                       int64_t rows, int64_t d, float eps, void *stream);
+
+/* Workspace bytes ffn_swiglu_block needs for this shape and variant (0 on a
+ * shape it would reject).  It holds n [M,d] and h [M,f] (plus G, U [M,f]
+ * for SPLIT), each 256-byte aligned. */
+size_t ffn_swiglu_block_workspace_size(ffn_dtype dt, int64_t M, int64_t d, int64_t f,
+                                       ffn_variant variant);
+
+/* The full block y = x + W_down (silu(W_gate n) * (W_up n)), n = rmsnorm(x) g.
+ *   dt        : FFN_BF16 (bf16 storage, fp32 accumulation; n and h are
+ *               rounded to bf16 where they are a matrix-core operand) or
+ *               FFN_F32 (all fp32).
+ *   x [M,d], g [d], w_gate [f,d], w_up [f,d], w_down [d,f], y [M,d]: device
+ *               pointers of dtype dt, 16-byte aligned.
+ *   d, f      : > 0; multiples of 8 (bf16) or 4 (fp32).
+ *   variant   : gate/up schedule (see ffn_variant).
+ *   workspace : device buffer of at least
+ *               ffn_swiglu_block_workspace_size(dt, M, d, f, variant) bytes,
+ *               256-byte aligned; its contents are scratch.
+ * Returns FFN_OK, INVALID_ARGUMENT, UNSUPPORTED, WORKSPACE or LAUNCH. */
+ffn_status ffn_swiglu_block(ffn_dtype dt, const void *x, const void *g,
+                            const void *w_gate, const void *w_up, const void *w_down,
+                            void *y, int64_t M, int64_t d, int64_t f, float eps,
+                            ffn_variant variant, void *workspace, size_t workspace_bytes,
+                            void *stream);
+
+/* Workspace bytes ffn_swiglu_block_q8 needs (n [M,d] and h [M,f] in bf16). */
+size_t ffn_swiglu_block_q8_workspace_size(int64_t M, int64_t d, int64_t f);
+
+/* The block with Q8_0 weights, bf16 activations:
+ *   x [M,d], g [d], y [M,d]: bf16 device pointers, 16-byte aligned.
+ *   w_gate, w_up : Q8_0 [f, d]; w_down : Q8_0 [d, f] (host structs holding
+ *                  device pointers).
+ *   d, f : multiples of 32 (so no block straddles a row).
+ * Weights are dequantised in registers (q * s, exact in fp32) and never
+ * written back; accumulation is fp32.
+ * Returns FFN_OK, INVALID_ARGUMENT, UNSUPPORTED, WORKSPACE or LAUNCH. */
+ffn_status ffn_swiglu_block_q8(const void *x, const void *g, const ffn_q8_matrix *w_gate,
+                               const ffn_q8_matrix *w_up, const ffn_q8_matrix *w_down,
+                               void *y, int64_t M, int64_t d, int64_t f, float eps,
+                               void *workspace, size_t workspace_bytes, void *stream);
+
+/* Human-readable name of a status. Never NULL. */
+const char *ffn_status_string(ffn_status s);
+
+/* Detail of the last non-OK return on the calling thread ("" if none). */
+const char *ffn_last_error(void);
+
+/* ---- measurement helpers -------------------------------------------------
+ * The pages separate a read-only streaming ceiling from a read+write one
+ * and warn that the wrong one understates weight streaming
+ * ("Unfusing a Kernel Made It 1.63x Faster", "Two published claims we got
+ * wrong", claim 1).  These two kernels measure both on this device. */
+
+/* Streams `bytes` (multiple of 16, >= 16) from src and writes one 16-byte
+ * value per workgroup into sink (>= 16 * ffn_probe_read_groups() bytes) so
+ * the loads cannot be removed. `waves_per_cu` (1..32) sets the grid. */
+ffn_status ffn_probe_read(const void *src, size_t bytes, void *sink, int waves_per_cu,
+                          void *stream);
+int ffn_probe_read_groups(int waves_per_cu);
+
+/* Copies `bytes` (multiple of 16) from src to dst with 16-byte loads/stores. */
+ffn_status ffn_probe_copy(const void *src, void *dst, size_t bytes, void *stream);
+
+/* ---- per-kernel timing ----------------------------------------------------
+ * When enabled, every kernel the library launches is bracketed by a pair of
+ * HIP events recorded on the same stream; ffn_timing_collect() waits for
+ * them and accumulates per-kernel totals.  Off by default; costs two event
+ * records per launch when on.  Not thread-safe while enabled. */
+ffn_status ffn_timing_enable(int on, int max_launches);
+ffn_status ffn_timing_collect(void);     /* synchronises the recorded events */
+int ffn_timing_count(void);              /* number of distinct kernel names   */
+ffn_status ffn_timing_get(int index, const char **name, int64_t *launches, double *total_ms);
+void ffn_timing_reset(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FFN_H */

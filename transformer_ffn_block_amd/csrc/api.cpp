@@ -1,0 +1,411 @@
+// C ABI of libffn (declared in include/ffn.h): argument validation, schedule
+// selection and kernel launches on the caller's stream.  No device memory is
+// allocated here, nothing synchronises (except ffn_timing_collect), nothing
+// prints.
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <string>
+#include <vector>
+
+#include "../../include/ffn.h"
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+ffn_status fail(ffn_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+ffn_status ok() {
+  g_err.clear();
+  return FFN_OK;
+}
+
+// ---- per-kernel timing ---------------------------------------------------
+struct Timing {
+  bool on = false;
+  int cap = 0;
+  int used = 0;
+  std::vector<hipEvent_t> ev;
+  std::vector<const char*> name;
+  std::map<std::string, std::pair<int64_t, double>> total;
+  std::vector<std::string> order;
+};
+Timing g_t;
+
+template <class F>
+hipError_t timed(const char* name, hipStream_t s, F&& f) {
+  if (!g_t.on || g_t.used >= g_t.cap) return f();
+  const int i = g_t.used++;
+  hipError_t e = hipEventRecord(g_t.ev[2 * i], s);
+  if (e != hipSuccess) return e;
+  e = f();
+  if (e != hipSuccess) return e;
+  g_t.name[i] = name;
+  return hipEventRecord(g_t.ev[2 * i + 1], s);
+}
+
+void release_events() {
+  for (hipEvent_t e : g_t.ev)
+    if (e) (void)hipEventDestroy(e);
+  g_t.ev.clear();
+  g_t.name.clear();
+  g_t.cap = g_t.used = 0;
+}
+
+// ---- validation helpers ----------------------------------------------------
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return na && nb && x < y + nb && y < x + na;
+}
+
+size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+constexpr int64_t kMaxChunks = 0x7FFFFFFF;  // 16-byte chunks addressable with int32 offsets
+
+size_t elem_size(ffn_dtype dt) { return dt == FFN_BF16 ? 2 : 4; }
+
+ffn_status check_dtype(ffn_dtype dt) {
+  if (dt != FFN_F32 && dt != FFN_BF16)
+    return fail(FFN_ERR_INVALID_ARGUMENT, "unknown dtype %d", (int)dt);
+  return FFN_OK;
+}
+
+ffn_status check_eps(float eps) {
+  if (!(eps >= 0.f) || !std::isfinite(eps))
+    return fail(FFN_ERR_INVALID_ARGUMENT, "eps must be finite and >= 0");
+  return FFN_OK;
+}
+
+// sizes shared by the dense and Q8 blocks
+ffn_status check_block_dims(int64_t M, int64_t d, int64_t f, int64_t mult) {
+  if (M < 0 || d <= 0 || f <= 0)
+    return fail(FFN_ERR_INVALID_ARGUMENT, "need M >= 0, d > 0, f > 0 (got %lld, %lld, %lld)",
+                (long long)M, (long long)d, (long long)f);
+  if (d % mult || f % mult)
+    return fail(FFN_ERR_UNSUPPORTED, "d and f must be multiples of %lld (got %lld, %lld)",
+                (long long)mult, (long long)d, (long long)f);
+  if (M > 0x7FFFFFFF || d > 0x7FFFFFFF || f > 0x7FFFFFFF)
+    return fail(FFN_ERR_UNSUPPORTED, "dimension exceeds 2^31-1");
+  const int64_t mx = M > f ? M : f;
+  if (mx * (d / 8) > kMaxChunks || (M > d ? M : d) * (f / 8) > kMaxChunks)
+    return fail(FFN_ERR_UNSUPPORTED, "tensor too large for 32-bit chunk offsets");
+  return FFN_OK;
+}
+
+struct WsLayout {
+  size_t n = 0, h = 0, G = 0, U = 0, total = 0;
+};
+
+WsLayout ws_layout(size_t es, int64_t M, int64_t d, int64_t f, bool split) {
+  WsLayout w;
+  size_t at = 0;
+  w.n = at;
+  at += round256((size_t)M * d * es);
+  w.h = at;
+  at += round256((size_t)M * f * es);
+  if (split) {
+    w.G = at;
+    at += round256((size_t)M * f * es);
+    w.U = at;
+    at += round256((size_t)M * f * es);
+  }
+  w.total = at;
+  return w;
+}
+
+#define FFN_TRY(expr)                 \
+  do {                                \
+    ffn_status st_ = (expr);          \
+    if (st_ != FFN_OK) return st_;    \
+  } while (0)
+
+#define FFN_LAUNCH(name, s, call)                                                          \
+  do {                                                                                     \
+    hipError_t e_ = timed(name, s, [&] { return (call); });                               \
+    if (e_ != hipSuccess)                                                                  \
+      return fail(FFN_ERR_LAUNCH, "%s: %s", name, hipGetErrorString(e_));                  \
+  } while (0)
+
+bool use_split(ffn_variant v) { return v == FFN_VARIANT_SPLIT; }
+
+}  // namespace
+
+extern "C" {
+
+const char* ffn_status_string(ffn_status s) {
+  switch (s) {
+    case FFN_OK: return "FFN_OK";
+    case FFN_ERR_INVALID_ARGUMENT: return "FFN_ERR_INVALID_ARGUMENT";
+    case FFN_ERR_UNSUPPORTED: return "FFN_ERR_UNSUPPORTED";
+    case FFN_ERR_WORKSPACE: return "FFN_ERR_WORKSPACE";
+    case FFN_ERR_LAUNCH: return "FFN_ERR_LAUNCH";
+  }
+  return "FFN_ERR_UNKNOWN";
+}
+
+const char* ffn_last_error(void) { return g_err.c_str(); }
+
+// ---------------------------------------------------------------------------
+ffn_status ffn_rmsnorm(ffn_dtype dt, const void* x, const void* g, void* y, int64_t rows,
+                       int64_t d, float eps, void* stream) {
+  FFN_TRY(check_dtype(dt));
+  if (!x || !g || !y) return fail(FFN_ERR_INVALID_ARGUMENT, "null pointer");
+  if (rows < 0 || d <= 0)
+    return fail(FFN_ERR_INVALID_ARGUMENT, "need rows >= 0 and d > 0");
+  FFN_TRY(check_eps(eps));
+  const size_t es = elem_size(dt);
+  const int64_t mult = 16 / (int64_t)es;
+  if (d % mult) return fail(FFN_ERR_UNSUPPORTED, "d must be a multiple of %lld", (long long)mult);
+  if (d / mult > kMaxChunks || rows > 0x7FFFFFFFLL)
+    return fail(FFN_ERR_UNSUPPORTED, "too large");
+  if (!aligned(x, 16) || !aligned(g, 16) || !aligned(y, 16))
+    return fail(FFN_ERR_UNSUPPORTED, "x, g and y must be 16-byte aligned");
+  const size_t nb = (size_t)rows * d * es;
+  if (overlap(y, nb, x, nb) || overlap(y, nb, g, (size_t)d * es))
+    return fail(FFN_ERR_INVALID_ARGUMENT, "y overlaps an input");
+  if (rows == 0) return ok();
+  hipStream_t s = (hipStream_t)stream;
+  FFN_LAUNCH("rmsnorm", s, ffn::launch_rmsnorm((int)es, x, g, y, rows, d, eps, s));
+  return ok();
+}
+
+size_t ffn_swiglu_block_workspace_size(ffn_dtype dt, int64_t M, int64_t d, int64_t f,
+                                       ffn_variant variant) {
+  if (dt != FFN_F32 && dt != FFN_BF16) return 0;
+  if (M < 0 || d <= 0 || f <= 0) return 0;
+  if (variant != FFN_VARIANT_AUTO && variant != FFN_VARIANT_FUSED && variant != FFN_VARIANT_SPLIT)
+    return 0;
+  return ws_layout(elem_size(dt), M, d, f, use_split(variant)).total;
+}
+
+ffn_status ffn_swiglu_block(ffn_dtype dt, const void* x, const void* g, const void* w_gate,
+                            const void* w_up, const void* w_down, void* y, int64_t M, int64_t d,
+                            int64_t f, float eps, ffn_variant variant, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  FFN_TRY(check_dtype(dt));
+  if (!x || !g || !w_gate || !w_up || !w_down || !y)
+    return fail(FFN_ERR_INVALID_ARGUMENT, "null pointer");
+  if (variant != FFN_VARIANT_AUTO && variant != FFN_VARIANT_FUSED && variant != FFN_VARIANT_SPLIT)
+    return fail(FFN_ERR_INVALID_ARGUMENT, "unknown variant %d", (int)variant);
+  FFN_TRY(check_eps(eps));
+  const size_t es = elem_size(dt);
+  FFN_TRY(check_block_dims(M, d, f, 16 / (int64_t)es));
+  if (!aligned(x, 16) || !aligned(g, 16) || !aligned(w_gate, 16) || !aligned(w_up, 16) ||
+      !aligned(w_down, 16) || !aligned(y, 16))
+    return fail(FFN_ERR_UNSUPPORTED, "tensors must be 16-byte aligned");
+  const bool split = use_split(variant);
+  const WsLayout L = ws_layout(es, M, d, f, split);
+  if (M > 0 && (!workspace || workspace_bytes < L.total))
+    return fail(FFN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total,
+                workspace ? workspace_bytes : (size_t)0);
+  if (workspace && !aligned(workspace, 256))
+    return fail(FFN_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
+  const size_t ny = (size_t)M * d * es, nw = (size_t)f * d * es;
+  if (overlap(y, ny, x, ny) || overlap(y, ny, g, (size_t)d * es) || overlap(y, ny, w_gate, nw) ||
+      overlap(y, ny, w_up, nw) || overlap(y, ny, w_down, nw) ||
+      overlap(y, ny, workspace, workspace ? L.total : 0))
+    return fail(FFN_ERR_INVALID_ARGUMENT, "y overlaps an input or the workspace");
+  if (M == 0) return ok();
+
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  void* n = ws + L.n;
+  void* h = ws + L.h;
+  const int Mi = (int)M, di = (int)d, fi = (int)f;
+
+  FFN_LAUNCH("rmsnorm", s, ffn::launch_rmsnorm((int)es, x, g, n, M, d, eps, s));
+  if (dt == FFN_F32) {
+    const float* nf = (const float*)n;
+    float* hf = (float*)h;
+    if (split) {
+      float* G = (float*)(ws + L.G);
+      float* U = (float*)(ws + L.U);
+      FFN_LAUNCH("f32_gemm_gate", s, ffn::launch_gemm_f32(ffn::F32_STORE, nf, (const float*)w_gate, nullptr, nullptr, G, Mi, fi, di, s));
+      FFN_LAUNCH("f32_gemm_up", s, ffn::launch_gemm_f32(ffn::F32_STORE, nf, (const float*)w_up, nullptr, nullptr, U, Mi, fi, di, s));
+      FFN_LAUNCH("f32_swiglu", s, ffn::launch_swiglu_f32(G, U, hf, (int64_t)M * f, s));
+    } else {
+      FFN_LAUNCH("f32_gemm_gateup_fused", s, ffn::launch_gemm_f32(ffn::F32_SWIGLU, nf, (const float*)w_gate, (const float*)w_up, nullptr, hf, Mi, fi, di, s));
+    }
+    FFN_LAUNCH("f32_gemm_down_residual", s, ffn::launch_gemm_f32(ffn::F32_RESIDUAL, hf, (const float*)w_down, nullptr, (const float*)x, (float*)y, Mi, di, fi, s));
+    return ok();
+  }
+
+  const bool decode = Mi <= ffn::decode_max_tokens();
+  if (split) {
+    void* G = ws + L.G;
+    void* U = ws + L.U;
+    FFN_LAUNCH("gemm_gate", s, ffn::launch_gemm_store(n, w_gate, G, Mi, fi, di, s));
+    FFN_LAUNCH("gemm_up", s, ffn::launch_gemm_store(n, w_up, U, Mi, fi, di, s));
+    FFN_LAUNCH("swiglu", s, ffn::launch_swiglu_bf16(G, U, h, (int64_t)M * f, s));
+  } else if (decode) {
+    FFN_LAUNCH("decode_gateup", s, ffn::launch_decode_gateup(n, w_gate, w_up, h, Mi, di, fi, s));
+  } else {
+    FFN_LAUNCH("gemm_gateup_fused", s, ffn::launch_gemm_gateup_fused(n, w_gate, w_up, h, Mi, di, fi, s));
+  }
+  if (decode) {
+    FFN_LAUNCH("decode_down", s, ffn::launch_decode_down(h, w_down, x, y, Mi, di, fi, s));
+  } else {
+    FFN_LAUNCH("gemm_down_residual", s, ffn::launch_gemm_residual(h, w_down, x, y, Mi, di, fi, s));
+  }
+  return ok();
+}
+
+size_t ffn_swiglu_block_q8_workspace_size(int64_t M, int64_t d, int64_t f) {
+  if (M < 0 || d <= 0 || f <= 0) return 0;
+  return ws_layout(2, M, d, f, false).total;
+}
+
+ffn_status ffn_swiglu_block_q8(const void* x, const void* g, const ffn_q8_matrix* w_gate,
+                               const ffn_q8_matrix* w_up, const ffn_q8_matrix* w_down, void* y,
+                               int64_t M, int64_t d, int64_t f, float eps, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  if (!x || !g || !y || !w_gate || !w_up || !w_down)
+    return fail(FFN_ERR_INVALID_ARGUMENT, "null pointer");
+  const ffn_q8_matrix* mats[3] = {w_gate, w_up, w_down};
+  for (const ffn_q8_matrix* m : mats) {
+    if (!m->qs || !m->scales) return fail(FFN_ERR_INVALID_ARGUMENT, "null Q8 matrix pointer");
+    if (!aligned(m->qs, 16) || !aligned(m->scales, 2))
+      return fail(FFN_ERR_UNSUPPORTED, "Q8 quants must be 16-byte aligned, scales 2-byte");
+  }
+  FFN_TRY(check_eps(eps));
+  FFN_TRY(check_block_dims(M, d, f, 32));
+  if (!aligned(x, 16) || !aligned(g, 16) || !aligned(y, 16))
+    return fail(FFN_ERR_UNSUPPORTED, "x, g and y must be 16-byte aligned");
+  const WsLayout L = ws_layout(2, M, d, f, false);
+  if (M > 0 && (!workspace || workspace_bytes < L.total))
+    return fail(FFN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total,
+                workspace ? workspace_bytes : (size_t)0);
+  if (workspace && !aligned(workspace, 256))
+    return fail(FFN_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
+  const size_t ny = (size_t)M * d * 2, nq = (size_t)f * d, ns = (size_t)f * d / 32 * 2;
+  bool ov = overlap(y, ny, x, ny) || overlap(y, ny, g, (size_t)d * 2) ||
+            overlap(y, ny, workspace, workspace ? L.total : 0);
+  for (const ffn_q8_matrix* m : mats) ov = ov || overlap(y, ny, m->qs, nq) || overlap(y, ny, m->scales, ns);
+  if (ov) return fail(FFN_ERR_INVALID_ARGUMENT, "y overlaps an input or the workspace");
+  if (M == 0) return ok();
+
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  char* n = ws + L.n;
+  char* h = ws + L.h;
+  FFN_LAUNCH("rmsnorm", s, ffn::launch_rmsnorm(2, x, g, n, M, d, eps, s));
+  const int step = ffn::q8_max_tokens();
+  for (int64_t m0 = 0; m0 < M; m0 += step) {
+    const int mc = (int)(M - m0 < step ? M - m0 : step);
+    FFN_LAUNCH("q8_gateup", s,
+               ffn::launch_q8_gateup(n + m0 * d * 2, w_gate->qs, w_gate->scales, w_up->qs,
+                                     w_up->scales, h + m0 * f * 2, mc, (int)d, (int)f, s));
+    FFN_LAUNCH("q8_down", s,
+               ffn::launch_q8_down(h + m0 * f * 2, w_down->qs, w_down->scales,
+                                   (const char*)x + m0 * d * 2, (char*)y + m0 * d * 2, mc,
+                                   (int)d, (int)f, s));
+  }
+  return ok();
+}
+
+// ---------------------------------------------------------------------------
+int ffn_probe_read_groups(int waves_per_cu) { return ffn::probe_read_groups(waves_per_cu); }
+
+ffn_status ffn_probe_read(const void* src, size_t bytes, void* sink, int waves_per_cu,
+                          void* stream) {
+  if (!src || !sink) return fail(FFN_ERR_INVALID_ARGUMENT, "null pointer");
+  if (bytes < 16 || bytes % 16 || waves_per_cu < 1 || waves_per_cu > 32)
+    return fail(FFN_ERR_INVALID_ARGUMENT, "bytes must be a positive multiple of 16, waves 1..32");
+  if (!aligned(src, 16) || !aligned(sink, 16)) return fail(FFN_ERR_UNSUPPORTED, "alignment");
+  hipStream_t s = (hipStream_t)stream;
+  FFN_LAUNCH("probe_read", s, ffn::launch_probe_read(src, bytes, sink, waves_per_cu, s));
+  return ok();
+}
+
+ffn_status ffn_probe_copy(const void* src, void* dst, size_t bytes, void* stream) {
+  if (!src || !dst) return fail(FFN_ERR_INVALID_ARGUMENT, "null pointer");
+  if (bytes % 16) return fail(FFN_ERR_INVALID_ARGUMENT, "bytes must be a multiple of 16");
+  if (!aligned(src, 16) || !aligned(dst, 16)) return fail(FFN_ERR_UNSUPPORTED, "alignment");
+  if (overlap(src, bytes, dst, bytes)) return fail(FFN_ERR_INVALID_ARGUMENT, "overlap");
+  if (bytes == 0) return ok();
+  hipStream_t s = (hipStream_t)stream;
+  FFN_LAUNCH("probe_copy", s, ffn::launch_probe_copy(src, dst, bytes, s));
+  return ok();
+}
+
+// ---------------------------------------------------------------------------
+ffn_status ffn_timing_enable(int on, int max_launches) {
+  if (!on) {
+    g_t.on = false;
+    return ok();
+  }
+  if (max_launches < 1 || max_launches > (1 << 20))
+    return fail(FFN_ERR_INVALID_ARGUMENT, "max_launches must be 1..2^20");
+  if (g_t.cap != max_launches) {
+    release_events();
+    g_t.ev.assign(2 * (size_t)max_launches, nullptr);
+    g_t.name.assign(max_launches, nullptr);
+    for (auto& e : g_t.ev) {
+      if (hipEventCreate(&e) != hipSuccess) {
+        release_events();
+        return fail(FFN_ERR_LAUNCH, "hipEventCreate failed");
+      }
+    }
+    g_t.cap = max_launches;
+  }
+  g_t.used = 0;
+  g_t.on = true;
+  return ok();
+}
+
+ffn_status ffn_timing_collect(void) {
+  for (int i = 0; i < g_t.used; ++i) {
+    if (hipEventSynchronize(g_t.ev[2 * i + 1]) != hipSuccess)
+      return fail(FFN_ERR_LAUNCH, "event synchronize failed");
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, g_t.ev[2 * i], g_t.ev[2 * i + 1]) != hipSuccess)
+      return fail(FFN_ERR_LAUNCH, "event elapsed time failed");
+    const std::string nm = g_t.name[i] ? g_t.name[i] : "?";
+    auto it = g_t.total.find(nm);
+    if (it == g_t.total.end()) {
+      g_t.order.push_back(nm);
+      g_t.total[nm] = {1, (double)ms};
+    } else {
+      it->second.first += 1;
+      it->second.second += ms;
+    }
+  }
+  g_t.used = 0;
+  return ok();
+}
+
+int ffn_timing_count(void) { return (int)g_t.order.size(); }
+
+ffn_status ffn_timing_get(int index, const char** name, int64_t* launches, double* total_ms) {
+  if (index < 0 || index >= (int)g_t.order.size() || !name || !launches || !total_ms)
+    return fail(FFN_ERR_INVALID_ARGUMENT, "bad timing index or null output");
+  const std::string& nm = g_t.order[index];
+  *name = nm.c_str();
+  *launches = g_t.total[nm].first;
+  *total_ms = g_t.total[nm].second;
+  return ok();
+}
+
+void ffn_timing_reset(void) {
+  g_t.total.clear();
+  g_t.order.clear();
+  g_t.used = 0;
+}
+
+}  // extern "C"

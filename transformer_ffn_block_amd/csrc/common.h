@@ -1,0 +1,79 @@
+// Device-side helpers shared by the gfx950 kernels of libffn.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ffn {
+
+typedef uint16_t bf16_t;  // raw bf16 storage
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// Streaming (non-temporal) loads: data read once, not worth keeping in cache.
+__device__ __forceinline__ uint4 ld_nt(const uint4* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 ld_nt(const uint2* p) {
+  const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+  return make_uint2(v.x, v.y);
+}
+
+// v if keep else 0, component-wise (a ternary on the struct type would go
+// through private memory)
+__device__ __forceinline__ uint4 keep_or_zero(bool keep, const uint4& v) {
+  const uint32_t m = keep ? 0xFFFFFFFFu : 0u;
+  return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
+}
+
+__device__ __forceinline__ float bf2f(uint32_t b16) { return __uint_as_float(b16 << 16); }
+
+// fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2 r;
+  r[0] = (__bf16)lo;
+  r[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, r);
+}
+__device__ __forceinline__ bf16_t f2bf(float v) {
+  return (bf16_t)(pack_bf16x2(v, 0.f) & 0xFFFFu);
+}
+
+// the 8 bf16 of a 16-byte chunk, widened to fp32
+__device__ __forceinline__ void unpack8(const uint4& v, float* o) {
+  o[0] = __uint_as_float(v.x << 16); o[1] = __uint_as_float(v.x & 0xFFFF0000u);
+  o[2] = __uint_as_float(v.y << 16); o[3] = __uint_as_float(v.y & 0xFFFF0000u);
+  o[4] = __uint_as_float(v.z << 16); o[5] = __uint_as_float(v.z & 0xFFFF0000u);
+  o[6] = __uint_as_float(v.w << 16); o[7] = __uint_as_float(v.w & 0xFFFF0000u);
+}
+__device__ __forceinline__ uint4 pack8(const float* o) {
+  return make_uint4(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]),
+                    pack_bf16x2(o[4], o[5]), pack_bf16x2(o[6], o[7]));
+}
+
+// silu(v) * u in fp32: v / (1 + e^-v) * u.  For v -> -inf, e^-v overflows to
+// +inf and the quotient is -0, the correct limit.
+__device__ __forceinline__ float silu_mul(float v, float u) {
+  return v / (1.0f + __expf(-v)) * u;
+}
+
+// Sum over the 64 lanes of a wavefront (butterfly, every lane gets the total).
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const uint4& v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ f32x4 mfma16(const uint4& a, const uint4& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+}  // namespace ffn

@@ -1,0 +1,56 @@
+// Host-side launchers of the gfx950 kernels (internal to libffn; the public
+// C ABI is include/ffn.h).  Each launcher assumes its arguments were already
+// validated by the API layer and only enqueues kernels on `s`.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ffn {
+
+// RMSNorm, one wavefront per row ("When to hand-write a GPU kernel on Apple
+// Silicon", Rung 2 / Rung 4).  elem_bytes 2 = bf16, 4 = fp32.
+hipError_t launch_rmsnorm(int elem_bytes, const void* x, const void* g, void* y,
+                          int64_t rows, int64_t d, float eps, hipStream_t s);
+
+// Decode (few tokens) weight-streaming projections on bf16 MFMA.
+//   gate/up: h[M,f] = silu(n Wg^T) * (n Wu^T)
+//   down   : y[M,d] = x + h Wd^T
+int decode_max_tokens();
+hipError_t launch_decode_gateup(const void* n, const void* wg, const void* wu, void* h,
+                                int M, int d, int f, hipStream_t s);
+hipError_t launch_decode_down(const void* h, const void* wd, const void* x, void* y,
+                              int M, int d, int f, hipStream_t s);
+
+// Prefill (many tokens) LDS-tiled bf16 MFMA GEMMs, C[m][n] = sum_k A[m][k] W[n][k].
+hipError_t launch_gemm_gateup_fused(const void* n, const void* wg, const void* wu, void* h,
+                                    int M, int d, int f, hipStream_t s);
+hipError_t launch_gemm_store(const void* a, const void* w, void* c, int M, int N, int K,
+                             hipStream_t s);
+hipError_t launch_gemm_residual(const void* a, const void* w, const void* resid, void* y,
+                                int M, int N, int K, hipStream_t s);
+// h = silu(G) * U elementwise over `count` bf16 values (count % 8 == 0).
+hipError_t launch_swiglu_bf16(const void* G, const void* U, void* h, int64_t count,
+                              hipStream_t s);
+
+// fp32 path (all fp32 arithmetic, SIMT tiles).
+enum F32Epi { F32_STORE = 0, F32_SWIGLU = 1, F32_RESIDUAL = 2 };
+hipError_t launch_gemm_f32(int epi, const float* a, const float* w0, const float* w1,
+                           const float* resid, float* c, int M, int N, int K, hipStream_t s);
+hipError_t launch_swiglu_f32(const float* G, const float* U, float* h, int64_t count,
+                             hipStream_t s);
+
+// Q8_0 weight-streaming projections (bf16 activations, in-register dequant).
+hipError_t launch_q8_gateup(const void* n, const int8_t* qg, const uint16_t* sg,
+                            const int8_t* qu, const uint16_t* su, void* h, int M, int d,
+                            int f, hipStream_t s);
+hipError_t launch_q8_down(const void* h, const int8_t* qd, const uint16_t* sd, const void* x,
+                          void* y, int M, int d, int f, hipStream_t s);
+int q8_max_tokens();
+
+// Bandwidth probes.
+int probe_read_groups(int waves_per_cu);
+hipError_t launch_probe_read(const void* src, size_t bytes, void* sink, int waves_per_cu,
+                             hipStream_t s);
+hipError_t launch_probe_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
+
+}  // namespace ffn

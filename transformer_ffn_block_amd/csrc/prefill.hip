@@ -1,0 +1,277 @@
+// Prefill-regime projections (thousands of tokens) on bf16 MFMA with
+// LDS-staged tiles.
+//
+//   C[m][n] = sum_k A[m][k] * W[n][k]      A = activations [M,K], W = weights [N,K]
+// with three epilogues:
+//   STORE    : C -> bf16                                  (split gate / split up)
+//   SWIGLU   : h = silu(A Wg^T) * (A Wu^T) -> bf16         (fused gate/up)
+//   RESIDUAL : y = resid + C -> bf16                       (down projection)
+// The fused-vs-split choice for gate/up is the subject of "Unfusing a Kernel
+// Made It 1.63x Faster", Finding 1 (fusion saves a memory pass but cost the
+// original kernel 64 extra accumulators per thread); "Finding 3" shows
+// threadgroup memory as the binding resource on that chip.
+//
+// gfx950 design (not the page's): the fused kernel is register-neutral.
+// A workgroup's weight tile holds BN/2 gate rows and the SAME BN/2 up rows,
+// and each wave's sub-tile covers matching gate and up rows, so a lane ends
+// the K loop with G and U for the same (token, column) pairs and applies
+// silu(G)*U in registers; the accumulator count equals the split GEMM's.
+//
+//  * v_mfma_f32_16x16x32_bf16, A operand = 16 weight rows, B operand = 16
+//    tokens; a lane's result is 4 consecutive output columns of one token.
+//  * BK = 64: every LDS row is 128 B = 8 chunks of 16 B; chunk c of row r is
+//    stored at c ^ swz(r), swz(r) = (r & 7) ^ ((r >> 3) & 1), which keeps the
+//    16 lanes of a ds_read_b128 phase on distinct banks.
+//  * two LDS stages; the next K tile is loaded into VGPRs while the MFMAs
+//    consume the current stage; one barrier per K tile.
+//  * workgroups are dispatched round-robin over the 8 XCDs; tile ids are
+//    remapped so each XCD works on a contiguous range of tiles, grouped 8
+//    token tiles deep, so concurrently running tiles share operands in the
+//    XCD's own L2.
+#include "common.h"
+#include "launch.h"
+
+namespace ffn {
+
+enum { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_RESIDUAL = 2 };
+
+__device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+
+template <int BM, int BN, int WM, int WN, int EPI>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_bf16(
+    const uint16_t* __restrict__ act,    // [M, K]
+    const uint16_t* __restrict__ w0,     // [N, K]  (gate for SWIGLU)
+    const uint16_t* __restrict__ w1,     // [N, K]  (up for SWIGLU)
+    const uint16_t* __restrict__ resid,  // [M, N]  (RESIDUAL)
+    uint16_t* __restrict__ out,          // [M, N]
+    int M, int N, int K) {
+  constexpr int NT = WM * WN * 64;
+  constexpr int TM = BM / WM;  // tokens per wave
+  constexpr int TN = BN / WN;  // weight rows per wave (half gate, half up for SWIGLU)
+  constexpr int FM = TM / 16, FN = TN / 16;
+  constexpr int BNO = EPI == EPI_SWIGLU ? BN / 2 : BN;  // output columns per tile
+  constexpr int ROWS = BN + BM;                           // LDS rows per stage
+  constexpr int CH = ROWS * 8 / NT;                       // 16-byte chunks per thread per stage
+  static_assert(ROWS * 8 % NT == 0 && (BN * 8) % NT == 0, "tile/thread mismatch");
+  static_assert(TM % 16 == 0 && TN % 16 == 0 && (EPI != EPI_SWIGLU || FN % 2 == 0), "bad wave tile");
+  static_assert((NT / 8) % 16 == 0, "row stride per chunk must keep the swizzle");
+  static_assert(EPI != EPI_SWIGLU || (BN / 2) % (NT / 8) == 0, "gate/up rows must split on chunk boundaries");
+
+  extern __shared__ uint4 lds[];  // [2][ROWS][8]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const int K8 = K >> 3;
+  const int nkt = (K8 + 7) >> 3;
+
+  // ---- tile coordinates: XCD-contiguous, then grouped 8 token tiles deep
+  const int ntm = (M + BM - 1) / BM, ntn = (N + BNO - 1) / BNO;
+  const int T = ntm * ntn;
+  int L = blockIdx.x;
+  if ((T & 7) == 0) L = (L & 7) * (T >> 3) + (L >> 3);
+  constexpr int GM = 8;
+  const int group = L / (GM * ntn);
+  const int first_m = group * GM;
+  const int gm = min(ntm - first_m, GM);
+  const int inner = L - group * GM * ntn;
+  const int tm = first_m + inner % gm;
+  const int tn = inner / gm;
+  const int m0 = tm * BM, n0 = tn * BNO;
+
+  // ---- per-thread global chunk sources (fixed over K).  Chunk i of this
+  // thread is LDS row i*(NT/8) + tid/8, 16-byte column tid%8; since NT/8 is a
+  // multiple of 16 the swizzle of every such row is swz(tid/8).  Sources are
+  // 32-bit chunk offsets into their matrix (-1 marks a row past M or N).
+  constexpr int CW = BN * 8 / NT;  // chunks per thread that come from weights
+  const int crow = tid >> 3, ccol = tid & 7;
+  const int sw_st = ccol ^ swz(crow);
+  int off[CH];
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int row = i * (NT / 8) + crow;
+    if (i < CW) {
+      int wr = n0 + row;
+      if (EPI == EPI_SWIGLU && row >= BN / 2) wr = n0 + row - BN / 2;
+      off[i] = wr < N ? wr * K8 : -1;
+    } else {
+      const int tok = m0 + row - BN;
+      off[i] = tok < M ? tok * K8 : -1;
+    }
+  }
+  const uint4* A4 = reinterpret_cast<const uint4*>(act);
+  const uint4* W0 = reinterpret_cast<const uint4*>(w0);
+  const uint4* W1 = reinterpret_cast<const uint4*>(EPI == EPI_SWIGLU ? w1 : w0);
+
+  uint4 pre[CH];
+  auto load_tile = [&](int kt) {
+    const int kc = kt * 8 + ccol;
+    const bool kin = kc < K8;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const uint4* base = i < CW ? ((EPI == EPI_SWIGLU && i >= CW / 2) ? W1 : W0) : A4;
+      const bool ok = kin && off[i] >= 0;
+      const uint4 v = base[ok ? off[i] + kc : 0];
+      pre[i] = keep_or_zero(ok, v);
+    }
+  };
+  auto store_tile = [&](int stage) {
+    uint4* L0 = lds + stage * ROWS * 8 + crow * 8 + sw_st;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) L0[i * (NT / 8) * 8] = pre[i];
+  };
+
+  // LDS rows read by this lane's fragments; all are congruent to fr mod 16,
+  // so they share the swizzle swz(fr).
+  const int fr = lane & 15, fq = lane >> 4;
+  const int sw_ld = swz(fr);
+  int arow[FN], brow[FM];
+#pragma unroll
+  for (int t = 0; t < FN; ++t) {
+    if (EPI == EPI_SWIGLU) {
+      const int half = t / (FN / 2), tt = t % (FN / 2);
+      arow[t] = half * (BN / 2) + wn * (TN / 2) + tt * 16 + fr;
+    } else {
+      arow[t] = wn * TN + t * 16 + fr;
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < FM; ++t) brow[t] = BN + wm * TM + t * 16 + fr;
+
+  f32x4 acc[FN][FM];
+#pragma unroll
+  for (int a = 0; a < FN; ++a)
+#pragma unroll
+    for (int b = 0; b < FM; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+
+  for (int kt = 0; kt < nkt; ++kt) {
+    const bool more = kt + 1 < nkt;
+    if (more) load_tile(kt + 1);
+    const uint4* L0 = lds + (kt & 1) * ROWS * 8;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int ch = ks * 4 + fq;
+      uint4 af[FN], bfr[FM];
+#pragma unroll
+      for (int t = 0; t < FN; ++t) af[t] = L0[arow[t] * 8 + (ch ^ sw_ld)];
+#pragma unroll
+      for (int t = 0; t < FM; ++t) bfr[t] = L0[brow[t] * 8 + (ch ^ sw_ld)];
+#pragma unroll
+      for (int a = 0; a < FN; ++a)
+#pragma unroll
+        for (int b = 0; b < FM; ++b) acc[a][b] = mfma16(af[a], bfr[b], acc[a][b]);
+    }
+    if (more) store_tile((kt + 1) & 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: lane holds D[4*fq + e][fr] of every (a, b) sub-tile
+  if (EPI == EPI_SWIGLU) {
+#pragma unroll
+    for (int a = 0; a < FN / 2; ++a) {
+      const int col = n0 + wn * (TN / 2) + a * 16 + 4 * fq;
+#pragma unroll
+      for (int b = 0; b < FM; ++b) {
+        const int tok = m0 + wm * TM + b * 16 + fr;
+        if (tok < M && col < N) {
+          const f32x4 gg = acc[a][b], uu = acc[a + FN / 2][b];
+          uint2 o;
+          o.x = pack_bf16x2(silu_mul(gg[0], uu[0]), silu_mul(gg[1], uu[1]));
+          o.y = pack_bf16x2(silu_mul(gg[2], uu[2]), silu_mul(gg[3], uu[3]));
+          *reinterpret_cast<uint2*>(out + (size_t)tok * N + col) = o;
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int a = 0; a < FN; ++a) {
+      const int col = n0 + wn * TN + a * 16 + 4 * fq;
+#pragma unroll
+      for (int b = 0; b < FM; ++b) {
+        const int tok = m0 + wm * TM + b * 16 + fr;
+        if (tok < M && col < N) {
+          const size_t off = (size_t)tok * N + col;
+          f32x4 v = acc[a][b];
+          if (EPI == EPI_RESIDUAL) {
+            const uint2 xr = *reinterpret_cast<const uint2*>(resid + off);
+            v[0] += bf2f(xr.x & 0xFFFFu);
+            v[1] += bf2f(xr.x >> 16);
+            v[2] += bf2f(xr.y & 0xFFFFu);
+            v[3] += bf2f(xr.y >> 16);
+          }
+          uint2 o;
+          o.x = pack_bf16x2(v[0], v[1]);
+          o.y = pack_bf16x2(v[2], v[3]);
+          *reinterpret_cast<uint2*>(out + off) = o;
+        }
+      }
+    }
+  }
+}
+
+// Tile configuration: 256 tokens x 256 weight rows, 8 waves as 2 x 4, each
+// wave 128 tokens x 64 weight rows (32 MFMA tiles, 128 fp32 accumulators).
+constexpr int kBM = 256, kBN = 256, kWM = 2, kWN = 4;
+constexpr int kLdsBytes = 2 * (kBM + kBN) * 128;
+
+template <int EPI>
+static hipError_t launch_cfg(const void* act, const void* w0, const void* w1, const void* resid,
+                             void* out, int M, int N, int K, hipStream_t s) {
+  constexpr int BNO = EPI == EPI_SWIGLU ? kBN / 2 : kBN;
+  const long tiles = (long)((M + kBM - 1) / kBM) * ((N + BNO - 1) / BNO);
+  auto kern = gemm_bf16<kBM, kBN, kWM, kWN, EPI>;
+  // allow more than the default dynamic LDS (per device, so done per launch)
+  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     kLdsBytes);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(kWM * kWN * 64), kLdsBytes, s,
+                     (const uint16_t*)act, (const uint16_t*)w0, (const uint16_t*)w1,
+                     (const uint16_t*)resid, (uint16_t*)out, M, N, K);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_gateup_fused(const void* n, const void* wg, const void* wu, void* h,
+                                    int M, int d, int f, hipStream_t s) {
+  return launch_cfg<EPI_SWIGLU>(n, wg, wu, nullptr, h, M, f, d, s);
+}
+hipError_t launch_gemm_store(const void* a, const void* w, void* c, int M, int N, int K,
+                             hipStream_t s) {
+  return launch_cfg<EPI_STORE>(a, w, nullptr, nullptr, c, M, N, K, s);
+}
+hipError_t launch_gemm_residual(const void* a, const void* w, const void* resid, void* y,
+                                int M, int N, int K, hipStream_t s) {
+  return launch_cfg<EPI_RESIDUAL>(a, w, nullptr, resid, y, M, N, K, s);
+}
+
+// ---- split-variant activation: h = silu(G) * U, 8 bf16 per 16-byte chunk
+__global__ __launch_bounds__(256) void swiglu_bf16(const uint4* __restrict__ G,
+                                                   const uint4* __restrict__ U,
+                                                   uint4* __restrict__ h, int64_t nchunk) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nchunk;
+       i += (int64_t)gridDim.x * 256) {
+    float gg[8], uu[8];
+    unpack8(G[i], gg);
+    unpack8(U[i], uu);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) gg[e] = silu_mul(gg[e], uu[e]);
+    h[i] = pack8(gg);
+  }
+}
+
+hipError_t launch_swiglu_bf16(const void* G, const void* U, void* h, int64_t count,
+                              hipStream_t s) {
+  const int64_t nchunk = count / 8;
+  int64_t blocks = (nchunk + 255) / 256;
+  if (blocks > 256 * 16) blocks = 256 * 16;  // grid-stride beyond 16 workgroups per CU
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(swiglu_bf16, dim3((unsigned)blocks), dim3(256), 0, s, (const uint4*)G,
+                     (const uint4*)U, (uint4*)h, nchunk);
+  return hipGetLastError();
+}
+
+}  // namespace ffn
