@@ -229,7 +229,8 @@ ffn_status ffn_swiglu_block(ffn_dtype dt, const void* x, const void* g, const vo
   void* h = ws + L.h;
   const int Mi = (int)M, di = (int)d, fi = (int)f;
 
-  FFN_LAUNCH("rmsnorm", s, ffn::launch_rmsnorm((int)es, x, g, n, M, d, eps, s));
+  const bool decode = dt == FFN_BF16 && !split && Mi <= ffn::decode_max_tokens();
+  if (!decode) FFN_LAUNCH("rmsnorm", s, ffn::launch_rmsnorm((int)es, x, g, n, M, d, eps, s));
   if (dt == FFN_F32) {
     const float* nf = (const float*)n;
     float* hf = (float*)h;
@@ -246,7 +247,6 @@ ffn_status ffn_swiglu_block(ffn_dtype dt, const void* x, const void* g, const vo
     return ok();
   }
 
-  const bool decode = Mi <= ffn::decode_max_tokens();
   if (split) {
     void* G = ws + L.G;
     void* U = ws + L.U;
@@ -254,11 +254,12 @@ ffn_status ffn_swiglu_block(ffn_dtype dt, const void* x, const void* g, const vo
     FFN_LAUNCH("gemm_up", s, ffn::launch_gemm_store(n, w_up, U, Mi, fi, di, s));
     FFN_LAUNCH("swiglu", s, ffn::launch_swiglu_bf16(G, U, h, (int64_t)M * f, s));
   } else if (decode) {
-    FFN_LAUNCH("decode_gateup", s, ffn::launch_decode_gateup(n, w_gate, w_up, h, Mi, di, fi, s));
+    // the norm is folded into the gate/up kernel: n is never materialised
+    FFN_LAUNCH("decode_gateup", s, ffn::launch_decode_gateup_norm(x, g, w_gate, w_up, h, Mi, di, fi, eps, s));
   } else {
     FFN_LAUNCH("gemm_gateup_fused", s, ffn::launch_gemm_gateup_fused(n, w_gate, w_up, h, Mi, di, fi, s));
   }
-  if (decode) {
+  if (Mi <= ffn::decode_max_tokens()) {
     FFN_LAUNCH("decode_down", s, ffn::launch_decode_down(h, w_down, x, y, Mi, di, fi, s));
   } else {
     FFN_LAUNCH("gemm_down_residual", s, ffn::launch_gemm_residual(h, w_down, x, y, Mi, di, fi, s));

@@ -1,0 +1,279 @@
+// Decode-regime projections (few tokens), weight streaming through LDS on
+// bf16 MFMA, with the RMSNorm folded into the gate/up kernel.
+//
+//   gate/up : h[m,j] = silu(r_m (Wg (x_m * g))_j) * (r_m (Wu (x_m * g))_j),
+//             r_m = 1 / sqrt(sum_k x[m,k]^2 / d + eps)
+//   down    : y[m,i] = x[m,i] + sum_j Wd[i,j] h[m,j]
+// (RMSNorm: "When to hand-write a GPU kernel on Apple Silicon", Rung 2;
+// gate/up of the SwiGLU MLP: "Unfusing a Kernel Made It 1.63x Faster",
+// Finding 1; FFN-down: "Megakernels on Mac", "Projection shape changes the
+// achieved rate"; the FFN weights dominate a decode pass's payload:
+// "Megakernels on Mac", "The 27.65 ms estimate".)
+//
+// The norm folds because W n_m = r_m W (x_m * g): the K loop multiplies
+// the weights with bf16(x * g) and accumulates sum x^2 from the same loads,
+// and the epilogue scales by r_m once the whole row's sum is known (the
+// full-row dependency of the norm, "Megakernels on Mac", "Dependencies and
+// synchronization", is respected: r_m is applied only after every K slice
+// has been reduced).  This removes the separate norm launch and the n round
+// trip.
+//
+// With M <= 64 tokens every weight is used M times, far below the flop:byte
+// ridge, so the kernels are bound by reading W from HBM once.  gfx950 design:
+//  * a workgroup owns 16 weight rows (per matrix); its W waves split K into
+//    contiguous slices of 128-k stages;
+//  * weights are fetched in 256-byte row segments (4 rows x 256 B per wave
+//    instruction), which streams markedly faster on this chip than the
+//    16-rows x 64-B pattern of the MFMA operand layout, then staged in a
+//    per-wave 4 KiB LDS buffer and read back in MFMA layout.  Within a row
+//    the 16-byte chunks are rotated by the row index, so both the stores and
+//    the ds_read_b128 fragment reads are bank-conflict free;
+//  * v_mfma_f32_16x16x32_bf16: A = 16 weight rows x 32 k (from LDS), B = 32 k
+//    x 16 tokens (activations, straight from L2), tokens past M are zero;
+//  * the K loop is software-pipelined over two register batches (the next
+//    stage's loads are in flight while the current one is staged and
+//    multiplied); the prefetch index is clamped at the slice end so every
+//    iteration issues the same loads (uniform wait counts);
+//  * the W partial tiles (and partial sums of squares) are reduced in a fixed
+//    order through LDS: deterministic, no atomics.
+#include "common.h"
+#include "launch.h"
+
+#ifndef FFN_DS_GU_WAVES
+#define FFN_DS_GU_WAVES 4
+#endif
+#ifndef FFN_DS_DN_WAVES
+#define FFN_DS_DN_WAVES 8
+#endif
+
+namespace ffn {
+
+template <int NMAT, int MT, int WAVES, bool FOLD>
+__global__ __launch_bounds__(WAVES * 64) void decode_stream(
+    const uint16_t* __restrict__ act,    // [M, K]: x (FOLD) or h
+    const uint16_t* __restrict__ gain,   // [K] (FOLD)
+    const uint16_t* __restrict__ w0,     // [N, K]
+    const uint16_t* __restrict__ w1,     // [N, K] (NMAT == 2)
+    const uint16_t* __restrict__ resid,  // [M, N] (NMAT == 1)
+    uint16_t* __restrict__ out,          // [M, N]
+    int M, int K, int N, float eps) {
+  constexpr int ST = 16;  // 16-byte chunks per row per stage (128 k)
+  __shared__ uint4 wb[WAVES][NMAT][256];            // per-wave weight stage
+  __shared__ float red[WAVES][MT][NMAT][4][64];     // cross-wave partial tiles
+  __shared__ float ssq[FOLD ? WAVES : 1][MT][16];   // partial sums of squares
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int r = lane & 15, q = lane >> 4;
+  const int j0 = blockIdx.x * 16;
+  const int K8 = K >> 3;
+  const int nst = (K8 + ST - 1) / ST;
+  const int sb = (int)(((long)nst * wave) / WAVES);
+  const int se = (int)(((long)nst * (wave + 1)) / WAVES);
+
+  // staged loads: instruction u fetches rows 4u..4u+3, lane -> (row 4u + q,
+  // chunk (r - (4u + q)) & 15) and lands at LDS slot u*64 + lane, so chunk c
+  // of tile row R sits at slot (R>>2)*64 + (R&3)*16 + ((c + R) & 15)
+  const uint4* gw[NMAT][4];
+  int cst[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int row = min(j0 + 4 * u + q, N - 1);  // rows past N: clamped, never stored
+    cst[u] = (r - (4 * u + q)) & 15;
+    gw[0][u] = reinterpret_cast<const uint4*>(w0) + (size_t)row * K8;
+    if (NMAT == 2) gw[NMAT - 1][u] = reinterpret_cast<const uint4*>(w1) + (size_t)row * K8;
+  }
+  const int rd_base = (r >> 2) * 64 + (r & 3) * 16;
+
+  const uint4* pa[MT];
+  bool av[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    const int tok = t * 16 + r;
+    av[t] = tok < M;
+    pa[t] = reinterpret_cast<const uint4*>(act) + (size_t)min(tok, M - 1) * K8;
+  }
+  const uint4* G4 = reinterpret_cast<const uint4*>(gain);
+
+  f32x4 acc[NMAT][MT];
+  float ss[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    ss[t] = 0.f;
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m) acc[m][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  struct Batch {
+    uint4 w[NMAT][4];
+    uint4 a[4][MT];
+    uint4 g[FOLD ? 4 : 1];
+  };
+  auto load = [&](Batch& B, int st) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int c = min(st * ST + cst[u], K8 - 1);
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m) B.w[m][u] = ld_nt(gw[m][u] + c);
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int c = min(st * ST + 4 * t + q, K8 - 1);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) B.a[t][mt] = pa[mt][c];
+      if (FOLD) B.g[t] = G4[c];
+    }
+  };
+  auto stage_and_compute = [&](const Batch& B, int st) {
+    const bool ragged = (st + 1) * ST > K8;  // only the last stage of a row can be partial
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m) {
+        uint4 v = B.w[m][u];
+        if (ragged) v = keep_or_zero(st * ST + cst[u] < K8, v);
+        wb[wave][m][u * 64 + lane] = v;
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const bool kin = st * ST + 4 * t + q < K8;
+      uint4 bb[MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const uint4 xa = keep_or_zero(av[mt] && kin, B.a[t][mt]);
+        if (FOLD) {
+          float xf[8], gf[8];
+          unpack8(xa, xf);
+          unpack8(B.g[t], gf);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            ss[mt] = __builtin_fmaf(xf[e], xf[e], ss[mt]);
+            xf[e] *= gf[e];
+          }
+          bb[mt] = pack8(xf);
+        } else {
+          bb[mt] = xa;
+        }
+      }
+      const int slot = rd_base + ((4 * t + q + r) & 15);
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m) {
+        const uint4 af = wb[wave][m][slot];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[m][mt] = mfma16(af, bb[mt], acc[m][mt]);
+      }
+    }
+  };
+
+  const int n = se - sb;
+  if (n >= 2) {
+    Batch X, Y;
+    load(X, sb);
+    load(Y, sb + 1);
+    for (int s = sb;;) {
+      __builtin_amdgcn_sched_barrier(0);
+      stage_and_compute(X, s);
+      __builtin_amdgcn_sched_barrier(0);
+      load(X, min(s + 2, se - 1));
+      if (++s >= se) break;
+      __builtin_amdgcn_sched_barrier(0);
+      stage_and_compute(Y, s);
+      __builtin_amdgcn_sched_barrier(0);
+      load(Y, min(s + 2, se - 1));
+      if (++s >= se) break;
+    }
+  } else if (n == 1) {
+    Batch X;
+    load(X, sb);
+    stage_and_compute(X, sb);
+  }
+
+  // ---- fixed-order reduction over the WAVES K slices
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) red[wave][t][m][e][lane] = acc[m][t][e];
+    if (FOLD) {
+      float v = ss[t];
+      v += __shfl_xor(v, 16, 64);
+      v += __shfl_xor(v, 32, 64);
+      if (q == 0) ssq[wave][t][r] = v;
+    }
+  }
+  __syncthreads();
+  for (int t = wave; t < MT; t += WAVES) {
+    const int tok = t * 16 + r;
+    const int col = j0 + 4 * q;  // four consecutive output columns
+    float v0[4], v1[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+      for (int w = 0; w < WAVES; ++w) {
+        s0 += red[w][t][0][e][lane];
+        if (NMAT == 2) s1 += red[w][t][NMAT - 1][e][lane];
+      }
+      v0[e] = s0;
+      v1[e] = s1;
+    }
+    if (tok < M && col < N) {
+      const size_t off = (size_t)tok * N + col;
+      uint2 o;
+      if (NMAT == 2) {
+        float rs = 1.f;
+        if (FOLD) {
+          float sum = 0.f;
+#pragma unroll
+          for (int w = 0; w < WAVES; ++w) sum += ssq[w][t][r];
+          rs = 1.0f / __builtin_sqrtf(sum / (float)K + eps);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v0[e] = silu_mul(v0[e] * rs, v1[e] * rs);
+        o.x = pack_bf16x2(v0[0], v0[1]);
+        o.y = pack_bf16x2(v0[2], v0[3]);
+      } else {
+        const uint2 xr = *reinterpret_cast<const uint2*>(resid + off);
+        o.x = pack_bf16x2(bf2f(xr.x & 0xFFFFu) + v0[0], bf2f(xr.x >> 16) + v0[1]);
+        o.y = pack_bf16x2(bf2f(xr.y & 0xFFFFu) + v0[2], bf2f(xr.y >> 16) + v0[3]);
+      }
+      *reinterpret_cast<uint2*>(out + off) = o;
+    }
+  }
+}
+
+int decode_max_tokens() { return 64; }
+
+template <int NMAT, int WAVES, bool FOLD>
+static hipError_t launch_ds(const void* act, const void* gain, const void* w0, const void* w1,
+                            const void* resid, void* out, int M, int K, int N, float eps,
+                            hipStream_t s) {
+  const dim3 grid((unsigned)((N + 15) / 16)), block(WAVES * 64);
+  const uint16_t* a = (const uint16_t*)act;
+  const uint16_t* gg = (const uint16_t*)gain;
+  const uint16_t* p0 = (const uint16_t*)w0;
+  const uint16_t* p1 = (const uint16_t*)w1;
+  const uint16_t* rr = (const uint16_t*)resid;
+  uint16_t* o = (uint16_t*)out;
+  if (M <= 16)
+    hipLaunchKernelGGL((decode_stream<NMAT, 1, WAVES, FOLD>), grid, block, 0, s, a, gg, p0, p1, rr, o, M, K, N, eps);
+  else if (M <= 32)
+    hipLaunchKernelGGL((decode_stream<NMAT, 2, WAVES, FOLD>), grid, block, 0, s, a, gg, p0, p1, rr, o, M, K, N, eps);
+  else
+    hipLaunchKernelGGL((decode_stream<NMAT, 4, WAVES, FOLD>), grid, block, 0, s, a, gg, p0, p1, rr, o, M, K, N, eps);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_gateup_norm(const void* x, const void* g, const void* wg, const void* wu,
+                                     void* h, int M, int d, int f, float eps, hipStream_t s) {
+  return launch_ds<2, FFN_DS_GU_WAVES, true>(x, g, wg, wu, nullptr, h, M, d, f, eps, s);
+}
+
+hipError_t launch_decode_down(const void* h, const void* wd, const void* x, void* y, int M,
+                              int d, int f, hipStream_t s) {
+  return launch_ds<1, FFN_DS_DN_WAVES, false>(h, nullptr, wd, nullptr, x, y, M, f, d, 0.f, s);
+}
+
+}  // namespace ffn

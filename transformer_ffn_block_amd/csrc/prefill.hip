@@ -82,8 +82,11 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16(
 
   // ---- per-thread global chunk sources (fixed over K).  Chunk i of this
   // thread is LDS row i*(NT/8) + tid/8, 16-byte column tid%8; since NT/8 is a
-  // multiple of 16 the swizzle of every such row is swz(tid/8).  Sources are
-  // 32-bit chunk offsets into their matrix (-1 marks a row past M or N).
+  // multiple of 16 the swizzle of every such row is swz(tid/8).  Rows past M
+  // or N are clamped to the last valid row: they only feed output rows or
+  // columns that are never stored, so they need no zeroing.  Only the ragged
+  // last K tile is masked (in store_tile, after the MFMAs of the previous
+  // tile, so the loads' latency stays hidden behind them).
   constexpr int CW = BN * 8 / NT;  // chunks per thread that come from weights
   const int crow = tid >> 3, ccol = tid & 7;
   const int sw_st = ccol ^ swz(crow);
@@ -94,10 +97,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16(
     if (i < CW) {
       int wr = n0 + row;
       if (EPI == EPI_SWIGLU && row >= BN / 2) wr = n0 + row - BN / 2;
-      off[i] = wr < N ? wr * K8 : -1;
+      off[i] = min(wr, N - 1) * K8;
     } else {
-      const int tok = m0 + row - BN;
-      off[i] = tok < M ? tok * K8 : -1;
+      off[i] = min(m0 + row - BN, M - 1) * K8;
     }
   }
   const uint4* A4 = reinterpret_cast<const uint4*>(act);
@@ -106,18 +108,20 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16(
 
   uint4 pre[CH];
   auto load_tile = [&](int kt) {
-    const int kc = kt * 8 + ccol;
-    const bool kin = kc < K8;
+    const int kc = min(kt * 8 + ccol, K8 - 1);
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       const uint4* base = i < CW ? ((EPI == EPI_SWIGLU && i >= CW / 2) ? W1 : W0) : A4;
-      const bool ok = kin && off[i] >= 0;
-      const uint4 v = base[ok ? off[i] + kc : 0];
-      pre[i] = keep_or_zero(ok, v);
+      pre[i] = base[off[i] + kc];
     }
   };
-  auto store_tile = [&](int stage) {
+  auto store_tile = [&](int stage, int kt) {
     uint4* L0 = lds + stage * ROWS * 8 + crow * 8 + sw_st;
+    if ((kt + 1) * 8 > K8) {  // ragged last K tile: zero the chunks past K
+      const bool kin = kt * 8 + ccol < K8;
+#pragma unroll
+      for (int i = 0; i < CH; ++i) pre[i] = keep_or_zero(kin, pre[i]);
+    }
 #pragma unroll
     for (int i = 0; i < CH; ++i) L0[i * (NT / 8) * 8] = pre[i];
   };
@@ -146,7 +150,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16(
     for (int b = 0; b < FM; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   load_tile(0);
-  store_tile(0);
+  store_tile(0, 0);
   __syncthreads();
 
   for (int kt = 0; kt < nkt; ++kt) {
@@ -166,7 +170,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16(
 #pragma unroll
         for (int b = 0; b < FM; ++b) acc[a][b] = mfma16(af[a], bfr[b], acc[a][b]);
     }
-    if (more) store_tile((kt + 1) & 1);
+    if (more) store_tile((kt + 1) & 1, kt + 1);
     __syncthreads();
   }
 
