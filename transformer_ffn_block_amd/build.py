@@ -35,9 +35,14 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found; libffn.so needs ROCm's hipcc to build")
 
 
+# MFMA results consumed by VALU (per-block scaling) stay in VGPRs instead of
+# round-tripping through AGPRs.
+EXTRA = {"q8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *COMMON, "-I", os.path.join(ROOT, "include"), "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *COMMON, *EXTRA.get(src, []), "-I", os.path.join(ROOT, "include"), "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -40,9 +40,11 @@ hipError_t launch_swiglu_f32(const float* G, const float* U, float* h, int64_t c
                              hipStream_t s);
 
 // Q8_0 weight-streaming projections (bf16 activations, in-register dequant).
+//   gate/up: h = silu(n Wg^T) * (n Wu^T)
+//   down   : y = x + h Wd^T
 hipError_t launch_q8_gateup(const void* n, const int8_t* qg, const uint16_t* sg,
-                            const int8_t* qu, const uint16_t* su, void* h, int M, int d,
-                            int f, hipStream_t s);
+                            const int8_t* qu, const uint16_t* su, void* h, int M, int d, int f,
+                            hipStream_t s);
 hipError_t launch_q8_down(const void* h, const int8_t* qd, const uint16_t* sd, const void* x,
                           void* y, int M, int d, int f, hipStream_t s);
 int q8_max_tokens();

@@ -6,196 +6,283 @@
 //
 //   gate/up : h[m,j] = silu(sum_k Wg[j,k] n[m,k]) * (sum_k Wu[j,k] n[m,k])
 //   down    : y[m,i] = x[m,i] + sum_j Wd[i,j] h[m,j]
+// n = rmsnorm(x) * g comes from the norm kernel: here the VALU is the scarce
+// unit (quant conversion and per-block scaling), so recomputing x * g in
+// every workgroup, as the bf16 decode kernels do, would cost more than the
+// norm launch it saves.
 //
-// gfx950 mapping.  Because a block of 32 quants is exactly one K step of
-// v_mfma_f32_16x16x32_bf16, the scale factors out of the block's dot product:
-//   sum_{k in b} q[j,k] s[j,b] n[m,k] = s[j,b] * sum_{k in b} q[j,k] n[m,k].
-// The quants themselves are exact in bf16 (|q| <= 128 needs 8 significant
-// bits), so the MFMA runs on the raw integers with a zero accumulator and the
-// lane then adds s[j,b] * partial in fp32: the dequantisation adds no
-// rounding at all.  Operands: A = 16 tokens x 32 k (bf16 activations), B =
-// 32 k x 16 weight rows (converted quants); lane l's result is D[4(l/16)+e][l%16]
-// = 4 tokens of weight row l%16, the same row whose quants and scale the
-// lane loaded, so no cross-lane exchange is needed.  Quants are streamed
-// straight into VGPRs (LDS staging of streamed quantised weights lost every
-// pair in "Megakernels on Mac", "Threadgroup staging").
+// gfx950 mapping.  A block of 32 quants is exactly one K step of
+// v_mfma_f32_16x16x32_bf16, so the scale factors out of the block's dot
+// product:  sum_{k in b} q[j,k] s[j,b] a[m,k] = s[j,b] * sum_{k in b} q[j,k] a[m,k].
+// The quants are exact in bf16 (|q| <= 128 needs 8 significant bits), so the
+// MFMA runs on the raw integers with a zero accumulator and the lane adds
+// s[j,b] * partial in fp32: the dequantisation adds no rounding at all.
+// Operands: A = 16 tokens x 32 k (bf16 activations), B = 32 k x 16 weight
+// rows (quants converted to bf16); lane l's result D[4(l/16)+e][l%16] holds 4
+// tokens of weight row l%16, so the lane needs the scales of one row only.
+//
+// Streaming: a workgroup owns 16 weight rows (per matrix); its waves split K
+// into 256-k stages.  Quants are fetched as 256-byte row segments (4 rows x
+// 256 B per wave instruction) into a per-wave 4 KiB LDS stage whose 16-byte
+// chunks are rotated per row so the 8-byte fragment reads are bank-conflict
+// free.  The 8 scales a row needs per stage are fetched by one 16-byte load
+// per lane when rows of scales are 16-byte aligned (K % 256 == 0); otherwise
+// lane (r, q) takes blocks 2q, 2q+1 of row r and hands them to the other lanes
+// of the row with cross-lane permutes.  Scale loads from 16 rows touch 16
+// cache lines each, so their count, not their bytes, is what costs.  The K loop is
+// pipelined over two register batches as in the bf16 decode kernels; partial
+// tiles are reduced across waves in a fixed order.
+// Activation rows past M are clamped copies of row M-1: they only feed
+// output rows that are never stored, so they need no masking.
 #include "common.h"
 #include "launch.h"
 
+#ifndef FFN_Q8_GU_WAVES
+#define FFN_Q8_GU_WAVES 4
+#endif
+#ifndef FFN_Q8_DN_WAVES
+#define FFN_Q8_DN_WAVES 4
+#endif
+
 namespace ffn {
 
-// 8 int8 quants -> 8 bf16 (exact)
-__device__ __forceinline__ uint4 q8x8_to_bf16(uint2 v) {
+// 8 int8 quants (two dwords) -> 8 bf16 (exact)
+__device__ __forceinline__ uint4 q8x8_to_bf16(uint32_t lo, uint32_t hi) {
   float f[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    f[i] = (float)(((int)(v.x << (24 - 8 * i))) >> 24);
-    f[4 + i] = (float)(((int)(v.y << (24 - 8 * i))) >> 24);
+    f[i] = (float)(((int)(lo << (24 - 8 * i))) >> 24);
+    f[4 + i] = (float)(((int)(hi << (24 - 8 * i))) >> 24);
   }
   return pack8(f);
 }
 
-__device__ __forceinline__ float f16bits_to_f32(uint16_t b) {
-  return (float)__builtin_bit_cast(_Float16, b);
+__device__ __forceinline__ float f16bits_to_f32(uint32_t b) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
 }
 
-template <int NMAT, int MT, int WAVES>
-__global__ __launch_bounds__(WAVES * 64) void q8_proj(
-    const uint16_t* __restrict__ act,                      // [M, K] bf16
+
+template <int NMAT, int MT, int WAVES, bool SALIGN>
+__global__ __launch_bounds__(WAVES * 64) void q8_stream(
+    const uint16_t* __restrict__ act,     // [M, K] bf16: n or h
     const int8_t* __restrict__ q0, const uint16_t* __restrict__ s0,  // [N, K], [N, K/32]
     const int8_t* __restrict__ q1, const uint16_t* __restrict__ s1,
-    const uint16_t* __restrict__ resid,                    // [M, N] (NMAT == 1)
-    uint16_t* __restrict__ out,                            // [M, N]
+    const uint16_t* __restrict__ resid,   // [M, N] (NMAT == 1)
+    uint16_t* __restrict__ out,           // [M, N]
     int M, int K, int N) {
-  constexpr int U = 8;  // blocks per unrolled step
+  constexpr int SB = 8;  // 32-quant blocks per stage (256 k, 256 B per row)
+  __shared__ uint4 wb[WAVES][NMAT][256];           // per-wave quant stage (4 KiB per matrix)
+  __shared__ float red[WAVES][MT][NMAT][4][64];
+
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int r = lane & 15, q = lane >> 4;
   const int j0 = blockIdx.x * 16;
-  const int jrow = min(j0 + r, N - 1);
-  const int nb = K >> 5;  // blocks per row
-  const int K8 = K >> 3;
+  const int nb = K >> 5;                // blocks per row
+  const int K16 = K >> 4;               // 16-byte quant chunks per row
+  const int K8 = K >> 3;                // 16-byte activation chunks per row
+  const int nst = (nb + SB - 1) / SB;
+  const int sb = (int)(((long)nst * wave) / WAVES);
+  const int se = (int)(((long)nst * (wave + 1)) / WAVES);
 
-  const uint2* pq0 = reinterpret_cast<const uint2*>(q0 + (size_t)jrow * K);
-  const uint2* pq1 = reinterpret_cast<const uint2*>((NMAT == 2 ? q1 : q0) + (size_t)jrow * K);
-  const uint16_t* ps0 = s0 + (size_t)jrow * nb;
-  const uint16_t* ps1 = (NMAT == 2 ? s1 : s0) + (size_t)jrow * nb;
-  const uint4* pa[MT];
-  bool av[MT];
+  // staged loads: instruction u covers tile rows 4u..4u+3; lane -> row
+  // 4u + q, LDS slot u*64 + lane, which holds chunk (r - (4u + q)) & 15 of the
+  // row's 256-byte stage segment; so chunk c of tile row R sits at slot
+  // (R >> 2)*64 + (R & 3)*16 + ((c + R) & 15)
+  const uint4* gq[NMAT][4];
+  int cst[4];
 #pragma unroll
-  for (int t = 0; t < MT; ++t) {
-    const int tok = t * 16 + r;
-    av[t] = tok < M;
-    pa[t] = reinterpret_cast<const uint4*>(act) + (size_t)min(tok, M - 1) * K8;
+  for (int u = 0; u < 4; ++u) {
+    const int row = min(j0 + 4 * u + q, N - 1);  // rows past N: clamped, never stored
+    cst[u] = (r - (4 * u + q)) & 15;
+    gq[0][u] = reinterpret_cast<const uint4*>(q0 + (size_t)row * K);
+    if (NMAT == 2) gq[NMAT - 1][u] = reinterpret_cast<const uint4*>(q1 + (size_t)row * K);
   }
-  f32x4 acc0[MT], acc1[MT];
+  // this lane's weight row (MFMA B operand) and its scales; lane (r, q)
+  // fetches blocks 2q, 2q+1 of each stage for row r
+  const int jr = min(j0 + r, N - 1);
+  const uint16_t* ps[NMAT];
+  ps[0] = s0 + (size_t)jr * nb;
+  if (NMAT == 2) ps[NMAT - 1] = s1 + (size_t)jr * nb;
+  const int rd_base = (r >> 2) * 64 + (r & 3) * 16;
+
+  const uint4* pa[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t)
+    pa[t] = reinterpret_cast<const uint4*>(act) + (size_t)min(t * 16 + r, M - 1) * K8;
+
+  f32x4 acc[NMAT][MT];
 #pragma unroll
   for (int t = 0; t < MT; ++t) {
-    acc0[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    acc1[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m) acc[m][t] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
 
-  const int bb = (int)(((long)nb * wave) / WAVES);
-  const int be = (int)(((long)nb * (wave + 1)) / WAVES);
-  auto step = [&](int b, uint2 w0v, uint2 w1v, uint16_t s0v, uint16_t s1v, const uint4* av4) {
-    const uint4 B0 = q8x8_to_bf16(w0v);
-    const float sc0 = f16bits_to_f32(s0v);
-    uint4 B1;
-    float sc1 = 0.f;
-    if (NMAT == 2) {
-      B1 = q8x8_to_bf16(w1v);
-      sc1 = f16bits_to_f32(s1v);
-    }
-#pragma unroll
-    for (int t = 0; t < MT; ++t) {
-      const f32x4 p0 = mfma16(av4[t], B0, z4);
-      acc0[t] += sc0 * p0;
-      if (NMAT == 2) {
-        const f32x4 p1 = mfma16(av4[t], B1, z4);
-        acc1[t] += sc1 * p1;
-      }
-    }
-    (void)b;
+  struct Batch {
+    uint4 w[NMAT][4];
+    uint4 s[NMAT];  // SALIGN: the stage's 8 scales of row r; else .x = blocks 2q, 2q+1
+    uint4 a[SB][MT];
   };
-
-  int b = bb;
-  for (; b + U <= be; b += U) {
-    uint2 w0v[U], w1v[U];
-    uint16_t s0v[U], s1v[U];
-    uint4 a[U][MT];
+  auto load = [&](Batch& B, int st) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int c8 = (b + u) * 4 + q;  // 8-byte unit index within the row
-      w0v[u] = ld_nt(pq0 + c8);
-      s0v[u] = ps0[b + u];
-      if (NMAT == 2) {
-        w1v[u] = ld_nt(pq1 + c8);
-        s1v[u] = ps1[b + u];
+    for (int u = 0; u < 4; ++u) {
+      const int c = min(st * 16 + cst[u], K16 - 1);
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m) B.w[m][u] = ld_nt(gq[m][u] + c);
+    }
+    if (SALIGN) {
+      const int c = min(st, (nb >> 3) - 1);
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m) B.s[m] = reinterpret_cast<const uint4*>(ps[m])[c];
+    } else {
+      const int b0 = min(st * SB + 2 * q, nb - 1), b1 = min(st * SB + 2 * q + 1, nb - 1);
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m)
+        B.s[m].x = (uint32_t)ps[m][b0] | ((uint32_t)ps[m][b1] << 16);
+    }
+#pragma unroll
+    for (int b = 0; b < SB; ++b) {
+      const int c = min(st * SB + b, nb - 1) * 4 + q;
+#pragma unroll
+      for (int t = 0; t < MT; ++t) B.a[b][t] = pa[t][c];
+    }
+  };
+  auto stage_and_compute = [&](const Batch& B, int st) {
+    const bool ragged = (st + 1) * SB > nb;  // only a row's last stage can be partial
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m) {
+        uint4 v = B.w[m][u];
+        if (ragged) v = keep_or_zero(st * 16 + cst[u] < K16, v);
+        wb[wave][m][u * 64 + lane] = v;
       }
+    }
+#pragma unroll
+    for (int b = 0; b < SB; ++b) {
+      uint4 aa[MT];
 #pragma unroll
       for (int t = 0; t < MT; ++t) {
-        const uint4 v = pa[t][c8];
-        a[u][t] = keep_or_zero(av[t], v);
+        aa[t] = B.a[b][t];
+        if (ragged) aa[t] = keep_or_zero(st * SB + b < nb, aa[t]);
+      }
+      // quants k = 32b + 8q .. +8 of row r: chunk 2b + q/2 of the stage, half q & 1
+      const int slot = rd_base + ((2 * b + (q >> 1) + r) & 15);
+      const int src_lane = r + 16 * (b >> 1);  // the lane of row r holding block b's scale
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m) {
+        const uint2 qv = reinterpret_cast<const uint2*>(&wb[wave][m][slot])[q & 1];
+        const uint4 Bq = q8x8_to_bf16(qv.x, qv.y);
+        uint32_t pair;
+        if (SALIGN) {
+          pair = (b >> 1) == 0 ? B.s[m].x : (b >> 1) == 1 ? B.s[m].y : (b >> 1) == 2 ? B.s[m].z : B.s[m].w;
+        } else {
+          pair = (uint32_t)__shfl((int)B.s[m].x, src_lane, 64);
+        }
+        const float sc = f16bits_to_f32((b & 1) ? (pair >> 16) : (pair & 0xFFFFu));
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+          const f32x4 p = mfma16(aa[t], Bq, z4);
+          acc[m][t] += sc * p;
+        }
       }
     }
-#pragma unroll
-    for (int u = 0; u < U; ++u) step(b + u, w0v[u], NMAT == 2 ? w1v[u] : w0v[u], s0v[u],
-                                     NMAT == 2 ? s1v[u] : s0v[u], a[u]);
-  }
-  for (; b < be; ++b) {
-    const int c8 = b * 4 + q;
-    uint4 a[MT];
-#pragma unroll
-    for (int t = 0; t < MT; ++t) {
-      const uint4 v = pa[t][c8];
-      a[t] = keep_or_zero(av[t], v);
+  };
+
+  const int n = se - sb;
+  if (n >= 2) {
+    Batch X, Y;
+    load(X, sb);
+    load(Y, sb + 1);
+    for (int s = sb;;) {
+      __builtin_amdgcn_sched_barrier(0);
+      stage_and_compute(X, s);
+      __builtin_amdgcn_sched_barrier(0);
+      load(X, min(s + 2, se - 1));
+      if (++s >= se) break;
+      __builtin_amdgcn_sched_barrier(0);
+      stage_and_compute(Y, s);
+      __builtin_amdgcn_sched_barrier(0);
+      load(Y, min(s + 2, se - 1));
+      if (++s >= se) break;
     }
-    step(b, pq0[c8], pq1[c8], ps0[b], ps1[b], a);
+  } else if (n == 1) {
+    Batch X;
+    load(X, sb);
+    stage_and_compute(X, sb);
   }
 
-  __shared__ float red[WAVES][MT][NMAT][4][64];
+  // ---- fixed-order reduction over the WAVES K slices
 #pragma unroll
-  for (int t = 0; t < MT; ++t) {
+  for (int t = 0; t < MT; ++t)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      red[wave][t][0][e][lane] = acc0[t][e];
-      if (NMAT == 2) red[wave][t][NMAT - 1][e][lane] = acc1[t][e];
-    }
-  }
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) red[wave][t][m][e][lane] = acc[m][t][e];
   __syncthreads();
   for (int t = wave; t < MT; t += WAVES) {
-    const int col = j0 + r;
+    const int col = j0 + r;  // lane's weight row = output column
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
+      const int tok = t * 16 + 4 * q + e;
       float v0 = 0.f, v1 = 0.f;
 #pragma unroll
       for (int w = 0; w < WAVES; ++w) {
         v0 += red[w][t][0][e][lane];
         if (NMAT == 2) v1 += red[w][t][NMAT - 1][e][lane];
       }
-      const int tok = t * 16 + 4 * q + e;
       if (tok < M && col < N) {
         const size_t off = (size_t)tok * N + col;
-        float o;
-        if (NMAT == 2)
-          o = silu_mul(v0, v1);
-        else
-          o = bf2f(resid[off]) + v0;
+        const float o = NMAT == 2 ? silu_mul(v0, v1) : bf2f(resid[off]) + v0;
         out[off] = f2bf(o);
       }
     }
   }
 }
 
-int q8_max_tokens() { return 64; }
+// Tokens per launch; the API walks larger M in chunks of this size (two
+// token tiles keep the kernels free of register spills).
+int q8_max_tokens() { return 32; }
+
+template <int NMAT, int WAVES, bool SALIGN>
+static void launch_q8_mt(const uint16_t* a, const int8_t* q0, const uint16_t* s0,
+                         const int8_t* q1, const uint16_t* s1, const uint16_t* rr, uint16_t* o,
+                         int M, int K, int N, hipStream_t s) {
+  const dim3 grid((unsigned)((N + 15) / 16)), block(WAVES * 64);
+  if (M <= 16)
+    hipLaunchKernelGGL((q8_stream<NMAT, 1, WAVES, SALIGN>), grid, block, 0, s, a, q0, s0, q1, s1, rr, o, M, K, N);
+  else
+    hipLaunchKernelGGL((q8_stream<NMAT, 2, WAVES, SALIGN>), grid, block, 0, s, a, q0, s0, q1, s1, rr, o, M, K, N);
+}
 
 template <int NMAT, int WAVES>
 static hipError_t launch_q8(const void* act, const int8_t* q0, const uint16_t* s0,
                             const int8_t* q1, const uint16_t* s1, const void* resid, void* out,
                             int M, int K, int N, hipStream_t s) {
-  const dim3 grid((unsigned)((N + 15) / 16)), block(WAVES * 64);
   const uint16_t* a = (const uint16_t*)act;
   const uint16_t* rr = (const uint16_t*)resid;
   uint16_t* o = (uint16_t*)out;
-  if (M <= 16)
-    hipLaunchKernelGGL((q8_proj<NMAT, 1, WAVES>), grid, block, 0, s, a, q0, s0, q1, s1, rr, o, M, K, N);
-  else if (M <= 32)
-    hipLaunchKernelGGL((q8_proj<NMAT, 2, WAVES>), grid, block, 0, s, a, q0, s0, q1, s1, rr, o, M, K, N);
+  // 16-byte scale loads need every row of scales (K/16 bytes) and the base
+  // pointers 16-byte aligned
+  const bool salign = K % 256 == 0 && ((uintptr_t)s0 % 16) == 0 &&
+                      (NMAT == 1 || ((uintptr_t)s1 % 16) == 0);
+  if (salign)
+    launch_q8_mt<NMAT, WAVES, true>(a, q0, s0, q1, s1, rr, o, M, K, N, s);
   else
-    hipLaunchKernelGGL((q8_proj<NMAT, 4, WAVES>), grid, block, 0, s, a, q0, s0, q1, s1, rr, o, M, K, N);
+    launch_q8_mt<NMAT, WAVES, false>(a, q0, s0, q1, s1, rr, o, M, K, N, s);
   return hipGetLastError();
 }
 
 hipError_t launch_q8_gateup(const void* n, const int8_t* qg, const uint16_t* sg,
                             const int8_t* qu, const uint16_t* su, void* h, int M, int d, int f,
                             hipStream_t s) {
-  return launch_q8<2, 4>(n, qg, sg, qu, su, nullptr, h, M, d, f, s);
+  return launch_q8<2, FFN_Q8_GU_WAVES>(n, qg, sg, qu, su, nullptr, h, M, d, f, s);
 }
 
 hipError_t launch_q8_down(const void* h, const int8_t* qd, const uint16_t* sd, const void* x,
                           void* y, int M, int d, int f, hipStream_t s) {
-  return launch_q8<1, 8>(h, qd, sd, nullptr, nullptr, x, y, M, f, d, s);
+  return launch_q8<1, FFN_Q8_DN_WAVES>(h, qd, sd, nullptr, nullptr, x, y, M, f, d, s);
 }
 
 }  // namespace ffn
