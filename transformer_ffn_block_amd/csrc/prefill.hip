@@ -19,11 +19,16 @@
 //
 //  * v_mfma_f32_16x16x32_bf16, A operand = 16 weight rows, B operand = 16
 //    tokens; a lane's result is 4 consecutive output columns of one token.
+//    (A 32x32x16 variant of this kernel measured slower in interleaved A/B
+//    runs on gfx950, so the 16x16 shape stays.)
 //  * BK = 64: every LDS row is 128 B = 8 chunks of 16 B; chunk c of row r is
-//    stored at c ^ swz(r), swz(r) = (r & 7) ^ ((r >> 3) & 1), which keeps the
-//    16 lanes of a ds_read_b128 phase on distinct banks.
-//  * two LDS stages; the next K tile is loaded into VGPRs while the MFMAs
-//    consume the current stage; one barrier per K tile.
+//    stored at c ^ (r & 7).  Measured on gfx950 with the LDS bank-conflict
+//    counter: the fragment reads (16 rows x one chunk column) and the tile
+//    writes are then conflict free, a ds_read_b128 takes 4 cycles; adding
+//    row bit 3 to the XOR doubles the read time.
+//  * two LDS stages and a register prefetch two K tiles ahead; the writes of
+//    the next tile into the free stage are interleaved with the MFMAs of the
+//    current one; one barrier per K tile.
 //  * workgroups are dispatched round-robin over the 8 XCDs; tile ids are
 //    remapped so each XCD works on a contiguous range of tiles, grouped 8
 //    token tiles deep, so concurrently running tiles share operands in the
@@ -31,11 +36,13 @@
 #include "common.h"
 #include "launch.h"
 
+#include <type_traits>
+
 namespace ffn {
 
 enum { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_RESIDUAL = 2 };
 
-__device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+__device__ __forceinline__ int swz(int row) { return row & 7; }
 
 template <int BM, int BN, int WM, int WN, int EPI>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16(
@@ -54,7 +61,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16(
   constexpr int CH = ROWS * 8 / NT;                       // 16-byte chunks per thread per stage
   static_assert(ROWS * 8 % NT == 0 && (BN * 8) % NT == 0, "tile/thread mismatch");
   static_assert(TM % 16 == 0 && TN % 16 == 0 && (EPI != EPI_SWIGLU || FN % 2 == 0), "bad wave tile");
-  static_assert((NT / 8) % 16 == 0, "row stride per chunk must keep the swizzle");
+  static_assert((NT / 8) % 8 == 0, "row stride per chunk must keep the swizzle");
   static_assert(EPI != EPI_SWIGLU || (BN / 2) % (NT / 8) == 0, "gate/up rows must split on chunk boundaries");
 
   extern __shared__ uint4 lds[];  // [2][ROWS][8]
@@ -82,7 +89,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16(
 
   // ---- per-thread global chunk sources (fixed over K).  Chunk i of this
   // thread is LDS row i*(NT/8) + tid/8, 16-byte column tid%8; since NT/8 is a
-  // multiple of 16 the swizzle of every such row is swz(tid/8).  Rows past M
+  // multiple of 8 the swizzle of every such row is swz(tid/8).  Rows past M
   // or N are clamped to the last valid row: they only feed output rows or
   // columns that are never stored, so they need no zeroing.  Only the ragged
   // last K tile is masked (in store_tile, after the MFMAs of the previous
@@ -149,30 +156,54 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16(
 #pragma unroll
     for (int b = 0; b < FM; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // Pipeline: LDS stage kt&1 holds tile kt, registers `pre` hold tile kt+1.
+  // Iteration kt: fragment reads of k-step 0, then its MFMAs interleaved with
+  // the LDS writes of tile kt+1 into the other stage (read by everyone in
+  // iteration kt-1, which ended with a barrier), then the global loads of
+  // tile kt+2 (a whole iteration to land), then k-step 1, then one barrier.
+  auto compute_ks = [&](const uint4* L0, int ks, uint4 (&af)[FN], uint4 (&bfr)[FM]) {
+    const int ch = ks * 4 + fq;
+#pragma unroll
+    for (int t = 0; t < FN; ++t) af[t] = L0[arow[t] * 8 + (ch ^ sw_ld)];
+#pragma unroll
+    for (int t = 0; t < FM; ++t) bfr[t] = L0[brow[t] * 8 + (ch ^ sw_ld)];
+  };
+  auto mfmas = [&](const uint4 (&af)[FN], const uint4 (&bfr)[FM]) {
+#pragma unroll
+    for (int a = 0; a < FN; ++a)
+#pragma unroll
+      for (int b = 0; b < FM; ++b) acc[a][b] = mfma16(af[a], bfr[b], acc[a][b]);
+  };
+  auto iter = [&](int kt, auto do_store, auto do_load) {
+    const uint4* L0 = lds + (kt & 1) * ROWS * 8;
+    uint4 af[FN], bfr[FM];
+    compute_ks(L0, 0, af, bfr);
+    if (decltype(do_store)::value) store_tile((kt + 1) & 1, kt + 1);
+    mfmas(af, bfr);
+    if (decltype(do_store)::value) {
+      // 12 fragment reads, then 4 MFMAs per LDS write
+      __builtin_amdgcn_sched_group_barrier(0x100, FN + FM, 0);
+#pragma unroll
+      for (int i = 0; i < CH; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, FN * FM / CH, 0);
+        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+      }
+    }
+    if (decltype(do_load)::value) load_tile(kt + 2);
+    compute_ks(L0, 1, af, bfr);
+    mfmas(af, bfr);
+    __syncthreads();
+  };
+  using T_ = std::integral_constant<bool, true>;
+  using F_ = std::integral_constant<bool, false>;
   load_tile(0);
   store_tile(0, 0);
+  if (nkt > 1) load_tile(1);
   __syncthreads();
-
-  for (int kt = 0; kt < nkt; ++kt) {
-    const bool more = kt + 1 < nkt;
-    if (more) load_tile(kt + 1);
-    const uint4* L0 = lds + (kt & 1) * ROWS * 8;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int ch = ks * 4 + fq;
-      uint4 af[FN], bfr[FM];
-#pragma unroll
-      for (int t = 0; t < FN; ++t) af[t] = L0[arow[t] * 8 + (ch ^ sw_ld)];
-#pragma unroll
-      for (int t = 0; t < FM; ++t) bfr[t] = L0[brow[t] * 8 + (ch ^ sw_ld)];
-#pragma unroll
-      for (int a = 0; a < FN; ++a)
-#pragma unroll
-        for (int b = 0; b < FM; ++b) acc[a][b] = mfma16(af[a], bfr[b], acc[a][b]);
-    }
-    if (more) store_tile((kt + 1) & 1, kt + 1);
-    __syncthreads();
-  }
+  int kt = 0;
+  for (; kt + 2 < nkt; ++kt) iter(kt, T_{}, T_{});
+  if (kt + 1 < nkt) iter(kt++, T_{}, F_{});
+  iter(kt, F_{}, F_{});
 
   // ---- epilogue: lane holds D[4*fq + e][fr] of every (a, b) sub-tile
   if (EPI == EPI_SWIGLU) {
@@ -229,6 +260,7 @@ static hipError_t launch_cfg(const void* act, const void* w0, const void* w1, co
   constexpr int BNO = EPI == EPI_SWIGLU ? kBN / 2 : kBN;
   const long tiles = (long)((M + kBM - 1) / kBM) * ((N + BNO - 1) / BNO);
   auto kern = gemm_bf16<kBM, kBN, kWM, kWN, EPI>;
+  // allow more than the default dynamic LDS (per device, so done per launch)
   // allow more than the default dynamic LDS (per device, so done per launch)
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      kLdsBytes);
