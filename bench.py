@@ -8,23 +8,31 @@ bf16, one whole C-ABI call per step, reported as algorithmic GB/s (weights
 
 The same JSON line also carries:
   roofline      - the dominant kernel (decode gate/up projection) against the
-                  8 TB/s HBM peak, its average duration taken from HIP events
-                  the library records around each of its launches on the
-                  call's stream during the timed steps;
+                  8 TB/s HBM peak; its average duration comes from HIP events
+                  that the library records around each of its launches, on the
+                  call's stream, during a second pass over the same timed
+                  steps (the first pass, which gives `value`, is left
+                  uninstrumented); `traffic` is the counter-measured HBM bytes
+                  of that kernel from the committed profile, when the kernel
+                  source is unchanged since the counters were taken;
   cpu_baseline  - the fp64 oracle on the host (1 BLAS thread) on the same
                   decode workload;
   extra         - the other workloads: prefill block (M=8192, d=4096,
                   f=14336) fused and split gate/up, interleaved call by call,
                   in TFLOP/s; the standalone RMSNorm (16384 x 4096 bf16);
                   the Q8_0 decode block (M=8, d=5120, f=17408); decode at
-                  M=1 and 4; measured HBM read-only and copy ceilings.
+                  M=1 and 4; measured HBM read-only and copy ceilings; torch
+                  matmul at the prefill shapes as vendor-library context.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra] [--no-cpu]
+       python bench.py --profile-run   (decode steps plus one 512 MiB copy, for
+                                        counter runs; prints nothing)
 Progress goes to stderr; stdout gets exactly one JSON line.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -40,6 +48,9 @@ PREFILL = dict(seed=4, M=8192, d=4096, f=14336)
 RMS = dict(seed=2, rows=16384, d=4096)
 Q8 = dict(seed=5, M=8, d=5120, f=17408)
 ROTATE = 4
+COPY_BYTES = 512 << 20
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_gateup_M16_hbm_traffic.txt")
+KERNEL_SOURCE = os.path.join(ROOT, "transformer_ffn_block_amd", "csrc", "decode_stream.hip")
 
 
 def log(*a):
@@ -54,15 +65,17 @@ def to_dev(a, torch):
 
 
 def decode_bytes(M, d, f):
+    """Algorithmic bytes of one decode block call: 3 weight matrices, x, y, g."""
     return 3 * f * d * 2 + 2 * M * d * 2 + d * 2
 
 
 def gateup_bytes(M, d, f):
-    return 2 * f * d * 2 + M * d * 2 + M * f * 2
+    """Algorithmic bytes of the fused norm + gate/up kernel: W_gate, W_up, x, g read; h written."""
+    return 2 * f * d * 2 + M * d * 2 + d * 2 + M * f * 2
 
 
 def time_calls(torch, fn, n):
-    """Average ms per call of fn() over n calls, HIP events on torch's current stream."""
+    """Average ms per call of fn(i) over n calls, HIP events on torch's current stream."""
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     s.record()
@@ -71,6 +84,30 @@ def time_calls(torch, fn, n):
     e.record()
     torch.cuda.synchronize()
     return s.elapsed_time(e) / n
+
+
+def sha256(path):
+    with open(path, "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()
+
+
+def read_traffic():
+    """HBM bytes per launch of the decode gate/up kernel from the committed
+    counter profile, or None when absent or taken on a different source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    with open(TRAFFIC_FILE) as fh:
+        for line in fh:
+            if "=" in line and not line.startswith("#"):
+                k, v = line.split("=", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("source_sha256") != sha256(KERNEL_SOURCE):
+        return None
+    try:
+        return int(float(kv["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(b, target_s=10.0):
@@ -92,6 +129,153 @@ def cpu_baseline(b, target_s=10.0):
                       f"{reps} call(s), {dt:.2f} s per call"}
 
 
+def extras(torch, np, ffn, I, sets, x, g, b, ws, extra):
+    M, d, f = b.M, b.d, b.f
+    # decode at M = 1 and 4 (first rows of the same draw)
+    for m in (1, 4):
+        xm = x[:m].contiguous()
+        ym = torch.empty_like(xm)
+
+        def stepm(i, xm=xm, ym=ym):
+            wg, wu, wd = sets[i % ROTATE]
+            ffn.swiglu_block(xm, g, wg, wu, wd, b.eps, "auto", out=ym, workspace=ws)
+        for i in range(20):
+            stepm(i)
+        msm = time_calls(torch, stepm, 200)
+        extra[f"decode_M{m}"] = {"us": round(msm * 1e3, 2),
+                                 "GBps": round(decode_bytes(m, d, f) / (msm * 1e-3) / 1e9, 1)}
+        log(f"decode M={m}: {msm * 1e3:.2f} us/call")
+    sets.clear()
+    torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------ HBM ceilings
+    nbytes = 4 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    sink = torch.empty(16 * ffn.lib().ffn_probe_read_groups(32), dtype=torch.uint8, device="cuda")
+    best, sweep = 0.0, {}
+    for wpc in (4, 8, 12, 16, 32):
+        for _ in range(2):
+            ffn.probe_read(buf, sink, wpc)
+        t = time_calls(torch, lambda i: ffn.probe_read(buf, sink, wpc), 5)
+        sweep[wpc] = round(nbytes / (t * 1e-3) / 1e9, 1)
+        best = max(best, sweep[wpc])
+    half = nbytes // 2
+    src, dst = buf[:half], buf[half:]
+    ffn.probe_copy(src, dst)
+    tc = time_calls(torch, lambda i: ffn.probe_copy(src, dst), 5)
+    copy_gbs = 2 * half / (tc * 1e-3) / 1e9
+    extra["hbm_read_ceiling_GBps"] = best
+    extra["hbm_read_sweep_waves_per_cu"] = sweep
+    extra["hbm_copy_ceiling_GBps"] = round(copy_gbs, 1)
+    extra["decode_M16_frac_of_read_ceiling"] = round(extra["decode_M16_GBps"] / best, 4)
+    log(f"HBM read ceiling {best:.0f} GB/s {sweep}, copy {copy_gbs:.0f} GB/s")
+    del buf, sink, src, dst
+    torch.cuda.empty_cache()
+
+    # ---------------------------------------------------------------- RMSNorm
+    log("generating rmsnorm inputs", RMS)
+    xr, gr, eps, _ = I.make_rmsnorm(RMS["seed"], RMS["rows"], RMS["d"], "bf16")
+    xs = [to_dev(xr, torch)]
+    xs += [xs[0].clone() for _ in range(ROTATE - 1)]
+    ys = [torch.empty_like(xs[0]) for _ in range(ROTATE)]
+    gd = to_dev(gr, torch)
+    for i in range(8):
+        ffn.rmsnorm(xs[i % ROTATE], gd, eps, out=ys[i % ROTATE])
+    tr = time_calls(torch, lambda i: ffn.rmsnorm(xs[i % ROTATE], gd, eps, out=ys[i % ROTATE]), 40)
+    rbytes = 2 * RMS["rows"] * RMS["d"] * 2 + RMS["d"] * 2
+    rgbs = rbytes / (tr * 1e-3) / 1e9
+    extra["rmsnorm"] = {"us": round(tr * 1e3, 2), "GBps": round(rgbs, 1),
+                        "frac_of_hbm_peak": round(rgbs / HBM_PEAK_GBS, 4),
+                        "frac_of_read_ceiling": round(rgbs / best, 4),
+                        "frac_of_copy_ceiling": round(rgbs / copy_gbs, 4)}
+    log("rmsnorm", extra["rmsnorm"])
+    del xs, ys
+    torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------------- Q8_0
+    log("generating q8 inputs", Q8)
+    q = I.make_q8_block(Q8["seed"], Q8["M"], Q8["d"], Q8["f"])
+    qx, qg = to_dev(q.x, torch), to_dev(q.g, torch)
+
+    def qdev(m):
+        return (torch.from_numpy(m.qs).to("cuda"), torch.from_numpy(m.scales.view(np.int16)).to("cuda"))
+    q0 = [qdev(m) for m in (q.w_gate, q.w_up, q.w_down)]
+    qsets = [q0] + [[(a.clone(), s.clone()) for a, s in q0] for _ in range(ROTATE - 1)]
+    qws = ffn.alloc_workspace(ffn.lib().ffn_swiglu_block_q8_workspace_size(Q8["M"], Q8["d"], Q8["f"]))
+    qy = torch.empty_like(qx)
+
+    def qstep(i):
+        a, bq, c = qsets[i % ROTATE]
+        ffn.swiglu_block_q8(qx, qg, a, bq, c, q.eps, out=qy, workspace=qws)
+    for i in range(20):
+        qstep(i)
+    tq = time_calls(torch, qstep, 200)
+    qbytes = 3 * (Q8["f"] * Q8["d"] + Q8["f"] * Q8["d"] // 32 * 2) + 2 * Q8["M"] * Q8["d"] * 2 + Q8["d"] * 2
+    qgbs = qbytes / (tq * 1e-3) / 1e9
+    extra["q8_decode"] = {"us": round(tq * 1e3, 2), "GBps": round(qgbs, 1),
+                          "frac_of_read_ceiling": round(qgbs / best, 4)}
+    log("q8", extra["q8_decode"])
+    del qsets, q0
+    torch.cuda.empty_cache()
+
+    # ---------------------------------------------------------------- prefill
+    Mp, dp, fp = PREFILL["M"], PREFILL["d"], PREFILL["f"]
+    log("generating prefill inputs", PREFILL)
+    bp = I.make_block(PREFILL["seed"], Mp, dp, fp, "bf16")
+    px, pg = to_dev(bp.x, torch), to_dev(bp.g, torch)
+    pw = [[to_dev(a, torch) for a in (bp.w_gate, bp.w_up, bp.w_down)]]
+    pw.append([t.clone() for t in pw[0]])
+    pws = ffn.alloc_workspace(ffn.workspace_size(ffn.FFN_BF16, Mp, dp, fp, "split"))
+    py = torch.empty_like(px)
+    flops = 6.0 * Mp * dp * fp
+
+    def pstep(i, variant):
+        wg, wu, wd = pw[i % 2]
+        ffn.swiglu_block(px, pg, wg, wu, wd, bp.eps, variant, out=py, workspace=pws)
+    for i in range(4):
+        pstep(i, "fused")
+        pstep(i, "split")
+    tf, ts = [], []
+    for i in range(10):  # interleaved call by call
+        tf.append(time_calls(torch, lambda j: pstep(i, "fused"), 1))
+        ts.append(time_calls(torch, lambda j: pstep(i, "split"), 1))
+    ffn.timing_reset()
+    ffn.timing_enable(True, 256)
+    for i in range(4):
+        pstep(i, "fused")
+        pstep(i, "split")
+    kp = ffn.timing_collect()
+    ffn.timing_enable(False)
+    mf, msp = float(np.median(tf)), float(np.median(ts))
+    extra["prefill"] = {
+        "fused_ms": round(mf, 3), "split_ms": round(msp, 3),
+        "fused_TFLOPs": round(flops / (mf * 1e-3) / 1e12, 1),
+        "split_TFLOPs": round(flops / (msp * 1e-3) / 1e12, 1),
+        "fused_frac_of_bf16_peak": round(flops / (mf * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+        "split_over_fused_time": round(msp / mf, 3),
+        "kernels_avg_ms_event_timed": {k: round(t / n, 4) for k, (n, t) in kp.items()}}
+    gu_ms = kp["gemm_gateup_fused"][1] / kp["gemm_gateup_fused"][0]
+    extra["prefill"]["gateup_fused_kernel_TFLOPs"] = round(4.0 * Mp * dp * fp / (gu_ms * 1e-3) / 1e12, 1)
+    log("prefill", extra["prefill"])
+
+    # vendor-library context at the same shapes (torch matmul -> hipBLASLt)
+    wgu = torch.cat([pw[0][0], pw[0][1]], 0)
+    hx = torch.empty((Mp, fp), dtype=torch.bfloat16, device="cuda").normal_()
+    for _ in range(2):
+        torch.nn.functional.linear(px, wgu)
+        torch.nn.functional.linear(hx, pw[0][2])
+    tgu = time_calls(torch, lambda i: torch.nn.functional.linear(px, wgu), 5)
+    tdn = time_calls(torch, lambda i: torch.nn.functional.linear(hx, pw[0][2]), 5)
+    extra["prefill_torch_matmul_context"] = {
+        "gate_up_concat_ms": round(tgu, 3), "down_ms": round(tdn, 3),
+        "gate_up_TFLOPs": round(4.0 * Mp * dp * fp / (tgu * 1e-3) / 1e12, 1),
+        "down_TFLOPs": round(2.0 * Mp * dp * fp / (tdn * 1e-3) / 1e12, 1)}
+    log("torch matmul context", extra["prefill_torch_matmul_context"])
+    del pw, hx, wgu
+    torch.cuda.empty_cache()
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -99,6 +283,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-extra", action="store_true", help="skip the secondary workloads")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--profile-run", action="store_true",
+                    help="decode steps plus one 512 MiB copy (counter calibration); no output")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the FFN block here is a single-GPU library "
@@ -131,161 +317,39 @@ def main() -> int:
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+    ms = time_calls(torch, step, args.steps)              # the timed region
+    value = decode_bytes(M, d, f) / (ms * 1e-3) / 1e9
+    log(f"decode M={M}: {ms * 1e3:.2f} us/call, {value:.1f} GB/s")
+
+    if args.profile_run:
+        half = COPY_BYTES
+        buf = torch.empty(2 * half, dtype=torch.uint8, device="cuda")
+        buf.fill_(1)
+        ffn.probe_copy(buf[:half], buf[half:])
+        torch.cuda.synchronize()
+        return 0
+
+    # per-kernel durations: the same steps again, each launch bracketed by events
     ffn.timing_reset()
     ffn.timing_enable(True, max_launches=4 * args.steps + 16)
-    ms = time_calls(torch, step, args.steps)
+    ms_instr = time_calls(torch, step, args.steps)
     kt = ffn.timing_collect()
     ffn.timing_enable(False)
-    value = decode_bytes(M, d, f) / (ms * 1e-3) / 1e9
-    log(f"decode M={M}: {ms * 1e3:.2f} us/call, {value:.1f} GB/s; kernels {kt}")
     n_gu, t_gu = kt["decode_gateup"]
     gu_us = t_gu / n_gu * 1e3
     gu_gbs = gateup_bytes(M, d, f) / (gu_us * 1e-6) / 1e9
-    roofline = {"bound": "hbm", "kernel": "decode_gateup", "achieved": round(gu_gbs, 1),
-                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gu_gbs / HBM_PEAK_GBS, 4),
-                "traffic": None, "avg_launch_us": round(gu_us, 2),
-                "bytes_per_launch": gateup_bytes(M, d, f)}
+    roofline = {"bound": "hbm", "kernel": "decode_gateup (fused RMSNorm + gate/up + SwiGLU)",
+                "achieved": round(gu_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": read_traffic(),
+                "avg_launch_us": round(gu_us, 2), "bytes_per_launch": gateup_bytes(M, d, f)}
     kernels = {k: {"launches": n, "avg_us": round(t / n * 1e3, 2)} for k, (n, t) in kt.items()}
-    # uninstrumented pass of the same steps, for the cost of the per-kernel events
-    ms_plain = time_calls(torch, step, args.steps)
-    log(f"decode uninstrumented: {ms_plain * 1e3:.2f} us/call")
+    log(f"kernels {kernels}; instrumented pass {ms_instr * 1e3:.2f} us/call")
 
-    extra = {"decode_M16_uninstrumented_GBps": round(decode_bytes(M, d, f) / (ms_plain * 1e-3) / 1e9, 1),
-             "decode_kernels": kernels}
-
+    extra = {"decode_M16_GBps": round(value, 1), "decode_M16_us": round(ms * 1e3, 2),
+             "decode_kernels_event_timed": kernels,
+             "decode_M16_instrumented_us": round(ms_instr * 1e3, 2)}
     if not args.no_extra:
-        # decode at M = 1 and 4 (first rows of the same draw)
-        for m in (1, 4):
-            xm = x[:m].contiguous()
-            ym = torch.empty_like(xm)
-
-            def stepm(i, xm=xm, ym=ym):
-                wg, wu, wd = sets[i % ROTATE]
-                ffn.swiglu_block(xm, g, wg, wu, wd, b.eps, "auto", out=ym, workspace=ws)
-            for i in range(20):
-                stepm(i)
-            msm = time_calls(torch, stepm, 100)
-            extra[f"decode_M{m}"] = {"us": round(msm * 1e3, 2),
-                                     "GBps": round(decode_bytes(m, d, f) / (msm * 1e-3) / 1e9, 1)}
-            log(f"decode M={m}: {msm * 1e3:.2f} us/call")
-        del sets, w0
-        torch.cuda.empty_cache()
-
-        # ------------------------------------------------------- HBM ceilings
-        nbytes = 4 << 30
-        buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
-        buf.fill_(1)
-        sink = torch.empty(16 * ffn.lib().ffn_probe_read_groups(32), dtype=torch.uint8, device="cuda")
-        best = 0.0
-        sweep = {}
-        for wpc in (4, 8, 16, 32):
-            for _ in range(2):
-                ffn.probe_read(buf, sink, wpc)
-            t = time_calls(torch, lambda i: ffn.probe_read(buf, sink, wpc), 5)
-            sweep[wpc] = round(nbytes / (t * 1e-3) / 1e9, 1)
-            best = max(best, sweep[wpc])
-        half = nbytes // 2
-        src, dst = buf[:half], buf[half:]
-        ffn.probe_copy(src, dst)
-        tc = time_calls(torch, lambda i: ffn.probe_copy(src, dst), 5)
-        copy_gbs = 2 * half / (tc * 1e-3) / 1e9
-        extra["hbm_read_ceiling_GBps"] = best
-        extra["hbm_read_sweep_waves_per_cu"] = sweep
-        extra["hbm_copy_ceiling_GBps"] = round(copy_gbs, 1)
-        log(f"HBM read ceiling {best:.0f} GB/s {sweep}, copy {copy_gbs:.0f} GB/s")
-        del buf, sink, src, dst
-        torch.cuda.empty_cache()
-
-        # ------------------------------------------------------------ RMSNorm
-        log("generating rmsnorm inputs", RMS)
-        xr, gr, eps, _ = I.make_rmsnorm(RMS["seed"], RMS["rows"], RMS["d"], "bf16")
-        xs = [to_dev(xr, torch)]
-        xs += [xs[0].clone() for _ in range(ROTATE - 1)]
-        ys = [torch.empty_like(xs[0]) for _ in range(ROTATE)]
-        gd = to_dev(gr, torch)
-        for i in range(8):
-            ffn.rmsnorm(xs[i % ROTATE], gd, eps, out=ys[i % ROTATE])
-        ffn.timing_reset()
-        ffn.timing_enable(True, 256)
-        tr = time_calls(torch, lambda i: ffn.rmsnorm(xs[i % ROTATE], gd, eps, out=ys[i % ROTATE]), 40)
-        kr = ffn.timing_collect()["rmsnorm"]
-        ffn.timing_enable(False)
-        rbytes = 2 * RMS["rows"] * RMS["d"] * 2 + RMS["d"] * 2
-        extra["rmsnorm"] = {"us": round(tr * 1e3, 2), "GBps": round(rbytes / (tr * 1e-3) / 1e9, 1),
-                            "kernel_avg_us": round(kr[1] / kr[0] * 1e3, 2),
-                            "frac_of_hbm_peak": round(rbytes / (tr * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                            "frac_of_read_ceiling": round(rbytes / (tr * 1e-3) / 1e9 / best, 4)}
-        log("rmsnorm", extra["rmsnorm"])
-        del xs, ys
-        torch.cuda.empty_cache()
-
-        # --------------------------------------------------------------- Q8_0
-        log("generating q8 inputs", Q8)
-        q = I.make_q8_block(Q8["seed"], Q8["M"], Q8["d"], Q8["f"])
-        qx, qg = to_dev(q.x, torch), to_dev(q.g, torch)
-
-        def qdev(m):
-            return (torch.from_numpy(m.qs).to("cuda"), torch.from_numpy(m.scales.view(np.int16)).to("cuda"))
-        q0 = [qdev(m) for m in (q.w_gate, q.w_up, q.w_down)]
-        qsets = [q0] + [[(a.clone(), s.clone()) for a, s in q0] for _ in range(ROTATE - 1)]
-        qws = ffn.alloc_workspace(ffn.lib().ffn_swiglu_block_q8_workspace_size(Q8["M"], Q8["d"], Q8["f"]))
-        qy = torch.empty_like(qx)
-
-        def qstep(i):
-            a, bq, c = qsets[i % ROTATE]
-            ffn.swiglu_block_q8(qx, qg, a, bq, c, q.eps, out=qy, workspace=qws)
-        for i in range(20):
-            qstep(i)
-        ffn.timing_reset()
-        ffn.timing_enable(True, 1024)
-        tq = time_calls(torch, qstep, 100)
-        kq = ffn.timing_collect()
-        ffn.timing_enable(False)
-        qbytes = 3 * (Q8["f"] * Q8["d"] + Q8["f"] * Q8["d"] // 32 * 2) + 2 * Q8["M"] * Q8["d"] * 2 + Q8["d"] * 2
-        extra["q8_decode"] = {"us": round(tq * 1e3, 2), "GBps": round(qbytes / (tq * 1e-3) / 1e9, 1),
-                              "kernels": {k: round(t / n * 1e3, 2) for k, (n, t) in kq.items()}}
-        log("q8", extra["q8_decode"])
-        del qsets, q0
-        torch.cuda.empty_cache()
-
-        # ------------------------------------------------------------ prefill
-        Mp, dp, fp = PREFILL["M"], PREFILL["d"], PREFILL["f"]
-        log("generating prefill inputs", PREFILL)
-        bp = I.make_block(PREFILL["seed"], Mp, dp, fp, "bf16")
-        px, pg = to_dev(bp.x, torch), to_dev(bp.g, torch)
-        pw = [[to_dev(a, torch) for a in (bp.w_gate, bp.w_up, bp.w_down)]]
-        pw.append([t.clone() for t in pw[0]])
-        pws = ffn.alloc_workspace(ffn.workspace_size(ffn.FFN_BF16, Mp, dp, fp, "split"))
-        py = torch.empty_like(px)
-        flops = 6.0 * Mp * dp * fp
-
-        def pstep(i, variant):
-            wg, wu, wd = pw[i % 2]
-            ffn.swiglu_block(px, pg, wg, wu, wd, bp.eps, variant, out=py, workspace=pws)
-        for i in range(3):
-            pstep(i, "fused")
-            pstep(i, "split")
-        ffn.timing_reset()
-        ffn.timing_enable(True, 1024)
-        tf, ts = [], []
-        for i in range(10):  # interleaved call by call
-            tf.append(time_calls(torch, lambda j: pstep(i, "fused"), 1))
-            ts.append(time_calls(torch, lambda j: pstep(i, "split"), 1))
-        kp = ffn.timing_collect()
-        ffn.timing_enable(False)
-        mf, msp = float(np.median(tf)), float(np.median(ts))
-        extra["prefill"] = {
-            "fused_ms": round(mf, 3), "split_ms": round(msp, 3),
-            "fused_TFLOPs": round(flops / (mf * 1e-3) / 1e12, 1),
-            "split_TFLOPs": round(flops / (msp * 1e-3) / 1e12, 1),
-            "fused_frac_of_bf16_peak": round(flops / (mf * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
-            "split_over_fused_time": round(msp / mf, 3),
-            "kernels_avg_ms": {k: round(t / n, 4) for k, (n, t) in kp.items()}}
-        gu_ms = kp["gemm_gateup_fused"][1] / kp["gemm_gateup_fused"][0]
-        extra["prefill"]["gateup_fused_kernel_TFLOPs"] = round(4.0 * Mp * dp * fp / (gu_ms * 1e-3) / 1e12, 1)
-        log("prefill", extra["prefill"])
-        del pw
-        torch.cuda.empty_cache()
+        extras(torch, np, ffn, I, sets, x, g, b, ws, extra)
 
     cpu = None
     if not args.no_cpu:

@@ -105,7 +105,8 @@ size_t ffn_swiglu_block_workspace_size(ffn_dtype dt, int64_t M, int64_t d, int64
  *               FFN_F32 (all fp32).
  *   x [M,d], g [d], w_gate [f,d], w_up [f,d], w_down [d,f], y [M,d]: device
  *               pointers of dtype dt, 16-byte aligned.
- *   d, f      : > 0; multiples of 8 (bf16) or 4 (fp32).
+ *   d, f      : > 0; multiples of 8 (bf16) or 4 (fp32); each weight matrix
+ *               smaller than 2 GiB (32-bit buffer offsets).
  *   variant   : gate/up schedule (see ffn_variant).
  *   workspace : device buffer of at least
  *               ffn_swiglu_block_workspace_size(dt, M, d, f, variant) bytes,
@@ -124,7 +125,7 @@ size_t ffn_swiglu_block_q8_workspace_size(int64_t M, int64_t d, int64_t f);
  *   x [M,d], g [d], y [M,d]: bf16 device pointers, 16-byte aligned.
  *   w_gate, w_up : Q8_0 [f, d]; w_down : Q8_0 [d, f] (host structs holding
  *                  device pointers).
- *   d, f : multiples of 32 (so no block straddles a row).
+ *   d, f : multiples of 32 (so no block straddles a row); f*d < 2^31.
  * Weights are dequantised in registers (q * s, exact in fp32) and never
  * written back; accumulation is fp32.
  * Returns FFN_OK, INVALID_ARGUMENT, UNSUPPORTED, WORKSPACE or LAUNCH. */

@@ -209,6 +209,8 @@ ffn_status ffn_swiglu_block(ffn_dtype dt, const void* x, const void* g, const vo
   if (!aligned(x, 16) || !aligned(g, 16) || !aligned(w_gate, 16) || !aligned(w_up, 16) ||
       !aligned(w_down, 16) || !aligned(y, 16))
     return fail(FFN_ERR_UNSUPPORTED, "tensors must be 16-byte aligned");
+  if ((size_t)f * d * es >= ((size_t)1 << 31))
+    return fail(FFN_ERR_UNSUPPORTED, "weight matrices must be smaller than 2 GiB");
   const bool split = use_split(variant);
   const WsLayout L = ws_layout(es, M, d, f, split);
   if (M > 0 && (!workspace || workspace_bytes < L.total))
@@ -286,6 +288,8 @@ ffn_status ffn_swiglu_block_q8(const void* x, const void* g, const ffn_q8_matrix
   }
   FFN_TRY(check_eps(eps));
   FFN_TRY(check_block_dims(M, d, f, 32));
+  if ((size_t)f * d >= ((size_t)1 << 31))
+    return fail(FFN_ERR_UNSUPPORTED, "weight matrices must be smaller than 2 GiB");
   if (!aligned(x, 16) || !aligned(g, 16) || !aligned(y, 16))
     return fail(FFN_ERR_UNSUPPORTED, "x, g and y must be 16-byte aligned");
   const WsLayout L = ws_layout(2, M, d, f, false);

@@ -32,6 +32,21 @@ __device__ __forceinline__ uint4 keep_or_zero(bool keep, const uint4& v) {
   return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
 }
 
+// Buffer resource over [base, base + bytes) (bytes < 2^31).  A buffer load
+// whose offset is past the range returns zeros without a memory access.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, long bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                           (int)(bytes < 0x7FFFFFFFL ? bytes : 0x7FFFFFFFL),
+                                           0x00020000);
+}
+constexpr unsigned kOutOfRange = 0x80000000u;  // a buffer offset that is never in range
+
+// 16-byte streaming (non-temporal) buffer load at a byte offset
+__device__ __forceinline__ uint4 buf_ld_nt(__amdgpu_buffer_rsrc_t r, unsigned off) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 2);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 __device__ __forceinline__ float bf2f(uint32_t b16) { return __uint_as_float(b16 << 16); }
 
 // fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).

@@ -29,11 +29,13 @@
 //    the 16-byte chunks are rotated by the row index, so both the stores and
 //    the ds_read_b128 fragment reads are bank-conflict free;
 //  * v_mfma_f32_16x16x32_bf16: A = 16 weight rows x 32 k (from LDS), B = 32 k
-//    x 16 tokens (activations, straight from L2), tokens past M are zero;
+//    x 16 tokens (activations, straight from L2); tokens past M repeat token
+//    M-1 and only feed output columns that are never stored;
 //  * the K loop is software-pipelined over two register batches (the next
 //    stage's loads are in flight while the current one is staged and
-//    multiplied); the prefetch index is clamped at the slice end so every
-//    iteration issues the same loads (uniform wait counts);
+//    multiplied); every iteration issues the same loads (uniform wait
+//    counts): past the slice end the weight loads get an out-of-range buffer
+//    offset, which returns zeros without touching memory;
 //  * the W partial tiles (and partial sums of squares) are reduced in a fixed
 //    order through LDS: deterministic, no atomics.
 #include "common.h"
@@ -74,25 +76,24 @@ __global__ __launch_bounds__(WAVES * 64) void decode_stream(
   // staged loads: instruction u fetches rows 4u..4u+3, lane -> (row 4u + q,
   // chunk (r - (4u + q)) & 15) and lands at LDS slot u*64 + lane, so chunk c
   // of tile row R sits at slot (R>>2)*64 + (R&3)*16 + ((c + R) & 15)
-  const uint4* gw[NMAT][4];
+  // weights through buffer resources: 32-bit byte offsets (matrices < 2 GiB)
+  __amdgpu_buffer_rsrc_t rw[NMAT];
+  rw[0] = make_rsrc(w0, (long)N * K * 2);
+  if (NMAT == 2) rw[NMAT - 1] = make_rsrc(w1, (long)N * K * 2);
+  unsigned gw[4];  // byte offset of this lane's row in each instruction
   int cst[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int row = min(j0 + 4 * u + q, N - 1);  // rows past N: clamped, never stored
     cst[u] = (r - (4 * u + q)) & 15;
-    gw[0][u] = reinterpret_cast<const uint4*>(w0) + (size_t)row * K8;
-    if (NMAT == 2) gw[NMAT - 1][u] = reinterpret_cast<const uint4*>(w1) + (size_t)row * K8;
+    gw[u] = (unsigned)row * (unsigned)K * 2u;
   }
   const int rd_base = (r >> 2) * 64 + (r & 3) * 16;
 
   const uint4* pa[MT];
-  bool av[MT];
 #pragma unroll
-  for (int t = 0; t < MT; ++t) {
-    const int tok = t * 16 + r;
-    av[t] = tok < M;
-    pa[t] = reinterpret_cast<const uint4*>(act) + (size_t)min(tok, M - 1) * K8;
-  }
+  for (int t = 0; t < MT; ++t)
+    pa[t] = reinterpret_cast<const uint4*>(act) + (size_t)min(t * 16 + r, M - 1) * K8;
   const uint4* G4 = reinterpret_cast<const uint4*>(gain);
 
   f32x4 acc[NMAT][MT];
@@ -109,12 +110,16 @@ __global__ __launch_bounds__(WAVES * 64) void decode_stream(
     uint4 a[4][MT];
     uint4 g[FOLD ? 4 : 1];
   };
-  auto load = [&](Batch& B, int st) {
+  // st < 0 marks a prefetch past the slice end: the weight loads then read
+  // nothing (out-of-range offset) and the activation loads hit cache
+  auto load = [&](Batch& B, int st_req) {
+    const int st = st_req < 0 ? se - 1 : st_req;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int c = min(st * ST + cst[u], K8 - 1);
+      const unsigned o = st_req < 0 ? kOutOfRange : gw[u] + (unsigned)c * 16u;
 #pragma unroll
-      for (int m = 0; m < NMAT; ++m) B.w[m][u] = ld_nt(gw[m][u] + c);
+      for (int m = 0; m < NMAT; ++m) B.w[m][u] = buf_ld_nt(rw[m], o);
     }
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
@@ -141,7 +146,10 @@ __global__ __launch_bounds__(WAVES * 64) void decode_stream(
       uint4 bb[MT];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const uint4 xa = keep_or_zero(av[mt] && kin, B.a[t][mt]);
+        // tokens past M are clamped copies of row M-1 that only feed output
+        // columns never stored, so only the ragged K tail needs masking
+        uint4 xa = B.a[t][mt];
+        if (ragged) xa = keep_or_zero(kin, xa);
         if (FOLD) {
           float xf[8], gf[8];
           unpack8(xa, xf);
@@ -175,12 +183,12 @@ __global__ __launch_bounds__(WAVES * 64) void decode_stream(
       __builtin_amdgcn_sched_barrier(0);
       stage_and_compute(X, s);
       __builtin_amdgcn_sched_barrier(0);
-      load(X, min(s + 2, se - 1));
+      load(X, s + 2 < se ? s + 2 : -1);
       if (++s >= se) break;
       __builtin_amdgcn_sched_barrier(0);
       stage_and_compute(Y, s);
       __builtin_amdgcn_sched_barrier(0);
-      load(Y, min(s + 2, se - 1));
+      load(Y, s + 2 < se ? s + 2 : -1);
       if (++s >= se) break;
     }
   } else if (n == 1) {

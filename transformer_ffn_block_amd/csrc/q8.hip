@@ -25,7 +25,8 @@
 // into 256-k stages.  Quants are fetched as 256-byte row segments (4 rows x
 // 256 B per wave instruction) into a per-wave 4 KiB LDS stage whose 16-byte
 // chunks are rotated per row so the 8-byte fragment reads are bank-conflict
-// free.  The 8 scales a row needs per stage are fetched by one 16-byte load
+// free; prefetches past a wave's K slice use an out-of-range buffer offset
+// and read nothing.  The 8 scales a row needs per stage are fetched by one 16-byte load
 // per lane when rows of scales are 16-byte aligned (K % 256 == 0); otherwise
 // lane (r, q) takes blocks 2q, 2q+1 of row r and hands them to the other lanes
 // of the row with cross-lane permutes.  Scale loads from 16 rows touch 16
@@ -89,14 +90,16 @@ __global__ __launch_bounds__(WAVES * 64) void q8_stream(
   // 4u + q, LDS slot u*64 + lane, which holds chunk (r - (4u + q)) & 15 of the
   // row's 256-byte stage segment; so chunk c of tile row R sits at slot
   // (R >> 2)*64 + (R & 3)*16 + ((c + R) & 15)
-  const uint4* gq[NMAT][4];
+  __amdgpu_buffer_rsrc_t rq[NMAT];  // quants through buffer resources (< 2 GiB)
+  rq[0] = make_rsrc(q0, (long)N * K);
+  if (NMAT == 2) rq[NMAT - 1] = make_rsrc(q1, (long)N * K);
+  unsigned gq[4];  // byte offset of this lane's quant row in each instruction
   int cst[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int row = min(j0 + 4 * u + q, N - 1);  // rows past N: clamped, never stored
     cst[u] = (r - (4 * u + q)) & 15;
-    gq[0][u] = reinterpret_cast<const uint4*>(q0 + (size_t)row * K);
-    if (NMAT == 2) gq[NMAT - 1][u] = reinterpret_cast<const uint4*>(q1 + (size_t)row * K);
+    gq[u] = (unsigned)row * (unsigned)K;
   }
   // this lane's weight row (MFMA B operand) and its scales; lane (r, q)
   // fetches blocks 2q, 2q+1 of each stage for row r
@@ -124,12 +127,16 @@ __global__ __launch_bounds__(WAVES * 64) void q8_stream(
     uint4 s[NMAT];  // SALIGN: the stage's 8 scales of row r; else .x = blocks 2q, 2q+1
     uint4 a[SB][MT];
   };
-  auto load = [&](Batch& B, int st) {
+  // st < 0 marks a prefetch past the slice end: the quant loads then read
+  // nothing (out-of-range offset) and the small loads hit cache
+  auto load = [&](Batch& B, int st_req) {
+    const int st = st_req < 0 ? se - 1 : st_req;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int c = min(st * 16 + cst[u], K16 - 1);
+      const unsigned o = st_req < 0 ? kOutOfRange : gq[u] + (unsigned)c * 16u;
 #pragma unroll
-      for (int m = 0; m < NMAT; ++m) B.w[m][u] = ld_nt(gq[m][u] + c);
+      for (int m = 0; m < NMAT; ++m) B.w[m][u] = buf_ld_nt(rq[m], o);
     }
     if (SALIGN) {
       const int c = min(st, (nb >> 3) - 1);
@@ -199,12 +206,12 @@ __global__ __launch_bounds__(WAVES * 64) void q8_stream(
       __builtin_amdgcn_sched_barrier(0);
       stage_and_compute(X, s);
       __builtin_amdgcn_sched_barrier(0);
-      load(X, min(s + 2, se - 1));
+      load(X, s + 2 < se ? s + 2 : -1);
       if (++s >= se) break;
       __builtin_amdgcn_sched_barrier(0);
       stage_and_compute(Y, s);
       __builtin_amdgcn_sched_barrier(0);
-      load(Y, min(s + 2, se - 1));
+      load(Y, s + 2 < se ? s + 2 : -1);
       if (++s >= se) break;
     }
   } else if (n == 1) {

@@ -1,0 +1,119 @@
+"""Summaries of rocprofv3 CSV output for the profiles/ folder.
+
+  python -m transformer_ffn_block_amd.profsum stats KERNEL_TRACE_CSV --command "..."
+      per-kernel dispatch count, average / min / max duration (us)
+  python -m transformer_ffn_block_amd.profsum traffic FETCH_CSV WRITE_CSV \\
+        --kernel SUBSTRING --copy-bytes N --source FILE --bytes-per-launch B --command "..."
+      HBM traffic per launch of the matching kernel from FETCH_SIZE and
+      WRITE_SIZE (KiB per dispatch), each scaled by what the same counter
+      reads for the library's plain copy kernel (probe_copy) of known size.
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import hashlib
+import statistics
+import sys
+
+
+def _rows(path):
+    with open(path, newline="") as fh:
+        return list(csv.DictReader(fh))
+
+
+def stats(trace_csv: str, command: str) -> str:
+    per = collections.defaultdict(list)
+    for r in _rows(trace_csv):
+        name = r.get("Kernel_Name") or r.get("Name")
+        dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0
+        per[name].append(dur)
+    out = [f"# rocprofv3 kernel trace summary", f"# command: {command}",
+           "# kernel | dispatches | avg_us | median_us | min_us | max_us"]
+    for name, d in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+        short = name.split("(")[0]
+        out.append(f"{short} | {len(d)} | {statistics.fmean(d):.2f} | {statistics.median(d):.2f} | "
+                   f"{min(d):.2f} | {max(d):.2f}")
+    return "\n".join(out) + "\n"
+
+
+def _counter(path: str, counter: str):
+    per = collections.defaultdict(list)
+    for r in _rows(path):
+        if r["Counter_Name"] == counter:
+            per[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+    return per
+
+
+def _pick(per, sub):
+    hits = [(k, v) for k, v in per.items() if sub in k]
+    if not hits:
+        raise SystemExit(f"no kernel matching {sub!r}")
+    k, v = max(hits, key=lambda kv: len(kv[1]))
+    return k, statistics.fmean(v), len(v)
+
+
+def traffic(fetch_csv, write_csv, kernel, copy_bytes, source, bytes_per_launch, command) -> str:
+    f_per, w_per = _counter(fetch_csv, "FETCH_SIZE"), _counter(write_csv, "WRITE_SIZE")
+    kname, f_kib, nf = _pick(f_per, kernel)
+    _, w_kib, nw = _pick(w_per, kernel)
+    _, cf_kib, _ = _pick(f_per, "probe_copy")
+    _, cw_kib, _ = _pick(w_per, "probe_copy")
+    f_scale = copy_bytes / (cf_kib * 1024.0)  # true bytes per counted byte (reads)
+    w_scale = copy_bytes / (cw_kib * 1024.0)  # (writes)
+    rd = f_kib * 1024.0 * f_scale
+    wr = w_kib * 1024.0 * w_scale
+    with open(source, "rb") as fh:
+        sha = hashlib.sha256(fh.read()).hexdigest()
+    lines = [
+        "# HBM traffic per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE (KiB per dispatch),",
+        "# each scaled by the same counter's reading for probe_copy moving copy_bytes",
+        f"# command (fetch pass): {command.replace('PMC', 'FETCH_SIZE')}",
+        f"# command (write pass): {command.replace('PMC', 'WRITE_SIZE')}",
+        f"kernel = {kname.split('(')[0]}",
+        f"dispatches_fetch = {nf}",
+        f"dispatches_write = {nw}",
+        f"fetch_kib_per_dispatch = {f_kib:.1f}",
+        f"write_kib_per_dispatch = {w_kib:.1f}",
+        f"copy_bytes = {copy_bytes}",
+        f"copy_fetch_kib = {cf_kib:.1f}",
+        f"copy_write_kib = {cw_kib:.1f}",
+        f"fetch_scale = {f_scale:.4f}",
+        f"write_scale = {w_scale:.4f}",
+        f"hbm_read_bytes_per_launch = {rd:.0f}",
+        f"hbm_write_bytes_per_launch = {wr:.0f}",
+        f"hbm_bytes_per_launch = {rd + wr:.0f}",
+        f"algorithmic_bytes_per_launch = {bytes_per_launch}",
+        f"traffic_over_algorithmic = {(rd + wr) / bytes_per_launch:.4f}",
+        f"source = {source.split('/root/repo/')[-1]}",
+        f"source_sha256 = {sha}",
+    ]
+    return "\n".join(lines) + "\n"
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("trace_csv")
+    s.add_argument("--command", required=True)
+    t = sub.add_parser("traffic")
+    t.add_argument("fetch_csv")
+    t.add_argument("write_csv")
+    t.add_argument("--kernel", required=True)
+    t.add_argument("--copy-bytes", type=int, required=True)
+    t.add_argument("--source", required=True)
+    t.add_argument("--bytes-per-launch", type=int, required=True)
+    t.add_argument("--command", required=True)
+    a = ap.parse_args(argv)
+    if a.cmd == "stats":
+        sys.stdout.write(stats(a.trace_csv, a.command))
+    else:
+        sys.stdout.write(traffic(a.fetch_csv, a.write_csv, a.kernel, a.copy_bytes, a.source,
+                                 a.bytes_per_launch, a.command))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
