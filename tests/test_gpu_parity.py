@@ -153,8 +153,9 @@ def test_block_decode_full_size(gpu_lib, decode_inputs, M):
     assert err <= TOL_BF16
 
 
-@pytest.mark.parametrize("M,d,f", [(2, 512, 704), (3, 520, 712), (5, 64, 8), (17, 256, 384),
-                                   (33, 1032, 520), (63, 512, 1024), (64, 264, 136)])
+@pytest.mark.parametrize("M,d,f", [(2, 512, 704), (3, 520, 712), (5, 64, 8), (9, 520, 712),
+                                   (12, 1032, 136), (17, 256, 384), (33, 1032, 520), (63, 512, 1024),
+                                   (64, 264, 136)])
 def test_block_decode_ragged(gpu_lib, M, d, f):
     from transformer_ffn_block_amd import ffn
     _say("block decode ragged", M, d, f)

@@ -255,16 +255,23 @@ ffn_status ffn_swiglu_block(ffn_dtype dt, const void* x, const void* g, const vo
     FFN_LAUNCH("gemm_gate", s, ffn::launch_gemm_store(n, w_gate, G, Mi, fi, di, s));
     FFN_LAUNCH("gemm_up", s, ffn::launch_gemm_store(n, w_up, U, Mi, fi, di, s));
     FFN_LAUNCH("swiglu", s, ffn::launch_swiglu_bf16(G, U, h, (int64_t)M * f, s));
-  } else if (decode) {
-    // the norm is folded into the gate/up kernel: n is never materialised
-    FFN_LAUNCH("decode_gateup", s, ffn::launch_decode_gateup_norm(x, g, w_gate, w_up, h, Mi, di, fi, eps, s));
-  } else {
+  } else if (!decode) {
     FFN_LAUNCH("gemm_gateup_fused", s, ffn::launch_gemm_gateup_fused(n, w_gate, w_up, h, Mi, di, fi, s));
   }
-  if (Mi <= ffn::decode_max_tokens()) {
-    FFN_LAUNCH("decode_down", s, ffn::launch_decode_down(h, w_down, x, y, Mi, di, fi, s));
-  } else {
+  if (Mi > ffn::decode_max_tokens()) {
     FFN_LAUNCH("gemm_down_residual", s, ffn::launch_gemm_residual(h, w_down, x, y, Mi, di, fi, s));
+    return ok();
+  }
+  // decode regime: launches of at most decode_chunk_tokens() tokens; the norm
+  // is folded into the gate/up kernel, so n is never materialised
+  const int step = ffn::decode_chunk_tokens();
+  for (int m0 = 0; m0 < Mi; m0 += step) {
+    const int mc = Mi - m0 < step ? Mi - m0 : step;
+    const char* xc = (const char*)x + (size_t)m0 * d * es;
+    char* hc = (char*)h + (size_t)m0 * f * es;
+    if (decode)
+      FFN_LAUNCH("decode_gateup", s, ffn::launch_decode_gateup_norm(xc, g, w_gate, w_up, hc, mc, di, fi, eps, s));
+    FFN_LAUNCH("decode_down", s, ffn::launch_decode_down(hc, w_down, xc, (char*)y + (size_t)m0 * d * es, mc, di, fi, s));
   }
   return ok();
 }

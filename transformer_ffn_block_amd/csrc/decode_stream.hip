@@ -28,9 +28,13 @@
 //    per-wave 4 KiB LDS buffer and read back in MFMA layout.  Within a row
 //    the 16-byte chunks are rotated by the row index, so both the stores and
 //    the ds_read_b128 fragment reads are bank-conflict free;
-//  * v_mfma_f32_16x16x32_bf16: A = 16 weight rows x 32 k (from LDS), B = 32 k
-//    x 16 tokens (activations, straight from L2); tokens past M repeat token
-//    M-1 and only feed output columns that are never stored;
+//  * the activation stage (16 tokens x 128 k) is fetched and staged the same
+//    way (tokens in place of rows): fetching it in the MFMA operand layout
+//    (16 tokens x 64 B per instruction) cost about 11 us of a 58 us decode
+//    call at 16 tokens; tokens past M repeat token M-1 and only feed output
+//    columns that are never stored;
+//  * v_mfma_f32_16x16x32_bf16: A = 16 weight rows x 32 k, B = 32 k x 16
+//    tokens, both read from the LDS stages;
 //  * the K loop is software-pipelined over two register batches (the next
 //    stage's loads are in flight while the current one is staged and
 //    multiplied); every iteration issues the same loads (uniform wait
@@ -48,10 +52,19 @@
 #define FFN_DS_DN_WAVES 8
 #endif
 
+#ifndef FFN_STREAM_WPE
+#define FFN_STREAM_ATTR
+#else
+#define FFN_STREAM_ATTR __attribute__((amdgpu_waves_per_eu(FFN_STREAM_WPE)))
+#endif
+
 namespace ffn {
 
-template <int NMAT, int MT, int WAVES, bool FOLD>
-__global__ __launch_bounds__(WAVES * 64) void decode_stream(
+// ASTAGE: activations fetched in 256-byte token segments and staged through
+// LDS (pays off from about 8 tokens); otherwise read straight from L2 in the
+// MFMA operand layout (for one token every lane reads the same 64 bytes).
+template <int NMAT, int MT, int WAVES, bool FOLD, bool ASTAGE>
+__global__ __launch_bounds__(WAVES * 64) FFN_STREAM_ATTR void decode_stream(
     const uint16_t* __restrict__ act,    // [M, K]: x (FOLD) or h
     const uint16_t* __restrict__ gain,   // [K] (FOLD)
     const uint16_t* __restrict__ w0,     // [N, K]
@@ -61,6 +74,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_stream(
     int M, int K, int N, float eps) {
   constexpr int ST = 16;  // 16-byte chunks per row per stage (128 k)
   __shared__ uint4 wb[WAVES][NMAT][256];            // per-wave weight stage
+  __shared__ uint4 ab[WAVES][ASTAGE ? MT : 1][ASTAGE ? 256 : 1];  // per-wave activation stage
   __shared__ float red[WAVES][MT][NMAT][4][64];     // cross-wave partial tiles
   __shared__ float ssq[FOLD ? WAVES : 1][MT][16];   // partial sums of squares
 
@@ -90,10 +104,17 @@ __global__ __launch_bounds__(WAVES * 64) void decode_stream(
   }
   const int rd_base = (r >> 2) * 64 + (r & 3) * 16;
 
-  const uint4* pa[MT];
+  // activations are staged the same way: tile "row" = token, instruction u
+  // fetches tokens 4u..4u+3 of each 16-token tile (tokens past M are clamped
+  // copies of row M-1 that only feed output columns never stored)
+  const uint4* pa[MT][4];
 #pragma unroll
   for (int t = 0; t < MT; ++t)
-    pa[t] = reinterpret_cast<const uint4*>(act) + (size_t)min(t * 16 + r, M - 1) * K8;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int tok = ASTAGE ? t * 16 + 4 * u + q : t * 16 + r;
+      pa[t][u] = reinterpret_cast<const uint4*>(act) + (size_t)min(tok, M - 1) * K8;
+    }
   const uint4* G4 = reinterpret_cast<const uint4*>(gain);
 
   f32x4 acc[NMAT][MT];
@@ -107,12 +128,12 @@ __global__ __launch_bounds__(WAVES * 64) void decode_stream(
 
   struct Batch {
     uint4 w[NMAT][4];
-    uint4 a[4][MT];
+    uint4 a[MT][4];
     uint4 g[FOLD ? 4 : 1];
   };
   // st < 0 marks a prefetch past the slice end: the weight loads then read
   // nothing (out-of-range offset) and the activation loads hit cache
-  auto load = [&](Batch& B, int st_req) {
+  auto load_w = [&](Batch& B, int st_req) {
     const int st = st_req < 0 ? se - 1 : st_req;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -121,15 +142,28 @@ __global__ __launch_bounds__(WAVES * 64) void decode_stream(
 #pragma unroll
       for (int m = 0; m < NMAT; ++m) B.w[m][u] = buf_ld_nt(rw[m], o);
     }
+  };
+  auto load_a = [&](Batch& B, int st_req) {
+    const int st = st_req < 0 ? se - 1 : st_req;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int c = min(st * ST + 4 * t + q, K8 - 1);
+    for (int u = 0; u < 4; ++u) {
+      // staged: chunk cst[u] of token 4u+q; direct: chunk 4u+q of token r
+      const int c = min(st * ST + (ASTAGE ? cst[u] : 4 * u + q), K8 - 1);
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) B.a[t][mt] = pa[mt][c];
-      if (FOLD) B.g[t] = G4[c];
+      for (int mt = 0; mt < MT; ++mt) B.a[mt][u] = pa[mt][u][c];
+    }
+    if (FOLD) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) B.g[t] = G4[min(st * ST + 4 * t + q, K8 - 1)];
     }
   };
-  auto stage_and_compute = [&](const Batch& B, int st) {
+  auto load = [&](Batch& B, int st_req) {
+    load_w(B, st_req);
+    load_a(B, st_req);
+  };
+  // the weights of a stage go to LDS first, which frees their registers for
+  // the next prefetch before the MFMAs of this stage run
+  auto stage = [&](const Batch& B, int st) {
     const bool ragged = (st + 1) * ST > K8;  // only the last stage of a row can be partial
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -139,17 +173,31 @@ __global__ __launch_bounds__(WAVES * 64) void decode_stream(
         if (ragged) v = keep_or_zero(st * ST + cst[u] < K8, v);
         wb[wave][m][u * 64 + lane] = v;
       }
+      if (ASTAGE) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          uint4 v = B.a[mt][u];
+          if (ragged) v = keep_or_zero(st * ST + cst[u] < K8, v);
+          ab[wave][ASTAGE ? mt : 0][ASTAGE ? u * 64 + lane : 0] = v;
+        }
+      }
     }
+  };
+  auto compute = [&](const Batch& B, int st) {
+    const bool ragged = (st + 1) * ST > K8;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const bool kin = st * ST + 4 * t + q < K8;
+      const int slot = rd_base + ((4 * t + q + r) & 15);
       uint4 bb[MT];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        // tokens past M are clamped copies of row M-1 that only feed output
-        // columns never stored, so only the ragged K tail needs masking
-        uint4 xa = B.a[t][mt];
-        if (ragged) xa = keep_or_zero(kin, xa);
+        uint4 xa;
+        if (ASTAGE) {
+          xa = ab[wave][ASTAGE ? mt : 0][ASTAGE ? slot : 0];  // chunks past K zeroed when staged
+        } else {
+          xa = B.a[mt][t];
+          if (ragged) xa = keep_or_zero(st * ST + 4 * t + q < K8, xa);
+        }
         if (FOLD) {
           float xf[8], gf[8];
           unpack8(xa, xf);
@@ -164,7 +212,6 @@ __global__ __launch_bounds__(WAVES * 64) void decode_stream(
           bb[mt] = xa;
         }
       }
-      const int slot = rd_base + ((4 * t + q + r) & 15);
 #pragma unroll
       for (int m = 0; m < NMAT; ++m) {
         const uint4 af = wb[wave][m][slot];
@@ -181,20 +228,29 @@ __global__ __launch_bounds__(WAVES * 64) void decode_stream(
     load(Y, sb + 1);
     for (int s = sb;;) {
       __builtin_amdgcn_sched_barrier(0);
-      stage_and_compute(X, s);
+      stage(X, s);
       __builtin_amdgcn_sched_barrier(0);
-      load(X, s + 2 < se ? s + 2 : -1);
+      load_w(X, s + 2 < se ? s + 2 : -1);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(X, s);
+      __builtin_amdgcn_sched_barrier(0);
+      load_a(X, s + 2 < se ? s + 2 : -1);
       if (++s >= se) break;
       __builtin_amdgcn_sched_barrier(0);
-      stage_and_compute(Y, s);
+      stage(Y, s);
       __builtin_amdgcn_sched_barrier(0);
-      load(Y, s + 2 < se ? s + 2 : -1);
+      load_w(Y, s + 2 < se ? s + 2 : -1);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(Y, s);
+      __builtin_amdgcn_sched_barrier(0);
+      load_a(Y, s + 2 < se ? s + 2 : -1);
       if (++s >= se) break;
     }
   } else if (n == 1) {
     Batch X;
     load(X, sb);
-    stage_and_compute(X, sb);
+    stage(X, sb);
+    compute(X, sb);
   }
 
   // ---- fixed-order reduction over the WAVES K slices
@@ -252,6 +308,9 @@ __global__ __launch_bounds__(WAVES * 64) void decode_stream(
   }
 }
 
+// Tokens per launch (two 16-token tiles keep the LDS stages within budget);
+// the API walks larger decode batches in chunks of this size.
+int decode_chunk_tokens() { return 32; }
 int decode_max_tokens() { return 64; }
 
 template <int NMAT, int WAVES, bool FOLD>
@@ -265,12 +324,12 @@ static hipError_t launch_ds(const void* act, const void* gain, const void* w0, c
   const uint16_t* p1 = (const uint16_t*)w1;
   const uint16_t* rr = (const uint16_t*)resid;
   uint16_t* o = (uint16_t*)out;
-  if (M <= 16)
-    hipLaunchKernelGGL((decode_stream<NMAT, 1, WAVES, FOLD>), grid, block, 0, s, a, gg, p0, p1, rr, o, M, K, N, eps);
-  else if (M <= 32)
-    hipLaunchKernelGGL((decode_stream<NMAT, 2, WAVES, FOLD>), grid, block, 0, s, a, gg, p0, p1, rr, o, M, K, N, eps);
+  if (M <= 8)
+    hipLaunchKernelGGL((decode_stream<NMAT, 1, WAVES, FOLD, false>), grid, block, 0, s, a, gg, p0, p1, rr, o, M, K, N, eps);
+  else if (M <= 16)
+    hipLaunchKernelGGL((decode_stream<NMAT, 1, WAVES, FOLD, true>), grid, block, 0, s, a, gg, p0, p1, rr, o, M, K, N, eps);
   else
-    hipLaunchKernelGGL((decode_stream<NMAT, 4, WAVES, FOLD>), grid, block, 0, s, a, gg, p0, p1, rr, o, M, K, N, eps);
+    hipLaunchKernelGGL((decode_stream<NMAT, 2, WAVES, FOLD, true>), grid, block, 0, s, a, gg, p0, p1, rr, o, M, K, N, eps);
   return hipGetLastError();
 }
 

@@ -15,7 +15,8 @@ hipError_t launch_rmsnorm(int elem_bytes, const void* x, const void* g, void* y,
 // Decode (few tokens) weight-streaming projections on bf16 MFMA.
 //   gate/up: h[M,f] = silu(n Wg^T) * (n Wu^T) with n = rmsnorm(x) * g folded in
 //   down   : y[M,d] = x + h Wd^T
-int decode_max_tokens();
+int decode_max_tokens();    // largest M routed to the decode kernels
+int decode_chunk_tokens();  // tokens per decode launch
 hipError_t launch_decode_gateup_norm(const void* x, const void* g, const void* wg, const void* wu,
                                      void* h, int M, int d, int f, float eps, hipStream_t s);
 hipError_t launch_decode_down(const void* h, const void* wd, const void* x, void* y,

@@ -45,6 +45,12 @@
 #define FFN_Q8_DN_WAVES 4
 #endif
 
+#ifndef FFN_STREAM_WPE
+#define FFN_STREAM_ATTR
+#else
+#define FFN_STREAM_ATTR __attribute__((amdgpu_waves_per_eu(FFN_STREAM_WPE)))
+#endif
+
 namespace ffn {
 
 // 8 int8 quants (two dwords) -> 8 bf16 (exact)
@@ -64,7 +70,7 @@ __device__ __forceinline__ float f16bits_to_f32(uint32_t b) {
 
 
 template <int NMAT, int MT, int WAVES, bool SALIGN>
-__global__ __launch_bounds__(WAVES * 64) void q8_stream(
+__global__ __launch_bounds__(WAVES * 64) FFN_STREAM_ATTR void q8_stream(
     const uint16_t* __restrict__ act,     // [M, K] bf16: n or h
     const int8_t* __restrict__ q0, const uint16_t* __restrict__ s0,  // [N, K], [N, K/32]
     const int8_t* __restrict__ q1, const uint16_t* __restrict__ s1,
