@@ -69,7 +69,10 @@ __device__ __forceinline__ float f16bits_to_f32(uint32_t b) {
 }
 
 
-template <int NMAT, int MT, int WAVES, bool SALIGN>
+// ASTAGE: 0 = activations read straight from L2 in the MFMA operand layout;
+// 8 = 8 token rows, 16 = 16 token rows fetched as 512-byte token segments and
+// staged through LDS (fewer, fuller cache-line requests).
+template <int NMAT, int MT, int WAVES, bool SALIGN, int ASTAGE>
 __global__ __launch_bounds__(WAVES * 64) FFN_STREAM_ATTR void q8_stream(
     const uint16_t* __restrict__ act,     // [M, K] bf16: n or h
     const int8_t* __restrict__ q0, const uint16_t* __restrict__ s0,  // [N, K], [N, K/32]
@@ -80,6 +83,7 @@ __global__ __launch_bounds__(WAVES * 64) FFN_STREAM_ATTR void q8_stream(
   constexpr int SB = 8;  // 32-quant blocks per stage (256 k, 256 B per row)
   __shared__ uint4 wb[WAVES][NMAT][256];           // per-wave quant stage (4 KiB per matrix)
   __shared__ float red[WAVES][MT][NMAT][4][64];
+  __shared__ uint4 abuf[WAVES][ASTAGE ? ASTAGE * 32 : 1];  // per-wave activation stage [rows][32]
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -115,10 +119,20 @@ __global__ __launch_bounds__(WAVES * 64) FFN_STREAM_ATTR void q8_stream(
   if (NMAT == 2) ps[NMAT - 1] = s1 + (size_t)jr * nb;
   const int rd_base = (r >> 2) * 64 + (r & 3) * 16;
 
-  const uint4* pa[MT];
+  // direct activations: token t*16 + r; staged: instruction v covers token
+  // rows 2v, 2v+1 (lane -> row 2v + lane/32, LDS slot v*64 + lane holding
+  // chunk ((lane & 31) - row) & 31 of the row's 512-byte stage segment)
+  constexpr int NA = ASTAGE ? ASTAGE / 2 : SB * MT;  // activation loads per batch
+  const uint4* pa[ASTAGE ? NA : MT];
+  if (ASTAGE) {
 #pragma unroll
-  for (int t = 0; t < MT; ++t)
-    pa[t] = reinterpret_cast<const uint4*>(act) + (size_t)min(t * 16 + r, M - 1) * K8;
+    for (int v = 0; v < NA; ++v)
+      pa[v] = reinterpret_cast<const uint4*>(act) + (size_t)min(2 * v + (lane >> 5), M - 1) * K8;
+  } else {
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+      pa[t] = reinterpret_cast<const uint4*>(act) + (size_t)min(t * 16 + r, M - 1) * K8;
+  }
 
   f32x4 acc[NMAT][MT];
 #pragma unroll
@@ -131,7 +145,7 @@ __global__ __launch_bounds__(WAVES * 64) FFN_STREAM_ATTR void q8_stream(
   struct Batch {
     uint4 w[NMAT][4];
     uint4 s[NMAT];  // SALIGN: the stage's 8 scales of row r; else .x = blocks 2q, 2q+1
-    uint4 a[SB][MT];
+    uint4 a[NA];
   };
   // st < 0 marks a prefetch past the slice end: the quant loads then read
   // nothing (out-of-range offset) and the small loads hit cache
@@ -154,11 +168,20 @@ __global__ __launch_bounds__(WAVES * 64) FFN_STREAM_ATTR void q8_stream(
       for (int m = 0; m < NMAT; ++m)
         B.s[m].x = (uint32_t)ps[m][b0] | ((uint32_t)ps[m][b1] << 16);
     }
+    if (ASTAGE) {
 #pragma unroll
-    for (int b = 0; b < SB; ++b) {
-      const int c = min(st * SB + b, nb - 1) * 4 + q;
+      for (int v = 0; v < NA; ++v) {
+        // row 2v + (lane>>5): chunk (lane&31 - row) & 31 of its stage segment
+        const int c = ((lane & 31) - (2 * v + (lane >> 5))) & 31;
+        B.a[v] = pa[v][min(st * 32 + c, K8 - 1)];
+      }
+    } else {
 #pragma unroll
-      for (int t = 0; t < MT; ++t) B.a[b][t] = pa[t][c];
+      for (int b = 0; b < SB; ++b) {
+        const int c = min(st * SB + b, nb - 1) * 4 + q;
+#pragma unroll
+        for (int t = 0; t < MT; ++t) B.a[b * MT + t] = pa[t][c];
+      }
     }
   };
   auto stage_and_compute = [&](const Batch& B, int st) {
@@ -172,34 +195,64 @@ __global__ __launch_bounds__(WAVES * 64) FFN_STREAM_ATTR void q8_stream(
         wb[wave][m][u * 64 + lane] = v;
       }
     }
+    if (ASTAGE) {
 #pragma unroll
-    for (int b = 0; b < SB; ++b) {
-      uint4 aa[MT];
-#pragma unroll
-      for (int t = 0; t < MT; ++t) {
-        aa[t] = B.a[b][t];
-        if (ragged) aa[t] = keep_or_zero(st * SB + b < nb, aa[t]);
-      }
-      // quants k = 32b + 8q .. +8 of row r: chunk 2b + q/2 of the stage, half q & 1
-      const int slot = rd_base + ((2 * b + (q >> 1) + r) & 15);
-      const int src_lane = r + 16 * (b >> 1);  // the lane of row r holding block b's scale
-#pragma unroll
-      for (int m = 0; m < NMAT; ++m) {
-        const uint2 qv = reinterpret_cast<const uint2*>(&wb[wave][m][slot])[q & 1];
-        const uint4 Bq = q8x8_to_bf16(qv.x, qv.y);
-        uint32_t pair;
-        if (SALIGN) {
-          pair = (b >> 1) == 0 ? B.s[m].x : (b >> 1) == 1 ? B.s[m].y : (b >> 1) == 2 ? B.s[m].z : B.s[m].w;
-        } else {
-          pair = (uint32_t)__shfl((int)B.s[m].x, src_lane, 64);
+      for (int v = 0; v < NA; ++v) {
+        uint4 a = B.a[v];
+        if (ragged) {
+          const int c = ((lane & 31) - (2 * v + (lane >> 5))) & 31;
+          a = keep_or_zero(st * 32 + c < K8, a);
         }
-        const float sc = f16bits_to_f32((b & 1) ? (pair >> 16) : (pair & 0xFFFFu));
+        abuf[wave][ASTAGE ? v * 64 + lane : 0] = a;
+      }
+    }
+    // per block: the MFMAs of a group of blocks first, then their scale FMAs,
+    // so the FMAs do not wait on each MFMA in turn
+    constexpr int GB = 4;
+#pragma unroll
+    for (int b0 = 0; b0 < SB; b0 += GB) {
+      f32x4 p[GB][NMAT][MT];
+      float scv[GB][NMAT];
+#pragma unroll
+      for (int bb = 0; bb < GB; ++bb) {
+        const int b = b0 + bb;
+        uint4 aa[MT];
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
-          const f32x4 p = mfma16(aa[t], Bq, z4);
-          acc[m][t] += sc * p;
+          if (ASTAGE) {
+            // token r, chunk 4b + q of the stage; with 8 staged rows, lanes of
+            // rows 8..15 re-read rows 0..7 (those outputs are never stored)
+            const int ar = r & (ASTAGE ? ASTAGE - 1 : 0);
+            aa[t] = abuf[wave][ASTAGE ? ar * 32 + ((4 * b + q + ar) & 31) : 0];
+          } else {
+            aa[t] = B.a[b * MT + t];
+            if (ragged) aa[t] = keep_or_zero(st * SB + b < nb, aa[t]);
+          }
+        }
+        // quants k = 32b + 8q .. +8 of row r: chunk 2b + q/2 of the stage, half q & 1
+        const int slot = rd_base + ((2 * b + (q >> 1) + r) & 15);
+        const int src_lane = r + 16 * (b >> 1);  // the lane of row r holding block b's scale
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m) {
+          const uint2 qv = reinterpret_cast<const uint2*>(&wb[wave][m][slot])[q & 1];
+          const uint4 Bq = q8x8_to_bf16(qv.x, qv.y);
+          uint32_t pair;
+          if (SALIGN) {
+            pair = (b >> 1) == 0 ? B.s[m].x : (b >> 1) == 1 ? B.s[m].y : (b >> 1) == 2 ? B.s[m].z : B.s[m].w;
+          } else {
+            pair = (uint32_t)__shfl((int)B.s[m].x, src_lane, 64);
+          }
+          scv[bb][m] = f16bits_to_f32((b & 1) ? (pair >> 16) : (pair & 0xFFFFu));
+#pragma unroll
+          for (int t = 0; t < MT; ++t) p[bb][m][t] = mfma16(aa[t], Bq, z4);
         }
       }
+#pragma unroll
+      for (int bb = 0; bb < GB; ++bb)
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+          for (int t = 0; t < MT; ++t) acc[m][t] += scv[bb][m] * p[bb][m][t];
     }
   };
 
@@ -263,10 +316,12 @@ static void launch_q8_mt(const uint16_t* a, const int8_t* q0, const uint16_t* s0
                          const int8_t* q1, const uint16_t* s1, const uint16_t* rr, uint16_t* o,
                          int M, int K, int N, hipStream_t s) {
   const dim3 grid((unsigned)((N + 15) / 16)), block(WAVES * 64);
-  if (M <= 16)
-    hipLaunchKernelGGL((q8_stream<NMAT, 1, WAVES, SALIGN>), grid, block, 0, s, a, q0, s0, q1, s1, rr, o, M, K, N);
+  if (M <= 8)
+    hipLaunchKernelGGL((q8_stream<NMAT, 1, WAVES, SALIGN, 8>), grid, block, 0, s, a, q0, s0, q1, s1, rr, o, M, K, N);
+  else if (M <= 16)
+    hipLaunchKernelGGL((q8_stream<NMAT, 1, WAVES, SALIGN, 16>), grid, block, 0, s, a, q0, s0, q1, s1, rr, o, M, K, N);
   else
-    hipLaunchKernelGGL((q8_stream<NMAT, 2, WAVES, SALIGN>), grid, block, 0, s, a, q0, s0, q1, s1, rr, o, M, K, N);
+    hipLaunchKernelGGL((q8_stream<NMAT, 2, WAVES, SALIGN, 0>), grid, block, 0, s, a, q0, s0, q1, s1, rr, o, M, K, N);
 }
 
 template <int NMAT, int WAVES>
