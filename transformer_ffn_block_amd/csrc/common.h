@@ -47,6 +47,14 @@ __device__ __forceinline__ uint4 buf_ld_nt(__amdgpu_buffer_rsrc_t r, unsigned of
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// 16-byte buffer load straight into LDS: lane i's 16 bytes land at
+// lds + 16*i (lds must be wave-uniform).  AUX 2 = streaming (non-temporal).
+template <int AUX>
+__device__ __forceinline__ void buf_ld_lds16(__amdgpu_buffer_rsrc_t r, void* lds, unsigned off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
+                                           (int)off, 0, 0, AUX);
+}
+
 __device__ __forceinline__ float bf2f(uint32_t b16) { return __uint_as_float(b16 << 16); }
 
 // fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
