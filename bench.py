@@ -16,7 +16,7 @@ The same JSON line also carries:
                   of that kernel from the committed profile, when the kernel
                   source is unchanged since the counters were taken;
   cpu_baseline  - the fp64 oracle on the host (1 BLAS thread) on the same
-                  decode workload;
+                  decode workload (extra also has an all-cores run);
   extra         - the other workloads: prefill block (M=8192, d=4096,
                   f=14336) fused and split gate/up, interleaved call by call,
                   in TFLOP/s; the standalone RMSNorm (16384 x 4096 bf16);
@@ -110,13 +110,15 @@ def read_traffic():
         return None
 
 
-def cpu_baseline(b, target_s=10.0):
-    """The oracle as it stands on the decode workload, 1 BLAS thread, repeated
-    until ~target_s of CPU time has been spent (at least once)."""
-    from threadpoolctl import threadpool_limits
+def cpu_baseline(b, target_s=10.0, threads=1):
+    """The oracle as it stands on the decode workload with `threads` BLAS
+    threads (None: the library's default, all host cores), repeated until
+    ~target_s of wall time has been spent (at least once)."""
+    from threadpoolctl import threadpool_info, threadpool_limits
     from oracle import ffn_oracle as O
     reps, t0 = 0, time.perf_counter()
-    with threadpool_limits(limits=1):
+    with threadpool_limits(limits=threads):
+        used = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
         while True:
             O.block_from_stored("bf16", b.x, b.g, b.w_gate, b.w_up, b.w_down, b.eps)
             reps += 1
@@ -124,7 +126,7 @@ def cpu_baseline(b, target_s=10.0):
                 break
     dt = (time.perf_counter() - t0) / reps
     gbs = decode_bytes(b.M, b.d, b.f) / dt / 1e9
-    return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": int(used), "kind": "oracle",
             "sample": f"whole decode block M={b.M} d={b.d} f={b.f} (bf16 inputs decoded to fp64), "
                       f"{reps} call(s), {dt:.2f} s per call"}
 
@@ -356,6 +358,8 @@ def main() -> int:
         log("timing the CPU oracle on the decode workload")
         cpu = cpu_baseline(b)
         log("cpu", cpu)
+        extra["cpu_oracle_all_cores"] = cpu_baseline(b, target_s=5.0, threads=None)
+        log("cpu (all cores)", extra["cpu_oracle_all_cores"])
 
     line = {
         "metric": "FFN block: decode GB/s & prefill TFLOP/s on 1 GPU, % of HBM/MFMA peak",

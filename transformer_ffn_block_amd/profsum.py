@@ -3,7 +3,7 @@
   python -m transformer_ffn_block_amd.profsum stats KERNEL_TRACE_CSV --command "..."
       per-kernel dispatch count, average / min / max duration (us)
   python -m transformer_ffn_block_amd.profsum traffic FETCH_CSV WRITE_CSV \\
-        --kernel SUBSTRING --copy-bytes N --source FILE --bytes-per-launch B --command "..."
+        --kernel SUBSTRING --copy-bytes N --source FILE --bytes-per-launch B --command "..." [--grid G]
       HBM traffic per launch of the matching kernel from FETCH_SIZE and
       WRITE_SIZE (KiB per dispatch), each scaled by what the same counter
       reads for the library's plain copy kernel (probe_copy) of known size.
@@ -38,11 +38,14 @@ def stats(trace_csv: str, command: str) -> str:
     return "\n".join(out) + "\n"
 
 
-def _counter(path: str, counter: str):
+def _counter(path: str, counter: str, grid=None):
     per = collections.defaultdict(list)
     for r in _rows(path):
-        if r["Counter_Name"] == counter:
-            per[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+        if r["Counter_Name"] != counter:
+            continue
+        if grid is not None and "probe_copy" not in r["Kernel_Name"] and int(r["Grid_Size"]) != grid:
+            continue
+        per[r["Kernel_Name"]].append(float(r["Counter_Value"]))
     return per
 
 
@@ -54,8 +57,9 @@ def _pick(per, sub):
     return k, statistics.fmean(v), len(v)
 
 
-def traffic(fetch_csv, write_csv, kernel, copy_bytes, source, bytes_per_launch, command) -> str:
-    f_per, w_per = _counter(fetch_csv, "FETCH_SIZE"), _counter(write_csv, "WRITE_SIZE")
+def traffic(fetch_csv, write_csv, kernel, copy_bytes, source, bytes_per_launch, command,
+            grid=None) -> str:
+    f_per, w_per = _counter(fetch_csv, "FETCH_SIZE", grid), _counter(write_csv, "WRITE_SIZE", grid)
     kname, f_kib, nf = _pick(f_per, kernel)
     _, w_kib, nw = _pick(w_per, kernel)
     _, cf_kib, _ = _pick(f_per, "probe_copy")
@@ -72,6 +76,7 @@ def traffic(fetch_csv, write_csv, kernel, copy_bytes, source, bytes_per_launch, 
         f"# command (fetch pass): {command.replace('PMC', 'FETCH_SIZE')}",
         f"# command (write pass): {command.replace('PMC', 'WRITE_SIZE')}",
         f"kernel = {kname.split('(')[0]}",
+        f"grid_size = {grid if grid is not None else 'any'}",
         f"dispatches_fetch = {nf}",
         f"dispatches_write = {nw}",
         f"fetch_kib_per_dispatch = {f_kib:.1f}",
@@ -106,12 +111,13 @@ def main(argv=None) -> int:
     t.add_argument("--source", required=True)
     t.add_argument("--bytes-per-launch", type=int, required=True)
     t.add_argument("--command", required=True)
+    t.add_argument("--grid", type=int, default=None, help="only dispatches of this grid size")
     a = ap.parse_args(argv)
     if a.cmd == "stats":
         sys.stdout.write(stats(a.trace_csv, a.command))
     else:
         sys.stdout.write(traffic(a.fetch_csv, a.write_csv, a.kernel, a.copy_bytes, a.source,
-                                 a.bytes_per_launch, a.command))
+                                 a.bytes_per_launch, a.command, a.grid))
     return 0
 
 
