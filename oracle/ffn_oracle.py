@@ -28,6 +28,8 @@ Readings taken where the pages leave a step open:
     pages never state where the norm sits);
   * Q8_0 blocks run along the reduction axis of each matrix; the 32 quants
     of a block share the block's fp16 scale;
+  * Q4_0 blocks likewise; inside a block byte i holds weight i (low nibble)
+    and weight i + 16 (high nibble), and a weight is (nibble - 8) * scale;
   * the oracle keeps every intermediate in fp64 (it does not mimic the
     GPU's bf16 roundings of n and h).
 
@@ -148,6 +150,39 @@ def swiglu_block_q8(x_bits, g_bits, wg, wu, wd, eps: float) -> np.ndarray:
     x = bf16_to_f64(x_bits)
     g = bf16_to_f64(g_bits)
     return swiglu_block(x, g, q8_dequant(*wg), q8_dequant(*wu), q8_dequant(*wd), eps)
+
+
+def q4_dequant(qs: np.ndarray, scale_bits: np.ndarray) -> np.ndarray:
+    """Q4_0 matrix -> fp64 weights [N, K].  The format (the 18-byte blocks of
+    "Unfusing a Kernel Made It 1.63x Faster", "The finding that keeps us
+    honest about microbenchmarks": one fp16 scale and 16 bytes whose low and
+    high nibbles hold different weights) is taken here as: per block of 32
+    weights along K, byte i of the block's 16 holds weight i in its low four
+    bits and weight i + 16 in its high four bits, and w = (nibble - 8) * s.
+    qs [N, K/2] bytes, scale_bits [N, K/32] fp16 bits."""
+    b = np.asarray(qs, dtype=np.uint8)
+    N, H = b.shape
+    K = 2 * H
+    s = f16_to_f64(scale_bits)
+    if K % 32 or s.shape != (N, K // 32):
+        raise ValueError("qs must be [N, K/2] and scales [N, K/32] with K % 32 == 0")
+    w = np.empty((N, K), dtype=np.float64)
+    for blk in range(K // 32):
+        byte = b[:, 16 * blk:16 * blk + 16].astype(np.int64)
+        low = (byte & 0x0F) - 8                      # weights 32*blk + 0 .. 15
+        high = (byte >> 4) - 8                       # weights 32*blk + 16 .. 31
+        w[:, 32 * blk:32 * blk + 16] = low * s[:, blk:blk + 1]
+        w[:, 32 * blk + 16:32 * blk + 32] = high * s[:, blk:blk + 1]
+    return w
+
+
+def swiglu_block_q4(x_bits, g_bits, wg, wu, wd, eps: float) -> np.ndarray:
+    """The block with Q4_0 weights (each matrix a pair (qs, scale_bits)) and
+    bf16 activations; weights are dequantised exactly (4-bit integer times an
+    fp16 scale) and the block is evaluated by swiglu_block in fp64."""
+    x = bf16_to_f64(x_bits)
+    g = bf16_to_f64(g_bits)
+    return swiglu_block(x, g, q4_dequant(*wg), q4_dequant(*wu), q4_dequant(*wd), eps)
 
 
 # ----------------------------------------------------------------------------

@@ -43,6 +43,11 @@ MUTANTS = {
     "f16_subnormals_flushed": ("return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)",
                                "v = np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)\n"
                                "    return np.where(np.abs(v) < 2.0 ** -14, 0.0, v)"),
+    "q4_nibble_halves_swapped": ("        low = (byte & 0x0F) - 8                      # weights 32*blk + 0 .. 15\n        high = (byte >> 4) - 8 ",
+                                 "        high = (byte & 0x0F) - 8\n        low = (byte >> 4) - 8 "),
+    "q4_offset_seven": ("        low = (byte & 0x0F) - 8 ", "        low = (byte & 0x0F) - 7 "),
+    "q4_scale_of_next_block": ("        w[:, 32 * blk:32 * blk + 16] = low * s[:, blk:blk + 1]",
+                               "        w[:, 32 * blk:32 * blk + 16] = low * s[:, (blk + 1) % s.shape[1]:(blk + 1) % s.shape[1] + 1]"),
     "bf16_low_half": ("return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)",
                       "return (b.astype(np.uint32) << np.uint32(15)).view(np.float32).astype(np.float64)"),
 }

@@ -325,3 +325,61 @@ def test_q8_dequant_product_is_exact_in_fp32():
     p32 = q.astype(np.float32) * s.astype(np.float32)
     p64 = q.astype(np.float64) * s.astype(np.float64)
     assert np.array_equal(p32.astype(np.float64), p64)
+
+
+# ----------------------------------------------------------------------------
+# Q4_0
+# ----------------------------------------------------------------------------
+def test_q4_dequant_golden_blocks():
+    gd = _load("q4_dequant_blocks.json")
+    w = O.q4_dequant(np.array(gd["qs"], dtype=np.uint8), np.array(gd["scale_bits"], dtype=np.uint16))
+    assert np.array_equal(w, np.array(gd["weights"], dtype=np.float64))
+
+
+def test_q4_nibble_positions_one_hot():
+    # every nibble 8 (weight 0) except one set to 9: the weight vector is the
+    # unit vector at that position, for each of the 32 positions of a block
+    for p in range(32):
+        b = np.full((1, 16), 0x88, dtype=np.uint8)
+        byte, shift = p % 16, (0 if p < 16 else 4)
+        b[0, byte] = (b[0, byte] & ~np.uint8(0xF << shift)) | np.uint8(9 << shift)
+        w = O.q4_dequant(b, np.array([[0x3C00]], dtype=np.uint16))
+        e = np.zeros((1, 32)); e[0, p] = 1.0
+        assert np.array_equal(w, e), p
+
+
+def test_q4_unit_scales_give_nibble_minus_eight():
+    rng = np.random.default_rng(21)
+    n = rng.integers(0, 16, size=(5, 128), dtype=np.uint8)
+    packed = n.reshape(5, 4, 2, 16)
+    qs = (packed[:, :, 0, :] | (packed[:, :, 1, :] << 4)).reshape(5, 64).astype(np.uint8)
+    ones = np.full((5, 4), 0x3C00, np.uint16)
+    assert np.array_equal(O.q4_dequant(qs, ones), n.astype(np.float64) - 8.0)
+
+
+def test_q4_block_equals_dense_block_on_dequantised_weights():
+    from transformer_ffn_block_amd import inputs as I
+    M, d, f = 2, 64, 96
+    q = I.make_q4_block(22, M, d, f)
+    y = O.swiglu_block_q4(q.x, q.g, (q.w_gate.qs, q.w_gate.scales), (q.w_up.qs, q.w_up.scales),
+                          (q.w_down.qs, q.w_down.scales), q.eps)
+
+    # an independently written dequant: split every byte with unpackbits
+    def deq(m):
+        N, H = m.qs.shape
+        bits = np.unpackbits(m.qs[..., None], axis=-1)          # msb first
+        hi = bits[..., :4] @ np.array([8, 4, 2, 1]); lo = bits[..., 4:] @ np.array([8, 4, 2, 1])
+        blk = np.concatenate([lo.reshape(N, -1, 16), hi.reshape(N, -1, 16)], axis=2).reshape(N, 2 * H)
+        s = m.scales.view(np.float16).astype(np.float64)
+        return (blk - 8.0) * np.kron(s, np.ones((1, 32)))
+    y2 = O.swiglu_block(O.bf16_to_f64(q.x), O.bf16_to_f64(q.g), deq(q.w_gate), deq(q.w_up), deq(q.w_down), q.eps)
+    assert np.array_equal(y, y2)
+
+
+def test_q4_block_form_roundtrip():
+    from transformer_ffn_block_amd import inputs as I
+    m = I.make_q4_matrix(np.random.default_rng(23), 3, 96)
+    m2 = I.q4_aos_to_soa(I.q4_soa_to_aos(m), 3, 96)
+    assert np.array_equal(m.qs, m2.qs) and np.array_equal(m.scales, m2.scales)
+    blocks = I.q4_soa_to_aos(m).reshape(3, 3, 18)
+    assert np.array_equal(blocks[1, 2, 2:], m.qs[1, 32:48])  # the 16 bytes follow the scale

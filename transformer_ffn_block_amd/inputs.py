@@ -202,6 +202,87 @@ def q8_soa_to_aos(m: Q8Matrix) -> np.ndarray:
     return out.reshape(-1)
 
 
+@dataclasses.dataclass
+class Q4Matrix:
+    qs: np.ndarray       # uint8 [N, K // 2]: per block of 32 weights along K, byte i
+                         # holds weight i (low four bits) and weight i + 16 (high four bits)
+    scales: np.ndarray   # uint16 (fp16 bits) [N, K // 32]
+
+
+@dataclasses.dataclass
+class Q4BlockInputs:
+    x: np.ndarray        # bf16 bits [M, d]
+    g: np.ndarray        # bf16 bits [d]
+    w_gate: Q4Matrix     # [f, d]
+    w_up: Q4Matrix       # [f, d]
+    w_down: Q4Matrix     # [d, f]
+    eps: float = EPS
+
+    @property
+    def M(self) -> int:
+        return self.x.shape[0]
+
+    @property
+    def d(self) -> int:
+        return self.x.shape[1]
+
+    @property
+    def f(self) -> int:
+        return self.w_gate.qs.shape[0]
+
+
+def pack_q4_nibbles(n: np.ndarray) -> np.ndarray:
+    """[N, K] nibbles (uint8 in [0, 15]) -> [N, K // 2] bytes, block layout
+    of Q4Matrix.qs (storage format only)."""
+    N, K = n.shape
+    b = n.reshape(N, K // 32, 2, 16)
+    return (b[:, :, 0, :] | (b[:, :, 1, :] << 4)).astype(np.uint8).reshape(N, K // 2)
+
+
+def make_q4_matrix(rng: np.random.Generator, N: int, K: int,
+                   s_std: float = 0.02) -> Q4Matrix:
+    """Q4_0 matrix [N, K]: nibbles uniform in [0, 15] (weight = nibble - 8);
+    one fp16 scale per 32 consecutive weights of a row, fp16(|N(0, s_std)| / 8 * 4)."""
+    if K % 32:
+        raise ValueError("Q4_0 needs K % 32 == 0")
+    n = rng.integers(0, 16, size=(N, K), dtype=np.uint8)
+    z = np.abs(rng.standard_normal(size=(N, K // 32), dtype=np.float32))
+    z *= np.float32(s_std)
+    s = (z / np.float32(8.0)) * np.float32(4.0)
+    return Q4Matrix(pack_q4_nibbles(n), f32_to_f16_bits(s))
+
+
+def make_q4_block(seed: int, M: int, d: int, f: int, eps: float = EPS) -> Q4BlockInputs:
+    """Seeded Q4_0 block inputs, draw order x, g, W_gate, W_up, W_down."""
+    rng = np.random.default_rng(seed)
+    x = f32_to_bf16_bits(_normal(rng, (M, d), 1.0))
+    g = f32_to_bf16_bits(_normal(rng, (d,), 0.1, 1.0))
+    wg = make_q4_matrix(rng, f, d)
+    wu = make_q4_matrix(rng, f, d)
+    wd = make_q4_matrix(rng, d, f)
+    return Q4BlockInputs(x, g, wg, wu, wd, eps)
+
+
+def q4_aos_to_soa(blocks: np.ndarray, N: int, K: int) -> Q4Matrix:
+    """Convert the interleaved 18-byte block form (2-byte fp16 scale, then 16
+    bytes of nibbles) of an [N, K] matrix into the split form the library
+    takes (qs [N, K/2] + scales [N, K/32])."""
+    b = np.ascontiguousarray(blocks, dtype=np.uint8).reshape(N, K // 32, 18)
+    scales = b[:, :, 0:2].copy().view(np.uint16).reshape(N, K // 32)
+    qs = b[:, :, 2:18].copy().reshape(N, K // 2)
+    return Q4Matrix(qs, scales)
+
+
+def q4_soa_to_aos(m: Q4Matrix) -> np.ndarray:
+    """Inverse of q4_aos_to_soa."""
+    N, H = m.qs.shape
+    nb = H // 16
+    out = np.empty((N, nb, 18), dtype=np.uint8)
+    out[:, :, 0:2] = m.scales.reshape(N, nb, 1).view(np.uint8).reshape(N, nb, 2)
+    out[:, :, 2:18] = m.qs.reshape(N, nb, 16)
+    return out.reshape(-1)
+
+
 # Named workloads (sizes of the pages' two regimes plus the tiny, norm and Q8 cases).
 WORKLOADS = {
     "tiny_f32":   dict(seed=1, M=8, d=256, f=704, dtype="f32"),
@@ -209,4 +290,5 @@ WORKLOADS = {
     "decode":     dict(seed=3, M=16, d=4096, f=11008, dtype="bf16"),
     "prefill":    dict(seed=4, M=8192, d=4096, f=14336, dtype="bf16"),
     "q8_decode":  dict(seed=5, M=8, d=5120, f=17408),
+    "q4_decode":  dict(seed=6, M=8, d=5120, f=17408),
 }
