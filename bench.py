@@ -47,6 +47,7 @@ DECODE = dict(seed=3, M=16, d=4096, f=11008)
 PREFILL = dict(seed=4, M=8192, d=4096, f=14336)
 RMS = dict(seed=2, rows=16384, d=4096)
 Q8 = dict(seed=5, M=8, d=5120, f=17408)
+Q4 = dict(seed=6, M=8, d=5120, f=17408)
 ROTATE = 4
 COPY_BYTES = 512 << 20
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_gateup_M16_hbm_traffic.txt")
@@ -219,6 +220,45 @@ def extras(torch, np, ffn, I, sets, x, g, b, ws, extra):
                           "frac_of_read_ceiling": round(qgbs / best, 4)}
     log("q8", extra["q8_decode"])
     del qsets, q0
+    torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------------- Q4_0
+    log("generating q4 inputs", Q4)
+    q4 = I.make_q4_block(Q4["seed"], Q4["M"], Q4["d"], Q4["f"])
+    q4x, q4g = to_dev(q4.x, torch), to_dev(q4.g, torch)
+    q40 = [qdev(m) for m in (q4.w_gate, q4.w_up, q4.w_down)]
+    q4sets = [q40] + [[(a.clone(), s.clone()) for a, s in q40] for _ in range(ROTATE - 1)]
+    q4ws = ffn.alloc_workspace(ffn.lib().ffn_swiglu_block_q4_workspace_size(Q4["M"], Q4["d"], Q4["f"]))
+    q4y = torch.empty_like(q4x)
+
+    def q4step(i):
+        a, bq, c = q4sets[i % ROTATE]
+        ffn.swiglu_block_q4(q4x, q4g, a, bq, c, q4.eps, out=q4y, workspace=q4ws)
+    for i in range(20):
+        q4step(i)
+    t4 = time_calls(torch, q4step, 200)
+    ffn.timing_reset()
+    ffn.timing_enable(True, 256)
+    for i in range(40):
+        q4step(i)
+    k4 = ffn.timing_collect()
+    ffn.timing_enable(False)
+    fd = Q4["f"] * Q4["d"]
+    q4_mat = fd // 2 + fd // 32 * 2          # nibbles + fp16 scales of one matrix
+    q4bytes = 3 * q4_mat + 2 * Q4["M"] * Q4["d"] * 2 + Q4["d"] * 2
+    q4gbs = q4bytes / (t4 * 1e-3) / 1e9
+    gu4 = k4["q4_gateup"][1] / k4["q4_gateup"][0] * 1e3     # us per launch
+    dn4 = k4["q4_down"][1] / k4["q4_down"][0] * 1e3
+    gu4_bytes = 2 * q4_mat + Q4["M"] * Q4["d"] * 2 + Q4["M"] * Q4["f"] * 2
+    dn4_bytes = q4_mat + Q4["M"] * Q4["f"] * 2 + 2 * Q4["M"] * Q4["d"] * 2
+    extra["q4_decode"] = {"us": round(t4 * 1e3, 2), "GBps": round(q4gbs, 1),
+                          "frac_of_read_ceiling": round(q4gbs / best, 4),
+                          "gateup_kernel_us": round(gu4, 2),
+                          "gateup_kernel_GBps": round(gu4_bytes / (gu4 * 1e-6) / 1e9, 1),
+                          "down_kernel_us": round(dn4, 2),
+                          "down_kernel_GBps": round(dn4_bytes / (dn4 * 1e-6) / 1e9, 1)}
+    log("q4", extra["q4_decode"])
+    del q4sets, q40
     torch.cuda.empty_cache()
 
     # ---------------------------------------------------------------- prefill

@@ -17,6 +17,10 @@
  *       "Megakernels on Mac", "Projection shape changes the achieved rate".
  *   - Q8_0 weights (32 int8 quants share one fp16 scale):
  *       "Unfusing a Kernel Made It 1.63x Faster", Finding 2 (format name).
+ *   - Q4_0 weights (18-byte blocks: one fp16 scale and 16 bytes whose low
+ *     and high nibbles are different weights), stored repacked:
+ *       "Unfusing a Kernel Made It 1.63x Faster", "The finding that keeps us
+ *       honest about microbenchmarks".
  *   - explicit supported shapes and failure behaviour, ownership of buffers
  *     that submitted work still reads:
  *       "Megakernels on Mac", "Choosing a fusion boundary" and
@@ -79,6 +83,20 @@ typedef struct {
   const uint16_t *scales;
 } ffn_q8_matrix;
 
+/* One Q4_0 weight matrix [N, K] in split (repacked) form:
+ *   qs     : uint8 [N, K/2]    16 bytes per 32-weight block; byte i of block
+ *                              b holds weight 32b + i in its low nibble and
+ *                              weight 32b + i + 16 in its high nibble
+ *   scales : fp16  [N, K/32]   IEEE binary16 bit patterns, one per block
+ * weight[j,k] = (nibble[j,k] - 8) * scales[j, k/32].  The 18-byte interleaved
+ * blocks of the format are this layout's rows of (scale, 16 bytes); keeping
+ * a row's nibble bytes contiguous lets every byte be fetched once.
+ * Both pointers are device pointers; qs 16-byte aligned, scales 2-byte. */
+typedef struct {
+  const uint8_t *qs;
+  const uint16_t *scales;
+} ffn_q4_matrix;
+
 /* RMSNorm of `rows` rows of length d:
  *   y[m,k] = x[m,k] * r_m * g[k],  r_m = 1/sqrt(sum_k x[m,k]^2 / d + eps)
  * ("When to hand-write a GPU kernel on Apple Silicon", Rung 2; the 16-byte
@@ -131,6 +149,26 @@ size_t ffn_swiglu_block_q8_workspace_size(int64_t M, int64_t d, int64_t f);
  * Returns FFN_OK, INVALID_ARGUMENT, UNSUPPORTED, WORKSPACE or LAUNCH. */
 ffn_status ffn_swiglu_block_q8(const void *x, const void *g, const ffn_q8_matrix *w_gate,
                                const ffn_q8_matrix *w_up, const ffn_q8_matrix *w_down,
+                               void *y, int64_t M, int64_t d, int64_t f, float eps,
+                               void *workspace, size_t workspace_bytes, void *stream);
+
+/* Workspace bytes ffn_swiglu_block_q4 needs (n [M,d] and h [M,f] in bf16). */
+size_t ffn_swiglu_block_q4_workspace_size(int64_t M, int64_t d, int64_t f);
+
+/* The block with Q4_0 weights, bf16 activations ("Unfusing a Kernel Made It
+ * 1.63x Faster", "The finding that keeps us honest about microbenchmarks"):
+ *   x [M,d], g [d], y [M,d]: bf16 device pointers, 16-byte aligned.
+ *   w_gate, w_up : Q4_0 [f, d]; w_down : Q4_0 [d, f] (host structs holding
+ *                  device pointers).
+ *   d, f : multiples of 32 (so no block straddles a row); f*d/2 < 2^31 bytes
+ *          of nibbles per matrix.
+ * Weights are dequantised in registers ((nibble - 8) * s, exact in fp32) and
+ * never written back; accumulation is fp32.  n and h are rounded to bf16.
+ * Returns FFN_OK, INVALID_ARGUMENT (null pointer, bad sizes or eps, y
+ * overlapping an input or the workspace), UNSUPPORTED (multiples, alignment,
+ * size limit), WORKSPACE or LAUNCH. */
+ffn_status ffn_swiglu_block_q4(const void *x, const void *g, const ffn_q4_matrix *w_gate,
+                               const ffn_q4_matrix *w_up, const ffn_q4_matrix *w_down,
                                void *y, int64_t M, int64_t d, int64_t f, float eps,
                                void *workspace, size_t workspace_bytes, void *stream);
 

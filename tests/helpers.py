@@ -17,6 +17,8 @@ def dev(a: np.ndarray, dtype: str = "bf16"):
         return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to("cuda")
     if dtype == "i8":
         return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int8)).to("cuda")
+    if dtype == "u8":
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint8)).to("cuda")
     if dtype == "u16":
         return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint16).view(np.int16)).to("cuda")
     raise ValueError(dtype)

@@ -39,7 +39,7 @@ def L():
 
 def test_header_declares_the_three_block_entry_points():
     names = declared_functions()
-    for n in ("ffn_rmsnorm", "ffn_swiglu_block", "ffn_swiglu_block_q8"):
+    for n in ("ffn_rmsnorm", "ffn_swiglu_block", "ffn_swiglu_block_q8", "ffn_swiglu_block_q4"):
         assert n in names
 
 
@@ -103,6 +103,8 @@ def test_workspace_sizes(L):
     assert L.ffn_swiglu_block_workspace_size(ffn.FFN_F32, 8, 256, 704, 0) == r256(8 * 256 * 4) + r256(8 * 704 * 4)
     assert L.ffn_swiglu_block_workspace_size(5, M, d, f, 0) == 0
     assert L.ffn_swiglu_block_q8_workspace_size(8, 5120, 17408) == r256(8 * 5120 * 2) + r256(8 * 17408 * 2)
+    assert L.ffn_swiglu_block_q4_workspace_size(8, 5120, 17408) == r256(8 * 5120 * 2) + r256(8 * 17408 * 2)
+    assert L.ffn_swiglu_block_q4_workspace_size(-1, 5120, 17408) == 0
 
 
 def test_rmsnorm_validation(L):
@@ -138,6 +140,34 @@ def test_q8_validation(L):
     assert call(wsb=10) == ffn.FFN_ERR_WORKSPACE
     assert call(M=0, ws=0, wsb=0) == ffn.FFN_OK
     assert L.ffn_swiglu_block_q8(A, B, None, ref(g2), ref(g3), Y, 8, 5120, 17408, 1e-6, WS, 1 << 30, None) == INV
+
+
+def test_q4_validation(L):
+    INV, UNS = ffn.FFN_ERR_INVALID_ARGUMENT, ffn.FFN_ERR_UNSUPPORTED
+    good = ffn.Q4Matrix(C, D)
+    g2 = ffn.Q4Matrix(E, E + 0x1000000)
+    g3 = ffn.Q4Matrix(E + 0x2000000, E + 0x3000000)
+    ref = ctypes.byref
+
+    def call(M=8, d=5120, f=17408, mg=good, mu=g2, md=g3, ws=WS, wsb=None, x=A, y=Y):
+        if wsb is None:
+            wsb = L.ffn_swiglu_block_q4_workspace_size(M, d, f)
+        return L.ffn_swiglu_block_q4(x, B, ref(mg), ref(mu), ref(md), y, M, d, f, 1e-6, ws, wsb, None)
+
+    assert call(d=5136) == UNS                       # d % 32 != 0
+    assert call(f=17400) == UNS                      # f % 32 != 0
+    assert call(mg=ffn.Q4Matrix(0, D)) == INV
+    assert call(md=ffn.Q4Matrix(E, 0)) == INV
+    assert call(mu=ffn.Q4Matrix(E + 8, E + 0x1000000)) == UNS   # nibbles 16-byte aligned
+    assert call(mu=ffn.Q4Matrix(E, E + 0x1000001)) == UNS       # scales 2-byte aligned
+    assert call(x=0) == INV
+    assert call(wsb=10) == ffn.FFN_ERR_WORKSPACE
+    assert call(M=0, ws=0, wsb=0) == ffn.FFN_OK
+    # 2^31 bytes of nibbles: d * f = 2^32 weights
+    assert call(M=1, d=65536, f=65536) == UNS
+    # just under the limit passes validation up to the aliasing check: y inside qs
+    assert call(M=1, d=65536, f=32768 - 32, y=C) == INV
+    assert L.ffn_swiglu_block_q4(A, B, None, ref(g2), ref(g3), Y, 8, 5120, 17408, 1e-6, WS, 1 << 30, None) == INV
 
 
 def test_probe_and_timing_validation(L):

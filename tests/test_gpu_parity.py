@@ -3,8 +3,10 @@
 Tolerances (per output tensor):
   * RMSNorm, strict per element |a - r| / |r|: 1e-2 for bf16 output (its own
     rounding alone is up to 2^-8), 1e-5 for fp32;
-  * the block, max_i |a_i - r_i| / max_i |r_i|: 1e-2 for bf16, 2e-2 for Q8_0,
-    1e-4 for the all-fp32 path (fp32 dot products of length K <= 1e3 carry at
+  * the block, max_i |a_i - r_i| / max_i |r_i|: 1e-2 for bf16, 2e-2 for Q8_0
+    and Q4_0 (their dequantisation is exact on both sides; the bf16 roundings
+    of n and h are the error, as in the bf16 block, with more cancellation in
+    the down projection's sums), 1e-4 for the all-fp32 path (fp32 dot products of length K <= 1e3 carry at
     most ~K * 2^-24 relative error).
 Every case is seeded; full-size cases use the sizes and launch configuration
 the benchmark times.
@@ -22,6 +24,7 @@ pytestmark = pytest.mark.gpu
 
 TOL_BF16 = 1e-2
 TOL_Q8 = 2e-2
+TOL_Q4 = 2e-2
 TOL_F32_BLOCK = 1e-4
 TOL_F32_NORM = 1e-5
 
@@ -298,3 +301,75 @@ def test_q8_subnormal_scales_are_not_flushed(gpu_lib):
     r = _q8_ref(q)
     assert max_norm_err(O.bf16_to_f64(q.x), r) > 0.5   # flushed scales would fail by far
     assert max_norm_err(a, r) <= TOL_Q8
+
+
+# ----------------------------------------------------------------------------
+# Q4_0
+# ----------------------------------------------------------------------------
+def _q4_dev(m: I.Q4Matrix):
+    return dev(m.qs, "u8"), dev(m.scales, "u16")
+
+
+def _q4_ref(q: I.Q4BlockInputs):
+    return O.swiglu_block_q4(q.x, q.g, (q.w_gate.qs, q.w_gate.scales),
+                             (q.w_up.qs, q.w_up.scales), (q.w_down.qs, q.w_down.scales), q.eps)
+
+
+def _run_q4(ffn, q: I.Q4BlockInputs, bits=False):
+    import torch
+    y = ffn.swiglu_block_q4(dev(q.x), dev(q.g), _q4_dev(q.w_gate), _q4_dev(q.w_up), _q4_dev(q.w_down), q.eps)
+    torch.cuda.synchronize()
+    return host_bits(y) if bits else host_f64(y)
+
+
+def test_q4_full_size(gpu_lib):
+    from transformer_ffn_block_amd import ffn
+    wl = I.WORKLOADS["q4_decode"]
+    _say("q4 full", wl)
+    q = I.make_q4_block(wl["seed"], wl["M"], wl["d"], wl["f"])
+    sub = np.count_nonzero((q.w_gate.scales & 0x7C00) == 0)
+    a = _run_q4(ffn, q)
+    r = _q4_ref(q)
+    err = max_norm_err(a, r)
+    _say("q4 err", err, "subnormal-or-zero gate scales", sub)
+    assert sub > 0
+    assert err <= TOL_Q4
+
+
+# M: 1..8 and 9..16 take the staged-activation kernels, 17..32 the two-tile
+# kernel, > 32 several launches; d, f not multiples of 256 leave a partial
+# last stage and use the per-block scale loads
+@pytest.mark.parametrize("M,d,f", [(1, 64, 32), (3, 160, 96), (12, 288, 352), (17, 512, 704),
+                                   (33, 256, 800), (70, 256, 256)])
+def test_q4_ragged_tokens(gpu_lib, M, d, f):
+    from transformer_ffn_block_amd import ffn
+    _say("q4 ragged", M, d, f)
+    q = I.make_q4_block(1800 + M, M, d, f)
+    assert max_norm_err(_run_q4(ffn, q), _q4_ref(q)) <= TOL_Q4
+
+
+def test_q4_subnormal_scales_are_not_flushed(gpu_lib):
+    """Every scale subnormal and eps = 0, as for Q8_0; the weights are ~16x
+    smaller than Q8_0's, so x is scaled by 2^-32 (still a normal bf16) for the
+    delta to dominate y: a flush-to-zero dequantisation would return y == x."""
+    from transformer_ffn_block_amd import ffn
+    q = I.make_q4_block(1900, 4, 128, 96)
+    rng = np.random.default_rng(1901)
+    for m in (q.w_gate, q.w_up, q.w_down):
+        m.scales[:] = rng.integers(0x0100, 0x0400, size=m.scales.shape, dtype=np.uint16)
+    q.x = I.f32_to_bf16_bits(I.bf16_bits_to_f32(q.x) * np.float32(2.0 ** -32))
+    q.eps = 0.0
+    a = _run_q4(ffn, q)
+    r = _q4_ref(q)
+    assert max_norm_err(O.bf16_to_f64(q.x), r) > 0.5
+    assert max_norm_err(a, r) <= TOL_Q4
+
+
+@pytest.mark.parametrize("M", [5, 40])
+def test_q4_zero_point_nibbles_return_x_bitwise(gpu_lib, M):
+    """Every down-projection nibble 8 (weight 0 under any scale): y = x + 0
+    exactly, whatever the gate/up path computes."""
+    from transformer_ffn_block_amd import ffn
+    q = I.make_q4_block(1950 + M, M, 288, 320)
+    q.w_down.qs[:] = 0x88
+    assert np.array_equal(_run_q4(ffn, q, bits=True), q.x)

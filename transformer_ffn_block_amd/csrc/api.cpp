@@ -276,6 +276,99 @@ ffn_status ffn_swiglu_block(ffn_dtype dt, const void* x, const void* g, const vo
   return ok();
 }
 
+}  // extern "C"
+
+namespace {
+
+// Q8_0 and Q4_0 blocks share validation and the launch sequence; the traits
+// give the storage of one matrix and its kernels.
+struct Q8Traits {
+  using Mat = ffn_q8_matrix;
+  static constexpr const char* name = "Q8";
+  static constexpr const char* gateup_name = "q8_gateup";
+  static constexpr const char* down_name = "q8_down";
+  static size_t quant_bytes(size_t weights) { return weights; }
+  static int max_tokens() { return ffn::q8_max_tokens(); }
+  static hipError_t gateup(const void* n, const Mat* g, const Mat* u, void* h, int M, int d, int f,
+                           hipStream_t s) {
+    return ffn::launch_q8_gateup(n, g->qs, g->scales, u->qs, u->scales, h, M, d, f, s);
+  }
+  static hipError_t down(const void* h, const Mat* w, const void* x, void* y, int M, int d, int f,
+                         hipStream_t s) {
+    return ffn::launch_q8_down(h, w->qs, w->scales, x, y, M, d, f, s);
+  }
+};
+struct Q4Traits {
+  using Mat = ffn_q4_matrix;
+  static constexpr const char* name = "Q4";
+  static constexpr const char* gateup_name = "q4_gateup";
+  static constexpr const char* down_name = "q4_down";
+  static size_t quant_bytes(size_t weights) { return weights / 2; }
+  static int max_tokens() { return ffn::q4_max_tokens(); }
+  static hipError_t gateup(const void* n, const Mat* g, const Mat* u, void* h, int M, int d, int f,
+                           hipStream_t s) {
+    return ffn::launch_q4_gateup(n, g->qs, g->scales, u->qs, u->scales, h, M, d, f, s);
+  }
+  static hipError_t down(const void* h, const Mat* w, const void* x, void* y, int M, int d, int f,
+                         hipStream_t s) {
+    return ffn::launch_q4_down(h, w->qs, w->scales, x, y, M, d, f, s);
+  }
+};
+
+template <class T>
+static ffn_status quant_block(const void* x, const void* g, const typename T::Mat* w_gate,
+                              const typename T::Mat* w_up, const typename T::Mat* w_down, void* y,
+                              int64_t M, int64_t d, int64_t f, float eps, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  if (!x || !g || !y || !w_gate || !w_up || !w_down)
+    return fail(FFN_ERR_INVALID_ARGUMENT, "null pointer");
+  const typename T::Mat* mats[3] = {w_gate, w_up, w_down};
+  for (const typename T::Mat* m : mats) {
+    if (!m->qs || !m->scales) return fail(FFN_ERR_INVALID_ARGUMENT, "null %s matrix pointer", T::name);
+    if (!aligned(m->qs, 16) || !aligned(m->scales, 2))
+      return fail(FFN_ERR_UNSUPPORTED, "%s quants must be 16-byte aligned, scales 2-byte", T::name);
+  }
+  FFN_TRY(check_eps(eps));
+  FFN_TRY(check_block_dims(M, d, f, 32));
+  if (T::quant_bytes((size_t)f * d) >= ((size_t)1 << 31))
+    return fail(FFN_ERR_UNSUPPORTED, "%s quant arrays must be smaller than 2 GiB", T::name);
+  if (!aligned(x, 16) || !aligned(g, 16) || !aligned(y, 16))
+    return fail(FFN_ERR_UNSUPPORTED, "x, g and y must be 16-byte aligned");
+  const WsLayout L = ws_layout(2, M, d, f, false);
+  if (M > 0 && (!workspace || workspace_bytes < L.total))
+    return fail(FFN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total,
+                workspace ? workspace_bytes : (size_t)0);
+  if (workspace && !aligned(workspace, 256))
+    return fail(FFN_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
+  const size_t ny = (size_t)M * d * 2, nq = T::quant_bytes((size_t)f * d), ns = (size_t)f * d / 32 * 2;
+  bool ov = overlap(y, ny, x, ny) || overlap(y, ny, g, (size_t)d * 2) ||
+            overlap(y, ny, workspace, workspace ? L.total : 0);
+  for (const typename T::Mat* m : mats)
+    ov = ov || overlap(y, ny, m->qs, nq) || overlap(y, ny, m->scales, ns);
+  if (ov) return fail(FFN_ERR_INVALID_ARGUMENT, "y overlaps an input or the workspace");
+  if (M == 0) return ok();
+
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  char* n = ws + L.n;
+  char* h = ws + L.h;
+  FFN_LAUNCH("rmsnorm", s, ffn::launch_rmsnorm(2, x, g, n, M, d, eps, s));
+  const int step = T::max_tokens();
+  for (int64_t m0 = 0; m0 < M; m0 += step) {
+    const int mc = (int)(M - m0 < step ? M - m0 : step);
+    FFN_LAUNCH(T::gateup_name, s,
+               T::gateup(n + m0 * d * 2, w_gate, w_up, h + m0 * f * 2, mc, (int)d, (int)f, s));
+    FFN_LAUNCH(T::down_name, s,
+               T::down(h + m0 * f * 2, w_down, (const char*)x + m0 * d * 2, (char*)y + m0 * d * 2,
+                       mc, (int)d, (int)f, s));
+  }
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
 size_t ffn_swiglu_block_q8_workspace_size(int64_t M, int64_t d, int64_t f) {
   if (M < 0 || d <= 0 || f <= 0) return 0;
   return ws_layout(2, M, d, f, false).total;
@@ -285,50 +378,21 @@ ffn_status ffn_swiglu_block_q8(const void* x, const void* g, const ffn_q8_matrix
                                const ffn_q8_matrix* w_up, const ffn_q8_matrix* w_down, void* y,
                                int64_t M, int64_t d, int64_t f, float eps, void* workspace,
                                size_t workspace_bytes, void* stream) {
-  if (!x || !g || !y || !w_gate || !w_up || !w_down)
-    return fail(FFN_ERR_INVALID_ARGUMENT, "null pointer");
-  const ffn_q8_matrix* mats[3] = {w_gate, w_up, w_down};
-  for (const ffn_q8_matrix* m : mats) {
-    if (!m->qs || !m->scales) return fail(FFN_ERR_INVALID_ARGUMENT, "null Q8 matrix pointer");
-    if (!aligned(m->qs, 16) || !aligned(m->scales, 2))
-      return fail(FFN_ERR_UNSUPPORTED, "Q8 quants must be 16-byte aligned, scales 2-byte");
-  }
-  FFN_TRY(check_eps(eps));
-  FFN_TRY(check_block_dims(M, d, f, 32));
-  if ((size_t)f * d >= ((size_t)1 << 31))
-    return fail(FFN_ERR_UNSUPPORTED, "weight matrices must be smaller than 2 GiB");
-  if (!aligned(x, 16) || !aligned(g, 16) || !aligned(y, 16))
-    return fail(FFN_ERR_UNSUPPORTED, "x, g and y must be 16-byte aligned");
-  const WsLayout L = ws_layout(2, M, d, f, false);
-  if (M > 0 && (!workspace || workspace_bytes < L.total))
-    return fail(FFN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total,
-                workspace ? workspace_bytes : (size_t)0);
-  if (workspace && !aligned(workspace, 256))
-    return fail(FFN_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
-  const size_t ny = (size_t)M * d * 2, nq = (size_t)f * d, ns = (size_t)f * d / 32 * 2;
-  bool ov = overlap(y, ny, x, ny) || overlap(y, ny, g, (size_t)d * 2) ||
-            overlap(y, ny, workspace, workspace ? L.total : 0);
-  for (const ffn_q8_matrix* m : mats) ov = ov || overlap(y, ny, m->qs, nq) || overlap(y, ny, m->scales, ns);
-  if (ov) return fail(FFN_ERR_INVALID_ARGUMENT, "y overlaps an input or the workspace");
-  if (M == 0) return ok();
+  return quant_block<Q8Traits>(x, g, w_gate, w_up, w_down, y, M, d, f, eps, workspace,
+                               workspace_bytes, stream);
+}
 
-  hipStream_t s = (hipStream_t)stream;
-  char* ws = (char*)workspace;
-  char* n = ws + L.n;
-  char* h = ws + L.h;
-  FFN_LAUNCH("rmsnorm", s, ffn::launch_rmsnorm(2, x, g, n, M, d, eps, s));
-  const int step = ffn::q8_max_tokens();
-  for (int64_t m0 = 0; m0 < M; m0 += step) {
-    const int mc = (int)(M - m0 < step ? M - m0 : step);
-    FFN_LAUNCH("q8_gateup", s,
-               ffn::launch_q8_gateup(n + m0 * d * 2, w_gate->qs, w_gate->scales, w_up->qs,
-                                     w_up->scales, h + m0 * f * 2, mc, (int)d, (int)f, s));
-    FFN_LAUNCH("q8_down", s,
-               ffn::launch_q8_down(h + m0 * f * 2, w_down->qs, w_down->scales,
-                                   (const char*)x + m0 * d * 2, (char*)y + m0 * d * 2, mc,
-                                   (int)d, (int)f, s));
-  }
-  return ok();
+size_t ffn_swiglu_block_q4_workspace_size(int64_t M, int64_t d, int64_t f) {
+  if (M < 0 || d <= 0 || f <= 0) return 0;
+  return ws_layout(2, M, d, f, false).total;
+}
+
+ffn_status ffn_swiglu_block_q4(const void* x, const void* g, const ffn_q4_matrix* w_gate,
+                               const ffn_q4_matrix* w_up, const ffn_q4_matrix* w_down, void* y,
+                               int64_t M, int64_t d, int64_t f, float eps, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  return quant_block<Q4Traits>(x, g, w_gate, w_up, w_down, y, M, d, f, eps, workspace,
+                               workspace_bytes, stream);
 }
 
 // ---------------------------------------------------------------------------

@@ -50,6 +50,15 @@ hipError_t launch_q8_down(const void* h, const int8_t* qd, const uint16_t* sd, c
                           void* y, int M, int d, int f, hipStream_t s);
 int q8_max_tokens();
 
+// Q4_0 weight-streaming projections (split nibble / scale arrays, bf16
+// activations, in-register dequant); same roles as the Q8_0 launchers.
+hipError_t launch_q4_gateup(const void* n, const uint8_t* qg, const uint16_t* sg,
+                            const uint8_t* qu, const uint16_t* su, void* h, int M, int d, int f,
+                            hipStream_t s);
+hipError_t launch_q4_down(const void* h, const uint8_t* qd, const uint16_t* sd, const void* x,
+                          void* y, int M, int d, int f, hipStream_t s);
+int q4_max_tokens();
+
 // Bandwidth probes.
 int probe_read_groups(int waves_per_cu);
 hipError_t launch_probe_read(const void* src, size_t bytes, void* sink, int waves_per_cu,

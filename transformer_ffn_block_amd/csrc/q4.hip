@@ -1,0 +1,333 @@
+// Q4_0 weight-streaming projections with in-register dequantisation.
+//
+// A Q4_0 block holds 32 weights along the reduction axis as one fp16 scale
+// and 16 bytes whose low and high nibbles carry different weights (the
+// 18-byte blocks of "Unfusing a Kernel Made It 1.63x Faster", "The finding
+// that keeps us honest about microbenchmarks").  Taken here: byte i holds
+// weight i (low nibble) and weight i + 16 (high nibble); w = (nibble - 8) * s.
+// The library stores the nibble bytes and the scales in separate arrays
+// (the repacked layout: a row's bytes are contiguous, so a 256-k stage of a
+// row is 128 consecutive bytes).  Activations stay bf16.
+//
+//   gate/up : h[m,j] = silu(sum_k Wg[j,k] n[m,k]) * (sum_k Wu[j,k] n[m,k])
+//   down    : y[m,i] = x[m,i] + sum_j Wd[i,j] h[m,j]
+//
+// gfx950 mapping (as the Q8_0 kernels).  A block is one K step of
+// v_mfma_f32_16x16x32_bf16, so the scale factors out of the block's dot
+// product.  Lane (r, q) feeds weights 8q..8q+7 of a block of row r: the low
+// nibbles (q < 2) or high nibbles (q >= 2) of bytes 8(q & 1) .. 8(q & 1) + 7.
+// A nibble n is moved to the top half of its byte and xor-ed with 0x80, which
+// makes the byte the int8 value 16 (n - 8); sign-extending byte conversion
+// then yields 16 (n - 8) exactly in bf16, and the lane scales the block's
+// partial by s / 16 (exact in fp32): the dequantisation adds no rounding.
+//
+// Streaming: a workgroup owns 16 weight rows (per matrix); its waves split K
+// into 256-k stages (128 bytes per row).  Each matrix's stage is 16 rows x 8
+// chunks of 16 bytes in a per-wave 2 KiB LDS buffer, fetched by two
+// instructions of 8 rows x 128 B; chunk c of row R sits at position
+// (c + R/2) & 7 of the row, so the 8-byte fragment reads of a block (16 rows
+// x two halves) hit all 64 banks once.  Prefetches past a wave's K slice use
+// an out-of-range buffer offset and read nothing.  Scales, activations, the
+// two-batch pipeline and the fixed-order cross-wave reduction are those of
+// the Q8_0 kernels.
+#include "common.h"
+#include "launch.h"
+
+namespace ffn {
+
+// 8 nibbles of one half (low: hi_half false) of bytes lo..hi -> 8 bf16 of
+// 16 * (nibble - 8)
+__device__ __forceinline__ uint4 q4x8_to_bf16(uint32_t lo, uint32_t hi, bool high_half) {
+  const uint32_t a = (high_half ? lo : lo << 4) & 0xF0F0F0F0u;
+  const uint32_t b = (high_half ? hi : hi << 4) & 0xF0F0F0F0u;
+  const uint32_t sa = a ^ 0x80808080u, sb = b ^ 0x80808080u;
+  float f[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[i] = (float)(((int)(sa << (24 - 8 * i))) >> 24);
+    f[4 + i] = (float)(((int)(sb << (24 - 8 * i))) >> 24);
+  }
+  return pack8(f);
+}
+
+__device__ __forceinline__ float q4_f16bits_to_f32(uint32_t b) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
+}
+
+template <int NMAT, int MT, int WAVES, bool SALIGN, int ASTAGE>
+__global__ __launch_bounds__(WAVES * 64) void q4_stream(
+    const uint16_t* __restrict__ act,     // [M, K] bf16: n or h
+    const uint8_t* __restrict__ q0, const uint16_t* __restrict__ s0,  // [N, K/2], [N, K/32]
+    const uint8_t* __restrict__ q1, const uint16_t* __restrict__ s1,
+    const uint16_t* __restrict__ resid,   // [M, N] (NMAT == 1)
+    uint16_t* __restrict__ out,           // [M, N]
+    int M, int K, int N) {
+  constexpr int SB = 8;  // 32-weight blocks per stage (256 k, 128 B per row)
+  __shared__ uint4 wb[WAVES][NMAT][128];           // per-wave nibble stage (2 KiB per matrix)
+  __shared__ float red[WAVES][MT][NMAT][4][64];
+  __shared__ uint4 abuf[WAVES][ASTAGE ? ASTAGE * 32 : 1];  // per-wave activation stage [rows][32]
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int r = lane & 15, q = lane >> 4;
+  const int j0 = blockIdx.x * 16;
+  const int nb = K >> 5;                // blocks per row
+  const int K32 = K >> 5;               // 16-byte nibble chunks per row (one per block)
+  const int K8 = K >> 3;                // 16-byte activation chunks per row
+  const int nst = (nb + SB - 1) / SB;
+  const int sb = (int)(((long)nst * wave) / WAVES);
+  const int se = (int)(((long)nst * (wave + 1)) / WAVES);
+
+  // staged loads: instruction u covers rows 8u..8u+7; lane -> row 8u + lane/8,
+  // LDS slot u*64 + lane, which holds chunk (lane%8 - row/2) & 7 of the row's
+  // 128-byte stage segment; chunk c of row R therefore sits at slot
+  // R*8 + ((c + R/2) & 7)
+  __amdgpu_buffer_rsrc_t rq[NMAT];  // nibbles through buffer resources (< 2 GiB)
+  rq[0] = make_rsrc(q0, (long)N * (K / 2));
+  if (NMAT == 2) rq[NMAT - 1] = make_rsrc(q1, (long)N * (K / 2));
+  unsigned gq[2];  // byte offset of this lane's row in each instruction
+  int cst[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int rr = 8 * u + (lane >> 3);
+    const int row = min(j0 + rr, N - 1);  // rows past N: clamped, never stored
+    cst[u] = ((lane & 7) - (rr >> 1)) & 7;
+    gq[u] = (unsigned)row * (unsigned)(K / 2);
+  }
+  // this lane's weight row (MFMA B operand) and its scales
+  const int jr = min(j0 + r, N - 1);
+  const uint16_t* ps[NMAT];
+  ps[0] = s0 + (size_t)jr * nb;
+  if (NMAT == 2) ps[NMAT - 1] = s1 + (size_t)jr * nb;
+
+  // direct activations: token t*16 + r; staged: instruction v covers token
+  // rows 2v, 2v+1 (lane -> row 2v + lane/32, LDS slot v*64 + lane holding
+  // chunk ((lane & 31) - row) & 31 of the row's 512-byte stage segment)
+  constexpr int NA = ASTAGE ? ASTAGE / 2 : SB * MT;  // activation loads per batch
+  const uint4* pa[ASTAGE ? NA : MT];
+  if (ASTAGE) {
+#pragma unroll
+    for (int v = 0; v < NA; ++v)
+      pa[v] = reinterpret_cast<const uint4*>(act) + (size_t)min(2 * v + (lane >> 5), M - 1) * K8;
+  } else {
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+      pa[t] = reinterpret_cast<const uint4*>(act) + (size_t)min(t * 16 + r, M - 1) * K8;
+  }
+
+  f32x4 acc[NMAT][MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m) acc[m][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+
+  struct Batch {
+    uint4 w[NMAT][2];
+    uint4 s[NMAT];  // SALIGN: the stage's 8 scales of row r; else .x = blocks 2q, 2q+1
+    uint4 a[NA];
+  };
+  // st < 0 marks a prefetch past the slice end: the nibble loads then read
+  // nothing (out-of-range offset) and the small loads hit cache
+  auto load = [&](Batch& B, int st_req) {
+    const int st = st_req < 0 ? se - 1 : st_req;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int c = min(st * 8 + cst[u], K32 - 1);
+      const unsigned o = st_req < 0 ? kOutOfRange : gq[u] + (unsigned)c * 16u;
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m) B.w[m][u] = buf_ld_nt(rq[m], o);
+    }
+    if (SALIGN) {
+      const int c = min(st, (nb >> 3) - 1);
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m) B.s[m] = reinterpret_cast<const uint4*>(ps[m])[c];
+    } else {
+      const int b0 = min(st * SB + 2 * q, nb - 1), b1 = min(st * SB + 2 * q + 1, nb - 1);
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m)
+        B.s[m].x = (uint32_t)ps[m][b0] | ((uint32_t)ps[m][b1] << 16);
+    }
+    if (ASTAGE) {
+#pragma unroll
+      for (int v = 0; v < NA; ++v) {
+        const int c = ((lane & 31) - (2 * v + (lane >> 5))) & 31;
+        B.a[v] = pa[v][min(st * 32 + c, K8 - 1)];
+      }
+    } else {
+#pragma unroll
+      for (int b = 0; b < SB; ++b) {
+        const int c = min(st * SB + b, nb - 1) * 4 + q;
+#pragma unroll
+        for (int t = 0; t < MT; ++t) B.a[b * MT + t] = pa[t][c];
+      }
+    }
+  };
+  auto stage_and_compute = [&](const Batch& B, int st) {
+    const bool ragged = (st + 1) * SB > nb;  // only a row's last stage can be partial
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m) {
+        uint4 x = B.w[m][u];
+        if (ragged) x = keep_or_zero(st * 8 + cst[u] < K32, x);
+        wb[wave][m][u * 64 + lane] = x;
+      }
+    }
+    if (ASTAGE) {
+#pragma unroll
+      for (int v = 0; v < NA; ++v) {
+        uint4 a = B.a[v];
+        if (ragged) {
+          const int c = ((lane & 31) - (2 * v + (lane >> 5))) & 31;
+          a = keep_or_zero(st * 32 + c < K8, a);
+        }
+        abuf[wave][ASTAGE ? v * 64 + lane : 0] = a;
+      }
+    }
+    // the MFMAs of a group of blocks first, then their scale FMAs
+    constexpr int GB = 4;
+#pragma unroll
+    for (int b0 = 0; b0 < SB; b0 += GB) {
+      f32x4 p[GB][NMAT][MT];
+      float scv[GB][NMAT];
+#pragma unroll
+      for (int bb = 0; bb < GB; ++bb) {
+        const int b = b0 + bb;
+        uint4 aa[MT];
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+          if (ASTAGE) {
+            const int ar = r & (ASTAGE ? ASTAGE - 1 : 0);
+            aa[t] = abuf[wave][ASTAGE ? ar * 32 + ((4 * b + q + ar) & 31) : 0];
+          } else {
+            aa[t] = B.a[b * MT + t];
+            if (ragged) aa[t] = keep_or_zero(st * SB + b < nb, aa[t]);
+          }
+        }
+        // block b of row r: chunk b of the stage, bytes 8(q & 1) .. +8
+        const int slot = r * 8 + ((b + (r >> 1)) & 7);
+        const int src_lane = r + 16 * (b >> 1);  // the lane of row r holding block b's scale
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m) {
+          const uint2 qv = reinterpret_cast<const uint2*>(&wb[wave][m][slot])[q & 1];
+          const uint4 Bq = q4x8_to_bf16(qv.x, qv.y, q >= 2);
+          uint32_t pair;
+          if (SALIGN) {
+            pair = (b >> 1) == 0 ? B.s[m].x : (b >> 1) == 1 ? B.s[m].y : (b >> 1) == 2 ? B.s[m].z : B.s[m].w;
+          } else {
+            pair = (uint32_t)__shfl((int)B.s[m].x, src_lane, 64);
+          }
+          // the MFMA sees 16 (n - 8): scale by s / 16
+          scv[bb][m] = q4_f16bits_to_f32((b & 1) ? (pair >> 16) : (pair & 0xFFFFu)) * 0.0625f;
+#pragma unroll
+          for (int t = 0; t < MT; ++t) p[bb][m][t] = mfma16(aa[t], Bq, z4);
+        }
+      }
+#pragma unroll
+      for (int bb = 0; bb < GB; ++bb)
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+          for (int t = 0; t < MT; ++t) acc[m][t] += scv[bb][m] * p[bb][m][t];
+    }
+  };
+
+  const int n = se - sb;
+  if (n >= 2) {
+    Batch X, Y;
+    load(X, sb);
+    load(Y, sb + 1);
+    for (int s = sb;;) {
+      __builtin_amdgcn_sched_barrier(0);
+      stage_and_compute(X, s);
+      __builtin_amdgcn_sched_barrier(0);
+      load(X, s + 2 < se ? s + 2 : -1);
+      if (++s >= se) break;
+      __builtin_amdgcn_sched_barrier(0);
+      stage_and_compute(Y, s);
+      __builtin_amdgcn_sched_barrier(0);
+      load(Y, s + 2 < se ? s + 2 : -1);
+      if (++s >= se) break;
+    }
+  } else if (n == 1) {
+    Batch X;
+    load(X, sb);
+    stage_and_compute(X, sb);
+  }
+
+  // ---- fixed-order reduction over the WAVES K slices
+#pragma unroll
+  for (int t = 0; t < MT; ++t)
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) red[wave][t][m][e][lane] = acc[m][t][e];
+  __syncthreads();
+  for (int t = wave; t < MT; t += WAVES) {
+    const int col = j0 + r;  // lane's weight row = output column
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int tok = t * 16 + 4 * q + e;
+      float v0 = 0.f, v1 = 0.f;
+#pragma unroll
+      for (int w = 0; w < WAVES; ++w) {
+        v0 += red[w][t][0][e][lane];
+        if (NMAT == 2) v1 += red[w][t][NMAT - 1][e][lane];
+      }
+      if (tok < M && col < N) {
+        const size_t off = (size_t)tok * N + col;
+        const float o = NMAT == 2 ? silu_mul(v0, v1) : bf2f(resid[off]) + v0;
+        out[off] = f2bf(o);
+      }
+    }
+  }
+}
+
+// Tokens per launch; the API walks larger M in chunks of this size.
+int q4_max_tokens() { return 32; }
+
+template <int NMAT, int WAVES, bool SALIGN>
+static void launch_q4_mt(const uint16_t* a, const uint8_t* q0, const uint16_t* s0,
+                         const uint8_t* q1, const uint16_t* s1, const uint16_t* rr, uint16_t* o,
+                         int M, int K, int N, hipStream_t s) {
+  const dim3 grid((unsigned)((N + 15) / 16)), block(WAVES * 64);
+  if (M <= 8)
+    hipLaunchKernelGGL((q4_stream<NMAT, 1, WAVES, SALIGN, 8>), grid, block, 0, s, a, q0, s0, q1, s1, rr, o, M, K, N);
+  else if (M <= 16)
+    hipLaunchKernelGGL((q4_stream<NMAT, 1, WAVES, SALIGN, 16>), grid, block, 0, s, a, q0, s0, q1, s1, rr, o, M, K, N);
+  else
+    hipLaunchKernelGGL((q4_stream<NMAT, 2, WAVES, SALIGN, 0>), grid, block, 0, s, a, q0, s0, q1, s1, rr, o, M, K, N);
+}
+
+template <int NMAT, int WAVES>
+static hipError_t launch_q4(const void* act, const uint8_t* q0, const uint16_t* s0,
+                            const uint8_t* q1, const uint16_t* s1, const void* resid, void* out,
+                            int M, int K, int N, hipStream_t s) {
+  const uint16_t* a = (const uint16_t*)act;
+  const uint16_t* rr = (const uint16_t*)resid;
+  uint16_t* o = (uint16_t*)out;
+  // 16-byte scale loads need every row of scales (K/16 bytes) and the base
+  // pointers 16-byte aligned
+  const bool salign = K % 256 == 0 && ((uintptr_t)s0 % 16) == 0 &&
+                      (NMAT == 1 || ((uintptr_t)s1 % 16) == 0);
+  if (salign)
+    launch_q4_mt<NMAT, WAVES, true>(a, q0, s0, q1, s1, rr, o, M, K, N, s);
+  else
+    launch_q4_mt<NMAT, WAVES, false>(a, q0, s0, q1, s1, rr, o, M, K, N, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_q4_gateup(const void* n, const uint8_t* qg, const uint16_t* sg,
+                            const uint8_t* qu, const uint16_t* su, void* h, int M, int d, int f,
+                            hipStream_t s) {
+  return launch_q4<2, 4>(n, qg, sg, qu, su, nullptr, h, M, d, f, s);
+}
+
+hipError_t launch_q4_down(const void* h, const uint8_t* qd, const uint16_t* sd, const void* x,
+                          void* y, int M, int d, int f, hipStream_t s) {
+  return launch_q4<1, 4>(h, qd, sd, nullptr, nullptr, x, y, M, f, d, s);
+}
+
+}  // namespace ffn

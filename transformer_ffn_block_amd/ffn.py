@@ -26,13 +26,20 @@ class Q8Matrix(ctypes.Structure):
     _fields_ = [("qs", ctypes.c_void_p), ("scales", ctypes.c_void_p)]
 
 
+class Q4Matrix(ctypes.Structure):
+    _fields_ = [("qs", ctypes.c_void_p), ("scales", ctypes.c_void_p)]
+
+
 _Q8P = ctypes.POINTER(Q8Matrix)
+_Q4P = ctypes.POINTER(Q4Matrix)
 SIGNATURES = [
     ("ffn_rmsnorm", _I, [_I, _VP, _VP, _VP, _I64, _I64, _F, _VP]),
     ("ffn_swiglu_block_workspace_size", _SZ, [_I, _I64, _I64, _I64, _I]),
     ("ffn_swiglu_block", _I, [_I, _VP, _VP, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _F, _I, _VP, _SZ, _VP]),
     ("ffn_swiglu_block_q8_workspace_size", _SZ, [_I64, _I64, _I64]),
     ("ffn_swiglu_block_q8", _I, [_VP, _VP, _Q8P, _Q8P, _Q8P, _VP, _I64, _I64, _I64, _F, _VP, _SZ, _VP]),
+    ("ffn_swiglu_block_q4_workspace_size", _SZ, [_I64, _I64, _I64]),
+    ("ffn_swiglu_block_q4", _I, [_VP, _VP, _Q4P, _Q4P, _Q4P, _VP, _I64, _I64, _I64, _F, _VP, _SZ, _VP]),
     ("ffn_status_string", ctypes.c_char_p, [_I]),
     ("ffn_last_error", ctypes.c_char_p, []),
     ("ffn_probe_read", _I, [_VP, _SZ, _VP, _I, _VP]),
@@ -169,6 +176,27 @@ def swiglu_block_q8(x, g, w_gate: Tuple, w_up: Tuple, w_down: Tuple, eps: float,
                                     ctypes.byref(md), _dev(y, "y"), M, d, f, eps, ws.data_ptr(),
                                     ws.numel() * ws.element_size(), _stream_handle(stream)),
           "ffn_swiglu_block_q8")
+    return y
+
+
+def q4_struct(qs, scales) -> Q4Matrix:
+    return Q4Matrix(_dev(qs, "qs"), _dev(scales, "scales"))
+
+
+def swiglu_block_q4(x, g, w_gate: Tuple, w_up: Tuple, w_down: Tuple, eps: float, out=None,
+                    workspace=None, stream=None):
+    """The block with Q4_0 weights; each weight is a (qs uint8 [N,K/2], scales int16/uint16-bits [N,K/32]) pair."""
+    torch = _torch()
+    M, d = x.shape
+    f = w_gate[0].shape[0]
+    need = lib().ffn_swiglu_block_q4_workspace_size(M, d, f)
+    ws = workspace if workspace is not None else alloc_workspace(need, x.device)
+    y = out if out is not None else torch.empty_like(x)
+    mg, mu, md = q4_struct(*w_gate), q4_struct(*w_up), q4_struct(*w_down)
+    check(lib().ffn_swiglu_block_q4(_dev(x, "x"), _dev(g, "g"), ctypes.byref(mg), ctypes.byref(mu),
+                                    ctypes.byref(md), _dev(y, "y"), M, d, f, eps, ws.data_ptr(),
+                                    ws.numel() * ws.element_size(), _stream_handle(stream)),
+          "ffn_swiglu_block_q4")
     return y
 
 
