@@ -338,9 +338,10 @@ def test_q4_full_size(gpu_lib):
 
 # M: 1..8 and 9..16 take the staged-activation kernels, 17..32 the two-tile
 # kernel, > 32 several launches; d, f not multiples of 256 leave a partial
-# last stage and use the per-block scale loads
+# last stage and use the per-block scale loads; the down projections split
+# K over 1..8 ranges (8 for d = 128, f = 4224)
 @pytest.mark.parametrize("M,d,f", [(1, 64, 32), (3, 160, 96), (12, 288, 352), (17, 512, 704),
-                                   (33, 256, 800), (70, 256, 256)])
+                                   (33, 256, 800), (70, 256, 256), (5, 128, 4224)])
 def test_q4_ragged_tokens(gpu_lib, M, d, f):
     from transformer_ffn_block_amd import ffn
     _say("q4 ragged", M, d, f)
@@ -353,7 +354,7 @@ def test_q4_subnormal_scales_are_not_flushed(gpu_lib):
     smaller than Q8_0's, so x is scaled by 2^-32 (still a normal bf16) for the
     delta to dominate y: a flush-to-zero dequantisation would return y == x."""
     from transformer_ffn_block_amd import ffn
-    q = I.make_q4_block(1900, 4, 128, 96)
+    q = I.make_q4_block(1900, 4, 128, 128)
     rng = np.random.default_rng(1901)
     for m in (q.w_gate, q.w_up, q.w_down):
         m.scales[:] = rng.integers(0x0100, 0x0400, size=m.scales.shape, dtype=np.uint16)
@@ -370,6 +371,6 @@ def test_q4_zero_point_nibbles_return_x_bitwise(gpu_lib, M):
     """Every down-projection nibble 8 (weight 0 under any scale): y = x + 0
     exactly, whatever the gate/up path computes."""
     from transformer_ffn_block_amd import ffn
-    q = I.make_q4_block(1950 + M, M, 288, 320)
+    q = I.make_q4_block(1950 + M, M, 384, 384)
     q.w_down.qs[:] = 0x88
     assert np.array_equal(_run_q4(ffn, q, bits=True), q.x)

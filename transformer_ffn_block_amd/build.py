@@ -20,7 +20,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libffn.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "rmsnorm.hip", "decode_stream.hip", "prefill.hip", "fp32.hip", "q8.hip", "q4.hip", "probes.hip"]
+SOURCES = ["api.cpp", "rmsnorm.hip", "decode_stream.hip", "prefill.hip", "fp32.hip", "q8.hip", "q4.hip", "splitk.hip", "probes.hip"]
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU ops.
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

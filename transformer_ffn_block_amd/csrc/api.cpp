@@ -285,35 +285,53 @@ namespace {
 struct Q8Traits {
   using Mat = ffn_q8_matrix;
   static constexpr const char* name = "Q8";
+  static constexpr int64_t k_multiple = 32;
   static constexpr const char* gateup_name = "q8_gateup";
   static constexpr const char* down_name = "q8_down";
   static size_t quant_bytes(size_t weights) { return weights; }
   static int max_tokens() { return ffn::q8_max_tokens(); }
+  static size_t part_bytes(int64_t, int64_t, int64_t) { return 0; }
   static hipError_t gateup(const void* n, const Mat* g, const Mat* u, void* h, int M, int d, int f,
                            hipStream_t s) {
     return ffn::launch_q8_gateup(n, g->qs, g->scales, u->qs, u->scales, h, M, d, f, s);
   }
-  static hipError_t down(const void* h, const Mat* w, const void* x, void* y, int M, int d, int f,
-                         hipStream_t s) {
+  static hipError_t down(const void* h, const Mat* w, const void* x, void* y, float*, int M, int d,
+                         int f, hipStream_t s) {
     return ffn::launch_q8_down(h, w->qs, w->scales, x, y, M, d, f, s);
   }
 };
 struct Q4Traits {
   using Mat = ffn_q4_matrix;
   static constexpr const char* name = "Q4";
+  static constexpr int64_t k_multiple = 32;
   static constexpr const char* gateup_name = "q4_gateup";
   static constexpr const char* down_name = "q4_down";
   static size_t quant_bytes(size_t weights) { return weights / 2; }
   static int max_tokens() { return ffn::q4_max_tokens(); }
+  // fp32 partial sums of the split-K down projection for Mc tokens
+  static size_t part_bytes(int64_t Mc, int64_t d, int64_t f) {
+    const int sp = ffn::q4_down_splits((int)d, (int)f);
+    return sp > 1 ? (size_t)sp * (size_t)Mc * (size_t)d * 4 : 0;
+  }
   static hipError_t gateup(const void* n, const Mat* g, const Mat* u, void* h, int M, int d, int f,
                            hipStream_t s) {
     return ffn::launch_q4_gateup(n, g->qs, g->scales, u->qs, u->scales, h, M, d, f, s);
   }
-  static hipError_t down(const void* h, const Mat* w, const void* x, void* y, int M, int d, int f,
-                         hipStream_t s) {
-    return ffn::launch_q4_down(h, w->qs, w->scales, x, y, M, d, f, s);
+  static hipError_t down(const void* h, const Mat* w, const void* x, void* y, float* part, int M,
+                         int d, int f, hipStream_t s) {
+    return ffn::launch_q4_down(h, w->qs, w->scales, x, y, part, M, d, f, s);
   }
 };
+
+// Workspace of a quantised block: n [M,d] and h [M,f] in bf16, then the
+// down projection's split-K partials for one chunk of tokens.
+template <class T>
+static size_t quant_ws_bytes(int64_t M, int64_t d, int64_t f, size_t* part_at) {
+  const WsLayout L = ws_layout(2, M, d, f, false);
+  const int64_t mc = M < T::max_tokens() ? M : T::max_tokens();
+  if (part_at) *part_at = L.total;
+  return L.total + round256(T::part_bytes(mc, d, f));
+}
 
 template <class T>
 static ffn_status quant_block(const void* x, const void* g, const typename T::Mat* w_gate,
@@ -329,20 +347,22 @@ static ffn_status quant_block(const void* x, const void* g, const typename T::Ma
       return fail(FFN_ERR_UNSUPPORTED, "%s quants must be 16-byte aligned, scales 2-byte", T::name);
   }
   FFN_TRY(check_eps(eps));
-  FFN_TRY(check_block_dims(M, d, f, 32));
+  FFN_TRY(check_block_dims(M, d, f, T::k_multiple));
   if (T::quant_bytes((size_t)f * d) >= ((size_t)1 << 31))
     return fail(FFN_ERR_UNSUPPORTED, "%s quant arrays must be smaller than 2 GiB", T::name);
   if (!aligned(x, 16) || !aligned(g, 16) || !aligned(y, 16))
     return fail(FFN_ERR_UNSUPPORTED, "x, g and y must be 16-byte aligned");
   const WsLayout L = ws_layout(2, M, d, f, false);
-  if (M > 0 && (!workspace || workspace_bytes < L.total))
-    return fail(FFN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total,
+  size_t part_at = 0;
+  const size_t ws_total = quant_ws_bytes<T>(M, d, f, &part_at);
+  if (M > 0 && (!workspace || workspace_bytes < ws_total))
+    return fail(FFN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", ws_total,
                 workspace ? workspace_bytes : (size_t)0);
   if (workspace && !aligned(workspace, 256))
     return fail(FFN_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
   const size_t ny = (size_t)M * d * 2, nq = T::quant_bytes((size_t)f * d), ns = (size_t)f * d / 32 * 2;
   bool ov = overlap(y, ny, x, ny) || overlap(y, ny, g, (size_t)d * 2) ||
-            overlap(y, ny, workspace, workspace ? L.total : 0);
+            overlap(y, ny, workspace, workspace ? ws_total : 0);
   for (const typename T::Mat* m : mats)
     ov = ov || overlap(y, ny, m->qs, nq) || overlap(y, ny, m->scales, ns);
   if (ov) return fail(FFN_ERR_INVALID_ARGUMENT, "y overlaps an input or the workspace");
@@ -352,6 +372,7 @@ static ffn_status quant_block(const void* x, const void* g, const typename T::Ma
   char* ws = (char*)workspace;
   char* n = ws + L.n;
   char* h = ws + L.h;
+  float* part = (float*)(ws + part_at);
   FFN_LAUNCH("rmsnorm", s, ffn::launch_rmsnorm(2, x, g, n, M, d, eps, s));
   const int step = T::max_tokens();
   for (int64_t m0 = 0; m0 < M; m0 += step) {
@@ -360,7 +381,7 @@ static ffn_status quant_block(const void* x, const void* g, const typename T::Ma
                T::gateup(n + m0 * d * 2, w_gate, w_up, h + m0 * f * 2, mc, (int)d, (int)f, s));
     FFN_LAUNCH(T::down_name, s,
                T::down(h + m0 * f * 2, w_down, (const char*)x + m0 * d * 2, (char*)y + m0 * d * 2,
-                       mc, (int)d, (int)f, s));
+                       part, mc, (int)d, (int)f, s));
   }
   return ok();
 }
@@ -370,8 +391,8 @@ static ffn_status quant_block(const void* x, const void* g, const typename T::Ma
 extern "C" {
 
 size_t ffn_swiglu_block_q8_workspace_size(int64_t M, int64_t d, int64_t f) {
-  if (M < 0 || d <= 0 || f <= 0) return 0;
-  return ws_layout(2, M, d, f, false).total;
+  if (M < 0 || d <= 0 || f <= 0 || d > INT32_MAX || f > INT32_MAX) return 0;
+  return quant_ws_bytes<Q8Traits>(M, d, f, nullptr);
 }
 
 ffn_status ffn_swiglu_block_q8(const void* x, const void* g, const ffn_q8_matrix* w_gate,
@@ -383,8 +404,8 @@ ffn_status ffn_swiglu_block_q8(const void* x, const void* g, const ffn_q8_matrix
 }
 
 size_t ffn_swiglu_block_q4_workspace_size(int64_t M, int64_t d, int64_t f) {
-  if (M < 0 || d <= 0 || f <= 0) return 0;
-  return ws_layout(2, M, d, f, false).total;
+  if (M < 0 || d <= 0 || f <= 0 || d > INT32_MAX || f > INT32_MAX) return 0;
+  return quant_ws_bytes<Q4Traits>(M, d, f, nullptr);
 }
 
 ffn_status ffn_swiglu_block_q4(const void* x, const void* g, const ffn_q4_matrix* w_gate,

@@ -55,9 +55,19 @@ int q8_max_tokens();
 hipError_t launch_q4_gateup(const void* n, const uint8_t* qg, const uint16_t* sg,
                             const uint8_t* qu, const uint16_t* su, void* h, int M, int d, int f,
                             hipStream_t s);
+// Down projection, split over K into q4_down_splits(d, f) ranges when that
+// is above 1: the fp32 partial sums go to part[splits][M][d] (caller's
+// workspace) and launch_splitk_residual adds them to x in range order.
+constexpr int kQ4MaxSplits = 8;
+int q4_down_splits(int N, int K);
 hipError_t launch_q4_down(const void* h, const uint8_t* qd, const uint16_t* sd, const void* x,
-                          void* y, int M, int d, int f, hipStream_t s);
+                          void* y, float* part, int M, int d, int f, hipStream_t s);
 int q4_max_tokens();
+
+// y[m,i] = bf16(x[m,i] + sum_{z < splits} part[z][m][i]), summed in z order
+// (N % 8 == 0).
+hipError_t launch_splitk_residual(const float* part, int splits, const void* x, void* y, int M,
+                                  int N, hipStream_t s);
 
 // Bandwidth probes.
 int probe_read_groups(int waves_per_cu);

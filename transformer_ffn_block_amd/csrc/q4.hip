@@ -16,10 +16,17 @@
 // v_mfma_f32_16x16x32_bf16, so the scale factors out of the block's dot
 // product.  Lane (r, q) feeds weights 8q..8q+7 of a block of row r: the low
 // nibbles (q < 2) or high nibbles (q >= 2) of bytes 8(q & 1) .. 8(q & 1) + 7.
-// A nibble n is moved to the top half of its byte and xor-ed with 0x80, which
-// makes the byte the int8 value 16 (n - 8); sign-extending byte conversion
-// then yields 16 (n - 8) exactly in bf16, and the lane scales the block's
-// partial by s / 16 (exact in fp32): the dequantisation adds no rounding.
+// Converting nibbles one by one through integer-to-float instructions costs
+// about three VALU operations per weight, which made the kernel VALU-bound.
+// Instead the lane masks its nibbles into the low four bits of each byte and
+// byte-permutes them under the constant 0x43: the bf16 pattern 0x430n is
+// exactly 128 + n (bf16 128.0 with n in the last mantissa bits), four
+// operations per four weights.  The offset goes into the MFMA's initial
+// accumulator: C = sum_k a_k * (-136), one extra MFMA per block shared by the
+// gate and up matrices, so the MFMA returns sum_k a_k (n_k - 8).  Every
+// product is exact in fp32; the fp32 sums run ~30x larger than the result,
+// costing ~5 of fp32's 24 bits (relative error ~2^-19 of the partial, far
+// below the bf16 rounding of the activations).
 //
 // Streaming: a workgroup owns 16 weight rows (per matrix); its waves split K
 // into 256-k stages (128 bytes per row).  Each matrix's stage is 16 rows x 8
@@ -30,39 +37,72 @@
 // an out-of-range buffer offset and read nothing.  Scales, activations, the
 // two-batch pipeline and the fixed-order cross-wave reduction are those of
 // the Q8_0 kernels.
+//
+// Split-K down projection.  With d = 5120 outputs the down projection has
+// only 320 row tiles for 256 compute units: a quarter of the units get two
+// tiles and set the kernel's length.  The K axis is therefore split into a
+// few contiguous ranges (enough for ~1024 workgroups); each workgroup writes
+// its fp32 partial tile and a second kernel adds the ranges in order, plus
+// the residual (deterministic, no atomics).  Measured per-wave timelines
+// show these kernels limited by the latency of each stage's dependent chain
+// (loads, LDS staging, conversion, MFMA, scaling) at one to four waves per
+// SIMD rather than by HBM: with every global load removed a 5120 x 17408
+// projection still takes ~14 us.  A dword-interleaved nibble layout that
+// skipped the LDS stage (16 rows x 64 B per load) was slower, as were two
+// row tiles per wave, more or fewer waves per workgroup and rotated stage
+// orders.
 #include "common.h"
 #include "launch.h"
 
+#ifndef FFN_Q4_GU_WAVES
+#define FFN_Q4_GU_WAVES 4
+#endif
+#ifndef FFN_Q4_DN_WAVES
+#define FFN_Q4_DN_WAVES 4
+#endif
+#ifndef FFN_Q4_DN_SPLIT_TARGET
+#define FFN_Q4_DN_SPLIT_TARGET 1024
+#endif
+
 namespace ffn {
 
-// 8 nibbles of one half (low: hi_half false) of bytes lo..hi -> 8 bf16 of
-// 16 * (nibble - 8)
-__device__ __forceinline__ uint4 q4x8_to_bf16(uint32_t lo, uint32_t hi, bool high_half) {
-  const uint32_t a = (high_half ? lo : lo << 4) & 0xF0F0F0F0u;
-  const uint32_t b = (high_half ? hi : hi << 4) & 0xF0F0F0F0u;
-  const uint32_t sa = a ^ 0x80808080u, sb = b ^ 0x80808080u;
-  float f[8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    f[i] = (float)(((int)(sa << (24 - 8 * i))) >> 24);
-    f[4 + i] = (float)(((int)(sb << (24 - 8 * i))) >> 24);
-  }
-  return pack8(f);
+// 8 nibbles of bytes lo (0..3), hi (4..7), the low ones (shift 0) or the
+// high ones (shift 4) -> 8 bf16 of value 128 + nibble, in byte order.
+// v_perm_b32(s0, s1, sel): result byte i = byte sel_i of the 8-byte value
+// s0:s1 (selectors 0..3 pick s1, 4..7 pick s0).
+__device__ __forceinline__ uint4 q4x8_to_bf16_biased(uint32_t lo, uint32_t hi, uint32_t shift) {
+  constexpr uint32_t kExp = 0x43434343u;  // high byte of bf16 128.0
+  const uint32_t a = (lo >> shift) & 0x0F0F0F0Fu;
+  const uint32_t b = (hi >> shift) & 0x0F0F0F0Fu;
+  uint4 o;
+  o.x = __builtin_amdgcn_perm(kExp, a, 0x04010400u);  // {0x43, n1, 0x43, n0} -> 128+n0, 128+n1
+  o.y = __builtin_amdgcn_perm(kExp, a, 0x04030402u);
+  o.z = __builtin_amdgcn_perm(kExp, b, 0x04010400u);
+  o.w = __builtin_amdgcn_perm(kExp, b, 0x04030402u);
+  return o;
 }
+
+// 8 copies of bf16 -136.0 (0xC308): the MFMA B operand of the offset term
+constexpr uint32_t kNegOffsetPair = 0xC308C308u;
 
 __device__ __forceinline__ float q4_f16bits_to_f32(uint32_t b) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
 }
 
-template <int NMAT, int MT, int WAVES, bool SALIGN, int ASTAGE>
+// PART: split-K pass (NMAT == 1): workgroup (tile, z) covers the z-th of
+// gridDim.y contiguous ranges of stages and writes its fp32 partial sums to
+// part[z][M][N] (no residual); a fixed-order reduce adds them up.
+template <int NMAT, int MT, int WAVES, bool SALIGN, int ASTAGE, bool PART>
 __global__ __launch_bounds__(WAVES * 64) void q4_stream(
     const uint16_t* __restrict__ act,     // [M, K] bf16: n or h
     const uint8_t* __restrict__ q0, const uint16_t* __restrict__ s0,  // [N, K/2], [N, K/32]
     const uint8_t* __restrict__ q1, const uint16_t* __restrict__ s1,
-    const uint16_t* __restrict__ resid,   // [M, N] (NMAT == 1)
-    uint16_t* __restrict__ out,           // [M, N]
+    const uint16_t* __restrict__ resid,   // [M, N] (NMAT == 1, !PART)
+    uint16_t* __restrict__ out,           // [M, N] (!PART)
+    float* __restrict__ part,             // [gridDim.y, M, N] (PART)
     int M, int K, int N) {
-  constexpr int SB = 8;  // 32-weight blocks per stage (256 k, 128 B per row)
+  constexpr int SB = 8;        // 32-weight blocks per stage (256 k, 128 B per row)
+  constexpr int NU = 2;        // nibble load instructions per matrix per stage (8 rows each)
   __shared__ uint4 wb[WAVES][NMAT][128];           // per-wave nibble stage (2 KiB per matrix)
   __shared__ float red[WAVES][MT][NMAT][4][64];
   __shared__ uint4 abuf[WAVES][ASTAGE ? ASTAGE * 32 : 1];  // per-wave activation stage [rows][32]
@@ -75,8 +115,10 @@ __global__ __launch_bounds__(WAVES * 64) void q4_stream(
   const int K32 = K >> 5;               // 16-byte nibble chunks per row (one per block)
   const int K8 = K >> 3;                // 16-byte activation chunks per row
   const int nst = (nb + SB - 1) / SB;
-  const int sb = (int)(((long)nst * wave) / WAVES);
-  const int se = (int)(((long)nst * (wave + 1)) / WAVES);
+  const int zs = PART ? (int)(((long)nst * blockIdx.y) / gridDim.y) : 0;        // this split's stages
+  const int ze = PART ? (int)(((long)nst * (blockIdx.y + 1)) / gridDim.y) : nst;
+  const int sb = zs + (int)(((long)(ze - zs) * wave) / WAVES);
+  const int se = zs + (int)(((long)(ze - zs) * (wave + 1)) / WAVES);
 
   // staged loads: instruction u covers rows 8u..8u+7; lane -> row 8u + lane/8,
   // LDS slot u*64 + lane, which holds chunk (lane%8 - row/2) & 7 of the row's
@@ -85,10 +127,10 @@ __global__ __launch_bounds__(WAVES * 64) void q4_stream(
   __amdgpu_buffer_rsrc_t rq[NMAT];  // nibbles through buffer resources (< 2 GiB)
   rq[0] = make_rsrc(q0, (long)N * (K / 2));
   if (NMAT == 2) rq[NMAT - 1] = make_rsrc(q1, (long)N * (K / 2));
-  unsigned gq[2];  // byte offset of this lane's row in each instruction
-  int cst[2];
+  unsigned gq[NU];  // byte offset of this lane's row in each instruction
+  int cst[NU];
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
+  for (int u = 0; u < NU; ++u) {
     const int rr = 8 * u + (lane >> 3);
     const int row = min(j0 + rr, N - 1);  // rows past N: clamped, never stored
     cst[u] = ((lane & 7) - (rr >> 1)) & 7;
@@ -122,9 +164,11 @@ __global__ __launch_bounds__(WAVES * 64) void q4_stream(
     for (int m = 0; m < NMAT; ++m) acc[m][t] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+  const uint4 negoff = make_uint4(kNegOffsetPair, kNegOffsetPair, kNegOffsetPair, kNegOffsetPair);
+  const uint32_t nib_shift = (uint32_t)(q >> 1) * 4u;  // lanes q >= 2 take the high nibbles
 
   struct Batch {
-    uint4 w[NMAT][2];
+    uint4 w[NMAT][NU];
     uint4 s[NMAT];  // SALIGN: the stage's 8 scales of row r; else .x = blocks 2q, 2q+1
     uint4 a[NA];
   };
@@ -133,7 +177,7 @@ __global__ __launch_bounds__(WAVES * 64) void q4_stream(
   auto load = [&](Batch& B, int st_req) {
     const int st = st_req < 0 ? se - 1 : st_req;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < NU; ++u) {
       const int c = min(st * 8 + cst[u], K32 - 1);
       const unsigned o = st_req < 0 ? kOutOfRange : gq[u] + (unsigned)c * 16u;
 #pragma unroll
@@ -167,7 +211,7 @@ __global__ __launch_bounds__(WAVES * 64) void q4_stream(
   auto stage_and_compute = [&](const Batch& B, int st) {
     const bool ragged = (st + 1) * SB > nb;  // only a row's last stage can be partial
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < NU; ++u) {
 #pragma unroll
       for (int m = 0; m < NMAT; ++m) {
         uint4 x = B.w[m][u];
@@ -199,6 +243,8 @@ __global__ __launch_bounds__(WAVES * 64) void q4_stream(
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
           if (ASTAGE) {
+            // token r, chunk 4b + q of the stage; with 8 staged rows, lanes of
+            // rows 8..15 re-read rows 0..7 (those outputs are never stored)
             const int ar = r & (ASTAGE ? ASTAGE - 1 : 0);
             aa[t] = abuf[wave][ASTAGE ? ar * 32 + ((4 * b + q + ar) & 31) : 0];
           } else {
@@ -206,23 +252,26 @@ __global__ __launch_bounds__(WAVES * 64) void q4_stream(
             if (ragged) aa[t] = keep_or_zero(st * SB + b < nb, aa[t]);
           }
         }
-        // block b of row r: chunk b of the stage, bytes 8(q & 1) .. +8
-        const int slot = r * 8 + ((b + (r >> 1)) & 7);
+        // offset term -136 * sum_k a_k of each token, shared by the matrices
+        f32x4 c0[MT];
+#pragma unroll
+        for (int t = 0; t < MT; ++t) c0[t] = mfma16(aa[t], negoff, z4);
         const int src_lane = r + 16 * (b >> 1);  // the lane of row r holding block b's scale
+        // block b of row r: chunk b of the row's stage segment, bytes 8(q & 1) .. +8
+        const int slot = r * 8 + ((b + (r >> 1)) & 7);
 #pragma unroll
         for (int m = 0; m < NMAT; ++m) {
           const uint2 qv = reinterpret_cast<const uint2*>(&wb[wave][m][slot])[q & 1];
-          const uint4 Bq = q4x8_to_bf16(qv.x, qv.y, q >= 2);
+          const uint4 Bq = q4x8_to_bf16_biased(qv.x, qv.y, nib_shift);
           uint32_t pair;
           if (SALIGN) {
             pair = (b >> 1) == 0 ? B.s[m].x : (b >> 1) == 1 ? B.s[m].y : (b >> 1) == 2 ? B.s[m].z : B.s[m].w;
           } else {
             pair = (uint32_t)__shfl((int)B.s[m].x, src_lane, 64);
           }
-          // the MFMA sees 16 (n - 8): scale by s / 16
-          scv[bb][m] = q4_f16bits_to_f32((b & 1) ? (pair >> 16) : (pair & 0xFFFFu)) * 0.0625f;
+          scv[bb][m] = q4_f16bits_to_f32((b & 1) ? (pair >> 16) : (pair & 0xFFFFu));
 #pragma unroll
-          for (int t = 0; t < MT; ++t) p[bb][m][t] = mfma16(aa[t], Bq, z4);
+          for (int t = 0; t < MT; ++t) p[bb][m][t] = mfma16(aa[t], Bq, c0[t]);
         }
       }
 #pragma unroll
@@ -278,8 +327,12 @@ __global__ __launch_bounds__(WAVES * 64) void q4_stream(
       }
       if (tok < M && col < N) {
         const size_t off = (size_t)tok * N + col;
-        const float o = NMAT == 2 ? silu_mul(v0, v1) : bf2f(resid[off]) + v0;
-        out[off] = f2bf(o);
+        if (PART) {
+          part[(size_t)blockIdx.y * M * N + off] = v0;
+        } else {
+          const float o = NMAT == 2 ? silu_mul(v0, v1) : bf2f(resid[off]) + v0;
+          out[off] = f2bf(o);
+        }
       }
     }
   }
@@ -288,46 +341,65 @@ __global__ __launch_bounds__(WAVES * 64) void q4_stream(
 // Tokens per launch; the API walks larger M in chunks of this size.
 int q4_max_tokens() { return 32; }
 
-template <int NMAT, int WAVES, bool SALIGN>
+template <int NMAT, int WAVES, bool SALIGN, bool PART>
 static void launch_q4_mt(const uint16_t* a, const uint8_t* q0, const uint16_t* s0,
                          const uint8_t* q1, const uint16_t* s1, const uint16_t* rr, uint16_t* o,
-                         int M, int K, int N, hipStream_t s) {
-  const dim3 grid((unsigned)((N + 15) / 16)), block(WAVES * 64);
+                         float* part, int splits, int M, int K, int N, hipStream_t s) {
+  const dim3 grid((unsigned)((N + 15) / 16), (unsigned)splits), block(WAVES * 64);
   if (M <= 8)
-    hipLaunchKernelGGL((q4_stream<NMAT, 1, WAVES, SALIGN, 8>), grid, block, 0, s, a, q0, s0, q1, s1, rr, o, M, K, N);
+    hipLaunchKernelGGL((q4_stream<NMAT, 1, WAVES, SALIGN, 8, PART>), grid, block, 0, s, a, q0, s0, q1, s1, rr, o, part, M, K, N);
   else if (M <= 16)
-    hipLaunchKernelGGL((q4_stream<NMAT, 1, WAVES, SALIGN, 16>), grid, block, 0, s, a, q0, s0, q1, s1, rr, o, M, K, N);
+    hipLaunchKernelGGL((q4_stream<NMAT, 1, WAVES, SALIGN, 16, PART>), grid, block, 0, s, a, q0, s0, q1, s1, rr, o, part, M, K, N);
   else
-    hipLaunchKernelGGL((q4_stream<NMAT, 2, WAVES, SALIGN, 0>), grid, block, 0, s, a, q0, s0, q1, s1, rr, o, M, K, N);
+    hipLaunchKernelGGL((q4_stream<NMAT, 2, WAVES, SALIGN, 0, PART>), grid, block, 0, s, a, q0, s0, q1, s1, rr, o, part, M, K, N);
 }
 
-template <int NMAT, int WAVES>
-static hipError_t launch_q4(const void* act, const uint8_t* q0, const uint16_t* s0,
-                            const uint8_t* q1, const uint16_t* s1, const void* resid, void* out,
-                            int M, int K, int N, hipStream_t s) {
-  const uint16_t* a = (const uint16_t*)act;
-  const uint16_t* rr = (const uint16_t*)resid;
-  uint16_t* o = (uint16_t*)out;
-  // 16-byte scale loads need every row of scales (K/16 bytes) and the base
-  // pointers 16-byte aligned
-  const bool salign = K % 256 == 0 && ((uintptr_t)s0 % 16) == 0 &&
-                      (NMAT == 1 || ((uintptr_t)s1 % 16) == 0);
-  if (salign)
-    launch_q4_mt<NMAT, WAVES, true>(a, q0, s0, q1, s1, rr, o, M, K, N, s);
-  else
-    launch_q4_mt<NMAT, WAVES, false>(a, q0, s0, q1, s1, rr, o, M, K, N, s);
-  return hipGetLastError();
+// 16-byte scale loads need every row of scales (K/16 bytes) and the base
+// pointers 16-byte aligned
+static bool q4_scales_aligned(int K, const uint16_t* s0, const uint16_t* s1) {
+  return K % 256 == 0 && ((uintptr_t)s0 % 16) == 0 && (s1 == nullptr || ((uintptr_t)s1 % 16) == 0);
 }
 
 hipError_t launch_q4_gateup(const void* n, const uint8_t* qg, const uint16_t* sg,
                             const uint8_t* qu, const uint16_t* su, void* h, int M, int d, int f,
                             hipStream_t s) {
-  return launch_q4<2, 4>(n, qg, sg, qu, su, nullptr, h, M, d, f, s);
+  constexpr int W = FFN_Q4_GU_WAVES;
+  const uint16_t* a = (const uint16_t*)n;
+  if (q4_scales_aligned(d, sg, su))
+    launch_q4_mt<2, W, true, false>(a, qg, sg, qu, su, nullptr, (uint16_t*)h, nullptr, 1, M, d, f, s);
+  else
+    launch_q4_mt<2, W, false, false>(a, qg, sg, qu, su, nullptr, (uint16_t*)h, nullptr, 1, M, d, f, s);
+  return hipGetLastError();
+}
+
+// Split-K factor of the down projection: enough (row tile, K range) workgroups
+// for about FFN_Q4_DN_SPLIT_TARGET of them in total (4 per compute unit on
+// 256 compute units), at most 8 ranges and no more than the 256-k stages.
+int q4_down_splits(int N, int K) {
+  const int target = FFN_Q4_DN_SPLIT_TARGET;
+  const int tiles = (N + 15) / 16;
+  const int nst = (K / 32 + 7) / 8;
+  int sp = target > 0 ? (target + tiles - 1) / tiles : 1;
+  sp = sp < 1 ? 1 : sp > kQ4MaxSplits ? kQ4MaxSplits : sp;
+  return sp > nst ? (nst > 0 ? nst : 1) : sp;
 }
 
 hipError_t launch_q4_down(const void* h, const uint8_t* qd, const uint16_t* sd, const void* x,
-                          void* y, int M, int d, int f, hipStream_t s) {
-  return launch_q4<1, 4>(h, qd, sd, nullptr, nullptr, x, y, M, f, d, s);
+                          void* y, float* part, int M, int d, int f, hipStream_t s) {
+  constexpr int W = FFN_Q4_DN_WAVES;
+  const uint16_t* a = (const uint16_t*)h;
+  const int sp = q4_down_splits(d, f);
+  const bool al = q4_scales_aligned(f, sd, nullptr);
+  if (sp == 1) {
+    if (al) launch_q4_mt<1, W, true, false>(a, qd, sd, nullptr, nullptr, (const uint16_t*)x, (uint16_t*)y, nullptr, 1, M, f, d, s);
+    else launch_q4_mt<1, W, false, false>(a, qd, sd, nullptr, nullptr, (const uint16_t*)x, (uint16_t*)y, nullptr, 1, M, f, d, s);
+    return hipGetLastError();
+  }
+  if (al) launch_q4_mt<1, W, true, true>(a, qd, sd, nullptr, nullptr, nullptr, nullptr, part, sp, M, f, d, s);
+  else launch_q4_mt<1, W, false, true>(a, qd, sd, nullptr, nullptr, nullptr, nullptr, part, sp, M, f, d, s);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_splitk_residual(part, sp, x, y, M, d, s);
 }
 
 }  // namespace ffn
