@@ -136,7 +136,10 @@ ffn_status ffn_swiglu_block(ffn_dtype dt, const void *x, const void *g,
                             ffn_variant variant, void *workspace, size_t workspace_bytes,
                             void *stream);
 
-/* Workspace bytes ffn_swiglu_block_q8 needs (n [M,d] and h [M,f] in bf16). */
+/* Workspace bytes ffn_swiglu_block_q8 needs: n [M,d] and h [M,f] in bf16,
+ * then the fp32 partial sums of the split-K down projection,
+ * [splits, min(M, 32), d] (splits, 1..8, is fixed by d and f); 0 on a shape
+ * the entry point would reject for its sizes. */
 size_t ffn_swiglu_block_q8_workspace_size(int64_t M, int64_t d, int64_t f);
 
 /* The block with Q8_0 weights, bf16 activations:

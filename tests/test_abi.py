@@ -102,9 +102,10 @@ def test_workspace_sizes(L):
     assert split == fused + 2 * r256(M * f * 2)
     assert L.ffn_swiglu_block_workspace_size(ffn.FFN_F32, 8, 256, 704, 0) == r256(8 * 256 * 4) + r256(8 * 704 * 4)
     assert L.ffn_swiglu_block_workspace_size(5, M, d, f, 0) == 0
-    assert L.ffn_swiglu_block_q8_workspace_size(8, 5120, 17408) == r256(8 * 5120 * 2) + r256(8 * 17408 * 2)
-    # Q4_0: plus the split-K partials of the down projection, 4 K ranges for
-    # 320 output tiles, [4, min(M, 32), d] fp32
+    # quantised blocks: plus the split-K partials of the down projection, 4 K
+    # ranges for 320 output tiles, [4, min(M, 32), d] fp32
+    assert L.ffn_swiglu_block_q8_workspace_size(8, 5120, 17408) == \
+        r256(8 * 5120 * 2) + r256(8 * 17408 * 2) + 4 * 8 * 5120 * 4
     assert L.ffn_swiglu_block_q4_workspace_size(8, 5120, 17408) == \
         r256(8 * 5120 * 2) + r256(8 * 17408 * 2) + 4 * 8 * 5120 * 4
     assert L.ffn_swiglu_block_q4_workspace_size(100, 5120, 17408) == \

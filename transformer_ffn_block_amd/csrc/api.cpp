@@ -290,14 +290,18 @@ struct Q8Traits {
   static constexpr const char* down_name = "q8_down";
   static size_t quant_bytes(size_t weights) { return weights; }
   static int max_tokens() { return ffn::q8_max_tokens(); }
-  static size_t part_bytes(int64_t, int64_t, int64_t) { return 0; }
+  // fp32 partial sums of the split-K down projection for Mc tokens
+  static size_t part_bytes(int64_t Mc, int64_t d, int64_t f) {
+    const int sp = ffn::q8_down_splits((int)d, (int)f);
+    return sp > 1 ? (size_t)sp * (size_t)Mc * (size_t)d * 4 : 0;
+  }
   static hipError_t gateup(const void* n, const Mat* g, const Mat* u, void* h, int M, int d, int f,
                            hipStream_t s) {
     return ffn::launch_q8_gateup(n, g->qs, g->scales, u->qs, u->scales, h, M, d, f, s);
   }
-  static hipError_t down(const void* h, const Mat* w, const void* x, void* y, float*, int M, int d,
-                         int f, hipStream_t s) {
-    return ffn::launch_q8_down(h, w->qs, w->scales, x, y, M, d, f, s);
+  static hipError_t down(const void* h, const Mat* w, const void* x, void* y, float* part, int M,
+                         int d, int f, hipStream_t s) {
+    return ffn::launch_q8_down(h, w->qs, w->scales, x, y, part, M, d, f, s);
   }
 };
 struct Q4Traits {

@@ -40,14 +40,20 @@ hipError_t launch_gemm_f32(int epi, const float* a, const float* w0, const float
 hipError_t launch_swiglu_f32(const float* G, const float* U, float* h, int64_t count,
                              hipStream_t s);
 
+// Most K ranges of a split-K down projection (quantised blocks).
+constexpr int kQuantMaxSplits = 8;
+
 // Q8_0 weight-streaming projections (bf16 activations, in-register dequant).
 //   gate/up: h = silu(n Wg^T) * (n Wu^T)
 //   down   : y = x + h Wd^T
 hipError_t launch_q8_gateup(const void* n, const int8_t* qg, const uint16_t* sg,
                             const int8_t* qu, const uint16_t* su, void* h, int M, int d, int f,
                             hipStream_t s);
+// Down projection, split over K into q8_down_splits(d, f) ranges when that
+// is above 1 (partials in part[splits][M][d], as for Q4_0 below).
+int q8_down_splits(int N, int K);
 hipError_t launch_q8_down(const void* h, const int8_t* qd, const uint16_t* sd, const void* x,
-                          void* y, int M, int d, int f, hipStream_t s);
+                          void* y, float* part, int M, int d, int f, hipStream_t s);
 int q8_max_tokens();
 
 // Q4_0 weight-streaming projections (split nibble / scale arrays, bf16
@@ -58,7 +64,6 @@ hipError_t launch_q4_gateup(const void* n, const uint8_t* qg, const uint16_t* sg
 // Down projection, split over K into q4_down_splits(d, f) ranges when that
 // is above 1: the fp32 partial sums go to part[splits][M][d] (caller's
 // workspace) and launch_splitk_residual adds them to x in range order.
-constexpr int kQ4MaxSplits = 8;
 int q4_down_splits(int N, int K);
 hipError_t launch_q4_down(const void* h, const uint8_t* qd, const uint16_t* sd, const void* x,
                           void* y, float* part, int M, int d, int f, hipStream_t s);

@@ -380,7 +380,7 @@ int q4_down_splits(int N, int K) {
   const int tiles = (N + 15) / 16;
   const int nst = (K / 32 + 7) / 8;
   int sp = target > 0 ? (target + tiles - 1) / tiles : 1;
-  sp = sp < 1 ? 1 : sp > kQ4MaxSplits ? kQ4MaxSplits : sp;
+  sp = sp < 1 ? 1 : sp > kQuantMaxSplits ? kQuantMaxSplits : sp;
   return sp > nst ? (nst > 0 ? nst : 1) : sp;
 }
 

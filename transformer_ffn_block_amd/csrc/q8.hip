@@ -35,6 +35,9 @@
 // tiles are reduced across waves in a fixed order.
 // Activation rows past M are clamped copies of row M-1: they only feed
 // output rows that are never stored, so they need no masking.
+// The down projection (320 row tiles at d = 5120) splits its K axis into a
+// few ranges with two waves per workgroup, as the Q4_0 one does; the ranges'
+// fp32 partials are added in order by launch_splitk_residual.
 #include "common.h"
 #include "launch.h"
 
@@ -42,7 +45,10 @@
 #define FFN_Q8_GU_WAVES 4
 #endif
 #ifndef FFN_Q8_DN_WAVES
-#define FFN_Q8_DN_WAVES 4
+#define FFN_Q8_DN_WAVES 2
+#endif
+#ifndef FFN_Q8_DN_SPLIT_TARGET
+#define FFN_Q8_DN_SPLIT_TARGET 1024
 #endif
 
 #ifndef FFN_STREAM_WPE
@@ -72,13 +78,17 @@ __device__ __forceinline__ float f16bits_to_f32(uint32_t b) {
 // ASTAGE: 0 = activations read straight from L2 in the MFMA operand layout;
 // 8 = 8 token rows, 16 = 16 token rows fetched as 512-byte token segments and
 // staged through LDS (fewer, fuller cache-line requests).
-template <int NMAT, int MT, int WAVES, bool SALIGN, int ASTAGE>
+// PART: split-K pass (NMAT == 1): workgroup (tile, z) covers the z-th of
+// gridDim.y contiguous ranges of stages and writes fp32 partial sums to
+// part[z][M][N]; launch_splitk_residual adds the ranges in order.
+template <int NMAT, int MT, int WAVES, bool SALIGN, int ASTAGE, bool PART>
 __global__ __launch_bounds__(WAVES * 64) FFN_STREAM_ATTR void q8_stream(
     const uint16_t* __restrict__ act,     // [M, K] bf16: n or h
     const int8_t* __restrict__ q0, const uint16_t* __restrict__ s0,  // [N, K], [N, K/32]
     const int8_t* __restrict__ q1, const uint16_t* __restrict__ s1,
     const uint16_t* __restrict__ resid,   // [M, N] (NMAT == 1)
-    uint16_t* __restrict__ out,           // [M, N]
+    uint16_t* __restrict__ out,           // [M, N] (!PART)
+    float* __restrict__ part,             // [gridDim.y, M, N] (PART)
     int M, int K, int N) {
   constexpr int SB = 8;  // 32-quant blocks per stage (256 k, 256 B per row)
   __shared__ uint4 wb[WAVES][NMAT][256];           // per-wave quant stage (4 KiB per matrix)
@@ -93,8 +103,10 @@ __global__ __launch_bounds__(WAVES * 64) FFN_STREAM_ATTR void q8_stream(
   const int K16 = K >> 4;               // 16-byte quant chunks per row
   const int K8 = K >> 3;                // 16-byte activation chunks per row
   const int nst = (nb + SB - 1) / SB;
-  const int sb = (int)(((long)nst * wave) / WAVES);
-  const int se = (int)(((long)nst * (wave + 1)) / WAVES);
+  const int zs = PART ? (int)(((long)nst * blockIdx.y) / gridDim.y) : 0;  // this split's stages
+  const int ze = PART ? (int)(((long)nst * (blockIdx.y + 1)) / gridDim.y) : nst;
+  const int sb = zs + (int)(((long)(ze - zs) * wave) / WAVES);
+  const int se = zs + (int)(((long)(ze - zs) * (wave + 1)) / WAVES);
 
   // staged loads: instruction u covers tile rows 4u..4u+3; lane -> row
   // 4u + q, LDS slot u*64 + lane, which holds chunk (r - (4u + q)) & 15 of the
@@ -300,8 +312,12 @@ __global__ __launch_bounds__(WAVES * 64) FFN_STREAM_ATTR void q8_stream(
       }
       if (tok < M && col < N) {
         const size_t off = (size_t)tok * N + col;
-        const float o = NMAT == 2 ? silu_mul(v0, v1) : bf2f(resid[off]) + v0;
-        out[off] = f2bf(o);
+        if (PART) {
+          part[(size_t)blockIdx.y * M * N + off] = v0;
+        } else {
+          const float o = NMAT == 2 ? silu_mul(v0, v1) : bf2f(resid[off]) + v0;
+          out[off] = f2bf(o);
+        }
       }
     }
   }
@@ -311,46 +327,65 @@ __global__ __launch_bounds__(WAVES * 64) FFN_STREAM_ATTR void q8_stream(
 // token tiles keep the kernels free of register spills).
 int q8_max_tokens() { return 32; }
 
-template <int NMAT, int WAVES, bool SALIGN>
+template <int NMAT, int WAVES, bool SALIGN, bool PART>
 static void launch_q8_mt(const uint16_t* a, const int8_t* q0, const uint16_t* s0,
                          const int8_t* q1, const uint16_t* s1, const uint16_t* rr, uint16_t* o,
-                         int M, int K, int N, hipStream_t s) {
-  const dim3 grid((unsigned)((N + 15) / 16)), block(WAVES * 64);
+                         float* part, int splits, int M, int K, int N, hipStream_t s) {
+  const dim3 grid((unsigned)((N + 15) / 16), (unsigned)splits), block(WAVES * 64);
   if (M <= 8)
-    hipLaunchKernelGGL((q8_stream<NMAT, 1, WAVES, SALIGN, 8>), grid, block, 0, s, a, q0, s0, q1, s1, rr, o, M, K, N);
+    hipLaunchKernelGGL((q8_stream<NMAT, 1, WAVES, SALIGN, 8, PART>), grid, block, 0, s, a, q0, s0, q1, s1, rr, o, part, M, K, N);
   else if (M <= 16)
-    hipLaunchKernelGGL((q8_stream<NMAT, 1, WAVES, SALIGN, 16>), grid, block, 0, s, a, q0, s0, q1, s1, rr, o, M, K, N);
+    hipLaunchKernelGGL((q8_stream<NMAT, 1, WAVES, SALIGN, 16, PART>), grid, block, 0, s, a, q0, s0, q1, s1, rr, o, part, M, K, N);
   else
-    hipLaunchKernelGGL((q8_stream<NMAT, 2, WAVES, SALIGN, 0>), grid, block, 0, s, a, q0, s0, q1, s1, rr, o, M, K, N);
+    hipLaunchKernelGGL((q8_stream<NMAT, 2, WAVES, SALIGN, 0, PART>), grid, block, 0, s, a, q0, s0, q1, s1, rr, o, part, M, K, N);
 }
 
-template <int NMAT, int WAVES>
-static hipError_t launch_q8(const void* act, const int8_t* q0, const uint16_t* s0,
-                            const int8_t* q1, const uint16_t* s1, const void* resid, void* out,
-                            int M, int K, int N, hipStream_t s) {
-  const uint16_t* a = (const uint16_t*)act;
-  const uint16_t* rr = (const uint16_t*)resid;
-  uint16_t* o = (uint16_t*)out;
-  // 16-byte scale loads need every row of scales (K/16 bytes) and the base
-  // pointers 16-byte aligned
-  const bool salign = K % 256 == 0 && ((uintptr_t)s0 % 16) == 0 &&
-                      (NMAT == 1 || ((uintptr_t)s1 % 16) == 0);
-  if (salign)
-    launch_q8_mt<NMAT, WAVES, true>(a, q0, s0, q1, s1, rr, o, M, K, N, s);
-  else
-    launch_q8_mt<NMAT, WAVES, false>(a, q0, s0, q1, s1, rr, o, M, K, N, s);
-  return hipGetLastError();
+// 16-byte scale loads need every row of scales (K/16 bytes) and the base
+// pointers 16-byte aligned
+static bool q8_scales_aligned(int K, const uint16_t* s0, const uint16_t* s1) {
+  return K % 256 == 0 && ((uintptr_t)s0 % 16) == 0 && (s1 == nullptr || ((uintptr_t)s1 % 16) == 0);
 }
 
 hipError_t launch_q8_gateup(const void* n, const int8_t* qg, const uint16_t* sg,
                             const int8_t* qu, const uint16_t* su, void* h, int M, int d, int f,
                             hipStream_t s) {
-  return launch_q8<2, FFN_Q8_GU_WAVES>(n, qg, sg, qu, su, nullptr, h, M, d, f, s);
+  constexpr int W = FFN_Q8_GU_WAVES;
+  const uint16_t* a = (const uint16_t*)n;
+  if (q8_scales_aligned(d, sg, su))
+    launch_q8_mt<2, W, true, false>(a, qg, sg, qu, su, nullptr, (uint16_t*)h, nullptr, 1, M, d, f, s);
+  else
+    launch_q8_mt<2, W, false, false>(a, qg, sg, qu, su, nullptr, (uint16_t*)h, nullptr, 1, M, d, f, s);
+  return hipGetLastError();
+}
+
+// Split-K factor of the down projection, as for Q4_0: about
+// FFN_Q8_DN_SPLIT_TARGET workgroups in total, at most kQuantMaxSplits ranges
+// and no more than the 256-k stages.
+int q8_down_splits(int N, int K) {
+  const int target = FFN_Q8_DN_SPLIT_TARGET;
+  const int tiles = (N + 15) / 16;
+  const int nst = (K / 32 + 7) / 8;
+  int sp = target > 0 ? (target + tiles - 1) / tiles : 1;
+  sp = sp < 1 ? 1 : sp > kQuantMaxSplits ? kQuantMaxSplits : sp;
+  return sp > nst ? (nst > 0 ? nst : 1) : sp;
 }
 
 hipError_t launch_q8_down(const void* h, const int8_t* qd, const uint16_t* sd, const void* x,
-                          void* y, int M, int d, int f, hipStream_t s) {
-  return launch_q8<1, FFN_Q8_DN_WAVES>(h, qd, sd, nullptr, nullptr, x, y, M, f, d, s);
+                          void* y, float* part, int M, int d, int f, hipStream_t s) {
+  constexpr int W = FFN_Q8_DN_WAVES;
+  const uint16_t* a = (const uint16_t*)h;
+  const int sp = q8_down_splits(d, f);
+  const bool al = q8_scales_aligned(f, sd, nullptr);
+  if (sp == 1) {
+    if (al) launch_q8_mt<1, W, true, false>(a, qd, sd, nullptr, nullptr, (const uint16_t*)x, (uint16_t*)y, nullptr, 1, M, f, d, s);
+    else launch_q8_mt<1, W, false, false>(a, qd, sd, nullptr, nullptr, (const uint16_t*)x, (uint16_t*)y, nullptr, 1, M, f, d, s);
+    return hipGetLastError();
+  }
+  if (al) launch_q8_mt<1, W, true, true>(a, qd, sd, nullptr, nullptr, nullptr, nullptr, part, sp, M, f, d, s);
+  else launch_q8_mt<1, W, false, true>(a, qd, sd, nullptr, nullptr, nullptr, nullptr, part, sp, M, f, d, s);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_splitk_residual(part, sp, x, y, M, d, s);
 }
 
 }  // namespace ffn
