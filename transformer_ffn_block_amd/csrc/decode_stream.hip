@@ -52,10 +52,11 @@
 #define FFN_DS_DN_WAVES 8
 #endif
 
-#ifndef FFN_STREAM_WPE
-#define FFN_STREAM_ATTR
-#else
-#define FFN_STREAM_ATTR __attribute__((amdgpu_waves_per_eu(FFN_STREAM_WPE)))
+// Waves per SIMD the 16-token gate/up kernel is register-allocated for: at
+// 3 (168 VGPRs, no spills; 49 KiB LDS) all 688 workgroups of an f = 11008
+// projection are resident at once instead of 512 plus a second round.
+#ifndef FFN_DS_GU_STAGED_WPE
+#define FFN_DS_GU_STAGED_WPE 3
 #endif
 
 namespace ffn {
@@ -64,7 +65,9 @@ namespace ffn {
 // LDS (pays off from about 8 tokens); otherwise read straight from L2 in the
 // MFMA operand layout (for one token every lane reads the same 64 bytes).
 template <int NMAT, int MT, int WAVES, bool FOLD, bool ASTAGE>
-__global__ __launch_bounds__(WAVES * 64) FFN_STREAM_ATTR void decode_stream(
+__global__ __launch_bounds__(WAVES * 64)
+__attribute__((amdgpu_waves_per_eu(NMAT == 2 && MT == 1 && ASTAGE ? FFN_DS_GU_STAGED_WPE : 1)))
+void decode_stream(
     const uint16_t* __restrict__ act,    // [M, K]: x (FOLD) or h
     const uint16_t* __restrict__ gain,   // [K] (FOLD)
     const uint16_t* __restrict__ w0,     // [N, K]
@@ -75,8 +78,13 @@ __global__ __launch_bounds__(WAVES * 64) FFN_STREAM_ATTR void decode_stream(
   constexpr int ST = 16;  // 16-byte chunks per row per stage (128 k)
   __shared__ uint4 wb[WAVES][NMAT][256];            // per-wave weight stage
   __shared__ uint4 ab[WAVES][ASTAGE ? MT : 1][ASTAGE ? 256 : 1];  // per-wave activation stage
-  __shared__ float red[WAVES][MT][NMAT][4][64];     // cross-wave partial tiles
   __shared__ float ssq[FOLD ? WAVES : 1][MT][16];   // partial sums of squares
+  // the cross-wave partial tiles reuse each wave's own weight stage once its
+  // K loop is done (MT * NMAT * 1 KiB <= NMAT * 4 KiB)
+  static_assert(MT <= 4, "partial tiles must fit the weight stage");
+  auto red = [&](int w, int t, int m, int e) -> float* {
+    return reinterpret_cast<float*>(&wb[w][0][0]) + ((t * NMAT + m) * 4 + e) * 64;
+  };
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -118,22 +126,27 @@ __global__ __launch_bounds__(WAVES * 64) FFN_STREAM_ATTR void decode_stream(
   const uint4* G4 = reinterpret_cast<const uint4*>(gain);
 
   f32x4 acc[NMAT][MT];
-  float ss[MT];
+  // sums of squares of x: direct layout, token r of tile t (ss[t][0]);
+  // staged layout, token 4u + q of tile t (ss[t][u])
+  float ss[MT][ASTAGE ? 4 : 1];
 #pragma unroll
   for (int t = 0; t < MT; ++t) {
-    ss[t] = 0.f;
+#pragma unroll
+    for (int u = 0; u < (ASTAGE ? 4 : 1); ++u) ss[t][u] = 0.f;
 #pragma unroll
     for (int m = 0; m < NMAT; ++m) acc[m][t] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  struct Batch {
+  struct WB {
     uint4 w[NMAT][4];
+  };
+  struct AB {
     uint4 a[MT][4];
     uint4 g[FOLD ? 4 : 1];
   };
   // st < 0 marks a prefetch past the slice end: the weight loads then read
   // nothing (out-of-range offset) and the activation loads hit cache
-  auto load_w = [&](Batch& B, int st_req) {
+  auto load_w = [&](WB& B, int st_req) {
     const int st = st_req < 0 ? se - 1 : st_req;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -143,7 +156,7 @@ __global__ __launch_bounds__(WAVES * 64) FFN_STREAM_ATTR void decode_stream(
       for (int m = 0; m < NMAT; ++m) B.w[m][u] = buf_ld_nt(rw[m], o);
     }
   };
-  auto load_a = [&](Batch& B, int st_req) {
+  auto load_a = [&](AB& B, int st_req) {
     const int st = st_req < 0 ? se - 1 : st_req;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -151,19 +164,25 @@ __global__ __launch_bounds__(WAVES * 64) FFN_STREAM_ATTR void decode_stream(
       const int c = min(st * ST + (ASTAGE ? cst[u] : 4 * u + q), K8 - 1);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) B.a[mt][u] = pa[mt][u][c];
-    }
-    if (FOLD) {
-#pragma unroll
-      for (int t = 0; t < 4; ++t) B.g[t] = G4[min(st * ST + 4 * t + q, K8 - 1)];
+      if (FOLD) B.g[u] = G4[c];  // the gain of the same chunk
     }
   };
-  auto load = [&](Batch& B, int st_req) {
-    load_w(B, st_req);
-    load_a(B, st_req);
+  // x * g in fp32, rounded once to bf16, and the sum of squares of x
+  auto fold = [&](const uint4& xa, const uint4& gv, float& s2) -> uint4 {
+    float xf[8], gf[8];
+    unpack8(xa, xf);
+    unpack8(gv, gf);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      s2 = __builtin_fmaf(xf[e], xf[e], s2);
+      xf[e] *= gf[e];
+    }
+    return pack8(xf);
   };
   // the weights of a stage go to LDS first, which frees their registers for
-  // the next prefetch before the MFMAs of this stage run
-  auto stage = [&](const Batch& B, int st) {
+  // the next prefetch before the MFMAs of this stage run; staged activations
+  // go to LDS already multiplied by the gain
+  auto stage = [&](const WB& B, const AB& A, int st) {
     const bool ragged = (st + 1) * ST > K8;  // only the last stage of a row can be partial
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -176,14 +195,15 @@ __global__ __launch_bounds__(WAVES * 64) FFN_STREAM_ATTR void decode_stream(
       if (ASTAGE) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-          uint4 v = B.a[mt][u];
+          uint4 v = A.a[mt][u];
           if (ragged) v = keep_or_zero(st * ST + cst[u] < K8, v);
+          if (FOLD) v = fold(v, A.g[u], ss[mt][ASTAGE ? u : 0]);
           ab[wave][ASTAGE ? mt : 0][ASTAGE ? u * 64 + lane : 0] = v;
         }
       }
     }
   };
-  auto compute = [&](const Batch& B, int st) {
+  auto compute = [&](const AB& A, int st) {
     const bool ragged = (st + 1) * ST > K8;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
@@ -191,25 +211,12 @@ __global__ __launch_bounds__(WAVES * 64) FFN_STREAM_ATTR void decode_stream(
       uint4 bb[MT];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        uint4 xa;
         if (ASTAGE) {
-          xa = ab[wave][ASTAGE ? mt : 0][ASTAGE ? slot : 0];  // chunks past K zeroed when staged
+          bb[mt] = ab[wave][ASTAGE ? mt : 0][ASTAGE ? slot : 0];  // chunks past K zeroed when staged
         } else {
-          xa = B.a[mt][t];
+          uint4 xa = A.a[mt][t];
           if (ragged) xa = keep_or_zero(st * ST + 4 * t + q < K8, xa);
-        }
-        if (FOLD) {
-          float xf[8], gf[8];
-          unpack8(xa, xf);
-          unpack8(B.g[t], gf);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            ss[mt] = __builtin_fmaf(xf[e], xf[e], ss[mt]);
-            xf[e] *= gf[e];
-          }
-          bb[mt] = pack8(xf);
-        } else {
-          bb[mt] = xa;
+          bb[mt] = FOLD ? fold(xa, A.g[t], ss[mt][0]) : xa;
         }
       }
 #pragma unroll
@@ -222,35 +229,68 @@ __global__ __launch_bounds__(WAVES * 64) FFN_STREAM_ATTR void decode_stream(
   };
 
   const int n = se - sb;
-  if (n >= 2) {
-    Batch X, Y;
-    load(X, sb);
-    load(Y, sb + 1);
+  if (ASTAGE && n >= 2) {
+    // activations single-buffered: the next stage's are loaded as soon as
+    // this stage's are in LDS, ahead of the weights two stages out (loads
+    // complete in order, so the wait before a stage leaves those in flight)
+    WB X, Y;
+    AB A;
+    load_w(X, sb);
+    load_a(A, sb);
+    load_w(Y, sb + 1);
     for (int s = sb;;) {
       __builtin_amdgcn_sched_barrier(0);
-      stage(X, s);
+      stage(X, A, s);
+      __builtin_amdgcn_sched_barrier(0);
+      load_a(A, s + 1 < se ? s + 1 : -1);
+      load_w(X, s + 2 < se ? s + 2 : -1);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(A, s);
+      if (++s >= se) break;
+      __builtin_amdgcn_sched_barrier(0);
+      stage(Y, A, s);
+      __builtin_amdgcn_sched_barrier(0);
+      load_a(A, s + 1 < se ? s + 1 : -1);
+      load_w(Y, s + 2 < se ? s + 2 : -1);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(A, s);
+      if (++s >= se) break;
+    }
+  } else if (n >= 2) {
+    // direct activations are read by the MFMA loop: two full batches
+    WB X, Y;
+    AB XA, YA;
+    load_w(X, sb);
+    load_a(XA, sb);
+    load_w(Y, sb + 1);
+    load_a(YA, sb + 1);
+    for (int s = sb;;) {
+      __builtin_amdgcn_sched_barrier(0);
+      stage(X, XA, s);
       __builtin_amdgcn_sched_barrier(0);
       load_w(X, s + 2 < se ? s + 2 : -1);
       __builtin_amdgcn_sched_barrier(0);
-      compute(X, s);
+      compute(XA, s);
       __builtin_amdgcn_sched_barrier(0);
-      load_a(X, s + 2 < se ? s + 2 : -1);
+      load_a(XA, s + 2 < se ? s + 2 : -1);
       if (++s >= se) break;
       __builtin_amdgcn_sched_barrier(0);
-      stage(Y, s);
+      stage(Y, YA, s);
       __builtin_amdgcn_sched_barrier(0);
       load_w(Y, s + 2 < se ? s + 2 : -1);
       __builtin_amdgcn_sched_barrier(0);
-      compute(Y, s);
+      compute(YA, s);
       __builtin_amdgcn_sched_barrier(0);
-      load_a(Y, s + 2 < se ? s + 2 : -1);
+      load_a(YA, s + 2 < se ? s + 2 : -1);
       if (++s >= se) break;
     }
   } else if (n == 1) {
-    Batch X;
-    load(X, sb);
-    stage(X, sb);
-    compute(X, sb);
+    WB X;
+    AB A;
+    load_w(X, sb);
+    load_a(A, sb);
+    stage(X, A, sb);
+    compute(A, sb);
   }
 
   // ---- fixed-order reduction over the WAVES K slices
@@ -259,12 +299,26 @@ __global__ __launch_bounds__(WAVES * 64) FFN_STREAM_ATTR void decode_stream(
 #pragma unroll
     for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) red[wave][t][m][e][lane] = acc[m][t][e];
+      for (int e = 0; e < 4; ++e) red(wave, t, m, e)[lane] = acc[m][t][e];
     if (FOLD) {
-      float v = ss[t];
-      v += __shfl_xor(v, 16, 64);
-      v += __shfl_xor(v, 32, 64);
-      if (q == 0) ssq[wave][t][r] = v;
+      if (ASTAGE) {
+        // token 4u + q: sum over the 16 lanes of group q (r = 0..15)
+#pragma unroll
+        for (int u = 0; u < (ASTAGE ? 4 : 1); ++u) {
+          float v = ss[t][u];
+          v += __shfl_xor(v, 1, 64);
+          v += __shfl_xor(v, 2, 64);
+          v += __shfl_xor(v, 4, 64);
+          v += __shfl_xor(v, 8, 64);
+          if (r == 0) ssq[wave][t][4 * u + q] = v;
+        }
+      } else {
+        // token r: sum over the four lane groups q
+        float v = ss[t][0];
+        v += __shfl_xor(v, 16, 64);
+        v += __shfl_xor(v, 32, 64);
+        if (q == 0) ssq[wave][t][r] = v;
+      }
     }
   }
   __syncthreads();
@@ -277,8 +331,8 @@ __global__ __launch_bounds__(WAVES * 64) FFN_STREAM_ATTR void decode_stream(
       float s0 = 0.f, s1 = 0.f;
 #pragma unroll
       for (int w = 0; w < WAVES; ++w) {
-        s0 += red[w][t][0][e][lane];
-        if (NMAT == 2) s1 += red[w][t][NMAT - 1][e][lane];
+        s0 += red(w, t, 0, e)[lane];
+        if (NMAT == 2) s1 += red(w, t, NMAT - 1, e)[lane];
       }
       v0[e] = s0;
       v1[e] = s1;
