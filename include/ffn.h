@@ -67,11 +67,20 @@ typedef enum {
 
 typedef enum { FFN_F32 = 0, FFN_BF16 = 1 } ffn_dtype;
 
-/* Gate/up schedule: FUSED computes both projections in one kernel whose
- * epilogue applies silu(G)*U; SPLIT runs the gate GEMM, the up GEMM and a
- * separate activation pass ("Unfusing a Kernel Made It 1.63x Faster",
- * Finding 1).  AUTO picks by measured speed for the shape. */
-typedef enum { FFN_VARIANT_AUTO = 0, FFN_VARIANT_FUSED = 1, FFN_VARIANT_SPLIT = 2 } ffn_variant;
+/* Schedule of the block.  FUSED computes both gate/up projections in one
+ * kernel whose epilogue applies silu(G)*U; SPLIT runs the gate GEMM, the up
+ * GEMM and a separate activation pass ("Unfusing a Kernel Made It 1.63x
+ * Faster", Finding 1).  PERSISTENT (bf16, 1 <= M <= 16 only) runs the whole
+ * block as one dispatch whose work items wait on device-scope completion
+ * counters instead of kernel boundaries ("Megakernels on Mac", the
+ * persistent-kernel experiment); a second, tiny launch before it clears the
+ * counters.  AUTO picks FUSED or SPLIT by measured speed for the shape. */
+typedef enum {
+  FFN_VARIANT_AUTO = 0,
+  FFN_VARIANT_FUSED = 1,
+  FFN_VARIANT_SPLIT = 2,
+  FFN_VARIANT_PERSISTENT = 3
+} ffn_variant;
 
 /* One Q8_0 weight matrix [N, K] in split (structure-of-arrays) form:
  *   qs     : int8  [N, K]      quants, 32 consecutive along K form a block
@@ -113,7 +122,9 @@ ffn_status ffn_rmsnorm(ffn_dtype dt, const void *x, const void *g, void *y,
 
 /* Workspace bytes ffn_swiglu_block needs for this shape and variant (0 on a
  * shape it would reject).  It holds n [M,d] and h [M,f] (plus G, U [M,f]
- * for SPLIT), each 256-byte aligned. */
+ * for SPLIT; for PERSISTENT, fp32 partial sums [S, M, d] and
+ * 4 * (2 + S + ceil(d/16)) bytes of counters, S = the schedule's number of
+ * K ranges of the down projection, 1 to 8), each 256-byte aligned. */
 size_t ffn_swiglu_block_workspace_size(ffn_dtype dt, int64_t M, int64_t d, int64_t f,
                                        ffn_variant variant);
 
@@ -130,6 +141,10 @@ size_t ffn_swiglu_block_workspace_size(ffn_dtype dt, int64_t M, int64_t d, int64
  *               ffn_swiglu_block_workspace_size(dt, M, d, f, variant) bytes,
  *               256-byte aligned; its contents are scratch.
  * Returns FFN_OK, INVALID_ARGUMENT, UNSUPPORTED, WORKSPACE or LAUNCH. */
+/* For PERSISTENT the workspace's counter words must not be shared with a
+ * call that overlaps on the device; after the call completes, counter word 1
+ * (at the start of the counter region) is nonzero if a work item gave up
+ * waiting (the result is then wrong). */
 ffn_status ffn_swiglu_block(ffn_dtype dt, const void *x, const void *g,
                             const void *w_gate, const void *w_up, const void *w_down,
                             void *y, int64_t M, int64_t d, int64_t f, float eps,

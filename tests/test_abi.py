@@ -87,6 +87,15 @@ def test_block_validation(L):
     assert "workspace" in L.ffn_last_error().decode() or True
 
 
+def test_persistent_variant_scope(L):
+    UNS = ffn.FFN_ERR_UNSUPPORTED
+    P = ffn.VARIANTS["persistent"]
+    assert _block(L, v=P, M=17) == UNS                       # at most 16 tokens
+    assert _block(L, v=P, dt=ffn.FFN_F32, d=256, f=704) == UNS  # bf16 only
+    assert _block(L, v=4) == ffn.FFN_ERR_INVALID_ARGUMENT
+    assert _block(L, v=P, M=0, ws=0, wsb=0) == ffn.FFN_OK
+
+
 def test_block_zero_tokens_is_a_noop(L):
     assert _block(L, M=0, ws=0, wsb=0) == ffn.FFN_OK
     assert L.ffn_last_error().decode() == ""
@@ -102,6 +111,9 @@ def test_workspace_sizes(L):
     assert split == fused + 2 * r256(M * f * 2)
     assert L.ffn_swiglu_block_workspace_size(ffn.FFN_F32, 8, 256, 704, 0) == r256(8 * 256 * 4) + r256(8 * 704 * 4)
     assert L.ffn_swiglu_block_workspace_size(5, M, d, f, 0) == 0
+    # persistent: plus [S, M, d] fp32 partials and 2 + S + d/16 counter words
+    pers = L.ffn_swiglu_block_workspace_size(ffn.FFN_BF16, M, d, f, 3)
+    assert any(pers == fused + r256(s * M * d * 4) + r256((2 + s + d // 16) * 4) for s in range(1, 9))
     # quantised blocks: plus the split-K partials of the down projection, 4 K
     # ranges for 320 output tiles, [4, min(M, 32), d] fp32
     assert L.ffn_swiglu_block_q8_workspace_size(8, 5120, 17408) == \

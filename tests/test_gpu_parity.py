@@ -170,6 +170,78 @@ def test_block_decode_ragged(gpu_lib, M, d, f):
 
 
 # ----------------------------------------------------------------------------
+# single-dispatch (persistent) decode schedule
+# ----------------------------------------------------------------------------
+def _r256(n):
+    return (n + 255) // 256 * 256
+
+
+def _run_persistent(ffn, xd, gd, wg, wu, wd, eps):
+    """The persistent schedule with an explicit workspace; returns y and the
+    kernel's error word (nonzero if a work item gave up waiting)."""
+    import torch
+    M, d = xd.shape
+    f = wg.shape[0]
+    need = ffn.workspace_size(ffn.FFN_BF16, M, d, f, "persistent")
+    ws = ffn.alloc_workspace(need)
+    y = ffn.swiglu_block(xd, gd, wg, wu, wd, eps, variant="persistent", workspace=ws)
+    torch.cuda.synchronize()
+    # the layout: n, h, partials [S, M, d] fp32, counters (2 + S + ceil(d/16) words)
+    base = _r256(M * d * 2) + _r256(M * f * 2)
+    offsets = {base + _r256(s_ * M * d * 4) for s_ in range(1, 9)
+               if base + _r256(s_ * M * d * 4) + _r256((2 + s_ + -(-d // 16)) * 4) == need}
+    assert len(offsets) == 1  # the counter region's offset is determined by the size
+    ctr = offsets.pop()
+    words = ws[ctr:ctr + 8].cpu().numpy().view(np.uint32)
+    return y, int(words[1])
+
+
+@pytest.mark.parametrize("M", [1, 4, 16])
+def test_block_persistent_full_size(gpu_lib, decode_inputs, M):
+    from transformer_ffn_block_amd import ffn
+    b16 = decode_inputs
+    _say("block persistent", M, b16.d, b16.f)
+    xd, gd, wg, wu, wd = _block_dev(b16)
+    y, err_word = _run_persistent(ffn, xd[:M].contiguous(), gd, wg, wu, wd, b16.eps)
+    r = O.block_from_stored("bf16", b16.x[:M], b16.g, b16.w_gate, b16.w_up, b16.w_down, b16.eps)
+    err = max_norm_err(host_f64(y), r)
+    _say("persistent err", err, "error word", err_word)
+    assert err_word == 0
+    assert err <= TOL_BF16
+
+
+# d, f not multiples of 16 (partial tiles) or of 128 (partial stages); f <= 384
+# gives fewer than four K ranges
+@pytest.mark.parametrize("M,d,f", [(1, 8, 8), (3, 520, 712), (11, 264, 136), (16, 1032, 384),
+                                   (7, 64, 2056)])
+def test_block_persistent_ragged(gpu_lib, M, d, f):
+    from transformer_ffn_block_amd import ffn
+    _say("block persistent ragged", M, d, f)
+    b = I.make_block(1400 + M, M, d, f, "bf16")
+    y, err_word = _run_persistent(ffn, *_block_dev(b), b.eps)
+    r = O.block_from_stored("bf16", b.x, b.g, b.w_gate, b.w_up, b.w_down, b.eps)
+    err = max_norm_err(host_f64(y), r)
+    _say("err", err, "error word", err_word)
+    assert err_word == 0
+    assert err <= TOL_BF16
+
+
+def test_block_persistent_deterministic_and_close_to_two_launch_path(gpu_lib):
+    from transformer_ffn_block_amd import ffn
+    import torch
+    b = I.make_block(1500, 16, 1024, 2816, "bf16")
+    dev = _block_dev(b)
+    y1, e1 = _run_persistent(ffn, *dev, b.eps)
+    y2, e2 = _run_persistent(ffn, *dev, b.eps)
+    y_ref = ffn.swiglu_block(*dev, b.eps, variant="fused")
+    torch.cuda.synchronize()
+    assert e1 == 0 and e2 == 0
+    assert np.array_equal(host_bits(y1), host_bits(y2))
+    # different summation order of the down projection: equal within rounding
+    assert max_norm_err(host_f64(y1), host_f64(y_ref)) <= TOL_BF16
+
+
+# ----------------------------------------------------------------------------
 # prefill regime (MFMA GEMMs), fused and split gate/up
 # ----------------------------------------------------------------------------
 @pytest.mark.parametrize("M,d,f", [(65, 512, 704), (300, 520, 712), (513, 1024, 2048), (1000, 256, 136)])

@@ -109,10 +109,10 @@ ffn_status check_block_dims(int64_t M, int64_t d, int64_t f, int64_t mult) {
 }
 
 struct WsLayout {
-  size_t n = 0, h = 0, G = 0, U = 0, total = 0;
+  size_t n = 0, h = 0, G = 0, U = 0, part = 0, ctr = 0, total = 0;
 };
 
-WsLayout ws_layout(size_t es, int64_t M, int64_t d, int64_t f, bool split) {
+WsLayout ws_layout(size_t es, int64_t M, int64_t d, int64_t f, bool split, bool persistent = false) {
   WsLayout w;
   size_t at = 0;
   w.n = at;
@@ -124,6 +124,13 @@ WsLayout ws_layout(size_t es, int64_t M, int64_t d, int64_t f, bool split) {
     at += round256((size_t)M * f * es);
     w.U = at;
     at += round256((size_t)M * f * es);
+  }
+  if (persistent) {
+    const int sp = ffn::decode_persistent_splits((int)d, (int)f);
+    w.part = at;
+    at += round256((size_t)sp * M * d * 4);
+    w.ctr = at;
+    at += round256(ffn::decode_persistent_counters((int)d, sp) * 4);
   }
   w.total = at;
   return w;
@@ -143,6 +150,7 @@ WsLayout ws_layout(size_t es, int64_t M, int64_t d, int64_t f, bool split) {
   } while (0)
 
 bool use_split(ffn_variant v) { return v == FFN_VARIANT_SPLIT; }
+bool use_persistent(ffn_variant v) { return v == FFN_VARIANT_PERSISTENT; }
 
 }  // namespace
 
@@ -189,9 +197,12 @@ size_t ffn_swiglu_block_workspace_size(ffn_dtype dt, int64_t M, int64_t d, int64
                                        ffn_variant variant) {
   if (dt != FFN_F32 && dt != FFN_BF16) return 0;
   if (M < 0 || d <= 0 || f <= 0) return 0;
-  if (variant != FFN_VARIANT_AUTO && variant != FFN_VARIANT_FUSED && variant != FFN_VARIANT_SPLIT)
+  if (variant != FFN_VARIANT_AUTO && variant != FFN_VARIANT_FUSED && variant != FFN_VARIANT_SPLIT &&
+      variant != FFN_VARIANT_PERSISTENT)
     return 0;
-  return ws_layout(elem_size(dt), M, d, f, use_split(variant)).total;
+  if (use_persistent(variant) && (dt != FFN_BF16 || M > 16 || d > INT32_MAX || f > INT32_MAX))
+    return 0;
+  return ws_layout(elem_size(dt), M, d, f, use_split(variant), use_persistent(variant)).total;
 }
 
 ffn_status ffn_swiglu_block(ffn_dtype dt, const void* x, const void* g, const void* w_gate,
@@ -201,18 +212,22 @@ ffn_status ffn_swiglu_block(ffn_dtype dt, const void* x, const void* g, const vo
   FFN_TRY(check_dtype(dt));
   if (!x || !g || !w_gate || !w_up || !w_down || !y)
     return fail(FFN_ERR_INVALID_ARGUMENT, "null pointer");
-  if (variant != FFN_VARIANT_AUTO && variant != FFN_VARIANT_FUSED && variant != FFN_VARIANT_SPLIT)
+  if (variant != FFN_VARIANT_AUTO && variant != FFN_VARIANT_FUSED && variant != FFN_VARIANT_SPLIT &&
+      variant != FFN_VARIANT_PERSISTENT)
     return fail(FFN_ERR_INVALID_ARGUMENT, "unknown variant %d", (int)variant);
   FFN_TRY(check_eps(eps));
   const size_t es = elem_size(dt);
   FFN_TRY(check_block_dims(M, d, f, 16 / (int64_t)es));
+  const bool persistent = use_persistent(variant);
+  if (persistent && (dt != FFN_BF16 || M > 16))
+    return fail(FFN_ERR_UNSUPPORTED, "the persistent schedule takes bf16 and at most 16 tokens");
   if (!aligned(x, 16) || !aligned(g, 16) || !aligned(w_gate, 16) || !aligned(w_up, 16) ||
       !aligned(w_down, 16) || !aligned(y, 16))
     return fail(FFN_ERR_UNSUPPORTED, "tensors must be 16-byte aligned");
   if ((size_t)f * d * es >= ((size_t)1 << 31))
     return fail(FFN_ERR_UNSUPPORTED, "weight matrices must be smaller than 2 GiB");
   const bool split = use_split(variant);
-  const WsLayout L = ws_layout(es, M, d, f, split);
+  const WsLayout L = ws_layout(es, M, d, f, split, persistent);
   if (M > 0 && (!workspace || workspace_bytes < L.total))
     return fail(FFN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total,
                 workspace ? workspace_bytes : (size_t)0);
@@ -231,6 +246,12 @@ ffn_status ffn_swiglu_block(ffn_dtype dt, const void* x, const void* g, const vo
   void* h = ws + L.h;
   const int Mi = (int)M, di = (int)d, fi = (int)f;
 
+  if (persistent) {
+    FFN_LAUNCH("decode_persistent", s,
+               ffn::launch_decode_persistent(x, g, w_gate, w_up, w_down, h, (float*)(ws + L.part),
+                                             (unsigned*)(ws + L.ctr), y, Mi, di, fi, eps, s));
+    return ok();
+  }
   const bool decode = dt == FFN_BF16 && !split && Mi <= ffn::decode_max_tokens();
   if (!decode) FFN_LAUNCH("rmsnorm", s, ffn::launch_rmsnorm((int)es, x, g, n, M, d, eps, s));
   if (dt == FFN_F32) {

@@ -61,39 +61,62 @@
 
 namespace ffn {
 
+// 8-byte store written through to the coherence point shared by all XCDs
+__device__ __forceinline__ void coh_st8(void* p, uint32_t lo, uint32_t hi) {
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), ((uint64_t)hi << 32) | lo, __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Epilogue of a tile: gate/up (h = silu(G) * U, with the folded norm),
+// down (y = x + acc) or an fp32 partial tile of a split reduction axis.
+enum { DS_EPI_GATEUP = 0, DS_EPI_DOWN = 1, DS_EPI_PARTIAL = 2 };
+
+// LDS of a tile body, in uint4 / float units
+template <int NMAT, int MT, int WAVES, bool ASTAGE>
+struct DsLds {
+  static constexpr int wb = WAVES * NMAT * 256;                 // per-wave weight stages
+  static constexpr int ab = ASTAGE ? WAVES * MT * 256 : 1;      // per-wave activation stages
+  static constexpr int ssq = WAVES * MT * 16;                   // partial sums of squares
+};
+
+// One 16-row output tile over stages [zs, ze) of the reduction axis (ze < 0:
+// all of it), split over the workgroup's WAVES waves.
 // ASTAGE: activations fetched in 256-byte token segments and staged through
 // LDS (pays off from about 8 tokens); otherwise read straight from L2 in the
 // MFMA operand layout (for one token every lane reads the same 64 bytes).
-template <int NMAT, int MT, int WAVES, bool FOLD, bool ASTAGE>
-__global__ __launch_bounds__(WAVES * 64)
-__attribute__((amdgpu_waves_per_eu(NMAT == 2 && MT == 1 && ASTAGE ? FFN_DS_GU_STAGED_WPE : 1)))
-void decode_stream(
+// COH: the output is written through to the coherence point shared by all
+// XCDs (it is read by other workgroups of the same launch).
+template <int NMAT, int MT, int WAVES, bool FOLD, bool ASTAGE, int EPI, bool COH>
+__device__ __forceinline__ void ds_tile(
     const uint16_t* __restrict__ act,    // [M, K]: x (FOLD) or h
     const uint16_t* __restrict__ gain,   // [K] (FOLD)
     const uint16_t* __restrict__ w0,     // [N, K]
     const uint16_t* __restrict__ w1,     // [N, K] (NMAT == 2)
-    const uint16_t* __restrict__ resid,  // [M, N] (NMAT == 1)
-    uint16_t* __restrict__ out,          // [M, N]
-    int M, int K, int N, float eps) {
+    const uint16_t* __restrict__ resid,  // [M, N] (DS_EPI_DOWN)
+    uint16_t* __restrict__ out,          // [M, N] bf16 (GATEUP, DOWN)
+    float* __restrict__ part,            // [M, N] fp32 (PARTIAL)
+    int M, int K, int N, float eps, int tile, int zs, int ze,
+    uint4* __restrict__ wbs, uint4* __restrict__ abs_, float* __restrict__ ssqs) {
   constexpr int ST = 16;  // 16-byte chunks per row per stage (128 k)
-  __shared__ uint4 wb[WAVES][NMAT][256];            // per-wave weight stage
-  __shared__ uint4 ab[WAVES][ASTAGE ? MT : 1][ASTAGE ? 256 : 1];  // per-wave activation stage
-  __shared__ float ssq[FOLD ? WAVES : 1][MT][16];   // partial sums of squares
+  auto lds_w = [&](int w, int m, int i) -> uint4& { return wbs[(w * NMAT + m) * 256 + i]; };
+  auto lds_a = [&](int w, int mt, int i) -> uint4& { return abs_[ASTAGE ? (w * MT + mt) * 256 + i : 0]; };
+  auto lds_ssq = [&](int w, int t, int i) -> float& { return ssqs[(w * MT + t) * 16 + i]; };
   // the cross-wave partial tiles reuse each wave's own weight stage once its
   // K loop is done (MT * NMAT * 1 KiB <= NMAT * 4 KiB)
   static_assert(MT <= 4, "partial tiles must fit the weight stage");
   auto red = [&](int w, int t, int m, int e) -> float* {
-    return reinterpret_cast<float*>(&wb[w][0][0]) + ((t * NMAT + m) * 4 + e) * 64;
+    return reinterpret_cast<float*>(&lds_w(w, 0, 0)) + ((t * NMAT + m) * 4 + e) * 64;
   };
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int r = lane & 15, q = lane >> 4;
-  const int j0 = blockIdx.x * 16;
+  const int j0 = tile * 16;
   const int K8 = K >> 3;
   const int nst = (K8 + ST - 1) / ST;
-  const int sb = (int)(((long)nst * wave) / WAVES);
-  const int se = (int)(((long)nst * (wave + 1)) / WAVES);
+  const int z0 = zs, z1 = ze < 0 ? nst : ze;
+  const int sb = z0 + (int)(((long)(z1 - z0) * wave) / WAVES);
+  const int se = z0 + (int)(((long)(z1 - z0) * (wave + 1)) / WAVES);
 
   // staged loads: instruction u fetches rows 4u..4u+3, lane -> (row 4u + q,
   // chunk (r - (4u + q)) & 15) and lands at LDS slot u*64 + lane, so chunk c
@@ -190,7 +213,7 @@ void decode_stream(
       for (int m = 0; m < NMAT; ++m) {
         uint4 v = B.w[m][u];
         if (ragged) v = keep_or_zero(st * ST + cst[u] < K8, v);
-        wb[wave][m][u * 64 + lane] = v;
+        lds_w(wave, m, u * 64 + lane) = v;
       }
       if (ASTAGE) {
 #pragma unroll
@@ -198,7 +221,7 @@ void decode_stream(
           uint4 v = A.a[mt][u];
           if (ragged) v = keep_or_zero(st * ST + cst[u] < K8, v);
           if (FOLD) v = fold(v, A.g[u], ss[mt][ASTAGE ? u : 0]);
-          ab[wave][ASTAGE ? mt : 0][ASTAGE ? u * 64 + lane : 0] = v;
+          lds_a(wave, mt, u * 64 + lane) = v;
         }
       }
     }
@@ -212,7 +235,7 @@ void decode_stream(
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         if (ASTAGE) {
-          bb[mt] = ab[wave][ASTAGE ? mt : 0][ASTAGE ? slot : 0];  // chunks past K zeroed when staged
+          bb[mt] = lds_a(wave, mt, slot);  // chunks past K zeroed when staged
         } else {
           uint4 xa = A.a[mt][t];
           if (ragged) xa = keep_or_zero(st * ST + 4 * t + q < K8, xa);
@@ -221,7 +244,7 @@ void decode_stream(
       }
 #pragma unroll
       for (int m = 0; m < NMAT; ++m) {
-        const uint4 af = wb[wave][m][slot];
+        const uint4 af = lds_w(wave, m, slot);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) acc[m][mt] = mfma16(af, bb[mt], acc[m][mt]);
       }
@@ -310,14 +333,14 @@ void decode_stream(
           v += __shfl_xor(v, 2, 64);
           v += __shfl_xor(v, 4, 64);
           v += __shfl_xor(v, 8, 64);
-          if (r == 0) ssq[wave][t][4 * u + q] = v;
+          if (r == 0) lds_ssq(wave, t, 4 * u + q) = v;
         }
       } else {
         // token r: sum over the four lane groups q
         float v = ss[t][0];
         v += __shfl_xor(v, 16, 64);
         v += __shfl_xor(v, 32, 64);
-        if (q == 0) ssq[wave][t][r] = v;
+        if (q == 0) lds_ssq(wave, t, r) = v;
       }
     }
   }
@@ -340,12 +363,22 @@ void decode_stream(
     if (tok < M && col < N) {
       const size_t off = (size_t)tok * N + col;
       uint2 o;
+      if (EPI == DS_EPI_PARTIAL) {
+        float* pp = part + off;
+        if (COH) {
+          coh_st8(pp, __float_as_uint(v0[0]), __float_as_uint(v0[1]));
+          coh_st8(pp + 2, __float_as_uint(v0[2]), __float_as_uint(v0[3]));
+        } else {
+          *reinterpret_cast<float4*>(pp) = make_float4(v0[0], v0[1], v0[2], v0[3]);
+        }
+        continue;
+      }
       if (NMAT == 2) {
         float rs = 1.f;
         if (FOLD) {
           float sum = 0.f;
 #pragma unroll
-          for (int w = 0; w < WAVES; ++w) sum += ssq[w][t][r];
+          for (int w = 0; w < WAVES; ++w) sum += lds_ssq(w, t, r);
           rs = 1.0f / __builtin_sqrtf(sum / (float)K + eps);
         }
 #pragma unroll
@@ -357,9 +390,31 @@ void decode_stream(
         o.x = pack_bf16x2(bf2f(xr.x & 0xFFFFu) + v0[0], bf2f(xr.x >> 16) + v0[1]);
         o.y = pack_bf16x2(bf2f(xr.y & 0xFFFFu) + v0[2], bf2f(xr.y >> 16) + v0[3]);
       }
-      *reinterpret_cast<uint2*>(out + off) = o;
+      if (COH)
+        coh_st8(out + off, o.x, o.y);
+      else
+        *reinterpret_cast<uint2*>(out + off) = o;
     }
   }
+}
+
+template <int NMAT, int MT, int WAVES, bool FOLD, bool ASTAGE>
+__global__ __launch_bounds__(WAVES * 64)
+__attribute__((amdgpu_waves_per_eu(NMAT == 2 && MT == 1 && ASTAGE ? FFN_DS_GU_STAGED_WPE : 1)))
+void decode_stream(
+    const uint16_t* __restrict__ act,    // [M, K]: x (FOLD) or h
+    const uint16_t* __restrict__ gain,   // [K] (FOLD)
+    const uint16_t* __restrict__ w0,     // [N, K]
+    const uint16_t* __restrict__ w1,     // [N, K] (NMAT == 2)
+    const uint16_t* __restrict__ resid,  // [M, N] (NMAT == 1)
+    uint16_t* __restrict__ out,          // [M, N]
+    int M, int K, int N, float eps) {
+  using L = DsLds<NMAT, MT, WAVES, ASTAGE>;
+  __shared__ uint4 wb[L::wb];
+  __shared__ uint4 ab[L::ab];
+  __shared__ float ssq[L::ssq];
+  ds_tile<NMAT, MT, WAVES, FOLD, ASTAGE, NMAT == 2 ? DS_EPI_GATEUP : DS_EPI_DOWN, false>(
+      act, gain, w0, w1, resid, out, nullptr, M, K, N, eps, blockIdx.x, 0, -1, wb, ab, ssq);
 }
 
 // Tokens per launch (two 16-token tiles keep the LDS stages within budget);
@@ -395,6 +450,173 @@ hipError_t launch_decode_gateup_norm(const void* x, const void* g, const void* w
 hipError_t launch_decode_down(const void* h, const void* wd, const void* x, void* y, int M,
                               int d, int f, hipStream_t s) {
   return launch_ds<1, FFN_DS_DN_WAVES, false>(h, nullptr, wd, nullptr, x, y, M, f, d, 0.f, s);
+}
+
+// ---------------------------------------------------------------------------
+// Single-dispatch decode block: the megakernel schedule of "Megakernels on
+// Mac" ("The 27.65 ms estimate" onward: one launch, work items that wait on
+// completion flags instead of dispatch boundaries), for 1..16 tokens.
+//
+// Workgroups take work items from a ticket counter: first the f/16 gate/up
+// tiles (norm folded, as in decode_stream), then the down projection as
+// (tile, K range) items, range-major.  A down item for K range z needs the h
+// columns of z, i.e. the gate/up tiles of z: their count is kept per range.
+// Every dependency points to a smaller ticket, and tickets are handed out in
+// order, so the items waited for are already owned by running workgroups and
+// never wait themselves: no deadlock whatever the residency.  The waits are
+// bounded: past spin_limit polls a workgroup records an error in counter 1
+// and stops waiting (the result is then wrong, but the kernel ends).
+// h and the fp32 partials cross XCDs: they are written with agent-scope
+// atomic stores (written through to the coherence point, so no cache
+// write-back is needed), each workgroup waits for its stores to complete
+// before it increments a counter; a down item, once its range is complete,
+// invalidates its caches (agent-scope acquire) and then reads h through
+// them, and the partials are read with agent-scope atomic loads.  The last of a down tile's S items adds the S partials
+// in range order and the residual: the same order as the two-pass
+// split-K reduce, deterministic.
+// Counters (caller's workspace, cleared by a preceding launch): [0] ticket,
+// [1] error, [2, 2+S) gate/up tiles done per range, [2+S, 2+S+d/16) down
+// items done per output tile.
+constexpr int kPersistWaves = 4;
+
+__global__ void clear_u32(unsigned* __restrict__ p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+// Two waves per SIMD: at three the two tile bodies together spill.
+#ifndef FFN_DS_PERSIST_WPE
+#define FFN_DS_PERSIST_WPE 2
+#endif
+
+__global__ __launch_bounds__(kPersistWaves * 64) __attribute__((amdgpu_waves_per_eu(FFN_DS_PERSIST_WPE)))
+void decode_persistent(const uint16_t* __restrict__ x, const uint16_t* __restrict__ g,
+                       const uint16_t* __restrict__ wg, const uint16_t* __restrict__ wu,
+                       const uint16_t* __restrict__ wd, uint16_t* __restrict__ h,
+                       float* __restrict__ part, uint16_t* __restrict__ y,
+                       unsigned* __restrict__ ctr, int M, int d, int f, float eps, int splits,
+                       unsigned spin_limit) {
+  constexpr int W = kPersistWaves;
+  using LG = DsLds<2, 1, W, true>;  // the gate/up body needs the most LDS
+  static_assert(DsLds<1, 1, W, true>::wb <= LG::wb && DsLds<1, 1, W, true>::ab <= LG::ab, "");
+  __shared__ uint4 wb[LG::wb];
+  __shared__ uint4 ab[LG::ab];
+  __shared__ float ssq[LG::ssq];
+  __shared__ int s_item, s_last;
+
+  const int n_gu = (f + 15) / 16, n_dt = (d + 15) / 16;
+  const int n_items = n_gu + n_dt * splits;
+  const int nst_f = (f / 8 + 15) / 16;  // 128-k stages of the down projection
+  unsigned* done_gu = ctr + 2;
+  unsigned* done_dt = ctr + 2 + splits;
+  auto range_lo = [&](int z) { return (int)(((long)nst_f * z) / splits); };
+
+  // (fetching the next ticket ahead of time was measured slower: it binds
+  // the last gate/up tiles to workgroups before they are free)
+  for (;;) {
+    if (threadIdx.x == 0)
+      s_item = (int)__hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const int item = s_item;
+    if (item >= n_items) break;
+    if (item < n_gu) {
+      ds_tile<2, 1, W, true, true, DS_EPI_GATEUP, true>(x, g, wg, wu, nullptr, h, nullptr, M, d, f,
+                                                         eps, item, 0, -1, wb, ab, ssq);
+      // h stores complete (written through) before the tile is counted
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        const int st = item / 8;  // the 128-k stage of h this tile's 16 columns fall in
+        int z = 0;
+        while (z + 1 < splits && range_lo(z + 1) <= st) ++z;
+        __hip_atomic_fetch_add(done_gu + z, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    } else {
+      const int dn = item - n_gu;
+      const int z = dn / n_dt, tile = dn % n_dt;  // range-major: early ranges first
+      const int zs = range_lo(z), ze = range_lo(z + 1);
+      if (threadIdx.x == 0) {
+        const unsigned need = (unsigned)(min(ze * 8, n_gu) - min(zs * 8, n_gu));
+        unsigned spins = 0;
+        while (__hip_atomic_load(done_gu + z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < need) {
+          if (++spins > spin_limit) {
+            __hip_atomic_store(ctr + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+          }
+          __builtin_amdgcn_s_sleep(8);
+        }
+        // acquire: drop possibly stale cached lines of h (an earlier call's)
+        // before this workgroup reads it through the caches
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      }
+      __syncthreads();
+      ds_tile<1, 1, W, false, true, DS_EPI_PARTIAL, true>(h, nullptr, wd, nullptr, nullptr, nullptr,
+                                                         part + (size_t)z * M * d, M, f, d, 0.f,
+                                                         tile, zs, ze, wb, ab, ssq);
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // partial stores complete before counting
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        const unsigned old =
+            __hip_atomic_fetch_add(done_dt + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = old == (unsigned)(splits - 1);
+      }
+      __syncthreads();
+      if (s_last) {
+        // y = x + sum_z partial[z], one output per thread (16 columns x M tokens)
+        for (int i = threadIdx.x; i < 16 * M; i += W * 64) {
+          const int tok = i >> 4, col = tile * 16 + (i & 15);
+          if (col < d) {
+            const size_t off = (size_t)tok * d + col;
+            float v = 0.f;
+            for (int zz = 0; zz < splits; ++zz)
+              v += __hip_atomic_load(part + (size_t)zz * M * d + off, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+            y[off] = f2bf(bf2f(x[off]) + v);
+          }
+        }
+      }
+    }
+    __syncthreads();  // s_item and s_last are rewritten by the next item
+  }
+}
+
+#ifndef FFN_DS_PERSIST_SPLITS
+#define FFN_DS_PERSIST_SPLITS 1
+#endif
+
+int decode_persistent_splits(int d, int f) {
+  (void)d;
+  const int nst_f = (f / 8 + 15) / 16;
+  const int sp = FFN_DS_PERSIST_SPLITS;
+  return nst_f < sp ? (nst_f > 0 ? nst_f : 1) : sp;
+}
+
+size_t decode_persistent_counters(int d, int splits) { return 2 + (size_t)splits + (d + 15) / 16; }
+
+hipError_t launch_decode_persistent(const void* x, const void* g, const void* wg, const void* wu,
+                                    const void* wd, void* h, float* part, unsigned* ctr, void* y,
+                                    int M, int d, int f, float eps, hipStream_t s) {
+  const int splits = decode_persistent_splits(d, f);
+  const int nc = (int)decode_persistent_counters(d, splits);
+  hipLaunchKernelGGL(clear_u32, dim3((unsigned)((nc + 255) / 256)), dim3(256), 0, s, ctr, nc);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  static int cus = 0;  // compute units of the device (gfx950 parts share one count)
+  if (cus == 0) {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+      cus = v;
+    else
+      cus = 256;
+  }
+  const int n_items = (f + 15) / 16 + ((d + 15) / 16) * splits;
+  const int grid = n_items < FFN_DS_PERSIST_WPE * cus ? n_items : FFN_DS_PERSIST_WPE * cus;
+  hipLaunchKernelGGL(decode_persistent, dim3((unsigned)grid), dim3(kPersistWaves * 64), 0, s,
+                     (const uint16_t*)x, (const uint16_t*)g, (const uint16_t*)wg,
+                     (const uint16_t*)wu, (const uint16_t*)wd, (uint16_t*)h, part, (uint16_t*)y,
+                     ctr, M, d, f, eps, splits, 1u << 20);
+  return hipGetLastError();
 }
 
 }  // namespace ffn

@@ -21,6 +21,14 @@ hipError_t launch_decode_gateup_norm(const void* x, const void* g, const void* w
                                      void* h, int M, int d, int f, float eps, hipStream_t s);
 hipError_t launch_decode_down(const void* h, const void* wd, const void* x, void* y,
                               int M, int d, int f, hipStream_t s);
+// Single-dispatch block for 1..16 tokens: gate/up tiles, then (tile, K range)
+// down items in one launch ordered by completion counters (ctr: caller's
+// workspace, cleared by a preceding launch; part: [splits, M, d] fp32).
+int decode_persistent_splits(int d, int f);
+size_t decode_persistent_counters(int d, int splits);
+hipError_t launch_decode_persistent(const void* x, const void* g, const void* wg, const void* wu,
+                                    const void* wd, void* h, float* part, unsigned* ctr, void* y,
+                                    int M, int d, int f, float eps, hipStream_t s);
 
 // Prefill (many tokens) LDS-tiled bf16 MFMA GEMMs, C[m][n] = sum_k A[m][k] W[n][k].
 hipError_t launch_gemm_gateup_fused(const void* n, const void* wg, const void* wu, void* h,
