@@ -148,6 +148,26 @@ def extras(torch, np, ffn, I, sets, x, g, b, ws, extra):
         extra[f"decode_M{m}"] = {"us": round(msm * 1e3, 2),
                                  "GBps": round(decode_bytes(m, d, f) / (msm * 1e-3) / 1e9, 1)}
         log(f"decode M={m}: {msm * 1e3:.2f} us/call")
+    # the single-dispatch (persistent) schedule at M = 16, interleaved with the
+    # default two-launch schedule
+    wsp = ffn.alloc_workspace(ffn.workspace_size(ffn.FFN_BF16, M, d, f, "persistent"))
+    yp = torch.empty_like(x)
+
+    def stepv(i, v):
+        wg, wu, wd = sets[i % ROTATE]
+        ffn.swiglu_block(x, g, wg, wu, wd, b.eps, v, out=yp, workspace=wsp if v == "persistent" else ws)
+    tv = {"auto": [], "persistent": []}
+    for v in tv:
+        for i in range(10):
+            stepv(i, v)
+    for _ in range(3):
+        for v in tv:
+            tv[v].append(time_calls(torch, lambda i, v=v: stepv(i, v), 50))
+    tp, ta = sorted(tv["persistent"])[1], sorted(tv["auto"])[1]
+    extra["decode_M16_persistent"] = {"us": round(tp * 1e3, 2), "two_launch_us": round(ta * 1e3, 2),
+                                      "persistent_over_two_launch": round(tp / ta, 3)}
+    log("persistent schedule", extra["decode_M16_persistent"])
+    del wsp, yp
     sets.clear()
     torch.cuda.empty_cache()
 
