@@ -304,6 +304,43 @@ def test_block_deterministic_and_row_permutation(gpu_lib, M):
     assert np.array_equal(yp, y1[p])
 
 
+def test_calls_on_a_side_stream_match_the_default_stream(gpu_lib):
+    """Every entry point enqueues on the stream it is given: results computed
+    on a side stream (inputs made on that stream, no device-wide sync before
+    the call) equal the default-stream ones bit for bit."""
+    from transformer_ffn_block_amd import ffn
+    import torch
+    b = I.make_block(1600, 12, 512, 704, "bf16")
+    q = I.make_q8_block(1601, 5, 256, 512)
+    q4 = I.make_q4_block(1602, 5, 256, 512)
+    bp = I.make_block(1603, 130, 256, 384, "bf16")
+
+    def run_all(stream):
+        out = []
+        x, g, wg, wu, wd = [t.clone() for t in _block_dev(b)]
+        out.append(ffn.swiglu_block(x, g, wg, wu, wd, b.eps, stream=stream))
+        out.append(ffn.swiglu_block(x, g, wg, wu, wd, b.eps, variant="persistent", stream=stream))
+        xp, gp, pg, pu, pd = [t.clone() for t in _block_dev(bp)]
+        out.append(ffn.swiglu_block(xp, gp, pg, pu, pd, bp.eps, stream=stream))
+        out.append(ffn.swiglu_block_q8(dev(q.x), dev(q.g), _q8_dev(q.w_gate), _q8_dev(q.w_up),
+                                       _q8_dev(q.w_down), q.eps, stream=stream))
+        out.append(ffn.swiglu_block_q4(dev(q4.x), dev(q4.g), _q4_dev(q4.w_gate), _q4_dev(q4.w_up),
+                                       _q4_dev(q4.w_down), q4.eps, stream=stream))
+        n = torch.empty_like(x)
+        ffn.rmsnorm(x, g, b.eps, out=n, stream=stream)
+        out.append(n)
+        return out
+
+    ref = [host_bits(t) for t in run_all(None)]
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        got = run_all(side)
+    side.synchronize()
+    for a, r in zip(got, ref):
+        assert np.array_equal(host_bits(a), r)
+
+
 @pytest.mark.parametrize("M", [4, 200])
 def test_block_zero_down_projection_returns_x_bitwise(gpu_lib, M):
     from transformer_ffn_block_amd import ffn
