@@ -256,6 +256,21 @@ def test_block_prefill_ragged(gpu_lib, M, d, f, variant):
     assert err <= TOL_BF16
 
 
+@pytest.mark.parametrize("M,d,f", [(256, 256, 128), (512, 512, 768), (768, 1024, 1280)])
+@pytest.mark.parametrize("variant", ["fused", "split"])
+def test_block_prefill_whole_tiles(gpu_lib, M, d, f, variant):
+    """Shapes made of whole 256-token tiles with an even number of 64-deep K
+    tiles, the ones the two-group (ping-pong) GEMM schedule takes; K = 128
+    is its shortest loop."""
+    from transformer_ffn_block_amd import ffn
+    _say("block prefill whole tiles", M, d, f, variant)
+    b = I.make_block(700 + M, M, d, f, "bf16")
+    r = O.block_from_stored("bf16", b.x, b.g, b.w_gate, b.w_up, b.w_down, b.eps)
+    err = max_norm_err(host_f64(_run_block(ffn, b, variant)), r)
+    _say("err", err)
+    assert err <= TOL_BF16
+
+
 @pytest.fixture(scope="module")
 def prefill_inputs():
     wl = I.WORKLOADS["prefill"]

@@ -55,6 +55,15 @@ __device__ __forceinline__ void buf_ld_lds16(__amdgpu_buffer_rsrc_t r, void* lds
                                            (int)off, 0, 0, AUX);
 }
 
+// The same with a wave-uniform byte offset added in the scalar offset
+// operand (every byte addressed must lie inside the resource).
+template <int AUX>
+__device__ __forceinline__ void buf_ld_lds16s(__amdgpu_buffer_rsrc_t r, void* lds, unsigned off,
+                                              int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
+                                           (int)off, soff, 0, AUX);
+}
+
 __device__ __forceinline__ float bf2f(uint32_t b16) { return __uint_as_float(b16 << 16); }
 
 // fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).

@@ -33,6 +33,20 @@
 //    staging registers and no LDS write instructions, measured 2-3% faster
 //    on the prefill block; BK = 32 with 3-5 stages measured slower (twice
 //    the barriers).
+//  * for whole tiles (M % 256, N % tile width, K % 128 all zero) the eight
+//    waves run as two groups of four, one wave of each group per SIMD, half
+//    a k-step apart: while one wave of a SIMD issues its k-step's MFMAs the
+//    other reads its next fragments from LDS (ping-pong), with a barrier
+//    between phases.  Each lane's fragment addresses are one base register
+//    per k-step plus immediate offsets, and the DMA sources one register per
+//    operand plus a scalar offset, so the kernel fits two waves per SIMD
+//    without spills.  Measured against the one-group schedule: fused gate/up
+//    GEMM 3-5% faster, down GEMM within +-2%.  With the tile DMA removed the
+//    same loop runs at ~2.07 PFLOP/s (MFMAs alone ~2.2): the time left is the
+//    wait for the next tile's global->LDS loads, which two 64 KB stages
+//    cannot hide further (a third does not fit in 160 KB of LDS).
+//  * the residual epilogue issues all of a lane's residual loads before the
+//    first add, one wait per tile instead of one per 16x16 sub-tile.
 //  * workgroups are dispatched round-robin over the 8 XCDs; tile ids are
 //    remapped so each XCD works on a contiguous range of tiles, grouped 8
 //    token tiles deep, so concurrently running tiles share operands in the
@@ -41,6 +55,7 @@
 #include "launch.h"
 
 #include <type_traits>
+#include <utility>
 
 namespace ffn {
 
@@ -227,6 +242,22 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16(
       }
     }
   } else {
+    // residual: every load is issued before the first add (an address
+    // outside the output reads element 0 and is never stored), so the
+    // tile waits for memory once rather than once per sub-tile
+    uint2 xr[FN][FM];
+    if (EPI == EPI_RESIDUAL) {
+#pragma unroll
+      for (int a = 0; a < FN; ++a) {
+        const int col = n0 + wn * TN + a * 16 + 4 * fq;
+#pragma unroll
+        for (int b = 0; b < FM; ++b) {
+          const int tok = m0 + wm * TM + b * 16 + fr;
+          const size_t off = (tok < M && col < N) ? (size_t)tok * N + col : 0;
+          xr[a][b] = *reinterpret_cast<const uint2*>(resid + off);
+        }
+      }
+    }
 #pragma unroll
     for (int a = 0; a < FN; ++a) {
       const int col = n0 + wn * TN + a * 16 + 4 * fq;
@@ -237,11 +268,10 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16(
           const size_t off = (size_t)tok * N + col;
           f32x4 v = acc[a][b];
           if (EPI == EPI_RESIDUAL) {
-            const uint2 xr = *reinterpret_cast<const uint2*>(resid + off);
-            v[0] += bf2f(xr.x & 0xFFFFu);
-            v[1] += bf2f(xr.x >> 16);
-            v[2] += bf2f(xr.y & 0xFFFFu);
-            v[3] += bf2f(xr.y >> 16);
+            v[0] += bf2f(xr[a][b].x & 0xFFFFu);
+            v[1] += bf2f(xr[a][b].x >> 16);
+            v[2] += bf2f(xr[a][b].y & 0xFFFFu);
+            v[3] += bf2f(xr[a][b].y >> 16);
           }
           uint2 o;
           o.x = pack_bf16x2(v[0], v[1]);
@@ -263,12 +293,50 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16(
 // Tile kt's LDS layout matches the register-staged kernel: row R holds its
 // CPR = BK/8 chunks, chunk c at position c ^ sw(R), so each load instruction
 // fills 1 KiB of consecutive LDS positions from lane-permuted sources.
+// Compile-time choices: FFN_PF_BK / FFN_PF_S configure the schedule in which
+// all eight waves read and multiply together; FFN_PF_PP selects the two-group
+// (ping-pong) schedule for whole tiles, FFN_PF_PP_BK / FFN_PF_PP_S its tile
+// depth and stage count.  Measured on gfx950 (prefill block): 64-deep tiles
+// in two stages are fastest for both; 32-deep tiles (two or four stages)
+// were 25% slower, and more than two stages of 32-deep tiles also make the
+// compiler wait for the newest DMA before some fragment reads.
+#ifndef FFN_PF_BK
+#define FFN_PF_BK 64
+#endif
+#ifndef FFN_PF_S
+#define FFN_PF_S 2
+#endif
+#ifndef FFN_PF_PP
+#define FFN_PF_PP 1
+#endif
+constexpr int kDmaBK = FFN_PF_BK, kDmaS = FFN_PF_S;
+#ifndef FFN_PF_PP_BK
+#define FFN_PF_PP_BK 64
+#endif
+#ifndef FFN_PF_PP_S
+#define FFN_PF_PP_S 2
+#endif
+constexpr bool kPingPong = FFN_PF_PP != 0;
+constexpr int kPpBK = FFN_PF_PP_BK, kPpS = FFN_PF_PP_S;
+
+constexpr std::integral_constant<int, 0> I0{};
+constexpr std::integral_constant<int, 1> I1{};
+// f(integral_constant<int, 0>) ... f(integral_constant<int, N-1>), unrolled
+template <class F, int... Is>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 template <int BK>
 __device__ __forceinline__ int dswz(int row) {
   return BK == 64 ? (row & 7) : ((row >> 2) & 3);
 }
 
-template <int BM, int BN, int WM, int WN, int EPI, int BK, int S>
+template <int BM, int BN, int WM, int WN, int EPI, int BK, int S, bool PP>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_dma(
     const uint16_t* __restrict__ act,    // [M, K]
     const uint16_t* __restrict__ w0,     // [N, K]  (gate for SWIGLU)
@@ -357,20 +425,24 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_dma(
     }
   };
 
-  // LDS rows read by this lane's fragments; all are congruent to fr mod 16
+  // LDS rows read by this lane's fragments: fr plus a multiple of 16 (the
+  // rows of fragment t are a compile-time offset from those of fragment 0),
+  // so every fragment of the lane shares one swizzle, and its address is a
+  // per-lane base per k-step plus an immediate offset.
   const int fr = lane & 15, fq = lane >> 4;
-  int arow[FN], brow[FM];
+  const int xo = dswz<BK>(fr);
+  const int arow0 = (EPI == EPI_SWIGLU ? wn * (TN / 2) : wn * TN) + fr;
+  const int brow0 = BN + wm * TM + fr;
+  static_assert(TN % 32 == 0 && TM % 16 == 0 && BN % 32 == 0, "fragment rows must stay congruent mod 16");
+  auto aoff = [](int t) {  // row offset of A fragment t (compile-time after unrolling)
+    return EPI == EPI_SWIGLU ? (t / (FN / 2)) * (BN / 2) + (t % (FN / 2)) * 16 : t * 16;
+  };
+  int abase[KS], bbase[KS];  // uint4 index within a stage
 #pragma unroll
-  for (int t = 0; t < FN; ++t) {
-    if (EPI == EPI_SWIGLU) {
-      const int half = t / (FN / 2), tt = t % (FN / 2);
-      arow[t] = half * (BN / 2) + wn * (TN / 2) + tt * 16 + fr;
-    } else {
-      arow[t] = wn * TN + t * 16 + fr;
-    }
+  for (int ks = 0; ks < KS; ++ks) {
+    abase[ks] = arow0 * CPR + ((ks * 4 + fq) ^ xo);
+    bbase[ks] = brow0 * CPR + ((ks * 4 + fq) ^ xo);
   }
-#pragma unroll
-  for (int t = 0; t < FM; ++t) brow[t] = BN + wm * TM + t * 16 + fr;
 
   f32x4 acc[FN][FM];
 #pragma unroll
@@ -382,12 +454,11 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_dma(
     const uint4* Ls = stage(i);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const int ch = ks * 4 + fq;
       uint4 af[FN], bfr[FM];
 #pragma unroll
-      for (int t = 0; t < FN; ++t) af[t] = Ls[arow[t] * CPR + (ch ^ dswz<BK>(arow[t]))];
+      for (int t = 0; t < FN; ++t) af[t] = Ls[abase[ks] + aoff(t) * CPR];
 #pragma unroll
-      for (int t = 0; t < FM; ++t) bfr[t] = Ls[brow[t] * CPR + (ch ^ dswz<BK>(brow[t]))];
+      for (int t = 0; t < FM; ++t) bfr[t] = Ls[bbase[ks] + t * 16 * CPR];
 #pragma unroll
       for (int a = 0; a < FN; ++a)
 #pragma unroll
@@ -406,6 +477,120 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_dma(
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
   };
 
+  if constexpr (PP) {
+    // Ping-pong schedule.  The waves with wm = 0 (group 0, one per SIMD) and
+    // those with wm = 1 (group 1, the other wave of each SIMD) run the same
+    // sequence -- read the fragments of one 32-deep k-step into registers,
+    // barrier, multiply them, barrier -- with group 1 one barrier behind, so
+    // that on every SIMD one wave multiplies while the other reads.  With
+    // h = KS kt + ks the k-step index, group g reads step h in phase 2h+g
+    // and multiplies it in phase 2h+1+g.  The S stages start full (tiles
+    // 0..S-1); tile kt+S-1 (kt >= 1) goes into the stage of tile kt-1 as each
+    // wave starts reading tile kt, after both groups' reads of tile kt-1
+    // (last in phase 2 KS kt - 1).  Tile kt+1 must be in LDS before group 0
+    // reads it in phase 2 KS (kt+1): every wave waits for its own loads of
+    // it in its last phase before that (group 0 after multiplying the last
+    // k-step of tile kt, group 1 after reading it), leaving its later tiles
+    // in flight.  Group 1 starts with one extra barrier and skips the last
+    // one, so both execute 2 KS nkt + 1 barriers.  nkt must be a multiple
+    // of S and the tiles whole.
+    static_assert(WM == 2, "ping-pong layout: two wave rows");
+    uint4 af[FN], bfr[FM];
+    auto readf = [&](int i, int ks) {
+      const uint4* Ls = stage(i);
+#pragma unroll
+      for (int t = 0; t < FN; ++t) af[t] = Ls[abase[ks] + aoff(t) * CPR];
+#pragma unroll
+      for (int t = 0; t < FM; ++t) bfr[t] = Ls[bbase[ks] + t * 16 * CPR];
+    };
+    auto mma = [&]() {
+#pragma unroll
+      for (int a = 0; a < FN; ++a)
+#pragma unroll
+        for (int b = 0; b < FM; ++b) acc[a][b] = mfma16(af[a], bfr[b], acc[a][b]);
+    };
+    auto bar = [&]() {
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    };
+    // waits stay where they are written (not hoisted above the MFMAs)
+    auto wait_lds = [&]() {  // lgkmcnt(0)
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+    };
+    // wait until tile kt+1 has landed: this wave's loads of the tiles after
+    // it (at most S-2 of them, fewer near the end) may stay in flight
+    auto wait_next = [&](int kt) {
+      const int after = min(S - 2, nkt - 2 - kt);
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      __builtin_amdgcn_sched_barrier(0);
+      if (S >= 4 && after >= 2) __builtin_amdgcn_s_waitcnt(0x0F70 | ((2 * J) & 15) | (((2 * J) >> 4) << 14));
+      else if (S >= 3 && after >= 1) __builtin_amdgcn_s_waitcnt(0x0F70 | (J & 15) | ((J >> 4) << 14));
+      else __builtin_amdgcn_s_waitcnt(0x0F70);
+    };
+    static_assert(S >= 2 && S <= 4, "wait_next covers up to two tiles in flight");
+    // DMA of tile kt (always < nkt here) into stage i, half of it by each
+    // group.  Tiles are whole (M % BM == 0, N % BNO == 0), so no row is
+    // clamped: every load's source is one of two per-lane offsets (weight
+    // rows, token rows) plus a wave-uniform row-block and K offset in the
+    // scalar operand.
+    const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+    const int rr = tid / CPR;
+    const unsigned cgp = (unsigned)((tid % CPR) ^ dswz<BK>(rr)) * 16u;
+    const unsigned vw = (unsigned)(n0 + rr) * (unsigned)K * 2u + cgp;
+    const unsigned va = (unsigned)(m0 + rr) * (unsigned)K * 2u + cgp;
+    const int blk = RJ * K * 2;  // bytes of one load instruction's row block
+    auto issue_pp = [&](int i, int kt) {
+      uint4* Ls = stage(i);
+      const int ko = kt * BK * 2;
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        uint4* dst = Ls + j * NT + wave_s * 64;
+        if (j * RJ < BN) {
+          const int rb = (EPI == EPI_SWIGLU ? j % (BN / 2 / RJ) : j);
+          if (EPI != EPI_SWIGLU || j * RJ < BN / 2) buf_ld_lds16s<0>(rw0, dst, vw, ko + rb * blk);
+          else buf_ld_lds16s<0>(rw1, dst, vw, ko + rb * blk);
+        } else {
+          buf_ld_lds16s<0>(ra, dst, va, ko + (j - BN / RJ) * blk);
+        }
+      }
+    };
+    static_for<S>([&](auto si) { issue_pp(decltype(si)::value, decltype(si)::value); });
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (((S - 1) * J) & 15) | ((((S - 1) * J) >> 4) << 14));  // tile 0
+    bar();
+    // S tiles per iteration keep every stage index a compile-time constant,
+    // and no path reaches a read of one stage with a DMA into that same
+    // stage pending: the compiler then adds no wait for the DMA before the
+    // reads.  body(i, ks, kt): k-step ks of tile kt, in stage i.  The group
+    // is a compile-time constant in each copy of the loop.
+    auto run = [&](auto gi) {
+      constexpr int G = decltype(gi)::value;
+      auto body = [&](auto si, auto ki, int kt) {
+        constexpr int i = decltype(si)::value, ks = decltype(ki)::value;
+        if (ks == 0 && kt >= 1 && kt + S - 1 < nkt) issue_pp((i + S - 1) % S, kt + S - 1);
+        readf(i, ks);
+        wait_lds();
+        if (ks == KS - 1 && G == 1) wait_next(kt);
+        bar();
+        mma();
+        if (ks == KS - 1 && G == 0) wait_next(kt);
+        if (ks < KS - 1 || G == 0 || kt + 1 < nkt) bar();
+      };
+      if (G == 1) bar();
+      for (int kt = 0; kt < nkt; kt += S) {
+        static_for<S>([&](auto si) {
+          static_for<KS>([&](auto ki) { body(si, ki, kt + decltype(si)::value); });
+        });
+      }
+    };
+    if (__builtin_amdgcn_readfirstlane(wm) == 0) run(I0);
+    else run(I1);
+  } else {
 #pragma unroll
   for (int i = 0; i < S - 1; ++i) issue(i, i);
   // main loop: whole groups of S tiles, no early exit
@@ -432,6 +617,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_dma(
       compute(i % S);
     }
   }
+  }
 
   // ---- epilogue: lane holds D[4*fq + e][fr] of every (a, b) sub-tile
   if (EPI == EPI_SWIGLU) {
@@ -451,6 +637,22 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_dma(
       }
     }
   } else {
+    // residual: every load is issued before the first add (an address
+    // outside the output reads element 0 and is never stored), so the
+    // tile waits for memory once rather than once per sub-tile
+    uint2 xr[FN][FM];
+    if (EPI == EPI_RESIDUAL) {
+#pragma unroll
+      for (int a = 0; a < FN; ++a) {
+        const int col = n0 + wn * TN + a * 16 + 4 * fq;
+#pragma unroll
+        for (int b = 0; b < FM; ++b) {
+          const int tok = m0 + wm * TM + b * 16 + fr;
+          const size_t off = (tok < M && col < N) ? (size_t)tok * N + col : 0;
+          xr[a][b] = *reinterpret_cast<const uint2*>(resid + off);
+        }
+      }
+    }
 #pragma unroll
     for (int a = 0; a < FN; ++a) {
       const int col = n0 + wn * TN + a * 16 + 4 * fq;
@@ -461,11 +663,10 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_dma(
           const size_t off = (size_t)tok * N + col;
           f32x4 v = acc[a][b];
           if (EPI == EPI_RESIDUAL) {
-            const uint2 xr = *reinterpret_cast<const uint2*>(resid + off);
-            v[0] += bf2f(xr.x & 0xFFFFu);
-            v[1] += bf2f(xr.x >> 16);
-            v[2] += bf2f(xr.y & 0xFFFFu);
-            v[3] += bf2f(xr.y >> 16);
+            v[0] += bf2f(xr[a][b].x & 0xFFFFu);
+            v[1] += bf2f(xr[a][b].x >> 16);
+            v[2] += bf2f(xr[a][b].y & 0xFFFFu);
+            v[3] += bf2f(xr[a][b].y >> 16);
           }
           uint2 o;
           o.x = pack_bf16x2(v[0], v[1]);
@@ -482,13 +683,6 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_dma(
 constexpr int kBM = 256, kBN = 256, kWM = 2, kWN = 4;
 constexpr int kLdsBytes = 2 * (kBM + kBN) * 128;
 
-#ifndef FFN_PF_BK
-#define FFN_PF_BK 64
-#endif
-#ifndef FFN_PF_S
-#define FFN_PF_S 2
-#endif
-constexpr int kDmaBK = FFN_PF_BK, kDmaS = FFN_PF_S;
 
 template <int EPI>
 static hipError_t launch_cfg(const void* act, const void* w0, const void* w1, const void* resid,
@@ -497,13 +691,18 @@ static hipError_t launch_cfg(const void* act, const void* w0, const void* w1, co
   const long tiles = (long)((M + kBM - 1) / kBM) * ((N + BNO - 1) / BNO);
   // whole K tiles and every operand addressable by a buffer resource: LDS-fed kernel
   if (K % kDmaBK == 0 && (size_t)M * K * 2 < ((size_t)1 << 31) && (size_t)N * K * 2 < ((size_t)1 << 31)) {
-    hipLaunchKernelGGL((gemm_dma<kBM, kBN, kWM, kWN, EPI, kDmaBK, kDmaS>), dim3((unsigned)tiles),
-                       dim3(kWM * kWN * 64), 0, s, (const uint16_t*)act, (const uint16_t*)w0,
-                       (const uint16_t*)w1, (const uint16_t*)resid, (uint16_t*)out, M, N, K);
+    // whole tiles and an even number of K tiles: the ping-pong schedule
+    if (kPingPong && M % kBM == 0 && N % BNO == 0 && K % (kPpS * kPpBK) == 0)
+      hipLaunchKernelGGL((gemm_dma<kBM, kBN, kWM, kWN, EPI, kPpBK, kPpS, true>), dim3((unsigned)tiles),
+                         dim3(kWM * kWN * 64), 0, s, (const uint16_t*)act, (const uint16_t*)w0,
+                         (const uint16_t*)w1, (const uint16_t*)resid, (uint16_t*)out, M, N, K);
+    else
+      hipLaunchKernelGGL((gemm_dma<kBM, kBN, kWM, kWN, EPI, kDmaBK, kDmaS, false>), dim3((unsigned)tiles),
+                         dim3(kWM * kWN * 64), 0, s, (const uint16_t*)act, (const uint16_t*)w0,
+                         (const uint16_t*)w1, (const uint16_t*)resid, (uint16_t*)out, M, N, K);
     return hipGetLastError();
   }
   auto kern = gemm_bf16<kBM, kBN, kWM, kWN, EPI>;
-  // allow more than the default dynamic LDS (per device, so done per launch)
   // allow more than the default dynamic LDS (per device, so done per launch)
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      kLdsBytes);
