@@ -20,11 +20,18 @@ The same JSON line also carries:
   extra         - the other workloads: prefill block (M=8192, d=4096,
                   f=14336) fused and split gate/up, interleaved call by call,
                   in TFLOP/s; the standalone RMSNorm (16384 x 4096 bf16);
-                  the Q8_0 decode block (M=8, d=5120, f=17408); decode at
-                  M=1 and 4; measured HBM read-only and copy ceilings; torch
-                  matmul at the prefill shapes as vendor-library context.
+                  the Q8_0 and Q4_0 decode blocks (M=8, d=5120, f=17408);
+                  decode at M=1 and 4; measured HBM read-only and copy
+                  ceilings; torch matmul at the prefill shapes as
+                  vendor-library context; one GPU's f/8 share of an 8-way
+                  tensor-parallel block (decode, prefill, Q8); per-call
+                  p10/median/p90 of the decode call and the GFX clock
+                  sampled during decode and prefill calls (separate passes,
+                  outside the timed region of `value`).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra] [--no-cpu]
+       (W untimed calls, continued until at least --min-warmup-s seconds, default 1,
+        have passed; then K timed)
        python bench.py --profile-run   (decode steps plus one 512 MiB copy, for
                                         counter runs; prints nothing)
 Progress goes to stderr; stdout gets exactly one JSON line.
@@ -87,6 +94,77 @@ def time_calls(torch, fn, n):
     return s.elapsed_time(e) / n
 
 
+def per_call_us(torch, fn, n):
+    """p10 / median / p90 of single-call durations (us), one event pair per call."""
+    import numpy as np
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    torch.cuda.synchronize()
+    for i, (s, e) in enumerate(evs):
+        s.record()
+        fn(i)
+        e.record()
+    torch.cuda.synchronize()
+    t = np.array([s.elapsed_time(e) * 1e3 for s, e in evs])
+    return {"p10": round(float(np.percentile(t, 10)), 2), "p50": round(float(np.median(t)), 2),
+            "p90": round(float(np.percentile(t, 90)), 2), "calls": n}
+
+
+class ClockSampler:
+    """Samples the GPU's current GFX clock (MHz) from a background thread while
+    work runs; None when the system management library is unavailable.  Used
+    outside the timed region of `value` (the sampler competes for the
+    interpreter lock with the launching thread)."""
+
+    def __init__(self, torch):
+        self.h, self.samples, self._stop, self._thr = None, [], False, None
+        try:
+            import amdsmi
+            self.smi = amdsmi
+            amdsmi.amdsmi_init()
+            pr = torch.cuda.get_device_properties(0)
+            bdf = f"{pr.pci_domain_id:04x}:{pr.pci_bus_id:02x}:{pr.pci_device_id:02x}.0"
+            hs = amdsmi.amdsmi_get_processor_handles()
+            match = [h for h in hs if str(amdsmi.amdsmi_get_gpu_device_bdf(h)).lower() == bdf]
+            self.h = match[0] if match else (hs[0] if len(hs) == 1 else None)
+        except Exception as ex:  # no library, no permission, no match: report nothing
+            log("clock sampling unavailable:", repr(ex))
+            self.h = None
+
+    def _read(self):
+        return float(self.smi.amdsmi_get_clock_info(self.h, self.smi.AmdSmiClkType.GFX)["clk"])
+
+    def __enter__(self):
+        import threading
+        self.samples, self._stop = [], False
+        if self.h is None:
+            return self
+
+        def run():
+            while not self._stop:
+                try:
+                    self.samples.append(self._read())
+                except Exception:
+                    return
+                time.sleep(0.002)
+        self._thr = threading.Thread(target=run, daemon=True)
+        self._thr.start()
+        return self
+
+    def __exit__(self, *a):
+        self._stop = True
+        if self._thr is not None:
+            self._thr.join()
+        return False
+
+    def summary(self):
+        import numpy as np
+        if not self.samples:
+            return None
+        t = np.array(self.samples)
+        return {"gfx_mhz_median": round(float(np.median(t)), 0), "gfx_mhz_min": round(float(t.min()), 0),
+                "gfx_mhz_max": round(float(t.max()), 0), "samples": int(t.size)}
+
+
 def sha256(path):
     with open(path, "rb") as fh:
         return hashlib.sha256(fh.read()).hexdigest()
@@ -132,7 +210,7 @@ def cpu_baseline(b, target_s=10.0, threads=1):
                       f"{reps} call(s), {dt:.2f} s per call"}
 
 
-def extras(torch, np, ffn, I, sets, x, g, b, ws, extra):
+def extras(torch, np, ffn, I, sets, x, g, b, ws, extra, clocks):
     M, d, f = b.M, b.d, b.f
     # decode at M = 1 and 4 (first rows of the same draw)
     for m in (1, 4):
@@ -302,6 +380,12 @@ def extras(torch, np, ffn, I, sets, x, g, b, ws, extra):
     for i in range(10):  # interleaved call by call
         tf.append(time_calls(torch, lambda j: pstep(i, "fused"), 1))
         ts.append(time_calls(torch, lambda j: pstep(i, "split"), 1))
+    mf = float(np.median(tf))
+    with clocks:  # the clock under MFMA load, in a separate ~0.3 s pass of the same calls
+        for i in range(max(1, int(0.3 / (mf * 1e-3)))):
+            pstep(i, "fused")
+        torch.cuda.synchronize()
+    extra["gpu_clock_during_prefill_calls"] = clocks.summary()
     ffn.timing_reset()
     ffn.timing_enable(True, 256)
     for i in range(4):
@@ -337,6 +421,79 @@ def extras(torch, np, ffn, I, sets, x, g, b, ws, extra):
     del pw, hx, wgu
     torch.cuda.empty_cache()
 
+    # ------------------------------------- one GPU's share at tensor parallel 8
+    tp8_shards(torch, np, ffn, I, extra, best)
+
+
+def tp8_shards(torch, np, ffn, I, extra, read_ceiling):
+    """The block on one GPU's f/8 slice (the kernels a rank of an 8-way
+    tensor-parallel split runs; the all-reduce of the partial sums is not
+    built).  Decode and Q8 rotate enough weight copies to exceed the 256 MB
+    last-level cache."""
+    out = {}
+    wl = I.WORKLOADS["decode_tp8_shard"]
+    M, d, f = wl["M"], wl["d"], wl["f"]
+    bb = I.make_block(wl["seed"], M, d, f, "bf16")
+    x, g = to_dev(bb.x, torch), to_dev(bb.g, torch)
+    w0 = [to_dev(a, torch) for a in (bb.w_gate, bb.w_up, bb.w_down)]
+    nrot = 10
+    sets = [w0] + [[t.clone() for t in w0] for _ in range(nrot - 1)]
+    ws = ffn.alloc_workspace(ffn.workspace_size(ffn.FFN_BF16, M, d, f, "auto"))
+    y = torch.empty_like(x)
+
+    def dstep(i):
+        wg, wu, wd = sets[i % nrot]
+        ffn.swiglu_block(x, g, wg, wu, wd, bb.eps, "auto", out=y, workspace=ws)
+    for i in range(50):
+        dstep(i)
+    t = time_calls(torch, dstep, 500)
+    gbs = decode_bytes(M, d, f) / (t * 1e-3) / 1e9
+    out["decode_M16_f1376"] = {"us": round(t * 1e3, 2), "GBps": round(gbs, 1),
+                               "frac_of_read_ceiling": round(gbs / read_ceiling, 4)}
+    del sets, w0
+    torch.cuda.empty_cache()
+
+    wl = I.WORKLOADS["prefill_tp8_shard"]
+    M, d, f = wl["M"], wl["d"], wl["f"]
+    bb = I.make_block(wl["seed"], M, d, f, "bf16")
+    x, g = to_dev(bb.x, torch), to_dev(bb.g, torch)
+    w = [to_dev(a, torch) for a in (bb.w_gate, bb.w_up, bb.w_down)]
+    ws = ffn.alloc_workspace(ffn.workspace_size(ffn.FFN_BF16, M, d, f, "fused"))
+    y = torch.empty_like(x)
+    for _ in range(3):
+        ffn.swiglu_block(x, g, *w, bb.eps, "fused", out=y, workspace=ws)
+    tp = time_calls(torch, lambda i: ffn.swiglu_block(x, g, *w, bb.eps, "fused", out=y, workspace=ws), 10)
+    tf = 6.0 * M * d * f / (tp * 1e-3) / 1e12
+    out["prefill_M8192_f1792_fused"] = {"ms": round(tp, 3), "TFLOPs": round(tf, 1),
+                                        "frac_of_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4)}
+    del w, x, y, ws
+    torch.cuda.empty_cache()
+
+    wl = I.WORKLOADS["q8_tp8_shard"]
+    M, d, f = wl["M"], wl["d"], wl["f"]
+    q = I.make_q8_block(wl["seed"], M, d, f)
+    qx, qg = to_dev(q.x, torch), to_dev(q.g, torch)
+    q0 = [(torch.from_numpy(m.qs).to("cuda"), torch.from_numpy(m.scales.view(np.int16)).to("cuda"))
+          for m in (q.w_gate, q.w_up, q.w_down)]
+    qsets = [q0] + [[(a.clone(), s.clone()) for a, s in q0] for _ in range(nrot - 1)]
+    qws = ffn.alloc_workspace(ffn.lib().ffn_swiglu_block_q8_workspace_size(M, d, f))
+    qy = torch.empty_like(qx)
+
+    def qstep(i):
+        a, bq, c = qsets[i % nrot]
+        ffn.swiglu_block_q8(qx, qg, a, bq, c, q.eps, out=qy, workspace=qws)
+    for i in range(50):
+        qstep(i)
+    tq = time_calls(torch, qstep, 500)
+    qbytes = 3 * (f * d + f * d // 32 * 2) + 2 * M * d * 2 + d * 2
+    qgbs = qbytes / (tq * 1e-3) / 1e9
+    out["q8_M8_f2176"] = {"us": round(tq * 1e3, 2), "GBps": round(qgbs, 1),
+                          "frac_of_read_ceiling": round(qgbs / read_ceiling, 4)}
+    del qsets, q0
+    torch.cuda.empty_cache()
+    extra["tp8_shard"] = out
+    log("tp8 shard", out)
+
 
 def main() -> int:
     ap = argparse.ArgumentParser()
@@ -345,6 +502,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-extra", action="store_true", help="skip the secondary workloads")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--min-warmup-s", type=float, default=1.0,
+                    help="continue the warm-up until this many seconds have passed (0: W calls only)")
     ap.add_argument("--profile-run", action="store_true",
                     help="decode steps plus one 512 MiB copy (counter calibration); no output")
     args = ap.parse_args()
@@ -376,9 +535,16 @@ def main() -> int:
         wg, wu, wd = sets[i % ROTATE]
         ffn.swiglu_block(x, g, wg, wu, wd, b.eps, "auto", out=y, workspace=ws)
 
-    for i in range(args.warmup):
+    # warm-up: W calls, continued until at least one second has passed
+    t0 = time.perf_counter()
+    i = 0
+    while i < args.warmup or time.perf_counter() - t0 < args.min_warmup_s:
         step(i)
+        i += 1
+        if i % 256 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
+    log(f"warm-up: {i} calls in {time.perf_counter() - t0:.2f} s")
     ms = time_calls(torch, step, args.steps)              # the timed region
     value = decode_bytes(M, d, f) / (ms * 1e-3) / 1e9
     log(f"decode M={M}: {ms * 1e3:.2f} us/call, {value:.1f} GB/s")
@@ -407,11 +573,23 @@ def main() -> int:
     kernels = {k: {"launches": n, "avg_us": round(t / n * 1e3, 2)} for k, (n, t) in kt.items()}
     log(f"kernels {kernels}; instrumented pass {ms_instr * 1e3:.2f} us/call")
 
+    pct = per_call_us(torch, step, args.steps)
+    # the clock under this load, over ~0.3 s of the same calls (the driver's
+    # clock readout refreshes every few ms; a shorter window reads idle)
+    clocks = ClockSampler(torch)
+    with clocks:
+        for i in range(max(1, int(0.3 / (ms * 1e-3)))):
+            step(i)
+        torch.cuda.synchronize()
+    log(f"decode per-call us {pct}; clock {clocks.summary()}")
+
     extra = {"decode_M16_GBps": round(value, 1), "decode_M16_us": round(ms * 1e3, 2),
              "decode_kernels_event_timed": kernels,
-             "decode_M16_instrumented_us": round(ms_instr * 1e3, 2)}
+             "decode_M16_instrumented_us": round(ms_instr * 1e3, 2),
+             "decode_M16_call_us_percentiles": pct,
+             "gpu_clock_during_decode_calls": clocks.summary()}
     if not args.no_extra:
-        extras(torch, np, ffn, I, sets, x, g, b, ws, extra)
+        extras(torch, np, ffn, I, sets, x, g, b, ws, extra, clocks)
 
     cpu = None
     if not args.no_cpu:

@@ -370,6 +370,93 @@ def test_block_zero_down_projection_returns_x_bitwise(gpu_lib, M):
 
 
 # ----------------------------------------------------------------------------
+# M-tail consistency: the first a rows of an M=b call, run as an M=a call
+# ----------------------------------------------------------------------------
+def _tail_pair(kind, a, b, d, f):
+    """(y of rows 0..a-1 from an M=a call, the same rows from an M=b call), bf16 bits."""
+    from transformer_ffn_block_amd import ffn
+    import torch
+    if kind == "bf16":
+        blk = I.make_block(2000 + a + b, b, d, f, "bf16")
+        x, g, wg, wu, wd = _block_dev(blk)
+        ya = ffn.swiglu_block(x[:a].contiguous(), g, wg, wu, wd, blk.eps, variant="auto")
+        yb = ffn.swiglu_block(x, g, wg, wu, wd, blk.eps, variant="auto")
+    elif kind == "q8":
+        q = I.make_q8_block(2100 + a + b, b, d, f)
+        mats = [_q8_dev(m) for m in (q.w_gate, q.w_up, q.w_down)]
+        x = dev(q.x)
+        ya = ffn.swiglu_block_q8(x[:a].contiguous(), dev(q.g), *mats, q.eps)
+        yb = ffn.swiglu_block_q8(x, dev(q.g), *mats, q.eps)
+    else:
+        q = I.make_q4_block(2200 + a + b, b, d, f)
+        mats = [_q4_dev(m) for m in (q.w_gate, q.w_up, q.w_down)]
+        x = dev(q.x)
+        ya = ffn.swiglu_block_q4(x[:a].contiguous(), dev(q.g), *mats, q.eps)
+        yb = ffn.swiglu_block_q4(x, dev(q.g), *mats, q.eps)
+    torch.cuda.synchronize()
+    return host_bits(ya), host_bits(yb)[:a]
+
+
+# Rows are independent and each kernel's summation order does not depend on
+# M, so rows shared by two calls that take the same kernels are bitwise equal:
+# decode 17 vs 32 tokens (the two-tile kernels), prefill 300 vs 512 tokens
+# (ragged tiles in the one-group schedule vs whole tiles in the two-group
+# one), Q8/Q4 5 vs 8 and 17 vs 32 tokens.
+@pytest.mark.parametrize("kind,a,b,d,f", [("bf16", 17, 32, 1024, 2816), ("bf16", 300, 512, 512, 768),
+                                          ("q8", 5, 8, 512, 1024), ("q8", 17, 32, 512, 704),
+                                          ("q4", 5, 8, 512, 1024), ("q4", 17, 32, 512, 704)])
+def test_m_tail_rows_bitwise_equal(gpu_lib, kind, a, b, d, f):
+    _say("m-tail", kind, a, b, d, f)
+    ya, yb = _tail_pair(kind, a, b, d, f)
+    assert np.array_equal(ya, yb)
+
+
+# ----------------------------------------------------------------------------
+# one GPU's share of the tensor-parallel block (f/8), at its real shapes
+# ----------------------------------------------------------------------------
+def test_tp8_shard_decode(gpu_lib):
+    from transformer_ffn_block_amd import ffn
+    wl = I.WORKLOADS["decode_tp8_shard"]
+    _say("tp8 shard decode", wl)
+    blk = I.make_block(wl["seed"], wl["M"], wl["d"], wl["f"], "bf16")
+    r = O.block_from_stored("bf16", blk.x, blk.g, blk.w_gate, blk.w_up, blk.w_down, blk.eps)
+    err = max_norm_err(host_f64(_run_block(ffn, blk, "auto")), r)
+    _say("err", err)
+    assert err <= TOL_BF16
+
+
+def test_tp8_shard_prefill_sampled_rows(gpu_lib):
+    from transformer_ffn_block_amd import ffn
+    wl = I.WORKLOADS["prefill_tp8_shard"]
+    _say("tp8 shard prefill", wl)
+    blk = I.make_block(wl["seed"], wl["M"], wl["d"], wl["f"], "bf16")
+    rows = np.unique(np.concatenate([[0, 255, 256, blk.M - 1],
+                                     np.random.default_rng(45).choice(blk.M, 28, replace=False)]))
+    r = O.block_from_stored("bf16", blk.x[rows], blk.g, blk.w_gate, blk.w_up, blk.w_down, blk.eps)
+    for variant in ("fused", "split"):
+        err = max_norm_err(host_f64(_run_block(ffn, blk, variant))[rows], r)
+        _say(variant, "err", err)
+        assert err <= TOL_BF16
+
+
+@pytest.mark.parametrize("kind", ["q8", "q4"])
+def test_tp8_shard_quantised(gpu_lib, kind):
+    from transformer_ffn_block_amd import ffn
+    wl = I.WORKLOADS[f"{kind}_tp8_shard"]
+    _say("tp8 shard", kind, wl)
+    if kind == "q8":
+        q = I.make_q8_block(wl["seed"], wl["M"], wl["d"], wl["f"])
+        err = max_norm_err(_run_q8(ffn, q), _q8_ref(q))
+        tol = TOL_Q8
+    else:
+        q = I.make_q4_block(wl["seed"], wl["M"], wl["d"], wl["f"])
+        err = max_norm_err(_run_q4(ffn, q), _q4_ref(q))
+        tol = TOL_Q4
+    _say("err", err)
+    assert err <= tol
+
+
+# ----------------------------------------------------------------------------
 # Q8_0
 # ----------------------------------------------------------------------------
 def _q8_dev(m: I.Q8Matrix):

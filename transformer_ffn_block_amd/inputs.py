@@ -291,4 +291,10 @@ WORKLOADS = {
     "prefill":    dict(seed=4, M=8192, d=4096, f=14336, dtype="bf16"),
     "q8_decode":  dict(seed=5, M=8, d=5120, f=17408),
     "q4_decode":  dict(seed=6, M=8, d=5120, f=17408),
+    # one GPU's share of a block tensor-parallel over f on 8 GPUs: W_gate and
+    # W_up keep f/8 rows, W_down f/8 columns (f/8 stays a multiple of 32)
+    "decode_tp8_shard":  dict(seed=7, M=16, d=4096, f=11008 // 8, dtype="bf16"),
+    "prefill_tp8_shard": dict(seed=8, M=8192, d=4096, f=14336 // 8, dtype="bf16"),
+    "q8_tp8_shard":      dict(seed=9, M=8, d=5120, f=17408 // 8),
+    "q4_tp8_shard":      dict(seed=10, M=8, d=5120, f=17408 // 8),
 }
