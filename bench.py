@@ -30,6 +30,7 @@ The same JSON line also carries:
                   outside the timed region of `value`).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra] [--no-cpu]
+                       [--extras decode_m,persistent,ceilings,rmsnorm,q8,q4,prefill,tp8]
        (W untimed calls, continued until at least --min-warmup-s seconds, default 1,
         have passed; then K timed)
        python bench.py --profile-run   (decode steps plus one 512 MiB copy, for
@@ -92,6 +93,14 @@ def time_calls(torch, fn, n):
     e.record()
     torch.cuda.synchronize()
     return s.elapsed_time(e) / n
+
+
+def ratio(a, b):
+    """a / b rounded, or None when the denominator was not measured."""
+    return round(a / b, 4) if b else None
+
+
+EXTRAS = ("decode_m", "persistent", "ceilings", "rmsnorm", "q8", "q4", "prefill", "tp8")
 
 
 def per_call_us(torch, fn, n):
@@ -210,219 +219,228 @@ def cpu_baseline(b, target_s=10.0, threads=1):
                       f"{reps} call(s), {dt:.2f} s per call"}
 
 
-def extras(torch, np, ffn, I, sets, x, g, b, ws, extra, clocks):
+def extras(torch, np, ffn, I, sets, x, g, b, ws, extra, clocks, want):
+    best = copy_gbs = None  # ceilings (GB/s), measured when "ceilings" is selected
     M, d, f = b.M, b.d, b.f
-    # decode at M = 1 and 4 (first rows of the same draw)
-    for m in (1, 4):
-        xm = x[:m].contiguous()
-        ym = torch.empty_like(xm)
+    if "decode_m" in want:
+        # decode at M = 1 and 4 (first rows of the same draw)
+        for m in (1, 4):
+            xm = x[:m].contiguous()
+            ym = torch.empty_like(xm)
 
-        def stepm(i, xm=xm, ym=ym):
+            def stepm(i, xm=xm, ym=ym):
+                wg, wu, wd = sets[i % ROTATE]
+                ffn.swiglu_block(xm, g, wg, wu, wd, b.eps, "auto", out=ym, workspace=ws)
+            for i in range(20):
+                stepm(i)
+            msm = time_calls(torch, stepm, 200)
+            extra[f"decode_M{m}"] = {"us": round(msm * 1e3, 2),
+                                     "GBps": round(decode_bytes(m, d, f) / (msm * 1e-3) / 1e9, 1)}
+            log(f"decode M={m}: {msm * 1e3:.2f} us/call")
+    if "persistent" in want:
+        # the single-dispatch (persistent) schedule at M = 16, interleaved with the
+        # default two-launch schedule
+        wsp = ffn.alloc_workspace(ffn.workspace_size(ffn.FFN_BF16, M, d, f, "persistent"))
+        yp = torch.empty_like(x)
+
+        def stepv(i, v):
             wg, wu, wd = sets[i % ROTATE]
-            ffn.swiglu_block(xm, g, wg, wu, wd, b.eps, "auto", out=ym, workspace=ws)
-        for i in range(20):
-            stepm(i)
-        msm = time_calls(torch, stepm, 200)
-        extra[f"decode_M{m}"] = {"us": round(msm * 1e3, 2),
-                                 "GBps": round(decode_bytes(m, d, f) / (msm * 1e-3) / 1e9, 1)}
-        log(f"decode M={m}: {msm * 1e3:.2f} us/call")
-    # the single-dispatch (persistent) schedule at M = 16, interleaved with the
-    # default two-launch schedule
-    wsp = ffn.alloc_workspace(ffn.workspace_size(ffn.FFN_BF16, M, d, f, "persistent"))
-    yp = torch.empty_like(x)
-
-    def stepv(i, v):
-        wg, wu, wd = sets[i % ROTATE]
-        ffn.swiglu_block(x, g, wg, wu, wd, b.eps, v, out=yp, workspace=wsp if v == "persistent" else ws)
-    tv = {"auto": [], "persistent": []}
-    for v in tv:
-        for i in range(10):
-            stepv(i, v)
-    for _ in range(3):
+            ffn.swiglu_block(x, g, wg, wu, wd, b.eps, v, out=yp, workspace=wsp if v == "persistent" else ws)
+        tv = {"auto": [], "persistent": []}
         for v in tv:
-            tv[v].append(time_calls(torch, lambda i, v=v: stepv(i, v), 50))
-    tp, ta = sorted(tv["persistent"])[1], sorted(tv["auto"])[1]
-    extra["decode_M16_persistent"] = {"us": round(tp * 1e3, 2), "two_launch_us": round(ta * 1e3, 2),
-                                      "persistent_over_two_launch": round(tp / ta, 3)}
-    log("persistent schedule", extra["decode_M16_persistent"])
-    del wsp, yp
-    sets.clear()
-    torch.cuda.empty_cache()
+            for i in range(10):
+                stepv(i, v)
+        for _ in range(3):
+            for v in tv:
+                tv[v].append(time_calls(torch, lambda i, v=v: stepv(i, v), 50))
+        tp, ta = sorted(tv["persistent"])[1], sorted(tv["auto"])[1]
+        extra["decode_M16_persistent"] = {"us": round(tp * 1e3, 2), "two_launch_us": round(ta * 1e3, 2),
+                                          "persistent_over_two_launch": round(tp / ta, 3)}
+        log("persistent schedule", extra["decode_M16_persistent"])
+        del wsp, yp
+        sets.clear()
+        torch.cuda.empty_cache()
 
-    # ------------------------------------------------------------ HBM ceilings
-    nbytes = 4 << 30
-    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
-    buf.fill_(1)
-    sink = torch.empty(16 * ffn.lib().ffn_probe_read_groups(32), dtype=torch.uint8, device="cuda")
-    best, sweep = 0.0, {}
-    for wpc in (4, 8, 12, 16, 32):
-        for _ in range(2):
-            ffn.probe_read(buf, sink, wpc)
-        t = time_calls(torch, lambda i: ffn.probe_read(buf, sink, wpc), 5)
-        sweep[wpc] = round(nbytes / (t * 1e-3) / 1e9, 1)
-        best = max(best, sweep[wpc])
-    half = nbytes // 2
-    src, dst = buf[:half], buf[half:]
-    ffn.probe_copy(src, dst)
-    tc = time_calls(torch, lambda i: ffn.probe_copy(src, dst), 5)
-    copy_gbs = 2 * half / (tc * 1e-3) / 1e9
-    extra["hbm_read_ceiling_GBps"] = best
-    extra["hbm_read_sweep_waves_per_cu"] = sweep
-    extra["hbm_copy_ceiling_GBps"] = round(copy_gbs, 1)
-    extra["decode_M16_frac_of_read_ceiling"] = round(extra["decode_M16_GBps"] / best, 4)
-    log(f"HBM read ceiling {best:.0f} GB/s {sweep}, copy {copy_gbs:.0f} GB/s")
-    del buf, sink, src, dst
-    torch.cuda.empty_cache()
+    if "ceilings" in want:
+        # ------------------------------------------------------------ HBM ceilings
+        nbytes = 4 << 30
+        buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        buf.fill_(1)
+        sink = torch.empty(16 * ffn.lib().ffn_probe_read_groups(32), dtype=torch.uint8, device="cuda")
+        best, sweep = 0.0, {}
+        for wpc in (4, 8, 12, 16, 32):
+            for _ in range(2):
+                ffn.probe_read(buf, sink, wpc)
+            t = time_calls(torch, lambda i: ffn.probe_read(buf, sink, wpc), 5)
+            sweep[wpc] = round(nbytes / (t * 1e-3) / 1e9, 1)
+            best = max(best, sweep[wpc])
+        half = nbytes // 2
+        src, dst = buf[:half], buf[half:]
+        ffn.probe_copy(src, dst)
+        tc = time_calls(torch, lambda i: ffn.probe_copy(src, dst), 5)
+        copy_gbs = 2 * half / (tc * 1e-3) / 1e9
+        extra["hbm_read_ceiling_GBps"] = best
+        extra["hbm_read_sweep_waves_per_cu"] = sweep
+        extra["hbm_copy_ceiling_GBps"] = round(copy_gbs, 1)
+        extra["decode_M16_frac_of_read_ceiling"] = ratio(extra["decode_M16_GBps"], best)
+        log(f"HBM read ceiling {best:.0f} GB/s {sweep}, copy {copy_gbs:.0f} GB/s")
+        del buf, sink, src, dst
+        torch.cuda.empty_cache()
 
-    # ---------------------------------------------------------------- RMSNorm
-    log("generating rmsnorm inputs", RMS)
-    xr, gr, eps, _ = I.make_rmsnorm(RMS["seed"], RMS["rows"], RMS["d"], "bf16")
-    xs = [to_dev(xr, torch)]
-    xs += [xs[0].clone() for _ in range(ROTATE - 1)]
-    ys = [torch.empty_like(xs[0]) for _ in range(ROTATE)]
-    gd = to_dev(gr, torch)
-    for i in range(8):
-        ffn.rmsnorm(xs[i % ROTATE], gd, eps, out=ys[i % ROTATE])
-    tr = time_calls(torch, lambda i: ffn.rmsnorm(xs[i % ROTATE], gd, eps, out=ys[i % ROTATE]), 40)
-    rbytes = 2 * RMS["rows"] * RMS["d"] * 2 + RMS["d"] * 2
-    rgbs = rbytes / (tr * 1e-3) / 1e9
-    extra["rmsnorm"] = {"us": round(tr * 1e3, 2), "GBps": round(rgbs, 1),
-                        "frac_of_hbm_peak": round(rgbs / HBM_PEAK_GBS, 4),
-                        "frac_of_read_ceiling": round(rgbs / best, 4),
-                        "frac_of_copy_ceiling": round(rgbs / copy_gbs, 4)}
-    log("rmsnorm", extra["rmsnorm"])
-    del xs, ys
-    torch.cuda.empty_cache()
+    if "rmsnorm" in want:
+        # ---------------------------------------------------------------- RMSNorm
+        log("generating rmsnorm inputs", RMS)
+        xr, gr, eps, _ = I.make_rmsnorm(RMS["seed"], RMS["rows"], RMS["d"], "bf16")
+        xs = [to_dev(xr, torch)]
+        xs += [xs[0].clone() for _ in range(ROTATE - 1)]
+        ys = [torch.empty_like(xs[0]) for _ in range(ROTATE)]
+        gd = to_dev(gr, torch)
+        for i in range(8):
+            ffn.rmsnorm(xs[i % ROTATE], gd, eps, out=ys[i % ROTATE])
+        tr = time_calls(torch, lambda i: ffn.rmsnorm(xs[i % ROTATE], gd, eps, out=ys[i % ROTATE]), 40)
+        rbytes = 2 * RMS["rows"] * RMS["d"] * 2 + RMS["d"] * 2
+        rgbs = rbytes / (tr * 1e-3) / 1e9
+        extra["rmsnorm"] = {"us": round(tr * 1e3, 2), "GBps": round(rgbs, 1),
+                            "frac_of_hbm_peak": round(rgbs / HBM_PEAK_GBS, 4),
+                            "frac_of_read_ceiling": ratio(rgbs, best),
+                            "frac_of_copy_ceiling": ratio(rgbs, copy_gbs)}
+        log("rmsnorm", extra["rmsnorm"])
+        del xs, ys
+        torch.cuda.empty_cache()
 
-    # ------------------------------------------------------------------- Q8_0
-    log("generating q8 inputs", Q8)
-    q = I.make_q8_block(Q8["seed"], Q8["M"], Q8["d"], Q8["f"])
-    qx, qg = to_dev(q.x, torch), to_dev(q.g, torch)
+    if "q8" in want:
+        # ------------------------------------------------------------------- Q8_0
+        log("generating q8 inputs", Q8)
+        q = I.make_q8_block(Q8["seed"], Q8["M"], Q8["d"], Q8["f"])
+        qx, qg = to_dev(q.x, torch), to_dev(q.g, torch)
 
-    def qdev(m):
-        return (torch.from_numpy(m.qs).to("cuda"), torch.from_numpy(m.scales.view(np.int16)).to("cuda"))
-    q0 = [qdev(m) for m in (q.w_gate, q.w_up, q.w_down)]
-    qsets = [q0] + [[(a.clone(), s.clone()) for a, s in q0] for _ in range(ROTATE - 1)]
-    qws = ffn.alloc_workspace(ffn.lib().ffn_swiglu_block_q8_workspace_size(Q8["M"], Q8["d"], Q8["f"]))
-    qy = torch.empty_like(qx)
+        def qdev(m):
+            return (torch.from_numpy(m.qs).to("cuda"), torch.from_numpy(m.scales.view(np.int16)).to("cuda"))
+        q0 = [qdev(m) for m in (q.w_gate, q.w_up, q.w_down)]
+        qsets = [q0] + [[(a.clone(), s.clone()) for a, s in q0] for _ in range(ROTATE - 1)]
+        qws = ffn.alloc_workspace(ffn.lib().ffn_swiglu_block_q8_workspace_size(Q8["M"], Q8["d"], Q8["f"]))
+        qy = torch.empty_like(qx)
 
-    def qstep(i):
-        a, bq, c = qsets[i % ROTATE]
-        ffn.swiglu_block_q8(qx, qg, a, bq, c, q.eps, out=qy, workspace=qws)
-    for i in range(20):
-        qstep(i)
-    tq = time_calls(torch, qstep, 200)
-    qbytes = 3 * (Q8["f"] * Q8["d"] + Q8["f"] * Q8["d"] // 32 * 2) + 2 * Q8["M"] * Q8["d"] * 2 + Q8["d"] * 2
-    qgbs = qbytes / (tq * 1e-3) / 1e9
-    extra["q8_decode"] = {"us": round(tq * 1e3, 2), "GBps": round(qgbs, 1),
-                          "frac_of_read_ceiling": round(qgbs / best, 4)}
-    log("q8", extra["q8_decode"])
-    del qsets, q0
-    torch.cuda.empty_cache()
+        def qstep(i):
+            a, bq, c = qsets[i % ROTATE]
+            ffn.swiglu_block_q8(qx, qg, a, bq, c, q.eps, out=qy, workspace=qws)
+        for i in range(20):
+            qstep(i)
+        tq = time_calls(torch, qstep, 200)
+        qbytes = 3 * (Q8["f"] * Q8["d"] + Q8["f"] * Q8["d"] // 32 * 2) + 2 * Q8["M"] * Q8["d"] * 2 + Q8["d"] * 2
+        qgbs = qbytes / (tq * 1e-3) / 1e9
+        extra["q8_decode"] = {"us": round(tq * 1e3, 2), "GBps": round(qgbs, 1),
+                              "frac_of_read_ceiling": ratio(qgbs, best)}
+        log("q8", extra["q8_decode"])
+        del qsets, q0
+        torch.cuda.empty_cache()
 
-    # ------------------------------------------------------------------- Q4_0
-    log("generating q4 inputs", Q4)
-    q4 = I.make_q4_block(Q4["seed"], Q4["M"], Q4["d"], Q4["f"])
-    q4x, q4g = to_dev(q4.x, torch), to_dev(q4.g, torch)
-    q40 = [qdev(m) for m in (q4.w_gate, q4.w_up, q4.w_down)]
-    q4sets = [q40] + [[(a.clone(), s.clone()) for a, s in q40] for _ in range(ROTATE - 1)]
-    q4ws = ffn.alloc_workspace(ffn.lib().ffn_swiglu_block_q4_workspace_size(Q4["M"], Q4["d"], Q4["f"]))
-    q4y = torch.empty_like(q4x)
+    if "q4" in want:
+        # ------------------------------------------------------------------- Q4_0
+        log("generating q4 inputs", Q4)
+        q4 = I.make_q4_block(Q4["seed"], Q4["M"], Q4["d"], Q4["f"])
+        q4x, q4g = to_dev(q4.x, torch), to_dev(q4.g, torch)
+        q40 = [qdev(m) for m in (q4.w_gate, q4.w_up, q4.w_down)]
+        q4sets = [q40] + [[(a.clone(), s.clone()) for a, s in q40] for _ in range(ROTATE - 1)]
+        q4ws = ffn.alloc_workspace(ffn.lib().ffn_swiglu_block_q4_workspace_size(Q4["M"], Q4["d"], Q4["f"]))
+        q4y = torch.empty_like(q4x)
 
-    def q4step(i):
-        a, bq, c = q4sets[i % ROTATE]
-        ffn.swiglu_block_q4(q4x, q4g, a, bq, c, q4.eps, out=q4y, workspace=q4ws)
-    for i in range(20):
-        q4step(i)
-    t4 = time_calls(torch, q4step, 200)
-    ffn.timing_reset()
-    ffn.timing_enable(True, 256)
-    for i in range(40):
-        q4step(i)
-    k4 = ffn.timing_collect()
-    ffn.timing_enable(False)
-    fd = Q4["f"] * Q4["d"]
-    q4_mat = fd // 2 + fd // 32 * 2          # nibbles + fp16 scales of one matrix
-    q4bytes = 3 * q4_mat + 2 * Q4["M"] * Q4["d"] * 2 + Q4["d"] * 2
-    q4gbs = q4bytes / (t4 * 1e-3) / 1e9
-    gu4 = k4["q4_gateup"][1] / k4["q4_gateup"][0] * 1e3     # us per launch
-    dn4 = k4["q4_down"][1] / k4["q4_down"][0] * 1e3
-    gu4_bytes = 2 * q4_mat + Q4["M"] * Q4["d"] * 2 + Q4["M"] * Q4["f"] * 2
-    dn4_bytes = q4_mat + Q4["M"] * Q4["f"] * 2 + 2 * Q4["M"] * Q4["d"] * 2
-    extra["q4_decode"] = {"us": round(t4 * 1e3, 2), "GBps": round(q4gbs, 1),
-                          "frac_of_read_ceiling": round(q4gbs / best, 4),
-                          "gateup_kernel_us": round(gu4, 2),
-                          "gateup_kernel_GBps": round(gu4_bytes / (gu4 * 1e-6) / 1e9, 1),
-                          "down_kernel_us": round(dn4, 2),
-                          "down_kernel_GBps": round(dn4_bytes / (dn4 * 1e-6) / 1e9, 1)}
-    log("q4", extra["q4_decode"])
-    del q4sets, q40
-    torch.cuda.empty_cache()
+        def q4step(i):
+            a, bq, c = q4sets[i % ROTATE]
+            ffn.swiglu_block_q4(q4x, q4g, a, bq, c, q4.eps, out=q4y, workspace=q4ws)
+        for i in range(20):
+            q4step(i)
+        t4 = time_calls(torch, q4step, 200)
+        ffn.timing_reset()
+        ffn.timing_enable(True, 256)
+        for i in range(40):
+            q4step(i)
+        k4 = ffn.timing_collect()
+        ffn.timing_enable(False)
+        fd = Q4["f"] * Q4["d"]
+        q4_mat = fd // 2 + fd // 32 * 2          # nibbles + fp16 scales of one matrix
+        q4bytes = 3 * q4_mat + 2 * Q4["M"] * Q4["d"] * 2 + Q4["d"] * 2
+        q4gbs = q4bytes / (t4 * 1e-3) / 1e9
+        gu4 = k4["q4_gateup"][1] / k4["q4_gateup"][0] * 1e3     # us per launch
+        dn4 = k4["q4_down"][1] / k4["q4_down"][0] * 1e3
+        gu4_bytes = 2 * q4_mat + Q4["M"] * Q4["d"] * 2 + Q4["M"] * Q4["f"] * 2
+        dn4_bytes = q4_mat + Q4["M"] * Q4["f"] * 2 + 2 * Q4["M"] * Q4["d"] * 2
+        extra["q4_decode"] = {"us": round(t4 * 1e3, 2), "GBps": round(q4gbs, 1),
+                              "frac_of_read_ceiling": ratio(q4gbs, best),
+                              "gateup_kernel_us": round(gu4, 2),
+                              "gateup_kernel_GBps": round(gu4_bytes / (gu4 * 1e-6) / 1e9, 1),
+                              "down_kernel_us": round(dn4, 2),
+                              "down_kernel_GBps": round(dn4_bytes / (dn4 * 1e-6) / 1e9, 1)}
+        log("q4", extra["q4_decode"])
+        del q4sets, q40
+        torch.cuda.empty_cache()
 
-    # ---------------------------------------------------------------- prefill
-    Mp, dp, fp = PREFILL["M"], PREFILL["d"], PREFILL["f"]
-    log("generating prefill inputs", PREFILL)
-    bp = I.make_block(PREFILL["seed"], Mp, dp, fp, "bf16")
-    px, pg = to_dev(bp.x, torch), to_dev(bp.g, torch)
-    pw = [[to_dev(a, torch) for a in (bp.w_gate, bp.w_up, bp.w_down)]]
-    pw.append([t.clone() for t in pw[0]])
-    pws = ffn.alloc_workspace(ffn.workspace_size(ffn.FFN_BF16, Mp, dp, fp, "split"))
-    py = torch.empty_like(px)
-    flops = 6.0 * Mp * dp * fp
+    if "prefill" in want:
+        # ---------------------------------------------------------------- prefill
+        Mp, dp, fp = PREFILL["M"], PREFILL["d"], PREFILL["f"]
+        log("generating prefill inputs", PREFILL)
+        bp = I.make_block(PREFILL["seed"], Mp, dp, fp, "bf16")
+        px, pg = to_dev(bp.x, torch), to_dev(bp.g, torch)
+        pw = [[to_dev(a, torch) for a in (bp.w_gate, bp.w_up, bp.w_down)]]
+        pw.append([t.clone() for t in pw[0]])
+        pws = ffn.alloc_workspace(ffn.workspace_size(ffn.FFN_BF16, Mp, dp, fp, "split"))
+        py = torch.empty_like(px)
+        flops = 6.0 * Mp * dp * fp
 
-    def pstep(i, variant):
-        wg, wu, wd = pw[i % 2]
-        ffn.swiglu_block(px, pg, wg, wu, wd, bp.eps, variant, out=py, workspace=pws)
-    for i in range(4):
-        pstep(i, "fused")
-        pstep(i, "split")
-    tf, ts = [], []
-    for i in range(10):  # interleaved call by call
-        tf.append(time_calls(torch, lambda j: pstep(i, "fused"), 1))
-        ts.append(time_calls(torch, lambda j: pstep(i, "split"), 1))
-    mf = float(np.median(tf))
-    with clocks:  # the clock under MFMA load, in a separate ~0.3 s pass of the same calls
-        for i in range(max(1, int(0.3 / (mf * 1e-3)))):
+        def pstep(i, variant):
+            wg, wu, wd = pw[i % 2]
+            ffn.swiglu_block(px, pg, wg, wu, wd, bp.eps, variant, out=py, workspace=pws)
+        for i in range(4):
             pstep(i, "fused")
-        torch.cuda.synchronize()
-    extra["gpu_clock_during_prefill_calls"] = clocks.summary()
-    ffn.timing_reset()
-    ffn.timing_enable(True, 256)
-    for i in range(4):
-        pstep(i, "fused")
-        pstep(i, "split")
-    kp = ffn.timing_collect()
-    ffn.timing_enable(False)
-    mf, msp = float(np.median(tf)), float(np.median(ts))
-    extra["prefill"] = {
-        "fused_ms": round(mf, 3), "split_ms": round(msp, 3),
-        "fused_TFLOPs": round(flops / (mf * 1e-3) / 1e12, 1),
-        "split_TFLOPs": round(flops / (msp * 1e-3) / 1e12, 1),
-        "fused_frac_of_bf16_peak": round(flops / (mf * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
-        "split_over_fused_time": round(msp / mf, 3),
-        "kernels_avg_ms_event_timed": {k: round(t / n, 4) for k, (n, t) in kp.items()}}
-    gu_ms = kp["gemm_gateup_fused"][1] / kp["gemm_gateup_fused"][0]
-    extra["prefill"]["gateup_fused_kernel_TFLOPs"] = round(4.0 * Mp * dp * fp / (gu_ms * 1e-3) / 1e12, 1)
-    log("prefill", extra["prefill"])
+            pstep(i, "split")
+        tf, ts = [], []
+        for i in range(10):  # interleaved call by call
+            tf.append(time_calls(torch, lambda j: pstep(i, "fused"), 1))
+            ts.append(time_calls(torch, lambda j: pstep(i, "split"), 1))
+        mf = float(np.median(tf))
+        with clocks:  # the clock under MFMA load, in a separate ~0.3 s pass of the same calls
+            for i in range(max(1, int(0.3 / (mf * 1e-3)))):
+                pstep(i, "fused")
+            torch.cuda.synchronize()
+        extra["gpu_clock_during_prefill_calls"] = clocks.summary()
+        ffn.timing_reset()
+        ffn.timing_enable(True, 256)
+        for i in range(4):
+            pstep(i, "fused")
+            pstep(i, "split")
+        kp = ffn.timing_collect()
+        ffn.timing_enable(False)
+        mf, msp = float(np.median(tf)), float(np.median(ts))
+        extra["prefill"] = {
+            "fused_ms": round(mf, 3), "split_ms": round(msp, 3),
+            "fused_TFLOPs": round(flops / (mf * 1e-3) / 1e12, 1),
+            "split_TFLOPs": round(flops / (msp * 1e-3) / 1e12, 1),
+            "fused_frac_of_bf16_peak": round(flops / (mf * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "split_over_fused_time": round(msp / mf, 3),
+            "kernels_avg_ms_event_timed": {k: round(t / n, 4) for k, (n, t) in kp.items()}}
+        gu_ms = kp["gemm_gateup_fused"][1] / kp["gemm_gateup_fused"][0]
+        extra["prefill"]["gateup_fused_kernel_TFLOPs"] = round(4.0 * Mp * dp * fp / (gu_ms * 1e-3) / 1e12, 1)
+        log("prefill", extra["prefill"])
 
-    # vendor-library context at the same shapes (torch matmul -> hipBLASLt)
-    wgu = torch.cat([pw[0][0], pw[0][1]], 0)
-    hx = torch.empty((Mp, fp), dtype=torch.bfloat16, device="cuda").normal_()
-    for _ in range(2):
-        torch.nn.functional.linear(px, wgu)
-        torch.nn.functional.linear(hx, pw[0][2])
-    tgu = time_calls(torch, lambda i: torch.nn.functional.linear(px, wgu), 5)
-    tdn = time_calls(torch, lambda i: torch.nn.functional.linear(hx, pw[0][2]), 5)
-    extra["prefill_torch_matmul_context"] = {
-        "gate_up_concat_ms": round(tgu, 3), "down_ms": round(tdn, 3),
-        "gate_up_TFLOPs": round(4.0 * Mp * dp * fp / (tgu * 1e-3) / 1e12, 1),
-        "down_TFLOPs": round(2.0 * Mp * dp * fp / (tdn * 1e-3) / 1e12, 1)}
-    log("torch matmul context", extra["prefill_torch_matmul_context"])
-    del pw, hx, wgu
-    torch.cuda.empty_cache()
+        # vendor-library context at the same shapes (torch matmul -> hipBLASLt)
+        wgu = torch.cat([pw[0][0], pw[0][1]], 0)
+        hx = torch.empty((Mp, fp), dtype=torch.bfloat16, device="cuda").normal_()
+        for _ in range(2):
+            torch.nn.functional.linear(px, wgu)
+            torch.nn.functional.linear(hx, pw[0][2])
+        tgu = time_calls(torch, lambda i: torch.nn.functional.linear(px, wgu), 5)
+        tdn = time_calls(torch, lambda i: torch.nn.functional.linear(hx, pw[0][2]), 5)
+        extra["prefill_torch_matmul_context"] = {
+            "gate_up_concat_ms": round(tgu, 3), "down_ms": round(tdn, 3),
+            "gate_up_TFLOPs": round(4.0 * Mp * dp * fp / (tgu * 1e-3) / 1e12, 1),
+            "down_TFLOPs": round(2.0 * Mp * dp * fp / (tdn * 1e-3) / 1e12, 1)}
+        log("torch matmul context", extra["prefill_torch_matmul_context"])
+        del pw, hx, wgu
+        torch.cuda.empty_cache()
 
-    # ------------------------------------- one GPU's share at tensor parallel 8
-    tp8_shards(torch, np, ffn, I, extra, best)
+    if "tp8" in want:
+        # ------------------------------------- one GPU's share at tensor parallel 8
+        tp8_shards(torch, np, ffn, I, extra, best)
 
 
 def tp8_shards(torch, np, ffn, I, extra, read_ceiling):
@@ -449,7 +467,7 @@ def tp8_shards(torch, np, ffn, I, extra, read_ceiling):
     t = time_calls(torch, dstep, 500)
     gbs = decode_bytes(M, d, f) / (t * 1e-3) / 1e9
     out["decode_M16_f1376"] = {"us": round(t * 1e3, 2), "GBps": round(gbs, 1),
-                               "frac_of_read_ceiling": round(gbs / read_ceiling, 4)}
+                               "frac_of_read_ceiling": ratio(gbs, read_ceiling)}
     del sets, w0
     torch.cuda.empty_cache()
 
@@ -488,7 +506,7 @@ def tp8_shards(torch, np, ffn, I, extra, read_ceiling):
     qbytes = 3 * (f * d + f * d // 32 * 2) + 2 * M * d * 2 + d * 2
     qgbs = qbytes / (tq * 1e-3) / 1e9
     out["q8_M8_f2176"] = {"us": round(tq * 1e3, 2), "GBps": round(qgbs, 1),
-                          "frac_of_read_ceiling": round(qgbs / read_ceiling, 4)}
+                          "frac_of_read_ceiling": ratio(qgbs, read_ceiling)}
     del qsets, q0
     torch.cuda.empty_cache()
     extra["tp8_shard"] = out
@@ -502,11 +520,17 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-extra", action="store_true", help="skip the secondary workloads")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--extras", default="all",
+                    help="comma-separated subset of the secondary workloads: " + ",".join(EXTRAS))
     ap.add_argument("--min-warmup-s", type=float, default=1.0,
                     help="continue the warm-up until this many seconds have passed (0: W calls only)")
     ap.add_argument("--profile-run", action="store_true",
                     help="decode steps plus one 512 MiB copy (counter calibration); no output")
     args = ap.parse_args()
+    want = set(EXTRAS) if args.extras == "all" else set(args.extras.split(","))
+    if not want <= set(EXTRAS):
+        print(f"unknown --extras {sorted(want - set(EXTRAS))}; choose from {','.join(EXTRAS)}", file=sys.stderr)
+        return 2
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the FFN block here is a single-GPU library "
               "(multi-GPU sharding is a design note, not built); run with --gpus 1", file=sys.stderr)
@@ -589,7 +613,7 @@ def main() -> int:
              "decode_M16_call_us_percentiles": pct,
              "gpu_clock_during_decode_calls": clocks.summary()}
     if not args.no_extra:
-        extras(torch, np, ffn, I, sets, x, g, b, ws, extra, clocks)
+        extras(torch, np, ffn, I, sets, x, g, b, ws, extra, clocks, want)
 
     cpu = None
     if not args.no_cpu:

@@ -7,6 +7,9 @@
       HBM traffic per launch of the matching kernel from FETCH_SIZE and
       WRITE_SIZE (KiB per dispatch), each scaled by what the same counter
       reads for the library's plain copy kernel (probe_copy) of known size.
+  python -m transformer_ffn_block_amd.profsum counters COUNTER_CSV --kernel SUBSTRING [--kernel ...] --command "..."
+      per-dispatch means of the counters of one --pmc run, and the MFMA busy
+      fraction when its counters are present.
 """
 from __future__ import annotations
 
@@ -97,6 +100,32 @@ def traffic(fetch_csv, write_csv, kernel, copy_bytes, source, bytes_per_launch, 
     return "\n".join(lines) + "\n"
 
 
+def counters(csv_path: str, kernels, command: str, xcds: int = 8, simds: int = 1024) -> str:
+    """Per-dispatch means of every counter in one --pmc run for each kernel
+    matching a substring; with SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE
+    also the MFMA busy fraction = busy cycles summed over SIMDs / (GUI-active
+    cycles per XCD x SIMDs)."""
+    per = collections.defaultdict(lambda: collections.defaultdict(list))
+    for r in _rows(csv_path):
+        per[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    out = ["# rocprofv3 counter summary (per-dispatch means)", f"# command: {command}",
+           f"# mfma_busy_frac = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / {xcds} * {simds})"]
+    for sub in kernels:
+        hits = [(k, v) for k, v in per.items() if sub in k]
+        if not hits:
+            raise SystemExit(f"no kernel matching {sub!r}")
+        k, cv = max(hits, key=lambda kv: max(len(x) for x in kv[1].values()))
+        out.append(f"kernel = {k.split('(')[0]}")
+        means = {c: statistics.fmean(v) for c, v in sorted(cv.items())}
+        out.append(f"  dispatches = {max(len(v) for v in cv.values())}")
+        for c, m in means.items():
+            out.append(f"  {c} = {m:.1f}")
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in means and means.get("GRBM_GUI_ACTIVE"):
+            frac = means["SQ_VALU_MFMA_BUSY_CYCLES"] / (means["GRBM_GUI_ACTIVE"] / xcds * simds)
+            out.append(f"  mfma_busy_frac = {frac:.4f}")
+    return "\n".join(out) + "\n"
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -112,9 +141,15 @@ def main(argv=None) -> int:
     t.add_argument("--bytes-per-launch", type=int, required=True)
     t.add_argument("--command", required=True)
     t.add_argument("--grid", type=int, default=None, help="only dispatches of this grid size")
+    c = sub.add_parser("counters")
+    c.add_argument("csv")
+    c.add_argument("--kernel", action="append", required=True, help="substring; repeatable")
+    c.add_argument("--command", required=True)
     a = ap.parse_args(argv)
     if a.cmd == "stats":
         sys.stdout.write(stats(a.trace_csv, a.command))
+    elif a.cmd == "counters":
+        sys.stdout.write(counters(a.csv, a.kernel, a.command))
     else:
         sys.stdout.write(traffic(a.fetch_csv, a.write_csv, a.kernel, a.copy_bytes, a.source,
                                  a.bytes_per_launch, a.command, a.grid))
