@@ -151,7 +151,9 @@ ffn_status ffn_swiglu_block(ffn_dtype dt, const void *x, const void *g,
                             ffn_variant variant, void *workspace, size_t workspace_bytes,
                             void *stream);
 
-/* Workspace bytes ffn_swiglu_block_q8 needs: n [M,d] and h [M,f] in bf16,
+/* Workspace bytes ffn_swiglu_block_q8 needs: n [M,d] (not when the norm is
+ * folded into the gate/up kernel: M <= 8 and (f/16) * (d/256) <= 10240,
+ * both rounded up) and h [M,f] in bf16,
  * then the fp32 partial sums of the split-K down projection,
  * [splits, min(M, 32), d] (splits, 1..8, is fixed by d and f); 0 on a shape
  * the entry point would reject for its sizes. */
@@ -165,6 +167,9 @@ size_t ffn_swiglu_block_q8_workspace_size(int64_t M, int64_t d, int64_t f);
  * Weights are dequantised in registers (q * s, exact in fp32) and never
  * written back; accumulation is fp32.
  * Returns FFN_OK, INVALID_ARGUMENT, UNSUPPORTED, WORKSPACE or LAUNCH. */
+/* With the norm folded (see the workspace size) the gate/up kernel stages
+ * bf16(x * g) and applies r_m to the fp32 sums, as the bf16 decode path
+ * does; otherwise n is materialised in bf16 first.  h is rounded to bf16. */
 ffn_status ffn_swiglu_block_q8(const void *x, const void *g, const ffn_q8_matrix *w_gate,
                                const ffn_q8_matrix *w_up, const ffn_q8_matrix *w_down,
                                void *y, int64_t M, int64_t d, int64_t f, float eps,

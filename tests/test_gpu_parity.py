@@ -497,6 +497,25 @@ def test_q8_ragged_tokens(gpu_lib, M, d, f):
     assert max_norm_err(_run_q8(ffn, q), _q8_ref(q)) <= TOL_Q8
 
 
+def test_q8_folded_and_materialised_norm_agree(gpu_lib):
+    """A narrow projection folds the norm into the gate/up kernel up to 8
+    tokens; from 9 on n is materialised first: the rows shared by an 8- and a
+    9-token call agree to the tolerance (different roundings of the
+    normalised activations)."""
+    from transformer_ffn_block_amd import ffn
+    import torch
+    q = I.make_q8_block(2400, 9, 512, 1024)
+    mats = [_q8_dev(m) for m in (q.w_gate, q.w_up, q.w_down)]
+    x = dev(q.x)
+    y8 = ffn.swiglu_block_q8(x[:8].contiguous(), dev(q.g), *mats, q.eps)
+    y9 = ffn.swiglu_block_q8(x, dev(q.g), *mats, q.eps)
+    torch.cuda.synchronize()
+    r = _q8_ref(q)
+    a8, a9 = host_f64(y8), host_f64(y9)
+    assert max_norm_err(a8, r[:8]) <= TOL_Q8 and max_norm_err(a9, r) <= TOL_Q8
+    assert max_norm_err(a8, a9[:8]) <= TOL_Q8
+
+
 def test_q8_subnormal_scales_are_not_flushed(gpu_lib):
     """Every scale subnormal (bits 0x0100..0x03FF).  x is scaled by 2^-20 and
     eps = 0, so n is unchanged while the residual no longer hides the tiny

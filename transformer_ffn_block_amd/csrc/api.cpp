@@ -302,7 +302,11 @@ ffn_status ffn_swiglu_block(ffn_dtype dt, const void* x, const void* g, const vo
 namespace {
 
 // Q8_0 and Q4_0 blocks share validation and the launch sequence; the traits
-// give the storage of one matrix and its kernels.
+// give the storage of one matrix and its kernels, and whether the gate/up
+// kernel folds the norm in (then n is never materialised).
+#ifndef FFN_Q8_FOLD
+#define FFN_Q8_FOLD 1
+#endif
 struct Q8Traits {
   using Mat = ffn_q8_matrix;
   static constexpr const char* name = "Q8";
@@ -316,9 +320,18 @@ struct Q8Traits {
     const int sp = ffn::q8_down_splits((int)d, (int)f);
     return sp > 1 ? (size_t)sp * (size_t)Mc * (size_t)d * 4 : 0;
   }
-  static hipError_t gateup(const void* n, const Mat* g, const Mat* u, void* h, int M, int d, int f,
-                           hipStream_t s) {
-    return ffn::launch_q8_gateup(n, g->qs, g->scales, u->qs, u->scales, h, M, d, f, s);
+  // The norm folds into the gate/up kernel when that saves more than it
+  // costs: the fold removes one launch (~5 us) but adds staging work in
+  // proportion to the row tiles x 256-k stages the kernel walks.  Measured:
+  // f = 2176 (136 tiles x 20 stages) 26.4 -> 23.8 us per block; f = 17408
+  // (1088 x 20) gate/up 45.2 -> 51.1 us, no net gain; 16 and 32 tokens
+  // slower.  So: up to 8 tokens and at most 10240 tile-stages.
+  static bool fold(int64_t M, int64_t d, int64_t f) {
+    return FFN_Q8_FOLD != 0 && M <= 8 && ((f + 15) / 16) * ((d + 255) / 256) <= 10240;
+  }
+  static hipError_t gateup(const void* act, const void* gain, float eps, const Mat* g, const Mat* u,
+                           void* h, int M, int d, int f, hipStream_t s) {
+    return ffn::launch_q8_gateup(act, gain, eps, g->qs, g->scales, u->qs, u->scales, h, M, d, f, s);
   }
   static hipError_t down(const void* h, const Mat* w, const void* x, void* y, float* part, int M,
                          int d, int f, hipStream_t s) {
@@ -338,9 +351,12 @@ struct Q4Traits {
     const int sp = ffn::q4_down_splits((int)d, (int)f);
     return sp > 1 ? (size_t)sp * (size_t)Mc * (size_t)d * 4 : 0;
   }
-  static hipError_t gateup(const void* n, const Mat* g, const Mat* u, void* h, int M, int d, int f,
-                           hipStream_t s) {
-    return ffn::launch_q4_gateup(n, g->qs, g->scales, u->qs, u->scales, h, M, d, f, s);
+  static bool fold(int64_t, int64_t, int64_t) { return false; }
+  static hipError_t gateup(const void* act, const void* gain, float eps, const Mat* g, const Mat* u,
+                           void* h, int M, int d, int f, hipStream_t s) {
+    (void)gain;
+    (void)eps;
+    return ffn::launch_q4_gateup(act, g->qs, g->scales, u->qs, u->scales, h, M, d, f, s);
   }
   static hipError_t down(const void* h, const Mat* w, const void* x, void* y, float* part, int M,
                          int d, int f, hipStream_t s) {
@@ -348,14 +364,27 @@ struct Q4Traits {
   }
 };
 
-// Workspace of a quantised block: n [M,d] and h [M,f] in bf16, then the
-// down projection's split-K partials for one chunk of tokens.
+// Workspace of a quantised block: n [M,d] (unless the norm is folded) and
+// h [M,f] in bf16, then the down projection's split-K partials for one
+// chunk of tokens.
+struct QuantWs {
+  size_t n = 0, h = 0, part = 0, total = 0;
+};
 template <class T>
-static size_t quant_ws_bytes(int64_t M, int64_t d, int64_t f, size_t* part_at) {
-  const WsLayout L = ws_layout(2, M, d, f, false);
+static QuantWs quant_ws(int64_t M, int64_t d, int64_t f) {
+  QuantWs w;
+  size_t at = 0;
+  if (!T::fold(M, d, f)) {
+    w.n = at;
+    at += round256((size_t)M * d * 2);
+  }
+  w.h = at;
+  at += round256((size_t)M * f * 2);
   const int64_t mc = M < T::max_tokens() ? M : T::max_tokens();
-  if (part_at) *part_at = L.total;
-  return L.total + round256(T::part_bytes(mc, d, f));
+  w.part = at;
+  at += round256(T::part_bytes(mc, d, f));
+  w.total = at;
+  return w;
 }
 
 template <class T>
@@ -377,9 +406,8 @@ static ffn_status quant_block(const void* x, const void* g, const typename T::Ma
     return fail(FFN_ERR_UNSUPPORTED, "%s quant arrays must be smaller than 2 GiB", T::name);
   if (!aligned(x, 16) || !aligned(g, 16) || !aligned(y, 16))
     return fail(FFN_ERR_UNSUPPORTED, "x, g and y must be 16-byte aligned");
-  const WsLayout L = ws_layout(2, M, d, f, false);
-  size_t part_at = 0;
-  const size_t ws_total = quant_ws_bytes<T>(M, d, f, &part_at);
+  const QuantWs L = quant_ws<T>(M, d, f);
+  const size_t ws_total = L.total;
   if (M > 0 && (!workspace || workspace_bytes < ws_total))
     return fail(FFN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", ws_total,
                 workspace ? workspace_bytes : (size_t)0);
@@ -397,13 +425,16 @@ static ffn_status quant_block(const void* x, const void* g, const typename T::Ma
   char* ws = (char*)workspace;
   char* n = ws + L.n;
   char* h = ws + L.h;
-  float* part = (float*)(ws + part_at);
-  FFN_LAUNCH("rmsnorm", s, ffn::launch_rmsnorm(2, x, g, n, M, d, eps, s));
+  float* part = (float*)(ws + L.part);
+  const bool fold = T::fold(M, d, f);
+  if (!fold) FFN_LAUNCH("rmsnorm", s, ffn::launch_rmsnorm(2, x, g, n, M, d, eps, s));
+  const char* act = fold ? (const char*)x : n;
   const int step = T::max_tokens();
   for (int64_t m0 = 0; m0 < M; m0 += step) {
     const int mc = (int)(M - m0 < step ? M - m0 : step);
     FFN_LAUNCH(T::gateup_name, s,
-               T::gateup(n + m0 * d * 2, w_gate, w_up, h + m0 * f * 2, mc, (int)d, (int)f, s));
+               T::gateup(act + m0 * d * 2, fold ? g : nullptr, eps, w_gate, w_up, h + m0 * f * 2, mc,
+                         (int)d, (int)f, s));
     FFN_LAUNCH(T::down_name, s,
                T::down(h + m0 * f * 2, w_down, (const char*)x + m0 * d * 2, (char*)y + m0 * d * 2,
                        part, mc, (int)d, (int)f, s));
@@ -417,7 +448,7 @@ extern "C" {
 
 size_t ffn_swiglu_block_q8_workspace_size(int64_t M, int64_t d, int64_t f) {
   if (M < 0 || d <= 0 || f <= 0 || d > INT32_MAX || f > INT32_MAX) return 0;
-  return quant_ws_bytes<Q8Traits>(M, d, f, nullptr);
+  return quant_ws<Q8Traits>(M, d, f).total;
 }
 
 ffn_status ffn_swiglu_block_q8(const void* x, const void* g, const ffn_q8_matrix* w_gate,
@@ -430,7 +461,7 @@ ffn_status ffn_swiglu_block_q8(const void* x, const void* g, const ffn_q8_matrix
 
 size_t ffn_swiglu_block_q4_workspace_size(int64_t M, int64_t d, int64_t f) {
   if (M < 0 || d <= 0 || f <= 0 || d > INT32_MAX || f > INT32_MAX) return 0;
-  return quant_ws_bytes<Q4Traits>(M, d, f, nullptr);
+  return quant_ws<Q4Traits>(M, d, f).total;
 }
 
 ffn_status ffn_swiglu_block_q4(const void* x, const void* g, const ffn_q4_matrix* w_gate,

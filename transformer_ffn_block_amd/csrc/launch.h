@@ -52,11 +52,13 @@ hipError_t launch_swiglu_f32(const float* G, const float* U, float* h, int64_t c
 constexpr int kQuantMaxSplits = 8;
 
 // Q8_0 weight-streaming projections (bf16 activations, in-register dequant).
-//   gate/up: h = silu(n Wg^T) * (n Wu^T)
+//   gate/up: h = silu(n Wg^T) * (n Wu^T); with gain != nullptr (M <= 8) act
+//            is x and n = rmsnorm(x) * gain is folded in (eps inside the
+//            root), otherwise act is n
 //   down   : y = x + h Wd^T
-hipError_t launch_q8_gateup(const void* n, const int8_t* qg, const uint16_t* sg,
-                            const int8_t* qu, const uint16_t* su, void* h, int M, int d, int f,
-                            hipStream_t s);
+hipError_t launch_q8_gateup(const void* act, const void* gain, float eps, const int8_t* qg,
+                            const uint16_t* sg, const int8_t* qu, const uint16_t* su, void* h,
+                            int M, int d, int f, hipStream_t s);
 // Down projection, split over K into q8_down_splits(d, f) ranges when that
 // is above 1 (partials in part[splits][M][d], as for Q4_0 below).
 int q8_down_splits(int N, int K);
