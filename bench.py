@@ -24,7 +24,7 @@ The same JSON line also carries:
                   decode at M=1 and 4; measured HBM read-only and copy
                   ceilings; torch matmul at the prefill shapes as
                   vendor-library context; one GPU's f/8 share of an 8-way
-                  tensor-parallel block (decode, prefill, Q8); per-call
+                  tensor-parallel block (decode, prefill, Q8, Q4); per-call
                   p10/median/p90 of the decode call and the GFX clock
                   sampled during decode and prefill calls (separate passes,
                   outside the timed region of `value`).
@@ -506,6 +506,29 @@ def tp8_shards(torch, np, ffn, I, extra, read_ceiling):
     qbytes = 3 * (f * d + f * d // 32 * 2) + 2 * M * d * 2 + d * 2
     qgbs = qbytes / (tq * 1e-3) / 1e9
     out["q8_M8_f2176"] = {"us": round(tq * 1e3, 2), "GBps": round(qgbs, 1),
+                          "frac_of_read_ceiling": ratio(qgbs, read_ceiling)}
+    del qsets, q0
+    torch.cuda.empty_cache()
+
+    wl = I.WORKLOADS["q4_tp8_shard"]
+    M, d, f = wl["M"], wl["d"], wl["f"]
+    q4 = I.make_q4_block(wl["seed"], M, d, f)
+    qx, qg = to_dev(q4.x, torch), to_dev(q4.g, torch)
+    q0 = [(torch.from_numpy(m.qs).to("cuda"), torch.from_numpy(m.scales.view(np.int16)).to("cuda"))
+          for m in (q4.w_gate, q4.w_up, q4.w_down)]
+    qsets = [q0] + [[(a.clone(), s.clone()) for a, s in q0] for _ in range(2 * nrot - 1)]
+    qws = ffn.alloc_workspace(ffn.lib().ffn_swiglu_block_q4_workspace_size(M, d, f))
+    qy = torch.empty_like(qx)
+
+    def q4step(i):
+        a, bq, c = qsets[i % (2 * nrot)]
+        ffn.swiglu_block_q4(qx, qg, a, bq, c, q4.eps, out=qy, workspace=qws)
+    for i in range(50):
+        q4step(i)
+    tq = time_calls(torch, q4step, 500)
+    qbytes = 3 * (f * d // 2 + f * d // 32 * 2) + 2 * M * d * 2 + d * 2
+    qgbs = qbytes / (tq * 1e-3) / 1e9
+    out["q4_M8_f2176"] = {"us": round(tq * 1e3, 2), "GBps": round(qgbs, 1),
                           "frac_of_read_ceiling": ratio(qgbs, read_ceiling)}
     del qsets, q0
     torch.cuda.empty_cache()

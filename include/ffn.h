@@ -175,7 +175,8 @@ ffn_status ffn_swiglu_block_q8(const void *x, const void *g, const ffn_q8_matrix
                                void *y, int64_t M, int64_t d, int64_t f, float eps,
                                void *workspace, size_t workspace_bytes, void *stream);
 
-/* Workspace bytes ffn_swiglu_block_q4 needs: n [M,d] and h [M,f] in bf16,
+/* Workspace bytes ffn_swiglu_block_q4 needs: n [M,d] (not when the norm is
+ * folded, on the same condition as for Q8_0) and h [M,f] in bf16,
  * then the fp32 partial sums of the split-K down projection,
  * [splits, min(M, 32), d] (splits, 1..8, is fixed by d and f); 0 on a shape
  * the entry point would reject for its sizes. */
@@ -189,7 +190,8 @@ size_t ffn_swiglu_block_q4_workspace_size(int64_t M, int64_t d, int64_t f);
  *   d, f : multiples of 32 (so no block straddles a row); f*d/2 < 2^31 bytes
  *          of nibbles per matrix.
  * Weights are dequantised in registers ((nibble - 8) * s, exact in fp32) and
- * never written back; accumulation is fp32.  n and h are rounded to bf16.
+ * never written back; accumulation is fp32.  n (or, with the norm folded,
+ * x * g) and h are rounded to bf16.
  * Returns FFN_OK, INVALID_ARGUMENT (null pointer, bad sizes or eps, y
  * overlapping an input or the workspace), UNSUPPORTED (multiples, alignment,
  * size limit), WORKSPACE or LAUNCH. */

@@ -579,6 +579,23 @@ def test_q4_ragged_tokens(gpu_lib, M, d, f):
     assert max_norm_err(_run_q4(ffn, q), _q4_ref(q)) <= TOL_Q4
 
 
+def test_q4_folded_and_materialised_norm_agree(gpu_lib):
+    """As for Q8_0: an 8-token call folds the norm, a 9-token call
+    materialises n; shared rows agree to the tolerance."""
+    from transformer_ffn_block_amd import ffn
+    import torch
+    q = I.make_q4_block(2500, 9, 512, 1024)
+    mats = [_q4_dev(m) for m in (q.w_gate, q.w_up, q.w_down)]
+    x = dev(q.x)
+    y8 = ffn.swiglu_block_q4(x[:8].contiguous(), dev(q.g), *mats, q.eps)
+    y9 = ffn.swiglu_block_q4(x, dev(q.g), *mats, q.eps)
+    torch.cuda.synchronize()
+    r = _q4_ref(q)
+    a8, a9 = host_f64(y8), host_f64(y9)
+    assert max_norm_err(a8, r[:8]) <= TOL_Q4 and max_norm_err(a9, r) <= TOL_Q4
+    assert max_norm_err(a8, a9[:8]) <= TOL_Q4
+
+
 def test_q4_subnormal_scales_are_not_flushed(gpu_lib):
     """Every scale subnormal and eps = 0, as for Q8_0; the weights are ~16x
     smaller than Q8_0's, so x is scaled by 2^-32 (still a normal bf16) for the

@@ -307,6 +307,12 @@ namespace {
 #ifndef FFN_Q8_FOLD
 #define FFN_Q8_FOLD 1
 #endif
+#ifndef FFN_Q4_FOLD
+#define FFN_Q4_FOLD 1
+#endif
+#ifndef FFN_Q4_FOLD_MAX
+#define FFN_Q4_FOLD_MAX 10240
+#endif
 struct Q8Traits {
   using Mat = ffn_q8_matrix;
   static constexpr const char* name = "Q8";
@@ -351,12 +357,14 @@ struct Q4Traits {
     const int sp = ffn::q4_down_splits((int)d, (int)f);
     return sp > 1 ? (size_t)sp * (size_t)Mc * (size_t)d * 4 : 0;
   }
-  static bool fold(int64_t, int64_t, int64_t) { return false; }
+  // the same bound as Q8_0 (measured: block 23.5 -> 21.0 us at f = 2176,
+  // 55.5 -> 58.1 us if folded at f = 17408)
+  static bool fold(int64_t M, int64_t d, int64_t f) {
+    return FFN_Q4_FOLD != 0 && M <= 8 && ((f + 15) / 16) * ((d + 255) / 256) <= FFN_Q4_FOLD_MAX;
+  }
   static hipError_t gateup(const void* act, const void* gain, float eps, const Mat* g, const Mat* u,
                            void* h, int M, int d, int f, hipStream_t s) {
-    (void)gain;
-    (void)eps;
-    return ffn::launch_q4_gateup(act, g->qs, g->scales, u->qs, u->scales, h, M, d, f, s);
+    return ffn::launch_q4_gateup(act, gain, eps, g->qs, g->scales, u->qs, u->scales, h, M, d, f, s);
   }
   static hipError_t down(const void* h, const Mat* w, const void* x, void* y, float* part, int M,
                          int d, int f, hipStream_t s) {

@@ -68,9 +68,9 @@ int q8_max_tokens();
 
 // Q4_0 weight-streaming projections (split nibble / scale arrays, bf16
 // activations, in-register dequant); same roles as the Q8_0 launchers.
-hipError_t launch_q4_gateup(const void* n, const uint8_t* qg, const uint16_t* sg,
-                            const uint8_t* qu, const uint16_t* su, void* h, int M, int d, int f,
-                            hipStream_t s);
+hipError_t launch_q4_gateup(const void* act, const void* gain, float eps, const uint8_t* qg,
+                            const uint16_t* sg, const uint8_t* qu, const uint16_t* su, void* h,
+                            int M, int d, int f, hipStream_t s);
 // Down projection, split over K into q4_down_splits(d, f) ranges when that
 // is above 1: the fp32 partial sums go to part[splits][M][d] (caller's
 // workspace) and launch_splitk_residual adds them to x in range order.

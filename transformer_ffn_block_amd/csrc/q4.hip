@@ -38,6 +38,13 @@
 // two-batch pipeline and the fixed-order cross-wave reduction are those of
 // the Q8_0 kernels.
 //
+// For narrow projections with up to 8 tokens the norm is folded into the
+// gate/up kernel (FOLD, as for Q8_0): the block then skips the norm launch,
+// which at f = 2176 takes the block from 23.5 to 21.0 us; at f = 17408 the
+// fold's staging work (and two more VGPRs than the three-waves-per-SIMD
+// budget) made the block slower (58.1 vs 55.5 us), so there n comes from the
+// norm kernel.
+//
 // Split-K down projection.  With d = 5120 outputs the down projection has
 // only 320 row tiles for 256 compute units: a quarter of the units get two
 // tiles and set the kernel's length.  The K axis is therefore split into a
@@ -92,20 +99,27 @@ __device__ __forceinline__ float q4_f16bits_to_f32(uint32_t b) {
 // PART: split-K pass (NMAT == 1): workgroup (tile, z) covers the z-th of
 // gridDim.y contiguous ranges of stages and writes its fp32 partial sums to
 // part[z][M][N] (no residual); a fixed-order reduce adds them up.
-template <int NMAT, int MT, int WAVES, bool SALIGN, int ASTAGE, bool PART>
+// FOLD (gate/up, up to 8 tokens): the RMSNorm is folded in, as in the Q8_0
+// and bf16 decode kernels: act is x, the staged activations are multiplied
+// by the gain while the sums of squares of x accumulate, and the epilogue
+// scales both projections by r_m.
+template <int NMAT, int MT, int WAVES, bool SALIGN, int ASTAGE, bool PART, bool FOLD>
 __global__ __launch_bounds__(WAVES * 64) void q4_stream(
-    const uint16_t* __restrict__ act,     // [M, K] bf16: n or h
+    const uint16_t* __restrict__ act,     // [M, K] bf16: x (FOLD), n or h
+    const uint16_t* __restrict__ gain,    // [K] (FOLD)
     const uint8_t* __restrict__ q0, const uint16_t* __restrict__ s0,  // [N, K/2], [N, K/32]
     const uint8_t* __restrict__ q1, const uint16_t* __restrict__ s1,
     const uint16_t* __restrict__ resid,   // [M, N] (NMAT == 1, !PART)
     uint16_t* __restrict__ out,           // [M, N] (!PART)
     float* __restrict__ part,             // [gridDim.y, M, N] (PART)
-    int M, int K, int N) {
+    int M, int K, int N, float eps) {
+  static_assert(!FOLD || (NMAT == 2 && !PART && ASTAGE == 8), "the norm folds into the 8-token gate/up kernel only");
   constexpr int SB = 8;        // 32-weight blocks per stage (256 k, 128 B per row)
   constexpr int NU = 2;        // nibble load instructions per matrix per stage (8 rows each)
   __shared__ uint4 wb[WAVES][NMAT][128];           // per-wave nibble stage (2 KiB per matrix)
   __shared__ float red[WAVES][MT][NMAT][4][64];
   __shared__ uint4 abuf[WAVES][ASTAGE ? ASTAGE * 32 : 1];  // per-wave activation stage [rows][32]
+  __shared__ float ssq[FOLD ? WAVES : 1][8];  // per-wave partial sums of squares (FOLD)
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -167,10 +181,30 @@ __global__ __launch_bounds__(WAVES * 64) void q4_stream(
   const uint4 negoff = make_uint4(kNegOffsetPair, kNegOffsetPair, kNegOffsetPair, kNegOffsetPair);
   const uint32_t nib_shift = (uint32_t)(q >> 1) * 4u;  // lanes q >= 2 take the high nibbles
 
+  // FOLD: lane -> chunk lane & 31 of every row it stages (one gain chunk per
+  // stage), written to slot v*64 + (lane/32)*32 + ((lane & 31) + row) & 31,
+  // the same LDS layout; sums of squares of x per staged row in ss[v]
+  const uint4* G4 = reinterpret_cast<const uint4*>(gain);
+  float ss[FOLD ? NA : 1];
+#pragma unroll
+  for (int i = 0; i < (FOLD ? NA : 1); ++i) ss[i] = 0.f;
+  auto fold = [&](const uint4& xa, const uint4& gv, float& s2) -> uint4 {
+    float xf[8], gf[8];
+    unpack8(xa, xf);
+    unpack8(gv, gf);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      s2 = __builtin_fmaf(xf[e], xf[e], s2);
+      xf[e] *= gf[e];
+    }
+    return pack8(xf);
+  };
+
   struct Batch {
     uint4 w[NMAT][NU];
     uint4 s[NMAT];  // SALIGN: the stage's 8 scales of row r; else .x = blocks 2q, 2q+1
     uint4 a[NA];
+    uint4 g;        // the stage's gain chunk lane & 31 (FOLD)
   };
   // st < 0 marks a prefetch past the slice end: the nibble loads then read
   // nothing (out-of-range offset) and the small loads hit cache
@@ -196,9 +230,10 @@ __global__ __launch_bounds__(WAVES * 64) void q4_stream(
     if (ASTAGE) {
 #pragma unroll
       for (int v = 0; v < NA; ++v) {
-        const int c = ((lane & 31) - (2 * v + (lane >> 5))) & 31;
+        const int c = FOLD ? (lane & 31) : ((lane & 31) - (2 * v + (lane >> 5))) & 31;
         B.a[v] = pa[v][min(st * 32 + c, K8 - 1)];
       }
+      if (FOLD) B.g = G4[min(st * 32 + (lane & 31), K8 - 1)];
     } else {
 #pragma unroll
       for (int b = 0; b < SB; ++b) {
@@ -222,12 +257,18 @@ __global__ __launch_bounds__(WAVES * 64) void q4_stream(
     if (ASTAGE) {
 #pragma unroll
       for (int v = 0; v < NA; ++v) {
+        const int row = 2 * v + (lane >> 5);
         uint4 a = B.a[v];
         if (ragged) {
-          const int c = ((lane & 31) - (2 * v + (lane >> 5))) & 31;
+          const int c = FOLD ? (lane & 31) : ((lane & 31) - row) & 31;
           a = keep_or_zero(st * 32 + c < K8, a);
         }
-        abuf[wave][ASTAGE ? v * 64 + lane : 0] = a;
+        if (FOLD) {
+          a = fold(a, B.g, ss[FOLD ? v : 0]);
+          abuf[wave][ASTAGE ? v * 64 + (lane & 32) + (((lane & 31) + row) & 31) : 0] = a;
+        } else {
+          abuf[wave][ASTAGE ? v * 64 + lane : 0] = a;
+        }
       }
     }
     // the MFMAs of a group of blocks first, then their scale FMAs
@@ -313,6 +354,16 @@ __global__ __launch_bounds__(WAVES * 64) void q4_stream(
     for (int m = 0; m < NMAT; ++m)
 #pragma unroll
       for (int e = 0; e < 4; ++e) red[wave][t][m][e][lane] = acc[m][t][e];
+  if (FOLD) {
+    // token 2v + h: the 32 lanes of half h hold its partial sums
+#pragma unroll
+    for (int v = 0; v < (FOLD ? NA : 1); ++v) {
+      float sv = ss[v];
+#pragma unroll
+      for (int o = 1; o < 32; o <<= 1) sv += __shfl_xor(sv, o, 64);
+      if ((lane & 31) == 0) ssq[FOLD ? wave : 0][2 * v + (lane >> 5)] = sv;
+    }
+  }
   __syncthreads();
   for (int t = wave; t < MT; t += WAVES) {
     const int col = j0 + r;  // lane's weight row = output column
@@ -330,6 +381,14 @@ __global__ __launch_bounds__(WAVES * 64) void q4_stream(
         if (PART) {
           part[(size_t)blockIdx.y * M * N + off] = v0;
         } else {
+          if (FOLD) {
+            float sum = 0.f;
+#pragma unroll
+            for (int w = 0; w < WAVES; ++w) sum += ssq[FOLD ? w : 0][tok & 7];
+            const float rs = 1.0f / __builtin_sqrtf(sum / (float)K + eps);
+            v0 *= rs;
+            v1 *= rs;
+          }
           const float o = NMAT == 2 ? silu_mul(v0, v1) : bf2f(resid[off]) + v0;
           out[off] = f2bf(o);
         }
@@ -341,17 +400,22 @@ __global__ __launch_bounds__(WAVES * 64) void q4_stream(
 // Tokens per launch; the API walks larger M in chunks of this size.
 int q4_max_tokens() { return 32; }
 
-template <int NMAT, int WAVES, bool SALIGN, bool PART>
-static void launch_q4_mt(const uint16_t* a, const uint8_t* q0, const uint16_t* s0,
-                         const uint8_t* q1, const uint16_t* s1, const uint16_t* rr, uint16_t* o,
-                         float* part, int splits, int M, int K, int N, hipStream_t s) {
+template <int NMAT, int WAVES, bool SALIGN, bool PART, bool FOLD = false>
+static void launch_q4_mt(const uint16_t* a, const uint16_t* gn, float eps, const uint8_t* q0,
+                         const uint16_t* s0, const uint8_t* q1, const uint16_t* s1,
+                         const uint16_t* rr, uint16_t* o, float* part, int splits, int M, int K,
+                         int N, hipStream_t s) {
   const dim3 grid((unsigned)((N + 15) / 16), (unsigned)splits), block(WAVES * 64);
-  if (M <= 8)
-    hipLaunchKernelGGL((q4_stream<NMAT, 1, WAVES, SALIGN, 8, PART>), grid, block, 0, s, a, q0, s0, q1, s1, rr, o, part, M, K, N);
-  else if (M <= 16)
-    hipLaunchKernelGGL((q4_stream<NMAT, 1, WAVES, SALIGN, 16, PART>), grid, block, 0, s, a, q0, s0, q1, s1, rr, o, part, M, K, N);
-  else
-    hipLaunchKernelGGL((q4_stream<NMAT, 2, WAVES, SALIGN, 0, PART>), grid, block, 0, s, a, q0, s0, q1, s1, rr, o, part, M, K, N);
+  if constexpr (FOLD) {
+    hipLaunchKernelGGL((q4_stream<NMAT, 1, WAVES, SALIGN, 8, PART, true>), grid, block, 0, s, a, gn, q0, s0, q1, s1, rr, o, part, M, K, N, eps);
+  } else {
+    if (M <= 8)
+      hipLaunchKernelGGL((q4_stream<NMAT, 1, WAVES, SALIGN, 8, PART, false>), grid, block, 0, s, a, gn, q0, s0, q1, s1, rr, o, part, M, K, N, eps);
+    else if (M <= 16)
+      hipLaunchKernelGGL((q4_stream<NMAT, 1, WAVES, SALIGN, 16, PART, false>), grid, block, 0, s, a, gn, q0, s0, q1, s1, rr, o, part, M, K, N, eps);
+    else
+      hipLaunchKernelGGL((q4_stream<NMAT, 2, WAVES, SALIGN, 0, PART, false>), grid, block, 0, s, a, gn, q0, s0, q1, s1, rr, o, part, M, K, N, eps);
+  }
 }
 
 // 16-byte scale loads need every row of scales (K/16 bytes) and the base
@@ -360,15 +424,21 @@ static bool q4_scales_aligned(int K, const uint16_t* s0, const uint16_t* s1) {
   return K % 256 == 0 && ((uintptr_t)s0 % 16) == 0 && (s1 == nullptr || ((uintptr_t)s1 % 16) == 0);
 }
 
-hipError_t launch_q4_gateup(const void* n, const uint8_t* qg, const uint16_t* sg,
-                            const uint8_t* qu, const uint16_t* su, void* h, int M, int d, int f,
-                            hipStream_t s) {
+hipError_t launch_q4_gateup(const void* act, const void* gain, float eps, const uint8_t* qg,
+                            const uint16_t* sg, const uint8_t* qu, const uint16_t* su, void* h,
+                            int M, int d, int f, hipStream_t s) {
   constexpr int W = FFN_Q4_GU_WAVES;
-  const uint16_t* a = (const uint16_t*)n;
-  if (q4_scales_aligned(d, sg, su))
-    launch_q4_mt<2, W, true, false>(a, qg, sg, qu, su, nullptr, (uint16_t*)h, nullptr, 1, M, d, f, s);
-  else
-    launch_q4_mt<2, W, false, false>(a, qg, sg, qu, su, nullptr, (uint16_t*)h, nullptr, 1, M, d, f, s);
+  const uint16_t* a = (const uint16_t*)act;
+  const uint16_t* gn = (const uint16_t*)gain;
+  const bool al = q4_scales_aligned(d, sg, su);
+  if (gain) {
+    if (M > 8) return hipErrorInvalidValue;  // the folded kernel stages at most 8 token rows
+    if (al) launch_q4_mt<2, W, true, false, true>(a, gn, eps, qg, sg, qu, su, nullptr, (uint16_t*)h, nullptr, 1, M, d, f, s);
+    else launch_q4_mt<2, W, false, false, true>(a, gn, eps, qg, sg, qu, su, nullptr, (uint16_t*)h, nullptr, 1, M, d, f, s);
+  } else {
+    if (al) launch_q4_mt<2, W, true, false>(a, nullptr, 0.f, qg, sg, qu, su, nullptr, (uint16_t*)h, nullptr, 1, M, d, f, s);
+    else launch_q4_mt<2, W, false, false>(a, nullptr, 0.f, qg, sg, qu, su, nullptr, (uint16_t*)h, nullptr, 1, M, d, f, s);
+  }
   return hipGetLastError();
 }
 
@@ -391,12 +461,12 @@ hipError_t launch_q4_down(const void* h, const uint8_t* qd, const uint16_t* sd, 
   const int sp = q4_down_splits(d, f);
   const bool al = q4_scales_aligned(f, sd, nullptr);
   if (sp == 1) {
-    if (al) launch_q4_mt<1, W, true, false>(a, qd, sd, nullptr, nullptr, (const uint16_t*)x, (uint16_t*)y, nullptr, 1, M, f, d, s);
-    else launch_q4_mt<1, W, false, false>(a, qd, sd, nullptr, nullptr, (const uint16_t*)x, (uint16_t*)y, nullptr, 1, M, f, d, s);
+    if (al) launch_q4_mt<1, W, true, false>(a, nullptr, 0.f, qd, sd, nullptr, nullptr, (const uint16_t*)x, (uint16_t*)y, nullptr, 1, M, f, d, s);
+    else launch_q4_mt<1, W, false, false>(a, nullptr, 0.f, qd, sd, nullptr, nullptr, (const uint16_t*)x, (uint16_t*)y, nullptr, 1, M, f, d, s);
     return hipGetLastError();
   }
-  if (al) launch_q4_mt<1, W, true, true>(a, qd, sd, nullptr, nullptr, nullptr, nullptr, part, sp, M, f, d, s);
-  else launch_q4_mt<1, W, false, true>(a, qd, sd, nullptr, nullptr, nullptr, nullptr, part, sp, M, f, d, s);
+  if (al) launch_q4_mt<1, W, true, true>(a, nullptr, 0.f, qd, sd, nullptr, nullptr, nullptr, nullptr, part, sp, M, f, d, s);
+  else launch_q4_mt<1, W, false, true>(a, nullptr, 0.f, qd, sd, nullptr, nullptr, nullptr, nullptr, part, sp, M, f, d, s);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_splitk_residual(part, sp, x, y, M, d, s);
