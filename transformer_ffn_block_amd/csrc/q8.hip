@@ -102,12 +102,17 @@ __global__ __launch_bounds__(WAVES * 64) FFN_STREAM_ATTR void q8_stream(
   static_assert(!FOLD || (NMAT == 2 && !PART && ASTAGE == 8), "the norm folds into the 8-token gate/up kernel only");
   constexpr int SB = 8;  // 32-quant blocks per stage (256 k, 256 B per row)
   __shared__ uint4 wb[WAVES][NMAT][256];           // per-wave quant stage (4 KiB per matrix)
-  __shared__ float red[WAVES][MT][NMAT][4][64];
   __shared__ uint4 abuf[WAVES][ASTAGE ? ASTAGE * 32 : 1];  // per-wave activation stage [rows][32]
   __shared__ float ssq[FOLD ? WAVES : 1][8];  // per-wave partial sums of squares (FOLD)
+  // the cross-wave partial tiles reuse each wave's own quant stage once its
+  // K loop is done (MT * NMAT KiB <= NMAT * 4 KiB)
+  static_assert(MT <= 4, "partial tiles must fit the quant stage");
+  auto red = [&](int w, int t, int m, int e) -> float* {
+    return reinterpret_cast<float*>(&wb[w][0][0]) + ((t * NMAT + m) * 4 + e) * 64;
+  };
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar loop control
   const int r = lane & 15, q = lane >> 4;
   const int j0 = blockIdx.x * 16;
   const int nb = K >> 5;                // blocks per row
@@ -337,7 +342,7 @@ __global__ __launch_bounds__(WAVES * 64) FFN_STREAM_ATTR void q8_stream(
 #pragma unroll
     for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) red[wave][t][m][e][lane] = acc[m][t][e];
+      for (int e = 0; e < 4; ++e) red(wave, t, m, e)[lane] = acc[m][t][e];
   if (FOLD) {
     // token 2v + h: the 32 lanes of half h hold its partial sums
 #pragma unroll
@@ -357,8 +362,8 @@ __global__ __launch_bounds__(WAVES * 64) FFN_STREAM_ATTR void q8_stream(
       float v0 = 0.f, v1 = 0.f;
 #pragma unroll
       for (int w = 0; w < WAVES; ++w) {
-        v0 += red[w][t][0][e][lane];
-        if (NMAT == 2) v1 += red[w][t][NMAT - 1][e][lane];
+        v0 += red(w, t, 0, e)[lane];
+        if (NMAT == 2) v1 += red(w, t, NMAT - 1, e)[lane];
       }
       if (tok < M && col < N) {
         const size_t off = (size_t)tok * N + col;
