@@ -47,6 +47,12 @@ __device__ __forceinline__ uint4 buf_ld_nt(__amdgpu_buffer_rsrc_t r, unsigned of
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// 16-byte cached buffer load at a byte offset
+__device__ __forceinline__ uint4 buf_ld16(__amdgpu_buffer_rsrc_t r, unsigned off) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // 16-byte buffer load straight into LDS: lane i's 16 bytes land at
 // lds + 16*i (lds must be wave-uniform).  AUX 2 = streaming (non-temporal).
 template <int AUX>

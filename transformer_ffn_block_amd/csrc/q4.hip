@@ -35,7 +35,7 @@
 // (c + R/2) & 7 of the row, so the 8-byte fragment reads of a block (16 rows
 // x two halves) hit all 64 banks once.  Prefetches past a wave's K slice use
 // an out-of-range buffer offset and read nothing.  Scales, activations, the
-// two-batch pipeline and the fixed-order cross-wave reduction are those of
+// software pipeline and the fixed-order cross-wave reduction are those of
 // the Q8_0 kernels.
 //
 // For narrow projections with up to 8 tokens the norm is folded into the
@@ -63,6 +63,18 @@
 
 #ifndef FFN_Q4_GU_WAVES
 #define FFN_Q4_GU_WAVES 4
+#endif
+// The 8-token gate/up kernel (norm not folded): waves per SIMD it is
+// register-allocated for (three: 165 VGPRs, no AGPRs, no spills), and the
+// 32-nibble blocks whose MFMAs are issued before their scale FMAs.
+#ifndef FFN_Q4_DEEP_DN8
+#define FFN_Q4_DEEP_DN8 0
+#endif
+#ifndef FFN_Q4_GU8_WPE
+#define FFN_Q4_GU8_WPE 3
+#endif
+#ifndef FFN_Q4_GU8_GB
+#define FFN_Q4_GU8_GB 4
 #endif
 #ifndef FFN_Q4_DN_WAVES
 #define FFN_Q4_DN_WAVES 4
@@ -104,7 +116,9 @@ __device__ __forceinline__ float q4_f16bits_to_f32(uint32_t b) {
 // by the gain while the sums of squares of x accumulate, and the epilogue
 // scales both projections by r_m.
 template <int NMAT, int MT, int WAVES, bool SALIGN, int ASTAGE, bool PART, bool FOLD>
-__global__ __launch_bounds__(WAVES * 64) void q4_stream(
+__global__ __launch_bounds__(WAVES * 64)
+__attribute__((amdgpu_waves_per_eu(NMAT == 2 && ASTAGE == 8 && !FOLD ? FFN_Q4_GU8_WPE : 1)))
+void q4_stream(
     const uint16_t* __restrict__ act,     // [M, K] bf16: x (FOLD), n or h
     const uint16_t* __restrict__ gain,    // [K] (FOLD)
     const uint8_t* __restrict__ q0, const uint16_t* __restrict__ s0,  // [N, K/2], [N, K/32]
@@ -155,16 +169,33 @@ __global__ __launch_bounds__(WAVES * 64) void q4_stream(
   const uint16_t* ps[NMAT];
   ps[0] = s0 + (size_t)jr * nb;
   if (NMAT == 2) ps[NMAT - 1] = s1 + (size_t)jr * nb;
+  // SALIGN: both matrices' scale rows at the same byte offset of their own
+  // buffer resources
+  __amdgpu_buffer_rsrc_t rs[NMAT];
+  rs[0] = make_rsrc(s0, (long)N * nb * 2);
+  if (NMAT == 2) rs[NMAT - 1] = make_rsrc(s1, (long)N * nb * 2);
+  const unsigned srow = (unsigned)jr * (unsigned)nb * 2u;
 
   // direct activations: token t*16 + r; staged: instruction v covers token
   // rows 2v, 2v+1 (lane -> row 2v + lane/32, LDS slot v*64 + lane holding
   // chunk ((lane & 31) - row) & 31 of the row's 512-byte stage segment)
   constexpr int NA = ASTAGE ? ASTAGE / 2 : SB * MT;  // activation loads per batch
-  const uint4* pa[ASTAGE ? NA : MT];
+  // the gate/up kernels address staged rows and scale rows through buffer
+  // resources with 32-bit offsets (fewer VGPRs); the down kernels keep plain
+  // pointers (the freed registers raised their occupancy and measured slower)
+  constexpr bool kBuf = NMAT == 2;
+  const uint4* pa[ASTAGE && kBuf ? 1 : (ASTAGE ? NA : MT)];
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(act, (long)M * K * 2);
+  unsigned aro[ASTAGE && kBuf ? NA : 1];
   if (ASTAGE) {
 #pragma unroll
-    for (int v = 0; v < NA; ++v)
-      pa[v] = reinterpret_cast<const uint4*>(act) + (size_t)min(2 * v + (lane >> 5), M - 1) * K8;
+    for (int v = 0; v < NA; ++v) {
+      const int row = min(2 * v + (lane >> 5), M - 1);
+      if (kBuf)
+        aro[kBuf ? v : 0] = (unsigned)row * (unsigned)K8 * 16u;
+      else
+        pa[kBuf ? 0 : v] = reinterpret_cast<const uint4*>(act) + (size_t)row * K8;
+    }
   } else {
 #pragma unroll
     for (int t = 0; t < MT; ++t)
@@ -208,7 +239,7 @@ __global__ __launch_bounds__(WAVES * 64) void q4_stream(
   };
   // st < 0 marks a prefetch past the slice end: the nibble loads then read
   // nothing (out-of-range offset) and the small loads hit cache
-  auto load = [&](Batch& B, int st_req) {
+  auto load_w = [&](Batch& B, int st_req) {
     const int st = st_req < 0 ? se - 1 : st_req;
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
@@ -217,21 +248,29 @@ __global__ __launch_bounds__(WAVES * 64) void q4_stream(
 #pragma unroll
       for (int m = 0; m < NMAT; ++m) B.w[m][u] = buf_ld_nt(rq[m], o);
     }
+  };
+  auto load_s = [&](Batch& B, int st_req) {
+    const int st = st_req < 0 ? se - 1 : st_req;
     if (SALIGN) {
       const int c = min(st, (nb >> 3) - 1);
 #pragma unroll
-      for (int m = 0; m < NMAT; ++m) B.s[m] = reinterpret_cast<const uint4*>(ps[m])[c];
+      for (int m = 0; m < NMAT; ++m)
+        B.s[m] = kBuf ? buf_ld16(rs[m], srow + (unsigned)c * 16u) : reinterpret_cast<const uint4*>(ps[m])[c];
     } else {
       const int b0 = min(st * SB + 2 * q, nb - 1), b1 = min(st * SB + 2 * q + 1, nb - 1);
 #pragma unroll
       for (int m = 0; m < NMAT; ++m)
         B.s[m].x = (uint32_t)ps[m][b0] | ((uint32_t)ps[m][b1] << 16);
     }
+  };
+  auto load_a = [&](Batch& B, int st_req) {
+    const int st = st_req < 0 ? se - 1 : st_req;
     if (ASTAGE) {
 #pragma unroll
       for (int v = 0; v < NA; ++v) {
         const int c = FOLD ? (lane & 31) : ((lane & 31) - (2 * v + (lane >> 5))) & 31;
-        B.a[v] = pa[v][min(st * 32 + c, K8 - 1)];
+        const int cc = min(st * 32 + c, K8 - 1);
+        B.a[v] = kBuf ? buf_ld16(ra, aro[kBuf ? v : 0] + (unsigned)cc * 16u) : pa[kBuf ? 0 : v][cc];
       }
       if (FOLD) B.g = G4[min(st * 32 + (lane & 31), K8 - 1)];
     } else {
@@ -243,13 +282,19 @@ __global__ __launch_bounds__(WAVES * 64) void q4_stream(
       }
     }
   };
-  auto stage_and_compute = [&](const Batch& B, int st) {
+  auto load = [&](Batch& B, int st_req) {
+    load_w(B, st_req);
+    load_s(B, st_req);
+    load_a(B, st_req);
+  };
+  // the nibbles (W) and the staged activations (B) of a stage go to LDS
+  auto stage = [&](const Batch& W, const Batch& B, int st) {
     const bool ragged = (st + 1) * SB > nb;  // only a row's last stage can be partial
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
 #pragma unroll
       for (int m = 0; m < NMAT; ++m) {
-        uint4 x = B.w[m][u];
+        uint4 x = W.w[m][u];
         if (ragged) x = keep_or_zero(st * 8 + cst[u] < K32, x);
         wb[wave][m][u * 64 + lane] = x;
       }
@@ -271,8 +316,13 @@ __global__ __launch_bounds__(WAVES * 64) void q4_stream(
         }
       }
     }
+  };
+  // the MFMAs and scale FMAs of a stage: W supplies the scales, B the direct
+  // activations (ASTAGE == 0)
+  auto compute = [&](const Batch& W, const Batch& B, int st) {
+    const bool ragged = (st + 1) * SB > nb;
     // the MFMAs of a group of blocks first, then their scale FMAs
-    constexpr int GB = 4;
+    constexpr int GB = NMAT == 2 && ASTAGE == 8 && !FOLD ? FFN_Q4_GU8_GB : 4;
 #pragma unroll
     for (int b0 = 0; b0 < SB; b0 += GB) {
       f32x4 p[GB][NMAT][MT];
@@ -306,9 +356,9 @@ __global__ __launch_bounds__(WAVES * 64) void q4_stream(
           const uint4 Bq = q4x8_to_bf16_biased(qv.x, qv.y, nib_shift);
           uint32_t pair;
           if (SALIGN) {
-            pair = (b >> 1) == 0 ? B.s[m].x : (b >> 1) == 1 ? B.s[m].y : (b >> 1) == 2 ? B.s[m].z : B.s[m].w;
+            pair = (b >> 1) == 0 ? W.s[m].x : (b >> 1) == 1 ? W.s[m].y : (b >> 1) == 2 ? W.s[m].z : W.s[m].w;
           } else {
-            pair = (uint32_t)__shfl((int)B.s[m].x, src_lane, 64);
+            pair = (uint32_t)__shfl((int)W.s[m].x, src_lane, 64);
           }
           scv[bb][m] = q4_f16bits_to_f32((b & 1) ? (pair >> 16) : (pair & 0xFFFFu));
 #pragma unroll
@@ -324,8 +374,47 @@ __global__ __launch_bounds__(WAVES * 64) void q4_stream(
     }
   };
 
+  auto stage_and_compute = [&](const Batch& B, int st) {
+    stage(B, B, st);
+    compute(B, B, st);
+  };
+
   const int n = se - sb;
-  if (n >= 2) {
+  // the deeper pipeline below, except in the 8-token down projection unless
+  // FFN_Q4_DEEP_DN8 is set (measured slower there)
+  constexpr bool kDeep = ASTAGE != 0 && !(NMAT == 1 && ASTAGE == 8 && !FFN_Q4_DEEP_DN8);
+  if (kDeep && n >= 2) {
+    // staged activations single-buffered, nibbles of two stages in flight
+    // during the MFMAs, scales reloaded after the MFMA loop that reads them
+    Batch X, Y, A;
+    load_w(X, sb);
+    load_s(X, sb);
+    load_a(A, sb);
+    load_w(Y, sb + 1);
+    load_s(Y, sb + 1);
+    for (int s = sb;;) {
+      __builtin_amdgcn_sched_barrier(0);
+      stage(X, A, s);
+      __builtin_amdgcn_sched_barrier(0);
+      load_a(A, s + 1 < se ? s + 1 : -1);
+      load_w(X, s + 2 < se ? s + 2 : -1);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(X, A, s);
+      __builtin_amdgcn_sched_barrier(0);
+      load_s(X, s + 2 < se ? s + 2 : -1);
+      if (++s >= se) break;
+      __builtin_amdgcn_sched_barrier(0);
+      stage(Y, A, s);
+      __builtin_amdgcn_sched_barrier(0);
+      load_a(A, s + 1 < se ? s + 1 : -1);
+      load_w(Y, s + 2 < se ? s + 2 : -1);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(Y, A, s);
+      __builtin_amdgcn_sched_barrier(0);
+      load_s(Y, s + 2 < se ? s + 2 : -1);
+      if (++s >= se) break;
+    }
+  } else if (n >= 2) {
     Batch X, Y;
     load(X, sb);
     load(Y, sb + 1);

@@ -34,9 +34,12 @@
 // per lane when rows of scales are 16-byte aligned (K % 256 == 0); otherwise
 // lane (r, q) takes blocks 2q, 2q+1 of row r and hands them to the other lanes
 // of the row with cross-lane permutes.  Scale loads from 16 rows touch 16
-// cache lines each, so their count, not their bytes, is what costs.  The K loop is
-// pipelined over two register batches as in the bf16 decode kernels; partial
-// tiles are reduced across waves in a fixed order.
+// cache lines each, so their count, not their bytes, is what costs.  The K
+// loop is software-pipelined: with staged activations the quants of two
+// stages are in flight while a stage's MFMAs run (quants and scales
+// double-buffered in registers, activations single-buffered: reloaded as soon
+// as they are in LDS; the scales, which the MFMA loop reads, are reloaded
+// after it); partial tiles are reduced across waves in a fixed order.
 // Activation rows past M are clamped copies of row M-1: they only feed
 // output rows that are never stored, so they need no masking.
 // The down projection (320 row tiles at d = 5120) splits its K axis into a
@@ -55,10 +58,19 @@
 #define FFN_Q8_DN_SPLIT_TARGET 1024
 #endif
 
-#ifndef FFN_STREAM_WPE
-#define FFN_STREAM_ATTR
-#else
-#define FFN_STREAM_ATTR __attribute__((amdgpu_waves_per_eu(FFN_STREAM_WPE)))
+// The 8-token gate/up kernel (two matrices, 8 staged token rows, norm not
+// folded): waves per SIMD it is register-allocated for, and the 32-quant
+// blocks whose MFMAs are issued before their scale FMAs (GB partial tiles
+// stay live).  At three waves (166 VGPRs, no AGPRs) the other waves cover the
+// wait of each FMA on its MFMA; GB = 2 or 4 at three waves spills.
+#ifndef FFN_Q8_DEEP_DN8
+#define FFN_Q8_DEEP_DN8 0
+#endif
+#ifndef FFN_Q8_GU8_WPE
+#define FFN_Q8_GU8_WPE 3
+#endif
+#ifndef FFN_Q8_GU8_GB
+#define FFN_Q8_GU8_GB 1
 #endif
 
 namespace ffn {
@@ -90,7 +102,9 @@ __device__ __forceinline__ float f16bits_to_f32(uint32_t b) {
 // gain while the sums of squares of x accumulate, and the epilogue scales
 // both projections by r_m.
 template <int NMAT, int MT, int WAVES, bool SALIGN, int ASTAGE, bool PART, bool FOLD>
-__global__ __launch_bounds__(WAVES * 64) FFN_STREAM_ATTR void q8_stream(
+__global__ __launch_bounds__(WAVES * 64)
+__attribute__((amdgpu_waves_per_eu(NMAT == 2 && ASTAGE == 8 && !FOLD ? FFN_Q8_GU8_WPE : 1)))
+void q8_stream(
     const uint16_t* __restrict__ act,     // [M, K] bf16: x (FOLD), n or h
     const uint16_t* __restrict__ gain,    // [K] (FOLD)
     const int8_t* __restrict__ q0, const uint16_t* __restrict__ s0,  // [N, K], [N, K/32]
@@ -145,6 +159,12 @@ __global__ __launch_bounds__(WAVES * 64) FFN_STREAM_ATTR void q8_stream(
   const uint16_t* ps[NMAT];
   ps[0] = s0 + (size_t)jr * nb;
   if (NMAT == 2) ps[NMAT - 1] = s1 + (size_t)jr * nb;
+  // SALIGN: both matrices' scale rows at the same byte offset of their own
+  // buffer resources (one 32-bit offset instead of two 64-bit pointers)
+  __amdgpu_buffer_rsrc_t rs[NMAT];
+  rs[0] = make_rsrc(s0, (long)N * nb * 2);
+  if (NMAT == 2) rs[NMAT - 1] = make_rsrc(s1, (long)N * nb * 2);
+  const unsigned srow = (unsigned)jr * (unsigned)nb * 2u;
   const int rd_base = (r >> 2) * 64 + (r & 3) * 16;
 
   // direct activations: token t*16 + r; staged: instruction v covers token
@@ -154,11 +174,14 @@ __global__ __launch_bounds__(WAVES * 64) FFN_STREAM_ATTR void q8_stream(
   // stage), written to slot v*64 + (lane/32)*32 + ((lane & 31) + row) & 31:
   // the same LDS layout (chunk c of row R at R*32 + ((c + R) & 31)).
   constexpr int NA = ASTAGE ? ASTAGE / 2 : SB * MT;  // activation loads per batch
-  const uint4* pa[ASTAGE ? NA : MT];
+  const uint4* pa[ASTAGE ? 1 : MT];
+  // staged rows through a buffer resource: 32-bit byte offsets per row
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(act, (long)M * K * 2);
+  unsigned aro[ASTAGE ? NA : 1];
   if (ASTAGE) {
 #pragma unroll
     for (int v = 0; v < NA; ++v)
-      pa[v] = reinterpret_cast<const uint4*>(act) + (size_t)min(2 * v + (lane >> 5), M - 1) * K8;
+      aro[ASTAGE ? v : 0] = (unsigned)min(2 * v + (lane >> 5), M - 1) * (unsigned)K8 * 16u;
   } else {
 #pragma unroll
     for (int t = 0; t < MT; ++t)
@@ -198,7 +221,7 @@ __global__ __launch_bounds__(WAVES * 64) FFN_STREAM_ATTR void q8_stream(
   };
   // st < 0 marks a prefetch past the slice end: the quant loads then read
   // nothing (out-of-range offset) and the small loads hit cache
-  auto load = [&](Batch& B, int st_req) {
+  auto load_w = [&](Batch& B, int st_req) {
     const int st = st_req < 0 ? se - 1 : st_req;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -207,23 +230,29 @@ __global__ __launch_bounds__(WAVES * 64) FFN_STREAM_ATTR void q8_stream(
 #pragma unroll
       for (int m = 0; m < NMAT; ++m) B.w[m][u] = buf_ld_nt(rq[m], o);
     }
+  };
+  auto load_s = [&](Batch& B, int st_req) {
+    const int st = st_req < 0 ? se - 1 : st_req;
     if (SALIGN) {
       const int c = min(st, (nb >> 3) - 1);
 #pragma unroll
-      for (int m = 0; m < NMAT; ++m) B.s[m] = reinterpret_cast<const uint4*>(ps[m])[c];
+      for (int m = 0; m < NMAT; ++m) B.s[m] = buf_ld16(rs[m], srow + (unsigned)c * 16u);
     } else {
       const int b0 = min(st * SB + 2 * q, nb - 1), b1 = min(st * SB + 2 * q + 1, nb - 1);
 #pragma unroll
       for (int m = 0; m < NMAT; ++m)
         B.s[m].x = (uint32_t)ps[m][b0] | ((uint32_t)ps[m][b1] << 16);
     }
+  };
+  auto load_a = [&](Batch& B, int st_req) {
+    const int st = st_req < 0 ? se - 1 : st_req;
     if (ASTAGE) {
 #pragma unroll
       for (int v = 0; v < NA; ++v) {
         // row 2v + (lane>>5): chunk (lane&31 - row) & 31 of its stage
         // segment, or chunk lane & 31 when folding
         const int c = FOLD ? (lane & 31) : ((lane & 31) - (2 * v + (lane >> 5))) & 31;
-        B.a[v] = pa[v][min(st * 32 + c, K8 - 1)];
+        B.a[v] = buf_ld16(ra, aro[ASTAGE ? v : 0] + (unsigned)min(st * 32 + c, K8 - 1) * 16u);
       }
       if (FOLD) B.g = G4[min(st * 32 + (lane & 31), K8 - 1)];
     } else {
@@ -235,13 +264,19 @@ __global__ __launch_bounds__(WAVES * 64) FFN_STREAM_ATTR void q8_stream(
       }
     }
   };
-  auto stage_and_compute = [&](const Batch& B, int st) {
+  auto load = [&](Batch& B, int st_req) {
+    load_w(B, st_req);
+    load_s(B, st_req);
+    load_a(B, st_req);
+  };
+  // the quants (W) and the staged activations (A) of a stage go to LDS
+  auto stage = [&](const Batch& W, const Batch& B, int st) {
     const bool ragged = (st + 1) * SB > nb;  // only a row's last stage can be partial
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
 #pragma unroll
       for (int m = 0; m < NMAT; ++m) {
-        uint4 v = B.w[m][u];
+        uint4 v = W.w[m][u];
         if (ragged) v = keep_or_zero(st * 16 + cst[u] < K16, v);
         wb[wave][m][u * 64 + lane] = v;
       }
@@ -263,9 +298,14 @@ __global__ __launch_bounds__(WAVES * 64) FFN_STREAM_ATTR void q8_stream(
         }
       }
     }
+  };
+  // the MFMAs and scale FMAs of a stage: W supplies the scales, B the direct
+  // activations (ASTAGE == 0)
+  auto compute = [&](const Batch& W, const Batch& B, int st) {
+    const bool ragged = (st + 1) * SB > nb;
     // per block: the MFMAs of a group of blocks first, then their scale FMAs,
     // so the FMAs do not wait on each MFMA in turn
-    constexpr int GB = 4;
+    constexpr int GB = NMAT == 2 && ASTAGE == 8 && !FOLD ? FFN_Q8_GU8_GB : 4;
 #pragma unroll
     for (int b0 = 0; b0 < SB; b0 += GB) {
       f32x4 p[GB][NMAT][MT];
@@ -295,9 +335,9 @@ __global__ __launch_bounds__(WAVES * 64) FFN_STREAM_ATTR void q8_stream(
           const uint4 Bq = q8x8_to_bf16(qv.x, qv.y);
           uint32_t pair;
           if (SALIGN) {
-            pair = (b >> 1) == 0 ? B.s[m].x : (b >> 1) == 1 ? B.s[m].y : (b >> 1) == 2 ? B.s[m].z : B.s[m].w;
+            pair = (b >> 1) == 0 ? W.s[m].x : (b >> 1) == 1 ? W.s[m].y : (b >> 1) == 2 ? W.s[m].z : W.s[m].w;
           } else {
-            pair = (uint32_t)__shfl((int)B.s[m].x, src_lane, 64);
+            pair = (uint32_t)__shfl((int)W.s[m].x, src_lane, 64);
           }
           scv[bb][m] = f16bits_to_f32((b & 1) ? (pair >> 16) : (pair & 0xFFFFu));
 #pragma unroll
@@ -313,8 +353,49 @@ __global__ __launch_bounds__(WAVES * 64) FFN_STREAM_ATTR void q8_stream(
     }
   };
 
+  auto stage_and_compute = [&](const Batch& B, int st) {
+    stage(B, B, st);
+    compute(B, B, st);
+  };
+
   const int n = se - sb;
-  if (n >= 2) {
+  // the deeper pipeline below, except in the 8-token down projection unless
+  // FFN_Q8_DEEP_DN8 is set (measured slower there)
+  constexpr bool kDeep = ASTAGE != 0 && !(NMAT == 1 && ASTAGE == 8 && !FFN_Q8_DEEP_DN8);
+  if (kDeep && n >= 2) {
+    // staged activations are single-buffered: the next stage's are loaded as
+    // soon as this stage's are in LDS, and the quants two stages out right
+    // after them, so two stages of quants are in flight during the MFMAs;
+    // the scales, still read by the MFMA loop, are reloaded after it
+    Batch X, Y, A;
+    load_w(X, sb);
+    load_s(X, sb);
+    load_a(A, sb);
+    load_w(Y, sb + 1);
+    load_s(Y, sb + 1);
+    for (int s = sb;;) {
+      __builtin_amdgcn_sched_barrier(0);
+      stage(X, A, s);
+      __builtin_amdgcn_sched_barrier(0);
+      load_a(A, s + 1 < se ? s + 1 : -1);
+      load_w(X, s + 2 < se ? s + 2 : -1);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(X, A, s);
+      __builtin_amdgcn_sched_barrier(0);
+      load_s(X, s + 2 < se ? s + 2 : -1);
+      if (++s >= se) break;
+      __builtin_amdgcn_sched_barrier(0);
+      stage(Y, A, s);
+      __builtin_amdgcn_sched_barrier(0);
+      load_a(A, s + 1 < se ? s + 1 : -1);
+      load_w(Y, s + 2 < se ? s + 2 : -1);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(Y, A, s);
+      __builtin_amdgcn_sched_barrier(0);
+      load_s(Y, s + 2 < se ? s + 2 : -1);
+      if (++s >= se) break;
+    }
+  } else if (n >= 2) {
     Batch X, Y;
     load(X, sb);
     load(Y, sb + 1);
