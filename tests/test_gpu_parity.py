@@ -489,7 +489,10 @@ def test_q8_full_size(gpu_lib):
     assert err <= TOL_Q8
 
 
-@pytest.mark.parametrize("M,d,f", [(1, 64, 32), (3, 160, 96), (17, 512, 704), (70, 256, 256)])
+# d, f not multiples of 256 leave a partial last stage in the 8-token (1, 3,
+# 5), 16-token (12) and direct (17, 33) kernels and in the split-K down pass
+@pytest.mark.parametrize("M,d,f", [(1, 64, 32), (3, 160, 96), (12, 288, 352), (17, 512, 704),
+                                   (33, 256, 800), (70, 256, 256), (5, 128, 4224)])
 def test_q8_ragged_tokens(gpu_lib, M, d, f):
     from transformer_ffn_block_amd import ffn
     _say("q8 ragged", M, d, f)
