@@ -152,8 +152,7 @@ ffn_status ffn_swiglu_block(ffn_dtype dt, const void *x, const void *g,
                             void *stream);
 
 /* Workspace bytes ffn_swiglu_block_q8 needs: n [M,d] (not when the norm is
- * folded into the gate/up kernel: M <= 8 and (f/16) * (d/256) <= 10240,
- * both rounded up) and h [M,f] in bf16,
+ * folded into the gate/up kernel: M <= 8) and h [M,f] in bf16,
  * then the fp32 partial sums of the split-K down projection,
  * [splits, min(M, 32), d] (splits, 1..8, is fixed by d and f); 0 on a shape
  * the entry point would reject for its sizes. */
@@ -176,7 +175,8 @@ ffn_status ffn_swiglu_block_q8(const void *x, const void *g, const ffn_q8_matrix
                                void *workspace, size_t workspace_bytes, void *stream);
 
 /* Workspace bytes ffn_swiglu_block_q4 needs: n [M,d] (not when the norm is
- * folded, on the same condition as for Q8_0) and h [M,f] in bf16,
+ * folded into the gate/up kernel: M <= 8 and (f/16) * (d/256) <= 10240,
+ * both rounded up) and h [M,f] in bf16,
  * then the fp32 partial sums of the split-K down projection,
  * [splits, min(M, 32), d] (splits, 1..8, is fixed by d and f); 0 on a shape
  * the entry point would reject for its sizes. */

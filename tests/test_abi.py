@@ -115,10 +115,10 @@ def test_workspace_sizes(L):
     pers = L.ffn_swiglu_block_workspace_size(ffn.FFN_BF16, M, d, f, 3)
     assert any(pers == fused + r256(s * M * d * 4) + r256((2 + s + d // 16) * 4) for s in range(1, 9))
     # quantised blocks: plus the split-K partials of the down projection, 4 K
-    # ranges for 320 output tiles, [4, min(M, 32), d] fp32; a narrow Q8
-    # projection with up to 8 tokens folds the norm and needs no n
+    # ranges for 320 output tiles, [4, min(M, 32), d] fp32; Q8 with up to 8
+    # tokens (Q4: narrow projections only) folds the norm and needs no n
     assert L.ffn_swiglu_block_q8_workspace_size(8, 5120, 17408) == \
-        r256(8 * 5120 * 2) + r256(8 * 17408 * 2) + 4 * 8 * 5120 * 4
+        r256(8 * 17408 * 2) + 4 * 8 * 5120 * 4
     sp = 4  # ceil(1024 / 320) ranges for the 320 row tiles of the down projection
     assert L.ffn_swiglu_block_q8_workspace_size(8, 5120, 2176) == \
         r256(8 * 2176 * 2) + r256(sp * 8 * 5120 * 4)

@@ -501,10 +501,9 @@ def test_q8_ragged_tokens(gpu_lib, M, d, f):
 
 
 def test_q8_folded_and_materialised_norm_agree(gpu_lib):
-    """A narrow projection folds the norm into the gate/up kernel up to 8
-    tokens; from 9 on n is materialised first: the rows shared by an 8- and a
-    9-token call agree to the tolerance (different roundings of the
-    normalised activations)."""
+    """Up to 8 tokens the norm is folded into the gate/up kernel; from 9 on n
+    is materialised first: the rows shared by an 8- and a 9-token call agree
+    to the tolerance (different roundings of the normalised activations)."""
     from transformer_ffn_block_amd import ffn
     import torch
     q = I.make_q8_block(2400, 9, 512, 1024)

@@ -333,7 +333,7 @@ struct Q8Traits {
   // (1088 x 20) gate/up 45.2 -> 51.1 us, no net gain; 16 and 32 tokens
   // slower.  So: up to 8 tokens and at most 10240 tile-stages.
   static bool fold(int64_t M, int64_t d, int64_t f) {
-    return FFN_Q8_FOLD != 0 && M <= 8 && ((f + 15) / 16) * ((d + 255) / 256) <= 10240;
+    return FFN_Q8_FOLD != 0 && M <= 8;
   }
   static hipError_t gateup(const void* act, const void* gain, float eps, const Mat* g, const Mat* u,
                            void* h, int M, int d, int f, hipStream_t s) {

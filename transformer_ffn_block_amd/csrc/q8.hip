@@ -6,14 +6,12 @@
 //
 //   gate/up : h[m,j] = silu(sum_k Wg[j,k] n[m,k]) * (sum_k Wu[j,k] n[m,k])
 //   down    : y[m,i] = x[m,i] + sum_j Wd[i,j] h[m,j]
-// n = rmsnorm(x) * g normally comes from the norm kernel.  For narrow
-// projections with up to 8 tokens the norm is folded into the gate/up kernel
-// instead (FOLD, as in the bf16 decode kernels: x * g where the activations
-// are staged, r_m in the epilogue): the fold saves the norm launch but adds
-// staging work on the VALU that quant conversion and block scaling already
-// load, so it pays only when the projection is small (measured: block 10%
-// faster at f = 2176, gate/up 13% slower at f = 17408, 3-17% slower at 16
-// and 32 tokens).
+// n = rmsnorm(x) * g normally comes from the norm kernel.  With up to 8
+// tokens the norm is folded into the gate/up kernel instead (FOLD, as in the
+// bf16 decode kernels: x * g where the activations are staged, r_m in the
+// epilogue): the fold saves the norm launch for some staging work (measured:
+// block 10% faster at f = 2176 and 2% faster at f = 17408; 3-17% slower at
+// 16 and 32 tokens, which keep the norm kernel).
 //
 // gfx950 mapping.  A block of 32 quants is exactly one K step of
 // v_mfma_f32_16x16x32_bf16, so the scale factors out of the block's dot
