@@ -623,3 +623,24 @@ def test_q4_zero_point_nibbles_return_x_bitwise(gpu_lib, M):
     q = I.make_q4_block(1950 + M, M, 384, 384)
     q.w_down.qs[:] = 0x88
     assert np.array_equal(_run_q4(ffn, q, bits=True), q.x)
+
+
+@pytest.mark.parametrize("kind", ["q8", "q4"])
+def test_prepared_quant_call_matches_wrapper(gpu_lib, kind):
+    """A call marshalled once (timing loops) gives the wrapper's output bitwise."""
+    from transformer_ffn_block_amd import ffn
+    import torch
+    _say("prepared", kind)
+    make = I.make_q8_block if kind == "q8" else I.make_q4_block
+    todev = _q8_dev if kind == "q8" else _q4_dev
+    q = make(2600, 8, 512, 1024)
+    mats = [todev(m) for m in (q.w_gate, q.w_up, q.w_down)]
+    x, g = dev(q.x), dev(q.g)
+    ref = (ffn.swiglu_block_q8 if kind == "q8" else ffn.swiglu_block_q4)(x, g, *mats, q.eps)
+    ws = ffn.alloc_workspace(getattr(ffn.lib(), f"ffn_swiglu_block_{kind}_workspace_size")(8, 512, 1024))
+    y = torch.empty_like(x)
+    call = ffn.prepare_swiglu_block_quant(kind, x, g, *mats, q.eps, y, ws)
+    call()
+    call()
+    torch.cuda.synchronize()
+    assert torch.equal(y, ref)

@@ -200,6 +200,33 @@ def swiglu_block_q4(x, g, w_gate: Tuple, w_up: Tuple, w_down: Tuple, eps: float,
     return y
 
 
+def prepare_swiglu_block_quant(kind: str, x, g, w_gate: Tuple, w_up: Tuple, w_down: Tuple,
+                               eps: float, out, workspace, stream=None):
+    """Marshal one ffn_swiglu_block_q8 / _q4 call (kind "q8" / "q4") once and
+    return a function that issues it and checks its status.  For loops that
+    repeat the same call (timing): the weight structs and pointers are built
+    here, not per call.  The tensors must stay alive and unchanged in place."""
+    M, d = x.shape
+    f = w_gate[0].shape[0]
+    L = lib()
+    need = getattr(L, f"ffn_swiglu_block_{kind}_workspace_size")(M, d, f)
+    nbytes = workspace.numel() * workspace.element_size()
+    if nbytes < need:
+        raise FFNError(FFN_ERR_WORKSPACE, f"ffn_swiglu_block_{kind}", f"workspace {nbytes} < {need} bytes")
+    mk = q8_struct if kind == "q8" else q4_struct
+    mats = [mk(*w) for w in (w_gate, w_up, w_down)]
+    fn = getattr(L, f"ffn_swiglu_block_{kind}")
+    args = (_dev(x, "x"), _dev(g, "g"), *[ctypes.byref(m) for m in mats], _dev(out, "y"), M, d, f, eps,
+            workspace.data_ptr(), nbytes, _stream_handle(stream))
+
+    def call():
+        st = fn(*args)
+        if st:
+            check(st, f"ffn_swiglu_block_{kind}")
+    call.mats = mats  # keeps the structs alive with the closure
+    return call
+
+
 # ----------------------------------------------------------------------------
 # measurement helpers
 # ----------------------------------------------------------------------------
