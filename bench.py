@@ -95,11 +95,14 @@ def time_calls(torch, fn, n):
     return s.elapsed_time(e) / n
 
 
-def warm_up(fn, n=20, seconds=1.0):
-    """At least n calls of fn(i), continued until `seconds` have passed (clocks settle)."""
+MIN_WARMUP_S = 1.0  # --min-warmup-s
+
+
+def warm_up(fn, n=20):
+    """At least n calls of fn(i), continued until --min-warmup-s seconds have passed (clocks settle)."""
     t0 = time.perf_counter()
     i = 0
-    while i < n or time.perf_counter() - t0 < seconds:
+    while i < n or time.perf_counter() - t0 < MIN_WARMUP_S:
         fn(i)
         i += 1
 
@@ -561,6 +564,8 @@ def main() -> int:
     ap.add_argument("--profile-run", action="store_true",
                     help="decode steps plus one 512 MiB copy (counter calibration); no output")
     args = ap.parse_args()
+    global MIN_WARMUP_S
+    MIN_WARMUP_S = args.min_warmup_s
     want = set(EXTRAS) if args.extras == "all" else set(args.extras.split(","))
     if not want <= set(EXTRAS):
         print(f"unknown --extras {sorted(want - set(EXTRAS))}; choose from {','.join(EXTRAS)}", file=sys.stderr)

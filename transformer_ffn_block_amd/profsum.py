@@ -27,15 +27,22 @@ def _rows(path):
 
 
 def stats(trace_csv: str, command: str) -> str:
+    """Per-kernel duration statistics; a kernel launched with several grid
+    sizes (one template at different shapes) gets one line per grid size."""
     per = collections.defaultdict(list)
+    grids = collections.defaultdict(set)
     for r in _rows(trace_csv):
         name = r.get("Kernel_Name") or r.get("Name")
+        grid = r.get("Grid_Size_X") or r.get("Grid_Size") or ""
         dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0
-        per[name].append(dur)
+        per[(name, grid)].append(dur)
+        grids[name].add(grid)
     out = [f"# rocprofv3 kernel trace summary", f"# command: {command}",
            "# kernel | dispatches | avg_us | median_us | min_us | max_us"]
-    for name, d in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+    for (name, grid), d in sorted(per.items(), key=lambda kv: -sum(kv[1])):
         short = name.split("(")[0]
+        if len(grids[name]) > 1:
+            short += f" [grid {grid}]"
         out.append(f"{short} | {len(d)} | {statistics.fmean(d):.2f} | {statistics.median(d):.2f} | "
                    f"{min(d):.2f} | {max(d):.2f}")
     return "\n".join(out) + "\n"
