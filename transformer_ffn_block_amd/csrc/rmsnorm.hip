@@ -57,10 +57,15 @@ struct Chunk<4> {
 };
 
 constexpr int kRowsPerBlock = 4;  // 4 wavefronts, one row each
+#ifndef FFN_RMS_PREG_ROWS
+#define FFN_RMS_PREG_ROWS 64
+#endif
 
 // CACHE = 16-byte chunks per lane kept in registers; requires
-// nchunk <= 64 * CACHE.
-template <int EB, int CACHE>
+// nchunk <= 64 * CACHE.  PREG: the gain chunks are loaded together with x
+// instead of after the reduction (one dependent memory round trip less; for
+// launches of a few rows, where that latency is the kernel's length).
+template <int EB, int CACHE, bool PREG>
 __global__ __launch_bounds__(256) void rmsnorm_cached(const uint4* __restrict__ x,
                                                       const uint4* __restrict__ g,
                                                       uint4* __restrict__ y, int64_t rows,
@@ -69,11 +74,12 @@ __global__ __launch_bounds__(256) void rmsnorm_cached(const uint4* __restrict__ 
   const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
   if (row >= rows) return;
   const uint4* xr = x + row * nchunk;
-  uint4 v[CACHE];
+  uint4 v[CACHE], gv[PREG ? CACHE : 1];
 #pragma unroll
   for (int i = 0; i < CACHE; ++i) {
     const int c = lane + 64 * i;
     v[i] = c < nchunk ? xr[c] : make_uint4(0, 0, 0, 0);
+    if (PREG) gv[PREG ? i : 0] = c < nchunk ? g[c] : make_uint4(0, 0, 0, 0);
   }
   float acc = 0.f;
 #pragma unroll
@@ -84,7 +90,7 @@ __global__ __launch_bounds__(256) void rmsnorm_cached(const uint4* __restrict__ 
 #pragma unroll
   for (int i = 0; i < CACHE; ++i) {
     const int c = lane + 64 * i;
-    if (c < nchunk) yr[c] = Chunk<EB>::scale(v[i], g[c], r);
+    if (c < nchunk) yr[c] = Chunk<EB>::scale(v[i], PREG ? gv[PREG ? i : 0] : g[c], r);
   }
 }
 
@@ -115,15 +121,23 @@ static hipError_t launch_eb(const void* x, const void* g, void* y, int64_t rows,
   const uint4* xx = (const uint4*)x;
   const uint4* gg = (const uint4*)g;
   uint4* yy = (uint4*)y;
-  if (nchunk <= 64 * 2)
-    hipLaunchKernelGGL((rmsnorm_cached<EB, 2>), grid, block, 0, s, xx, gg, yy, rows, nchunk, inv_d, eps);
-  else if (nchunk <= 64 * 4)
-    hipLaunchKernelGGL((rmsnorm_cached<EB, 4>), grid, block, 0, s, xx, gg, yy, rows, nchunk, inv_d, eps);
-  else if (nchunk <= 64 * 8)
-    hipLaunchKernelGGL((rmsnorm_cached<EB, 8>), grid, block, 0, s, xx, gg, yy, rows, nchunk, inv_d, eps);
-  else if (nchunk <= 64 * 16)
-    hipLaunchKernelGGL((rmsnorm_cached<EB, 16>), grid, block, 0, s, xx, gg, yy, rows, nchunk, inv_d, eps);
-  else
+  // a few rows: latency-bound, gain fetched with x; many rows: the gain
+  // (L2-resident) is fetched after the reduction, keeping registers free
+  const bool few = rows <= FFN_RMS_PREG_ROWS;
+#define FFN_RMS_CACHED(C)                                                                              \
+  if (few)                                                                                           \
+    hipLaunchKernelGGL((rmsnorm_cached<EB, C, true>), grid, block, 0, s, xx, gg, yy, rows, nchunk, inv_d, eps); \
+  else                                                                                               \
+    hipLaunchKernelGGL((rmsnorm_cached<EB, C, false>), grid, block, 0, s, xx, gg, yy, rows, nchunk, inv_d, eps);
+  if (nchunk <= 64 * 2) {
+    FFN_RMS_CACHED(2)
+  } else if (nchunk <= 64 * 4) {
+    FFN_RMS_CACHED(4)
+  } else if (nchunk <= 64 * 8) {
+    FFN_RMS_CACHED(8)
+  } else if (nchunk <= 64 * 16) {
+    FFN_RMS_CACHED(16)
+  } else
     hipLaunchKernelGGL((rmsnorm_stream<EB>), grid, block, 0, s, xx, gg, yy, rows, nchunk, inv_d, eps);
   return hipGetLastError();
 }
