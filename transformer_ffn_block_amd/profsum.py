@@ -113,10 +113,15 @@ def counters(csv_path: str, kernels, command: str, xcds: int = 8, simds: int = 1
     also the MFMA busy fraction = busy cycles summed over SIMDs / (GUI-active
     cycles per XCD x SIMDs)."""
     per = collections.defaultdict(lambda: collections.defaultdict(list))
+    names = set()
     for r in _rows(csv_path):
         per[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))
-    out = ["# rocprofv3 counter summary (per-dispatch means)", f"# command: {command}",
-           f"# mfma_busy_frac = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / {xcds} * {simds})"]
+        names.add(r["Counter_Name"])
+    out = ["# rocprofv3 counter summary (per-dispatch means)", f"# command: {command}"]
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in names:
+        out.append(f"# mfma_busy_frac = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / {xcds} * {simds})")
+    if "SQ_WAVE_CYCLES" in names:
+        out.append("# wave-cycle shares: SQ_WAIT_INST_ANY, SQ_WAIT_ANY and SQ_ACTIVE_INST_* over SQ_WAVE_CYCLES")
     for sub in kernels:
         hits = [(k, v) for k, v in per.items() if sub in k]
         if not hits:
