@@ -34,7 +34,10 @@ Readings taken where the pages leave a step open:
     GPU's bf16 roundings of n and h).
 
 Parity status: every function here is pinned by the CPU tests (closed
-forms, invariants, hand-derived fixtures, special cases); none is unpinned.
+forms, invariants, hand-derived fixtures, special cases), the stored-format
+wrappers at the end included (hand-worked fixtures encoded as bf16 and fp32
+bit patterns, known-bit fp32 values); planted mistakes in each of them make
+the pins fail.
 """
 from __future__ import annotations
 
@@ -189,10 +192,13 @@ def swiglu_block_q4(x_bits, g_bits, wg, wu, wd, eps: float) -> np.ndarray:
 # convenience wrappers taking stored-format inputs
 # ----------------------------------------------------------------------------
 def block_from_stored(dtype: str, x, g, w_gate, w_up, w_down, eps: float) -> np.ndarray:
-    """swiglu_block on stored-format inputs ('bf16' bit patterns or 'f32')."""
+    """swiglu_block on stored-format inputs ('bf16' bit patterns or 'f32'):
+    each tensor is decoded exactly to fp64 by as_f64, then the block's
+    definition is evaluated with the operands in their own roles."""
     return swiglu_block(as_f64(x, dtype), as_f64(g, dtype), as_f64(w_gate, dtype),
                         as_f64(w_up, dtype), as_f64(w_down, dtype), eps)
 
 
 def rmsnorm_from_stored(dtype: str, x, g, eps: float) -> np.ndarray:
+    """rmsnorm on stored-format inputs ('bf16' bit patterns or 'f32')."""
     return rmsnorm(as_f64(x, dtype), as_f64(g, dtype), eps)

@@ -50,6 +50,18 @@ MUTANTS = {
                                "        w[:, 32 * blk:32 * blk + 16] = low * s[:, (blk + 1) % s.shape[1]:(blk + 1) % s.shape[1] + 1]"),
     "bf16_low_half": ("return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)",
                       "return (b.astype(np.uint32) << np.uint32(15)).view(np.float32).astype(np.float64)"),
+    "wrapper_gate_up_swapped": ("as_f64(w_gate, dtype),\n                        as_f64(w_up, dtype)",
+                                "as_f64(w_up, dtype),\n                        as_f64(w_gate, dtype)"),
+    "wrapper_down_from_up": ("as_f64(w_up, dtype), as_f64(w_down, dtype), eps)",
+                             "as_f64(w_up, dtype), as_f64(w_up, dtype).T, eps)"),
+    "wrapper_f32_through_f16": ("return np.asarray(a, dtype=np.float32).astype(np.float64)",
+                                "return np.asarray(a, dtype=np.float16).astype(np.float64)"),
+    "wrapper_f32_truncated_to_bf16": ("return np.asarray(a, dtype=np.float32).astype(np.float64)",
+                                      "return bf16_to_f64(np.asarray(a, dtype=np.float32).view(np.uint32) >> 16)"),
+    "rmsnorm_wrapper_gain_decoded_as_f32": ("return rmsnorm(as_f64(x, dtype), as_f64(g, dtype), eps)",
+                                            "return rmsnorm(as_f64(x, dtype), as_f64(g, \"f32\"), eps)"),
+    "rmsnorm_wrapper_gain_dropped": ("return rmsnorm(as_f64(x, dtype), as_f64(g, dtype), eps)",
+                                     "return rmsnorm(as_f64(x, dtype), np.ones(np.shape(g)), eps)"),
 }
 
 

@@ -5,7 +5,9 @@ copy of the oracle: eps outside the root, the mean replaced by the sum, the
 gain dropped or turned into 1+g, a sign flip or a sigmoid in silu, gate and
 up swapped, the residual dropped or taken from n, a transposed weight, the
 wrong Q8 block axis, unsigned quants, flushed fp16 subnormals, a wrong bf16
-decode), the pin suite run against the mutated oracle must fail.  The
+decode; in the stored-format wrappers, gate and up weights swapped, the down
+weights taken from another operand, fp32 decoded through fp16 or truncated
+to bf16, the norm's gain decoded in the wrong format or dropped), the pin suite run against the mutated oracle must fail.  The
 mutants run on the CPU, each in its own interpreter.
 """
 import os

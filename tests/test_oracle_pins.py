@@ -383,3 +383,106 @@ def test_q4_block_form_roundtrip():
     assert np.array_equal(m.qs, m2.qs) and np.array_equal(m.scales, m2.scales)
     blocks = I.q4_soa_to_aos(m).reshape(3, 3, 18)
     assert np.array_equal(blocks[1, 2, 2:], m.qs[1, 32:48])  # the 16 bytes follow the scale
+
+
+# ----------------------------------------------------------------------------
+# stored-format wrappers (what every GPU parity test uses as its reference)
+# ----------------------------------------------------------------------------
+def _f32_bits(v: float) -> int:
+    """IEEE binary32 bit pattern of v, by the standard library's packer."""
+    import struct
+    return struct.unpack(">I", struct.pack(">f", v))[0]
+
+
+def _bf16_bits_exact(a) -> np.ndarray:
+    """bf16 bit patterns of values that bf16 holds exactly (the top 16 bits of
+    their binary32 pattern; the low 16 bits must be zero)."""
+    a = np.asarray(a, dtype=np.float64)
+    out = np.empty(a.shape, dtype=np.uint16)
+    for idx, v in np.ndenumerate(a):
+        b = _f32_bits(float(v))
+        assert b & 0xFFFF == 0, f"{v} is not a bf16 value"
+        out[idx] = b >> 16
+    return out
+
+
+def test_as_f64_f32_known_bits():
+    # 1 + 2^-23, -(1/6 rounded to binary32), 2^-149 (smallest subnormal),
+    # 3.4028234663852886e38 (largest finite): none of them fits bf16 or fp16
+    bits = np.array([0x3F800001, 0xBE2AAAAB, 0x00000001, 0x7F7FFFFF], dtype=np.uint32)
+    want = [1.0 + 2.0 ** -23, -0.1666666716337204, 2.0 ** -149, 3.4028234663852886e38]
+    got = O.as_f64(bits.view(np.float32), "f32")
+    assert got.dtype == np.float64 and list(got) == want
+    assert list(O.as_f64(np.array([0x3F80, 0xBF00], np.uint16), "bf16")) == [1.0, -0.5]
+
+
+@pytest.mark.parametrize("name", ["block_handcalc_gain.json", "block_handcalc_eps.json"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_block_from_stored_on_golden_fixtures(name, dtype):
+    """The hand-worked blocks, handed over as stored bit patterns, reproduce
+    the hand-worked outputs: each operand reaches its own role."""
+    gd = _load(name)
+    keys = ("x", "g", "w_gate", "w_up", "w_down")
+    if dtype == "bf16":
+        stored = [_bf16_bits_exact(gd[k]) for k in keys]
+    else:
+        stored = [np.array(gd[k], dtype=np.float32) for k in keys]
+    y = O.block_from_stored(dtype, *stored, gd["eps"])
+    assert y.dtype == np.float64
+    assert np.allclose(y, gd["y"], rtol=gd["tol"], atol=0)
+
+
+def test_block_from_stored_f32_values_outside_bf16():
+    """fp32 inputs that bf16 cannot hold: the wrapper equals the block on the
+    same values decoded by the standard library's unpacker."""
+    import struct
+    rng = np.random.default_rng(31)
+    M, d, f = 2, 8, 6
+    raw = [rng.integers(0, 1 << 16, size=s, dtype=np.uint32) for s in ((M, d), (d,), (f, d), (f, d), (d, f))]
+    # exponent fields of 1/64 .. 2, random low mantissa bits, random signs
+    stored = []
+    for r in raw:
+        e = rng.integers(121, 128, size=r.shape, dtype=np.uint32)
+        sgn = rng.integers(0, 2, size=r.shape, dtype=np.uint32)
+        stored.append(((sgn << 31) | (e << 23) | (r * 127 % (1 << 23))).astype(np.uint32).view(np.float32))
+    assert all(np.any(s.view(np.uint32) & 0xFFFF) for s in stored)
+    dec = [np.vectorize(lambda b: struct.unpack(">f", struct.pack(">I", int(b)))[0])(s.view(np.uint32))
+           for s in stored]
+    want = O.swiglu_block(*dec, 1e-6)
+    assert np.array_equal(O.block_from_stored("f32", *stored, 1e-6), want)
+
+
+def test_block_from_stored_gate_and_up_roles():
+    """One-hot weights as bf16 bits: gate reads n_1, up reads n_4, down adds
+    to y_2; swapping any two weight roles changes the result."""
+    M, d, f = 2, 6, 5
+    x = np.array([[1.0, -2.0, 0.5, 4.0, 1.5, -1.0], [0.25, 1.0, -3.0, 2.0, -0.5, 1.0]])
+    g = np.array([1.0, 2.0, 0.5, 1.0, 4.0, 1.0])
+    wg = np.zeros((f, d)); wg[3, 1] = 1.0
+    wu = np.zeros((f, d)); wu[3, 4] = 1.0
+    wd = np.zeros((d, f)); wd[2, 3] = 1.0
+    n = O.rmsnorm(x, g, 0.0)
+    expect = x.copy()
+    expect[:, 2] += O.silu(n[:, 1]) * n[:, 4]
+    bits = [_bf16_bits_exact(a) for a in (x, g, wg, wu, wd)]
+    assert np.allclose(O.block_from_stored("bf16", *bits, 0.0), expect, rtol=1e-15, atol=0)
+    swapped = O.block_from_stored("bf16", bits[0], bits[1], bits[3], bits[2], bits[4], 0.0)
+    assert not np.allclose(swapped, expect, rtol=1e-6, atol=0)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_rmsnorm_from_stored_on_golden_onehot(dtype):
+    gd = _load("rmsnorm_onehot.json")
+    if dtype == "bf16":
+        x, g = _bf16_bits_exact(gd["x"]), _bf16_bits_exact(gd["g"])
+    else:
+        x, g = np.array(gd["x"], np.float32), np.array(gd["g"], np.float32)
+    n = O.rmsnorm_from_stored(dtype, x, g, gd["eps"])
+    assert n.dtype == np.float64 and np.array_equal(n, np.array(gd["n"]))
+
+
+def test_rmsnorm_from_stored_bf16_gain_per_column():
+    # constant row 1, eps = 3: n_k = g_k / 2 exactly; g as bf16 bits
+    g = np.arange(1.0, 9.0)
+    n = O.rmsnorm_from_stored("bf16", _bf16_bits_exact(np.ones((1, 8))), _bf16_bits_exact(g), 3.0)
+    assert np.array_equal(n[0], g / 2)
