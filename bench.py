@@ -257,7 +257,8 @@ def extras(torch, np, ffn, I, sets, x, g, b, ws, extra, clocks, want):
 
         def stepv(i, v):
             wg, wu, wd = sets[i % ROTATE]
-            ffn.swiglu_block(x, g, wg, wu, wd, b.eps, v, out=yp, workspace=wsp if v == "persistent" else ws)
+            ffn.swiglu_block(x, g, wg, wu, wd, b.eps, v, out=yp, workspace=wsp if v == "persistent" else ws,
+                             check_status=False)
         tv = {"auto": [], "persistent": []}
         for v in tv:
             for i in range(10):
@@ -265,6 +266,9 @@ def extras(torch, np, ffn, I, sets, x, g, b, ws, extra, clocks, want):
         for _ in range(3):
             for v in tv:
                 tv[v].append(time_calls(torch, lambda i, v=v: stepv(i, v), 50))
+        torch.cuda.synchronize()
+        if ffn.persistent_status(wsp, M, d, f) != 0:
+            raise RuntimeError("persistent schedule: a work item gave up waiting")
         tp, ta = sorted(tv["persistent"])[1], sorted(tv["auto"])[1]
         extra["decode_M16_persistent"] = {"us": round(tp * 1e3, 2), "two_launch_us": round(ta * 1e3, 2),
                                           "persistent_over_two_launch": round(tp / ta, 3)}

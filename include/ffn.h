@@ -74,7 +74,10 @@ typedef enum { FFN_F32 = 0, FFN_BF16 = 1 } ffn_dtype;
  * block as one dispatch whose work items wait on device-scope completion
  * counters instead of kernel boundaries ("Megakernels on Mac", the
  * persistent-kernel experiment); a second, tiny launch before it clears the
- * counters.  AUTO picks FUSED or SPLIT by measured speed for the shape. */
+ * counters.  AUTO takes, for bf16, the weight-streaming decode kernels up
+ * to 64 tokens (the norm folded into the gate/up kernel, FUSED's
+ * schedule) and FUSED beyond (measured faster than SPLIT at the prefill
+ * shapes on this device); for fp32 it is FUSED. */
 typedef enum {
   FFN_VARIANT_AUTO = 0,
   FFN_VARIANT_FUSED = 1,
@@ -141,27 +144,37 @@ size_t ffn_swiglu_block_workspace_size(ffn_dtype dt, int64_t M, int64_t d, int64
  *               ffn_swiglu_block_workspace_size(dt, M, d, f, variant) bytes,
  *               256-byte aligned; its contents are scratch.
  * Returns FFN_OK, INVALID_ARGUMENT, UNSUPPORTED, WORKSPACE or LAUNCH. */
-/* For PERSISTENT the workspace's counter words must not be shared with a
- * call that overlaps on the device; after the call completes, counter word 1
- * (at the start of the counter region) is nonzero if a work item gave up
- * waiting (the result is then wrong). */
+/* PERSISTENT's bounded waits: a work item that gives up waiting for the
+ * items it depends on (which only a fault elsewhere on the device could
+ * cause) sets a 32-bit error word in the workspace and the call's result is
+ * then wrong.  After the call has completed, the uint32 at byte offset
+ * ffn_swiglu_block_persistent_status_offset(M, d, f) of the workspace is 0
+ * on success and nonzero otherwise.  Its counter words must not be shared
+ * with a call that overlaps on the device. */
 ffn_status ffn_swiglu_block(ffn_dtype dt, const void *x, const void *g,
                             const void *w_gate, const void *w_up, const void *w_down,
                             void *y, int64_t M, int64_t d, int64_t f, float eps,
                             ffn_variant variant, void *workspace, size_t workspace_bytes,
                             void *stream);
 
+/* Byte offset, inside a PERSISTENT call's workspace, of its uint32 error
+ * word (see above); 0 for a shape PERSISTENT rejects (bf16, 1 <= M <= 16). */
+size_t ffn_swiglu_block_persistent_status_offset(int64_t M, int64_t d, int64_t f);
+
 /* Workspace bytes ffn_swiglu_block_q8 needs: n [M,d] (not when the norm is
  * folded into the gate/up kernel: M <= 8) and h [M,f] in bf16,
  * then the fp32 partial sums of the split-K down projection,
  * [splits, min(M, 32), d] (splits, 1..8, is fixed by d and f); 0 on a shape
- * the entry point would reject for its sizes. */
+ * the entry point would reject for its sizes (M > 64 included). */
 size_t ffn_swiglu_block_q8_workspace_size(int64_t M, int64_t d, int64_t f);
 
 /* The block with Q8_0 weights, bf16 activations:
  *   x [M,d], g [d], y [M,d]: bf16 device pointers, 16-byte aligned.
  *   w_gate, w_up : Q8_0 [f, d]; w_down : Q8_0 [d, f] (host structs holding
  *                  device pointers).
+ *   M    : 0..64.  The weights stream from memory once per launch of at most
+ *          32 tokens, so this is a weight-streaming (decode) entry point;
+ *          M > 64 returns UNSUPPORTED.
  *   d, f : multiples of 32 (so no block straddles a row); f*d < 2^31.
  * Weights are dequantised in registers (q * s, exact in fp32) and never
  * written back; accumulation is fp32.
@@ -179,7 +192,7 @@ ffn_status ffn_swiglu_block_q8(const void *x, const void *g, const ffn_q8_matrix
  * both rounded up) and h [M,f] in bf16,
  * then the fp32 partial sums of the split-K down projection,
  * [splits, min(M, 32), d] (splits, 1..8, is fixed by d and f); 0 on a shape
- * the entry point would reject for its sizes. */
+ * the entry point would reject for its sizes (M > 64 included). */
 size_t ffn_swiglu_block_q4_workspace_size(int64_t M, int64_t d, int64_t f);
 
 /* The block with Q4_0 weights, bf16 activations ("Unfusing a Kernel Made It
@@ -187,6 +200,8 @@ size_t ffn_swiglu_block_q4_workspace_size(int64_t M, int64_t d, int64_t f);
  *   x [M,d], g [d], y [M,d]: bf16 device pointers, 16-byte aligned.
  *   w_gate, w_up : Q4_0 [f, d]; w_down : Q4_0 [d, f] (host structs holding
  *                  device pointers).
+ *   M    : 0..64 (weight-streaming regime, as for Q8_0; M > 64 returns
+ *          UNSUPPORTED).
  *   d, f : multiples of 32 (so no block straddles a row); f*d/2 < 2^31 bytes
  *          of nibbles per matrix.
  * Weights are dequantised in registers ((nibble - 8) * s, exact in fp32) and
@@ -223,11 +238,17 @@ int ffn_probe_read_groups(int waves_per_cu);
 ffn_status ffn_probe_copy(const void *src, void *dst, size_t bytes, void *stream);
 
 /* ---- per-kernel timing ----------------------------------------------------
- * When enabled, every kernel the library launches is bracketed by a pair of
- * HIP events recorded on the same stream; ffn_timing_collect() waits for
- * them and accumulates per-kernel totals.  Off by default; costs two event
- * records per launch when on.  Not thread-safe while enabled. */
+ * When enabled, every kernel the library launches FROM THE CALLING THREAD is
+ * bracketed by a pair of HIP events recorded on the same stream;
+ * ffn_timing_collect() waits for them and accumulates per-kernel totals.
+ * The state (switch, events, totals) is the calling thread's own: timing
+ * enabled on one thread neither records nor changes anything on another,
+ * so the library stays reentrant.  Off by default; costs two event records
+ * per launch when on (events are created at a thread's first timed launch
+ * and destroyed when that thread disables timing).  At most max_launches
+ * launches are recorded between two collects; later ones run untimed. */
 ffn_status ffn_timing_enable(int on, int max_launches);
+int ffn_timing_enabled(void);            /* 1 if on for the calling thread  */
 ffn_status ffn_timing_collect(void);     /* synchronises the recorded events */
 int ffn_timing_count(void);              /* number of distinct kernel names   */
 ffn_status ffn_timing_get(int index, const char **name, int64_t *launches, double *total_ms);

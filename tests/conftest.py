@@ -21,3 +21,21 @@ def gpu_lib():
         pytest.fail("GPU test collected on a host without a GPU")
     from transformer_ffn_block_amd import ffn
     return ffn.lib()
+
+
+def pytest_sessionfinish(session, exitstatus):
+    """Write the achieved parity errors of this session (tests/helpers.record)
+    to the file FFN_PARITY_LOG names, one JSON object per case."""
+    path = os.environ.get("FFN_PARITY_LOG")
+    if not path:
+        return
+    helpers = sys.modules.get("helpers")
+    if helpers is None or not getattr(helpers, "PARITY", None):
+        return
+    import json
+    d = os.path.dirname(path)
+    if d:
+        os.makedirs(d, exist_ok=True)
+    with open(path, "w") as fh:
+        for row in helpers.PARITY:
+            fh.write(json.dumps(row) + "\n")

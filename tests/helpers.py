@@ -61,3 +61,15 @@ def elementwise_rel_err(a: np.ndarray, r: np.ndarray) -> float:
 
 def rel_l2(a: np.ndarray, r: np.ndarray) -> float:
     return float(np.linalg.norm(a - r) / max(np.linalg.norm(r), 1e-300))
+
+
+# achieved error per parity case: (case, metric, error, tolerance), written
+# out at the end of the session when FFN_PARITY_LOG names a file
+PARITY = []
+
+
+def record(case: str, err: float, tol: float, metric: str = "max_norm") -> float:
+    """Log one parity figure (printed, and kept for the session's summary)."""
+    PARITY.append({"case": case, "metric": metric, "err": float(err), "tol": float(tol)})
+    print(f"[parity] {case}: {metric} {err:.3e} (tol {tol:g})", flush=True)
+    return err

@@ -84,7 +84,9 @@ def test_block_validation(L):
     assert _block(L, ws=0) == WSE
     assert _block(L, y=A) == INV                       # y aliases x
     assert _block(L, y=WS) == INV                      # y inside the workspace
-    assert "workspace" in L.ffn_last_error().decode() or True
+    assert "overlaps" in L.ffn_last_error().decode()
+    assert _block(L, wsb=100) == WSE
+    assert "workspace" in L.ffn_last_error().decode()
 
 
 def test_persistent_variant_scope(L):
@@ -126,9 +128,12 @@ def test_workspace_sizes(L):
         r256(9 * 5120 * 2) + r256(9 * 2176 * 2) + r256(sp * 9 * 5120 * 4)
     assert L.ffn_swiglu_block_q4_workspace_size(8, 5120, 17408) == \
         r256(8 * 5120 * 2) + r256(8 * 17408 * 2) + 4 * 8 * 5120 * 4
-    assert L.ffn_swiglu_block_q4_workspace_size(100, 5120, 17408) == \
-        r256(100 * 5120 * 2) + r256(100 * 17408 * 2) + 4 * 32 * 5120 * 4
+    assert L.ffn_swiglu_block_q4_workspace_size(64, 5120, 17408) == \
+        r256(64 * 5120 * 2) + r256(64 * 17408 * 2) + 4 * 32 * 5120 * 4
     assert L.ffn_swiglu_block_q4_workspace_size(-1, 5120, 17408) == 0
+    # beyond the weight-streaming regime the quantised blocks take no call
+    assert L.ffn_swiglu_block_q4_workspace_size(65, 5120, 17408) == 0
+    assert L.ffn_swiglu_block_q8_workspace_size(65, 5120, 17408) == 0
 
 
 def test_rmsnorm_validation(L):
@@ -163,6 +168,8 @@ def test_q8_validation(L):
     assert call(x=0) == INV
     assert call(wsb=10) == ffn.FFN_ERR_WORKSPACE
     assert call(M=0, ws=0, wsb=0) == ffn.FFN_OK
+    assert call(M=65, wsb=1 << 30) == UNS            # more tokens than the streaming regime
+    assert "at most 64 tokens" in L.ffn_last_error().decode()
     assert L.ffn_swiglu_block_q8(A, B, None, ref(g2), ref(g3), Y, 8, 5120, 17408, 1e-6, WS, 1 << 30, None) == INV
 
 
@@ -187,11 +194,80 @@ def test_q4_validation(L):
     assert call(x=0) == INV
     assert call(wsb=10) == ffn.FFN_ERR_WORKSPACE
     assert call(M=0, ws=0, wsb=0) == ffn.FFN_OK
+    assert call(M=65, wsb=1 << 30) == UNS            # more tokens than the streaming regime
     # 2^31 bytes of nibbles: d * f = 2^32 weights
     assert call(M=1, d=65536, f=65536) == UNS
     # just under the limit passes validation up to the aliasing check: y inside qs
     assert call(M=1, d=65536, f=32768 - 32, y=C) == INV
     assert L.ffn_swiglu_block_q4(A, B, None, ref(g2), ref(g3), Y, 8, 5120, 17408, 1e-6, WS, 1 << 30, None) == INV
+
+
+def test_persistent_status_offset(L):
+    def r256(n):
+        return (n + 255) // 256 * 256
+    M, d, f = 16, 4096, 11008
+    need = L.ffn_swiglu_block_workspace_size(ffn.FFN_BF16, M, d, f, 3)
+    off = L.ffn_swiglu_block_persistent_status_offset(M, d, f)
+    # word 1 of the counter region, which ends the workspace: 2 + S + d/16 words
+    assert any(off == need - r256((2 + s + d // 16) * 4) + 4 for s in range(1, 9))
+    assert off > r256(M * d * 2) + r256(M * f * 2)
+    assert L.ffn_swiglu_block_persistent_status_offset(17, d, f) == 0
+    assert L.ffn_swiglu_block_persistent_status_offset(0, d, f) == 0
+
+
+def test_timing_state_is_per_thread(L):
+    """Timing switched on in one thread is invisible to another; the other
+    thread's calls and its own switch are unaffected (no process-global
+    mutable state besides the library's code)."""
+    import threading
+    seen = {}
+    ev_on, ev_checked = threading.Event(), threading.Event()
+
+    def a():
+        seen["a_enable"] = L.ffn_timing_enable(1, 64)
+        seen["a_on"] = L.ffn_timing_enabled()
+        ev_on.set()
+        ev_checked.wait(10)
+        seen["a_still_on"] = L.ffn_timing_enabled()
+        seen["a_disable"] = L.ffn_timing_enable(0, 0)
+        seen["a_off"] = L.ffn_timing_enabled()
+
+    def b():
+        ev_on.wait(10)
+        seen["b_on"] = L.ffn_timing_enabled()
+        seen["b_count"] = L.ffn_timing_count()
+        # validation errors on this thread leave the other thread's state alone
+        seen["b_call"] = _block(L, x=0)
+        seen["b_err"] = L.ffn_last_error().decode()
+        seen["b_disable"] = L.ffn_timing_enable(0, 0)
+        ev_checked.set()
+
+    ta, tb = threading.Thread(target=a), threading.Thread(target=b)
+    ta.start(); tb.start(); ta.join(20); tb.join(20)
+    assert seen["a_enable"] == ffn.FFN_OK and seen["a_on"] == 1
+    assert seen["b_on"] == 0 and seen["b_count"] == 0
+    assert seen["b_call"] == ffn.FFN_ERR_INVALID_ARGUMENT and "null" in seen["b_err"]
+    assert seen["b_disable"] == ffn.FFN_OK
+    assert seen["a_still_on"] == 1                    # b's switch did not touch a's
+    assert seen["a_disable"] == ffn.FFN_OK and seen["a_off"] == 0
+    assert L.ffn_timing_enabled() == 0                # nor the main thread's
+
+
+def test_error_text_is_per_thread(L):
+    import threading
+    got = {}
+    assert _block(L, d=4100) == ffn.FFN_ERR_UNSUPPORTED
+    main_err = L.ffn_last_error().decode()
+
+    def other():
+        got["fresh"] = L.ffn_last_error().decode()
+        _block(L, x=0)
+        got["own"] = L.ffn_last_error().decode()
+    t = threading.Thread(target=other)
+    t.start(); t.join(10)
+    assert got["fresh"] == ""
+    assert "null" in got["own"]
+    assert L.ffn_last_error().decode() == main_err
 
 
 def test_probe_and_timing_validation(L):

@@ -35,35 +35,53 @@ ffn_status ok() {
 }
 
 // ---- per-kernel timing ---------------------------------------------------
+// Timing state belongs to the calling thread: only launches issued by the
+// thread that enabled timing are bracketed, and the totals are that
+// thread's.  Events are created on first use (so enabling touches no device)
+// and destroyed when the thread disables timing.  No HIP call is made from
+// a thread-exit destructor: a thread that ends with timing still enabled
+// leaks its events.
 struct Timing {
   bool on = false;
   int cap = 0;
   int used = 0;
-  std::vector<hipEvent_t> ev;
+  std::vector<hipEvent_t> ev;  // 2 per launch slot, created on demand
   std::vector<const char*> name;
   std::map<std::string, std::pair<int64_t, double>> total;
   std::vector<std::string> order;
 };
-Timing g_t;
+thread_local Timing t_timing;
 
 template <class F>
 hipError_t timed(const char* name, hipStream_t s, F&& f) {
-  if (!g_t.on || g_t.used >= g_t.cap) return f();
-  const int i = g_t.used++;
-  hipError_t e = hipEventRecord(g_t.ev[2 * i], s);
+  Timing& T = t_timing;
+  if (!T.on || T.used >= T.cap) return f();
+  const int i = T.used;
+  for (int k = 2 * i; k < 2 * i + 2; ++k) {
+    if (!T.ev[k]) {
+      const hipError_t e = hipEventCreate(&T.ev[k]);
+      if (e != hipSuccess) {
+        T.ev[k] = nullptr;
+        return e;
+      }
+    }
+  }
+  hipError_t e = hipEventRecord(T.ev[2 * i], s);
   if (e != hipSuccess) return e;
   e = f();
   if (e != hipSuccess) return e;
-  g_t.name[i] = name;
-  return hipEventRecord(g_t.ev[2 * i + 1], s);
+  T.name[i] = name;
+  T.used = i + 1;
+  return hipEventRecord(T.ev[2 * i + 1], s);
 }
 
 void release_events() {
-  for (hipEvent_t e : g_t.ev)
+  Timing& T = t_timing;
+  for (hipEvent_t e : T.ev)
     if (e) (void)hipEventDestroy(e);
-  g_t.ev.clear();
-  g_t.name.clear();
-  g_t.cap = g_t.used = 0;
+  T.ev.clear();
+  T.name.clear();
+  T.cap = T.used = 0;
 }
 
 // ---- validation helpers ----------------------------------------------------
@@ -205,6 +223,11 @@ size_t ffn_swiglu_block_workspace_size(ffn_dtype dt, int64_t M, int64_t d, int64
   return ws_layout(elem_size(dt), M, d, f, use_split(variant), use_persistent(variant)).total;
 }
 
+size_t ffn_swiglu_block_persistent_status_offset(int64_t M, int64_t d, int64_t f) {
+  if (M < 1 || M > 16 || d <= 0 || f <= 0 || d > INT32_MAX || f > INT32_MAX) return 0;
+  return ws_layout(2, M, d, f, false, true).ctr + 4;
+}
+
 ffn_status ffn_swiglu_block(ffn_dtype dt, const void* x, const void* g, const void* w_gate,
                             const void* w_up, const void* w_down, void* y, int64_t M, int64_t d,
                             int64_t f, float eps, ffn_variant variant, void* workspace,
@@ -326,13 +349,14 @@ struct Q8Traits {
     const int sp = ffn::q8_down_splits((int)d, (int)f);
     return sp > 1 ? (size_t)sp * (size_t)Mc * (size_t)d * 4 : 0;
   }
-  // The norm folds into the gate/up kernel when that saves more than it
-  // costs: the fold removes one launch (~5 us) but adds staging work in
-  // proportion to the row tiles x 256-k stages the kernel walks.  Measured:
-  // f = 2176 (136 tiles x 20 stages) 26.4 -> 23.8 us per block; f = 17408
-  // (1088 x 20) gate/up 45.2 -> 51.1 us, no net gain; 16 and 32 tokens
-  // slower.  So: up to 8 tokens and at most 10240 tile-stages.
+  // The norm folds into the gate/up kernel for every call of up to 8
+  // tokens: the fold removes the norm launch (~5 us) and the n round trip.
+  // Measured with the deeper quantised pipeline: block 26.4 -> 23.8 us at
+  // f = 2176 and 74.2 -> 72.8 us at f = 17408 (8 tokens); at 16 and 32
+  // tokens the folded kernel was slower, so those calls keep the norm kernel.
   static bool fold(int64_t M, int64_t d, int64_t f) {
+    (void)d;
+    (void)f;
     return FFN_Q8_FOLD != 0 && M <= 8;
   }
   static hipError_t gateup(const void* act, const void* gain, float eps, const Mat* g, const Mat* u,
@@ -372,6 +396,12 @@ struct Q4Traits {
   }
 };
 
+// The quantised blocks stream every weight once per launch of at most
+// T::max_tokens() tokens, so their cost grows with M in steps of whole
+// weight passes; they take the weight-streaming regime only (two launches
+// at most), and larger token counts are rejected.
+constexpr int64_t kQuantMaxTokens = 64;
+
 // Workspace of a quantised block: n [M,d] (unless the norm is folded) and
 // h [M,f] in bf16, then the down projection's split-K partials for one
 // chunk of tokens.
@@ -410,6 +440,10 @@ static ffn_status quant_block(const void* x, const void* g, const typename T::Ma
   }
   FFN_TRY(check_eps(eps));
   FFN_TRY(check_block_dims(M, d, f, T::k_multiple));
+  if (M > kQuantMaxTokens)
+    return fail(FFN_ERR_UNSUPPORTED,
+                "%s block takes at most %d tokens (weight-streaming regime; got %lld)", T::name,
+                kQuantMaxTokens, (long long)M);
   if (T::quant_bytes((size_t)f * d) >= ((size_t)1 << 31))
     return fail(FFN_ERR_UNSUPPORTED, "%s quant arrays must be smaller than 2 GiB", T::name);
   if (!aligned(x, 16) || !aligned(g, 16) || !aligned(y, 16))
@@ -455,7 +489,7 @@ static ffn_status quant_block(const void* x, const void* g, const typename T::Ma
 extern "C" {
 
 size_t ffn_swiglu_block_q8_workspace_size(int64_t M, int64_t d, int64_t f) {
-  if (M < 0 || d <= 0 || f <= 0 || d > INT32_MAX || f > INT32_MAX) return 0;
+  if (M < 0 || M > kQuantMaxTokens || d <= 0 || f <= 0 || d > INT32_MAX || f > INT32_MAX) return 0;
   return quant_ws<Q8Traits>(M, d, f).total;
 }
 
@@ -468,7 +502,7 @@ ffn_status ffn_swiglu_block_q8(const void* x, const void* g, const ffn_q8_matrix
 }
 
 size_t ffn_swiglu_block_q4_workspace_size(int64_t M, int64_t d, int64_t f) {
-  if (M < 0 || d <= 0 || f <= 0 || d > INT32_MAX || f > INT32_MAX) return 0;
+  if (M < 0 || M > kQuantMaxTokens || d <= 0 || f <= 0 || d > INT32_MAX || f > INT32_MAX) return 0;
   return quant_ws<Q4Traits>(M, d, f).total;
 }
 
@@ -507,66 +541,67 @@ ffn_status ffn_probe_copy(const void* src, void* dst, size_t bytes, void* stream
 
 // ---------------------------------------------------------------------------
 ffn_status ffn_timing_enable(int on, int max_launches) {
+  Timing& T = t_timing;
   if (!on) {
-    g_t.on = false;
+    T.on = false;
+    release_events();
     return ok();
   }
   if (max_launches < 1 || max_launches > (1 << 20))
     return fail(FFN_ERR_INVALID_ARGUMENT, "max_launches must be 1..2^20");
-  if (g_t.cap != max_launches) {
+  if (T.cap != max_launches) {
     release_events();
-    g_t.ev.assign(2 * (size_t)max_launches, nullptr);
-    g_t.name.assign(max_launches, nullptr);
-    for (auto& e : g_t.ev) {
-      if (hipEventCreate(&e) != hipSuccess) {
-        release_events();
-        return fail(FFN_ERR_LAUNCH, "hipEventCreate failed");
-      }
-    }
-    g_t.cap = max_launches;
+    T.ev.assign(2 * (size_t)max_launches, nullptr);
+    T.name.assign(max_launches, nullptr);
+    T.cap = max_launches;
   }
-  g_t.used = 0;
-  g_t.on = true;
+  T.used = 0;
+  T.on = true;
   return ok();
 }
 
+int ffn_timing_enabled(void) { return t_timing.on ? 1 : 0; }
+
 ffn_status ffn_timing_collect(void) {
-  for (int i = 0; i < g_t.used; ++i) {
-    if (hipEventSynchronize(g_t.ev[2 * i + 1]) != hipSuccess)
+  Timing& T = t_timing;
+  for (int i = 0; i < T.used; ++i) {
+    if (hipEventSynchronize(T.ev[2 * i + 1]) != hipSuccess)
       return fail(FFN_ERR_LAUNCH, "event synchronize failed");
     float ms = 0.f;
-    if (hipEventElapsedTime(&ms, g_t.ev[2 * i], g_t.ev[2 * i + 1]) != hipSuccess)
+    if (hipEventElapsedTime(&ms, T.ev[2 * i], T.ev[2 * i + 1]) != hipSuccess)
       return fail(FFN_ERR_LAUNCH, "event elapsed time failed");
-    const std::string nm = g_t.name[i] ? g_t.name[i] : "?";
-    auto it = g_t.total.find(nm);
-    if (it == g_t.total.end()) {
-      g_t.order.push_back(nm);
-      g_t.total[nm] = {1, (double)ms};
+    const std::string nm = T.name[i] ? T.name[i] : "?";
+    auto it = T.total.find(nm);
+    if (it == T.total.end()) {
+      T.order.push_back(nm);
+      T.total[nm] = {1, (double)ms};
     } else {
       it->second.first += 1;
       it->second.second += ms;
     }
   }
-  g_t.used = 0;
+  T.used = 0;
   return ok();
 }
 
-int ffn_timing_count(void) { return (int)g_t.order.size(); }
+int ffn_timing_count(void) { return (int)t_timing.order.size(); }
 
 ffn_status ffn_timing_get(int index, const char** name, int64_t* launches, double* total_ms) {
-  if (index < 0 || index >= (int)g_t.order.size() || !name || !launches || !total_ms)
+  Timing& T = t_timing;
+  if (index < 0 || index >= (int)T.order.size() || !name || !launches || !total_ms)
     return fail(FFN_ERR_INVALID_ARGUMENT, "bad timing index or null output");
-  const std::string& nm = g_t.order[index];
+  const std::string& nm = T.order[index];
   *name = nm.c_str();
-  *launches = g_t.total[nm].first;
-  *total_ms = g_t.total[nm].second;
+  *launches = T.total[nm].first;
+  *total_ms = T.total[nm].second;
   return ok();
 }
 
 void ffn_timing_reset(void) {
-  g_t.total.clear();
-  g_t.order.clear();
-  g_t.used = 0;
+  Timing& T = t_timing;
+  T.total.clear();
+  T.order.clear();
+  T.used = 0;
 }
 
 }  // extern "C"

@@ -36,6 +36,7 @@ SIGNATURES = [
     ("ffn_rmsnorm", _I, [_I, _VP, _VP, _VP, _I64, _I64, _F, _VP]),
     ("ffn_swiglu_block_workspace_size", _SZ, [_I, _I64, _I64, _I64, _I]),
     ("ffn_swiglu_block", _I, [_I, _VP, _VP, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _F, _I, _VP, _SZ, _VP]),
+    ("ffn_swiglu_block_persistent_status_offset", _SZ, [_I64, _I64, _I64]),
     ("ffn_swiglu_block_q8_workspace_size", _SZ, [_I64, _I64, _I64]),
     ("ffn_swiglu_block_q8", _I, [_VP, _VP, _Q8P, _Q8P, _Q8P, _VP, _I64, _I64, _I64, _F, _VP, _SZ, _VP]),
     ("ffn_swiglu_block_q4_workspace_size", _SZ, [_I64, _I64, _I64]),
@@ -46,6 +47,7 @@ SIGNATURES = [
     ("ffn_probe_read_groups", _I, [_I]),
     ("ffn_probe_copy", _I, [_VP, _VP, _SZ, _VP]),
     ("ffn_timing_enable", _I, [_I, _I]),
+    ("ffn_timing_enabled", _I, []),
     ("ffn_timing_collect", _I, []),
     ("ffn_timing_count", _I, []),
     ("ffn_timing_get", _I, [_I, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(_I64),
@@ -121,11 +123,75 @@ def _dev(t, name: str):
     return t.data_ptr()
 
 
+def _expect(t, name: str, shape, dtypes, device) -> None:
+    """Raise ValueError unless t has exactly `shape`, one of `dtypes`, is
+    contiguous and lives on `device` (checked before any library call, so a
+    mismatched tensor never reaches the kernels as a raw pointer)."""
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {' or '.join(str(d) for d in dtypes)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _expect_2d(x, name: str = "x"):
+    if x.dim() != 2:
+        raise ValueError(f"{name} must be a 2-D [tokens, d] tensor, got shape {tuple(x.shape)}")
+    return x.shape
+
+
+def _workspace(workspace, need: int, device):
+    if workspace is None:
+        return alloc_workspace(need, device)
+    if not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    if workspace.device != device:
+        raise ValueError(f"workspace is on {workspace.device}, expected {device}")
+    nbytes = workspace.numel() * workspace.element_size()
+    if nbytes < need:
+        raise FFNError(FFN_ERR_WORKSPACE, "workspace", f"{nbytes} bytes given, {need} needed")
+    return workspace
+
+
+def _output(out, like, name="out"):
+    torch = _torch()
+    if out is None:
+        return torch.empty_like(like)
+    _expect(out, name, like.shape, (like.dtype,), like.device)
+    return out
+
+
+def _quant_operands(x, g, w_gate, w_up, w_down, qs_dtype, nibbles: bool):
+    """Check a quantised block's operands: x [M,d] and g [d] bf16, each
+    weight a (qs, scales) pair with qs [N, K] (Q8_0, int8) or [N, K/2]
+    (Q4_0, uint8) and scales [N, K/32] 16-bit fp16 patterns."""
+    torch = _torch()
+    M, d = _expect_2d(x)
+    _expect(x, "x", (M, d), (torch.bfloat16,), x.device)
+    _expect(g, "g", (d,), (torch.bfloat16,), x.device)
+    for name, w in (("w_gate", w_gate), ("w_up", w_up), ("w_down", w_down)):
+        if not isinstance(w, (tuple, list)) or len(w) != 2:
+            raise ValueError(f"{name} must be a (qs, scales) pair")
+    if w_gate[0].dim() != 2:
+        raise ValueError(f"w_gate quants must be 2-D, got shape {tuple(w_gate[0].shape)}")
+    f = w_gate[0].shape[0]
+    for name, (qs, sc), N, K in (("w_gate", w_gate, f, d), ("w_up", w_up, f, d), ("w_down", w_down, d, f)):
+        if K % 32 or N <= 0:
+            raise ValueError(f"{name}: the reduction length {K} must be a positive multiple of 32")
+        _expect(qs, f"{name} quants", (N, K // 2 if nibbles else K), (qs_dtype,), x.device)
+        _expect(sc, f"{name} scales", (N, K // 32), (torch.int16, torch.uint16), x.device)
+    return M, d, f
+
+
 def rmsnorm(x, g, eps: float, out=None, stream=None):
     """y = rmsnorm(x) * g over the last dim of a [rows, d] tensor."""
-    torch = _torch()
-    rows, d = x.shape
-    y = out if out is not None else torch.empty_like(x)
+    rows, d = _expect_2d(x)
+    _dt(x)
+    _expect(g, "g", (d,), (x.dtype,), x.device)
+    y = _output(out, x)
     check(lib().ffn_rmsnorm(_dt(x), _dev(x, "x"), _dev(g, "g"), _dev(y, "y"), rows, d, eps,
                             _stream_handle(stream)), "ffn_rmsnorm")
     return y
@@ -141,21 +207,54 @@ def alloc_workspace(nbytes: int, device="cuda"):
     return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
 
-def swiglu_block(x, g, w_gate, w_up, w_down, eps: float, variant: str = "auto", out=None,
-                 workspace=None, stream=None):
-    """y = x + W_down (silu(W_gate n) * (W_up n)), n = rmsnorm(x) * g."""
-    torch = _torch()
-    M, d = x.shape
-    f = w_gate.shape[0]
+def _block_operands(x, g, w_gate, w_up, w_down):
+    M, d = _expect_2d(x)
     dt = _dt(x)
+    if w_gate.dim() != 2:
+        raise ValueError(f"w_gate must be a 2-D [f, d] tensor, got shape {tuple(w_gate.shape)}")
+    f = w_gate.shape[0]
+    _expect(g, "g", (d,), (x.dtype,), x.device)
+    _expect(w_gate, "w_gate", (f, d), (x.dtype,), x.device)
+    _expect(w_up, "w_up", (f, d), (x.dtype,), x.device)
+    _expect(w_down, "w_down", (d, f), (x.dtype,), x.device)
+    return M, d, f, dt
+
+
+def swiglu_block(x, g, w_gate, w_up, w_down, eps: float, variant: str = "auto", out=None,
+                 workspace=None, stream=None, check_status: bool = True):
+    """y = x + W_down (silu(W_gate n) * (W_up n)), n = rmsnorm(x) * g.
+
+    variant "persistent" has bounded device-side waits; with check_status
+    (the default) the call synchronises the stream and raises FFNError if a
+    wait gave up (the result is then wrong).  Timing loops pass
+    check_status=False and read persistent_status() themselves."""
+    if variant not in VARIANTS:
+        raise ValueError(f"unknown variant {variant!r}; choose from {sorted(VARIANTS)}")
+    M, d, f, dt = _block_operands(x, g, w_gate, w_up, w_down)
     need = workspace_size(dt, M, d, f, variant)
-    ws = workspace if workspace is not None else alloc_workspace(need, x.device)
-    y = out if out is not None else torch.empty_like(x)
+    ws = _workspace(workspace, need, x.device)
+    y = _output(out, x)
     check(lib().ffn_swiglu_block(dt, _dev(x, "x"), _dev(g, "g"), _dev(w_gate, "w_gate"),
                                  _dev(w_up, "w_up"), _dev(w_down, "w_down"), _dev(y, "y"), M, d, f,
                                  eps, VARIANTS[variant], ws.data_ptr(), ws.numel() * ws.element_size(),
                                  _stream_handle(stream)), "ffn_swiglu_block")
+    if variant == "persistent" and check_status and M > 0:
+        (stream if stream is not None else _torch().cuda.current_stream()).synchronize()
+        word = persistent_status(ws, M, d, f)
+        if word != 0:
+            raise FFNError(FFN_ERR_LAUNCH, "ffn_swiglu_block(persistent)",
+                           f"a work item gave up waiting (error word {word:#x}); the result is invalid")
     return y
+
+
+def persistent_status(workspace, M: int, d: int, f: int) -> int:
+    """The error word a completed PERSISTENT call left in its workspace (0 = ok).
+    Reads device memory: call after the call's stream has been synchronised."""
+    off = lib().ffn_swiglu_block_persistent_status_offset(M, d, f)
+    if off == 0:
+        raise ValueError(f"no persistent schedule for M={M}, d={d}, f={f}")
+    b = workspace.view(-1)[off:off + 4].to("cpu").numpy()
+    return int(b.view("<u4")[0])
 
 
 def q8_struct(qs, scales) -> Q8Matrix:
@@ -166,11 +265,10 @@ def swiglu_block_q8(x, g, w_gate: Tuple, w_up: Tuple, w_down: Tuple, eps: float,
                     workspace=None, stream=None):
     """The block with Q8_0 weights; each weight is a (qs int8 [N,K], scales int16/uint16-bits [N,K/32]) pair."""
     torch = _torch()
-    M, d = x.shape
-    f = w_gate[0].shape[0]
+    M, d, f = _quant_operands(x, g, w_gate, w_up, w_down, torch.int8, nibbles=False)
     need = lib().ffn_swiglu_block_q8_workspace_size(M, d, f)
-    ws = workspace if workspace is not None else alloc_workspace(need, x.device)
-    y = out if out is not None else torch.empty_like(x)
+    ws = _workspace(workspace, need, x.device)
+    y = _output(out, x)
     mg, mu, md = q8_struct(*w_gate), q8_struct(*w_up), q8_struct(*w_down)
     check(lib().ffn_swiglu_block_q8(_dev(x, "x"), _dev(g, "g"), ctypes.byref(mg), ctypes.byref(mu),
                                     ctypes.byref(md), _dev(y, "y"), M, d, f, eps, ws.data_ptr(),
@@ -187,11 +285,10 @@ def swiglu_block_q4(x, g, w_gate: Tuple, w_up: Tuple, w_down: Tuple, eps: float,
                     workspace=None, stream=None):
     """The block with Q4_0 weights; each weight is a (qs uint8 [N,K/2], scales int16/uint16-bits [N,K/32]) pair."""
     torch = _torch()
-    M, d = x.shape
-    f = w_gate[0].shape[0]
+    M, d, f = _quant_operands(x, g, w_gate, w_up, w_down, torch.uint8, nibbles=True)
     need = lib().ffn_swiglu_block_q4_workspace_size(M, d, f)
-    ws = workspace if workspace is not None else alloc_workspace(need, x.device)
-    y = out if out is not None else torch.empty_like(x)
+    ws = _workspace(workspace, need, x.device)
+    y = _output(out, x)
     mg, mu, md = q4_struct(*w_gate), q4_struct(*w_up), q4_struct(*w_down)
     check(lib().ffn_swiglu_block_q4(_dev(x, "x"), _dev(g, "g"), ctypes.byref(mg), ctypes.byref(mu),
                                     ctypes.byref(md), _dev(y, "y"), M, d, f, eps, ws.data_ptr(),
@@ -206,13 +303,16 @@ def prepare_swiglu_block_quant(kind: str, x, g, w_gate: Tuple, w_up: Tuple, w_do
     return a function that issues it and checks its status.  For loops that
     repeat the same call (timing): the weight structs and pointers are built
     here, not per call.  The tensors must stay alive and unchanged in place."""
-    M, d = x.shape
-    f = w_gate[0].shape[0]
+    torch = _torch()
+    if kind not in ("q8", "q4"):
+        raise ValueError(f"kind must be 'q8' or 'q4', got {kind!r}")
+    M, d, f = _quant_operands(x, g, w_gate, w_up, w_down, torch.int8 if kind == "q8" else torch.uint8,
+                              nibbles=kind == "q4")
+    _output(out, x)
     L = lib()
     need = getattr(L, f"ffn_swiglu_block_{kind}_workspace_size")(M, d, f)
+    _workspace(workspace, need, x.device)
     nbytes = workspace.numel() * workspace.element_size()
-    if nbytes < need:
-        raise FFNError(FFN_ERR_WORKSPACE, f"ffn_swiglu_block_{kind}", f"workspace {nbytes} < {need} bytes")
     mk = q8_struct if kind == "q8" else q4_struct
     mats = [mk(*w) for w in (w_gate, w_up, w_down)]
     fn = getattr(L, f"ffn_swiglu_block_{kind}")
@@ -242,6 +342,11 @@ def probe_copy(src, dst, stream=None) -> None:
 
 def timing_enable(on: bool, max_launches: int = 4096) -> None:
     check(lib().ffn_timing_enable(1 if on else 0, max_launches), "ffn_timing_enable")
+
+
+def timing_enabled() -> bool:
+    """Whether per-kernel timing is on for the calling thread."""
+    return bool(lib().ffn_timing_enabled())
 
 
 def timing_collect() -> dict:
