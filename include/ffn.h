@@ -157,6 +157,34 @@ ffn_status ffn_swiglu_block(ffn_dtype dt, const void *x, const void *g,
                             ffn_variant variant, void *workspace, size_t workspace_bytes,
                             void *stream);
 
+/* Size of the library's own scratch array, per GPU (see below). */
+#define FFN_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/* ffn_swiglu_block for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, kernels and results as ffn_swiglu_block
+ * minus the workspace: the intermediates live in a device array the
+ * library itself holds, FFN_NOALLOC_SCRATCH_BYTES on every GPU it runs on,
+ * from the library's load until the process ends.  The call allocates
+ * nothing (no hipMalloc, hipFree or allocating library routine); the
+ * caller still passes every input and the output, on the current device.
+ *   - A shape whose ffn_swiglu_block_workspace_size exceeds the array
+ *     returns FFN_ERR_UNSUPPORTED (e.g. M = 64 fits for d + f up to 131072
+ *     with FUSED; the 8192-token prefill shapes do not).
+ *   - Every call on one GPU shares that GPU's array, which keeps the last
+ *     call's contents: calls that overlap on one GPU (two streams, two
+ *     threads) race and give wrong results; serialise them.  Nothing in
+ *     the array has to start at zero (PERSISTENT clears its counters with
+ *     a kernel of its own).  PERSISTENT's error word is at
+ *     ffn_swiglu_block_persistent_status_offset in that array, which the
+ *     caller cannot read: use ffn_swiglu_block to check it.
+ * Returns what ffn_swiglu_block returns, plus UNSUPPORTED as above and
+ * LAUNCH if the array's device address cannot be found. */
+ffn_status ffn_swiglu_block_noalloc(ffn_dtype dt, const void *x, const void *g,
+                                    const void *w_gate, const void *w_up, const void *w_down,
+                                    void *y, int64_t M, int64_t d, int64_t f, float eps,
+                                    ffn_variant variant, void *stream);
+
 /* Byte offset, inside a PERSISTENT call's workspace, of its uint32 error
  * word (see above); 0 for a shape PERSISTENT rejects (bf16, 1 <= M <= 16). */
 size_t ffn_swiglu_block_persistent_status_offset(int64_t M, int64_t d, int64_t f);

@@ -9,6 +9,7 @@
 #include <cstdio>
 #include <cstring>
 #include <map>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -602,6 +603,68 @@ void ffn_timing_reset(void) {
   T.total.clear();
   T.order.clear();
   T.used = 0;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// The block for callers that cannot allocate: its workspace is `scratch`, a
+// file-scope device array each GPU holds from the library's load until the
+// process ends.  In host code `scratch` names a host-side stand-in, so the
+// array's device address is looked up once per device (with that device
+// current) and only that address is handed to kernels.
+static __device__ __align__(256) unsigned char scratch[FFN_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr size_t kNoAllocScratchBytes = (size_t)FFN_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // written once per device under the mutex
+
+ffn_status scratch_for_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(FFN_ERR_LAUNCH, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(FFN_ERR_UNSUPPORTED, "device ordinal %d beyond the %d the library tracks", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(FFN_ERR_LAUNCH, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return FFN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ffn_status ffn_swiglu_block_noalloc(ffn_dtype dt, const void* x, const void* g, const void* w_gate,
+                                    const void* w_up, const void* w_down, void* y, int64_t M,
+                                    int64_t d, int64_t f, float eps, ffn_variant variant,
+                                    void* stream) {
+  // a shape the block would reject gets the block's own error below
+  const size_t need = ffn_swiglu_block_workspace_size(dt, M, d, f, variant);
+  if (need > kNoAllocScratchBytes)
+    return fail(FFN_ERR_UNSUPPORTED,
+                "this shape needs %zu bytes of workspace; the library's scratch array holds %zu "
+                "(use ffn_swiglu_block with a caller workspace)",
+                need, kNoAllocScratchBytes);
+  if (M == 0 || need == 0)  // nothing to launch, or an invalid call: no device lookup
+    return ffn_swiglu_block(dt, x, g, w_gate, w_up, w_down, y, M, d, f, eps, variant, nullptr, 0,
+                            stream);
+  void* ws = nullptr;
+  FFN_TRY(scratch_for_current_device(&ws));
+  return ffn_swiglu_block(dt, x, g, w_gate, w_up, w_down, y, M, d, f, eps, variant, ws,
+                          kNoAllocScratchBytes, stream);
 }
 
 }  // extern "C"

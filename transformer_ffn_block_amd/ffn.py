@@ -36,6 +36,7 @@ SIGNATURES = [
     ("ffn_rmsnorm", _I, [_I, _VP, _VP, _VP, _I64, _I64, _F, _VP]),
     ("ffn_swiglu_block_workspace_size", _SZ, [_I, _I64, _I64, _I64, _I]),
     ("ffn_swiglu_block", _I, [_I, _VP, _VP, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _F, _I, _VP, _SZ, _VP]),
+    ("ffn_swiglu_block_noalloc", _I, [_I, _VP, _VP, _VP, _VP, _VP, _VP, _I64, _I64, _I64, _F, _I, _VP]),
     ("ffn_swiglu_block_persistent_status_offset", _SZ, [_I64, _I64, _I64]),
     ("ffn_swiglu_block_q8_workspace_size", _SZ, [_I64, _I64, _I64]),
     ("ffn_swiglu_block_q8", _I, [_VP, _VP, _Q8P, _Q8P, _Q8P, _VP, _I64, _I64, _I64, _F, _VP, _SZ, _VP]),
@@ -244,6 +245,22 @@ def swiglu_block(x, g, w_gate, w_up, w_down, eps: float, variant: str = "auto", 
         if word != 0:
             raise FFNError(FFN_ERR_LAUNCH, "ffn_swiglu_block(persistent)",
                            f"a work item gave up waiting (error word {word:#x}); the result is invalid")
+    return y
+
+
+def swiglu_block_noalloc(x, g, w_gate, w_up, w_down, eps: float, variant: str = "auto", out=None,
+                         stream=None):
+    """The block with the library's own scratch array as its workspace (no
+    device allocation by the library; `out` preallocated by the caller for
+    the same guarantee on this side).  Calls that overlap on one GPU race."""
+    if variant not in VARIANTS:
+        raise ValueError(f"unknown variant {variant!r}; choose from {sorted(VARIANTS)}")
+    M, d, f, dt = _block_operands(x, g, w_gate, w_up, w_down)
+    y = _output(out, x)
+    check(lib().ffn_swiglu_block_noalloc(dt, _dev(x, "x"), _dev(g, "g"), _dev(w_gate, "w_gate"),
+                                         _dev(w_up, "w_up"), _dev(w_down, "w_down"), _dev(y, "y"),
+                                         M, d, f, eps, VARIANTS[variant], _stream_handle(stream)),
+          "ffn_swiglu_block_noalloc")
     return y
 
 
