@@ -9,28 +9,32 @@ bf16, one whole C-ABI call per step, reported as algorithmic GB/s (weights
 The same JSON line also carries:
   roofline      - the dominant kernel (decode gate/up projection) against the
                   8 TB/s HBM peak; its average duration comes from HIP events
-                  that the library records around each of its launches, on the
-                  call's stream, during a second pass over the same timed
-                  steps (the first pass, which gives `value`, is left
-                  uninstrumented); `traffic` is the counter-measured HBM bytes
-                  of that kernel from the committed profile, when the kernel
-                  source is unchanged since the counters were taken;
-  cpu_baseline  - the fp64 oracle on the host (1 BLAS thread) on the same
-                  decode workload (extra also has an all-cores run);
+                  the library binds to each of its kernel dispatches
+                  (hipExtLaunchKernel: the kernel's own begin/end, as a
+                  profiler's kernel trace reports it), recorded on the call's
+                  stream during a second pass over the same timed steps (the
+                  first pass, which gives `value`, is left uninstrumented);
+                  `traffic` is the counter-measured HBM bytes of that kernel
+                  from the committed profile, when the kernel source is
+                  unchanged since the counters were taken;
+  cpu_baseline  - the fp64 oracle on the host (1 thread) on the same decode
+                  workload;
   extra         - the other workloads: prefill block (M=8192, d=4096,
                   f=14336) fused and split gate/up, interleaved call by call,
-                  in TFLOP/s; the standalone RMSNorm (16384 x 4096 bf16);
-                  the Q8_0 and Q4_0 decode blocks (M=8, d=5120, f=17408);
-                  decode at M=1 and 4; measured HBM read-only and copy
-                  ceilings; torch matmul at the prefill shapes as
-                  vendor-library context; one GPU's f/8 share of an 8-way
-                  tensor-parallel block (decode, prefill, Q8, Q4); per-call
-                  p10/median/p90 of the decode call and the GFX clock
-                  sampled during decode and prefill calls (separate passes,
-                  outside the timed region of `value`).
+                  in TFLOP/s against both the 2.5 PFLOP/s spec and an
+                  MFMA-loop peak measured in this run; the standalone RMSNorm
+                  (16384 x 4096 bf16); the Q8_0 and Q4_0 decode blocks (M=8,
+                  d=5120, f=17408); decode at M=1 and 4; measured HBM
+                  read-only and read+write ceilings (swept probes); torch
+                  matmul at the prefill shapes as vendor-library context; one
+                  GPU's f/8 share of an 8-way tensor-parallel block; per-call
+                  p10/median/p90 of the decode call; clocks; and the CPU leg:
+                  the oracle timed on every workload (1 thread and all host
+                  threads; the prefill from sampled rows, extrapolated) with
+                  each workload's error of this run's GPU output against it.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra] [--no-cpu]
-                       [--extras decode_m,persistent,ceilings,rmsnorm,q8,q4,prefill,tp8]
+                       [--extras decode_m,persistent,ceilings,rmsnorm,q8,q4,prefill,tiny,tp8]
        (W untimed calls, continued until at least --min-warmup-s seconds, default 1,
         have passed; then K timed)
        python bench.py --profile-run   (decode steps plus one 512 MiB copy, for
@@ -51,11 +55,13 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+FLOP_PER_CU_CLK = 4096          # dense bf16 MFMA flop per compute unit per clock
 DECODE = dict(seed=3, M=16, d=4096, f=11008)
 PREFILL = dict(seed=4, M=8192, d=4096, f=14336)
 RMS = dict(seed=2, rows=16384, d=4096)
 Q8 = dict(seed=5, M=8, d=5120, f=17408)
 Q4 = dict(seed=6, M=8, d=5120, f=17408)
+TINY = dict(seed=1, M=8, d=256, f=704)
 ROTATE = 4
 COPY_BYTES = 512 << 20
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_gateup_M16_hbm_traffic.txt")
@@ -73,6 +79,16 @@ def to_dev(a, torch):
     return torch.from_numpy(a).to("cuda")
 
 
+def to_host(t):
+    """Device tensor -> stored-format numpy array (bf16 as uint16 bits)."""
+    import numpy as np
+    import torch
+    t = t.detach().to("cpu")
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16).copy()
+    return t.numpy().copy()
+
+
 def decode_bytes(M, d, f):
     """Algorithmic bytes of one decode block call: 3 weight matrices, x, y, g."""
     return 3 * f * d * 2 + 2 * M * d * 2 + d * 2
@@ -81,6 +97,19 @@ def decode_bytes(M, d, f):
 def gateup_bytes(M, d, f):
     """Algorithmic bytes of the fused norm + gate/up kernel: W_gate, W_up, x, g read; h written."""
     return 2 * f * d * 2 + M * d * 2 + d * 2 + M * f * 2
+
+
+def down_bytes(M, d, f):
+    """Algorithmic bytes of the decode down kernel: W_down, h, x read; y written."""
+    return d * f * 2 + M * f * 2 + 2 * M * d * 2
+
+
+def q8_matrix_bytes(N, K):
+    return N * K + N * K // 32 * 2
+
+
+def q4_matrix_bytes(N, K):
+    return N * K // 2 + N * K // 32 * 2
 
 
 def time_calls(torch, fn, n):
@@ -112,7 +141,19 @@ def ratio(a, b):
     return round(a / b, 4) if b else None
 
 
-EXTRAS = ("decode_m", "persistent", "ceilings", "rmsnorm", "q8", "q4", "prefill", "tp8")
+def kernel_times(ffn, fn, n):
+    """{kernel: avg us per launch} over n calls of fn(i), from the events the
+    library binds to each dispatch (a separate, instrumented pass)."""
+    ffn.timing_reset()
+    ffn.timing_enable(True, max_launches=8 * n + 16)
+    for i in range(n):
+        fn(i)
+    kt = ffn.timing_collect()
+    ffn.timing_enable(False)
+    return {k: round(t / c * 1e3, 2) for k, (c, t) in kt.items()}
+
+
+EXTRAS = ("decode_m", "persistent", "ceilings", "rmsnorm", "q8", "q4", "prefill", "tiny", "tp8")
 
 
 def per_call_us(torch, fn, n):
@@ -131,13 +172,16 @@ def per_call_us(torch, fn, n):
 
 
 class ClockSampler:
-    """Samples the GPU's current GFX clock (MHz) from a background thread while
-    work runs; None when the system management library is unavailable.  Used
-    outside the timed region of `value` (the sampler competes for the
-    interpreter lock with the launching thread)."""
+    """Samples the GFX clock (MHz) that the system management library reports,
+    from a background thread while work runs; None when the library is
+    unavailable.  Used outside the timed region of `value` (the sampler
+    competes for the interpreter lock with the launching thread).  The
+    library's figure is the firmware's current setting; the clock the
+    matrix cores actually hold is reported separately, from the MFMA-loop
+    probe's rate."""
 
     def __init__(self, torch):
-        self.h, self.samples, self._stop, self._thr = None, [], False, None
+        self.h, self.samples, self._stop, self._thr, self.smi = None, [], False, None, None
         try:
             import amdsmi
             self.smi = amdsmi
@@ -153,6 +197,17 @@ class ClockSampler:
 
     def _read(self):
         return float(self.smi.amdsmi_get_clock_info(self.h, self.smi.AmdSmiClkType.GFX)["clk"])
+
+    def average_gfxclk(self):
+        """The firmware's running average GFX clock (MHz) from the GPU metrics table, or None."""
+        if self.h is None:
+            return None
+        try:
+            m = self.smi.amdsmi_get_gpu_metrics_info(self.h)
+            v = m.get("average_gfxclk_frequency")
+            return None if v in (None, "N/A", 0xFFFF) else float(v)
+        except Exception:
+            return None
 
     def __enter__(self):
         import threading
@@ -183,7 +238,17 @@ class ClockSampler:
             return None
         t = np.array(self.samples)
         return {"gfx_mhz_median": round(float(np.median(t)), 0), "gfx_mhz_min": round(float(t.min()), 0),
-                "gfx_mhz_max": round(float(t.max()), 0), "samples": int(t.size)}
+                "gfx_mhz_max": round(float(t.max()), 0), "samples": int(t.size),
+                "firmware_average_gfxclk_mhz": self.average_gfxclk(),
+                "source": "system management library (firmware setting)"}
+
+    def close(self):
+        if self.smi is not None:
+            try:
+                self.smi.amdsmi_shut_down()
+            except Exception:
+                pass
+            self.smi, self.h = None, None
 
 
 def sha256(path):
@@ -210,29 +275,79 @@ def read_traffic():
         return None
 
 
-def cpu_baseline(b, target_s=10.0, threads=1):
-    """The oracle as it stands on the decode workload with `threads` BLAS
-    threads (None: the library's default, all host cores), repeated until
-    ~target_s of wall time has been spent (at least once)."""
-    from threadpoolctl import threadpool_info, threadpool_limits
-    from oracle import ffn_oracle as O
-    reps, t0 = 0, time.perf_counter()
-    with threadpool_limits(limits=threads):
-        used = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
-        while True:
-            O.block_from_stored("bf16", b.x, b.g, b.w_gate, b.w_up, b.w_down, b.eps)
-            reps += 1
-            if time.perf_counter() - t0 >= target_s:
-                break
-    dt = (time.perf_counter() - t0) / reps
-    gbs = decode_bytes(b.M, b.d, b.f) / dt / 1e9
-    return {"value": round(gbs, 4), "unit": "GB/s", "cores": int(used), "kind": "oracle",
-            "sample": f"whole decode block M={b.M} d={b.d} f={b.f} (bf16 inputs decoded to fp64), "
-                      f"{reps} call(s), {dt:.2f} s per call"}
+def software_versions(torch):
+    v = {"torch": torch.__version__, "torch_hip": getattr(torch.version, "hip", None)}
+    for path in ("/opt/rocm/.info/version", "/opt/rocm/.info/version-dev"):
+        try:
+            with open(path) as fh:
+                v["rocm"] = fh.read().strip()
+            break
+        except OSError:
+            continue
+    return v
 
 
-def extras(torch, np, ffn, I, sets, x, g, b, ws, extra, clocks, want):
-    best = copy_gbs = None  # ceilings (GB/s), measured when "ceilings" is selected
+# ----------------------------------------------------------------------------
+# GPU measurements
+# ----------------------------------------------------------------------------
+def ceilings(torch, ffn, extra, clocks):
+    """Read-only and read+write HBM ceilings (swept probes) and the MFMA-loop
+    peak at the clock the chip holds under that load."""
+    nbytes = 4 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    sink = torch.empty(16 * ffn.lib().ffn_probe_read_groups(32), dtype=torch.uint8, device="cuda")
+    best, sweep = 0.0, {}
+    for wpc in (4, 8, 12, 16, 32):
+        for _ in range(2):
+            ffn.probe_read(buf, sink, wpc)
+        t = time_calls(torch, lambda i: ffn.probe_read(buf, sink, wpc), 5)
+        sweep[wpc] = round(nbytes / (t * 1e-3) / 1e9, 1)
+        best = max(best, sweep[wpc])
+    half = nbytes // 2
+    src, dst = buf[:half], buf[half:]
+    copy_best, csweep = 0.0, {}
+    for gpc in (0, 2, 4, 8, 16):
+        for nt in (False, True):
+            ffn.probe_copy(src, dst, gpc, nt)
+            tc = time_calls(torch, lambda i: ffn.probe_copy(src, dst, gpc, nt), 5)
+            gbs = 2 * half / (tc * 1e-3) / 1e9
+            key = ("chunked_16KiB" if gpc == 0 else f"stride_{gpc}_per_cu") + ("_nt_stores" if nt else "")
+            csweep[key] = round(gbs, 1)
+            copy_best = max(copy_best, gbs)
+    extra["hbm_read_ceiling_GBps"] = best
+    extra["hbm_read_sweep_waves_per_cu"] = sweep
+    extra["hbm_copy_ceiling_GBps"] = round(copy_best, 1)
+    extra["hbm_copy_sweep"] = csweep
+    log(f"HBM read ceiling {best:.0f} GB/s {sweep}, copy {copy_best:.0f} GB/s {csweep}")
+    del buf, sink, src, dst
+    torch.cuda.empty_cache()
+
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    msink = torch.empty(4 * 256 * ffn.lib().ffn_probe_mfma_groups(32), dtype=torch.uint8, device="cuda")
+    iters = 20000
+    msweep, mbest = {}, 0.0
+    with clocks:
+        for wpc in (8, 16):
+            flop = ffn.probe_mfma(iters, wpc, msink)
+            ffn.probe_mfma(iters, wpc, msink)
+            t = time_calls(torch, lambda i: ffn.probe_mfma(iters, wpc, msink), 5)
+            tf = flop / (t * 1e-3) / 1e12
+            msweep[wpc] = round(tf, 1)
+            mbest = max(mbest, tf)
+    extra["mfma_loop_peak"] = {
+        "TFLOPs": round(mbest, 1), "sweep_waves_per_cu": msweep,
+        "frac_of_spec_peak": round(mbest / BF16_PEAK_TFLOPS, 4),
+        "implied_clock_GHz": round(mbest * 1e12 / (cus * FLOP_PER_CU_CLK) / 1e9, 3),
+        "what": "v_mfma_f32_16x16x32_bf16 chains from registers; clock = rate / (CUs x 4096 flop/clk)",
+        "smi_clock_during": clocks.summary()}
+    log("mfma loop", extra["mfma_loop_peak"])
+    del msink
+    return best, copy_best, mbest
+
+
+def extras(torch, np, ffn, I, sets, x, g, b, ws, extra, clocks, want, keep):
+    best = copy_gbs = mfma_peak = None  # ceilings, measured when "ceilings" is selected
     M, d, f = b.M, b.d, b.f
     if "decode_m" in want:
         # decode at M = 1 and 4 (first rows of the same draw)
@@ -243,11 +358,12 @@ def extras(torch, np, ffn, I, sets, x, g, b, ws, extra, clocks, want):
             def stepm(i, xm=xm, ym=ym):
                 wg, wu, wd = sets[i % ROTATE]
                 ffn.swiglu_block(xm, g, wg, wu, wd, b.eps, "auto", out=ym, workspace=ws)
-            for i in range(20):
-                stepm(i)
+            warm_up(stepm)
             msm = time_calls(torch, stepm, 200)
             extra[f"decode_M{m}"] = {"us": round(msm * 1e3, 2),
                                      "GBps": round(decode_bytes(m, d, f) / (msm * 1e-3) / 1e9, 1)}
+            keep[f"C3 decode M={m}"] = dict(kind="block", inputs=(b, m), gpu=to_host(ym),
+                                            work=decode_bytes(m, d, f), unit="GB/s")
             log(f"decode M={m}: {msm * 1e3:.2f} us/call")
     if "persistent" in want:
         # the single-dispatch (persistent) schedule at M = 16, interleaved with the
@@ -274,34 +390,21 @@ def extras(torch, np, ffn, I, sets, x, g, b, ws, extra, clocks, want):
                                           "persistent_over_two_launch": round(tp / ta, 3)}
         log("persistent schedule", extra["decode_M16_persistent"])
         del wsp, yp
-        sets.clear()
-        torch.cuda.empty_cache()
+    sets.clear()
+    torch.cuda.empty_cache()
 
     if "ceilings" in want:
-        # ------------------------------------------------------------ HBM ceilings
-        nbytes = 4 << 30
-        buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
-        buf.fill_(1)
-        sink = torch.empty(16 * ffn.lib().ffn_probe_read_groups(32), dtype=torch.uint8, device="cuda")
-        best, sweep = 0.0, {}
-        for wpc in (4, 8, 12, 16, 32):
-            for _ in range(2):
-                ffn.probe_read(buf, sink, wpc)
-            t = time_calls(torch, lambda i: ffn.probe_read(buf, sink, wpc), 5)
-            sweep[wpc] = round(nbytes / (t * 1e-3) / 1e9, 1)
-            best = max(best, sweep[wpc])
-        half = nbytes // 2
-        src, dst = buf[:half], buf[half:]
-        ffn.probe_copy(src, dst)
-        tc = time_calls(torch, lambda i: ffn.probe_copy(src, dst), 5)
-        copy_gbs = 2 * half / (tc * 1e-3) / 1e9
-        extra["hbm_read_ceiling_GBps"] = best
-        extra["hbm_read_sweep_waves_per_cu"] = sweep
-        extra["hbm_copy_ceiling_GBps"] = round(copy_gbs, 1)
+        best, copy_gbs, mfma_peak = ceilings(torch, ffn, extra, clocks)
         extra["decode_M16_frac_of_read_ceiling"] = ratio(extra["decode_M16_GBps"], best)
-        log(f"HBM read ceiling {best:.0f} GB/s {sweep}, copy {copy_gbs:.0f} GB/s")
-        del buf, sink, src, dst
-        torch.cuda.empty_cache()
+        for m in (1, 4):
+            if f"decode_M{m}" in extra:
+                extra[f"decode_M{m}"]["frac_of_read_ceiling"] = ratio(extra[f"decode_M{m}"]["GBps"], best)
+        kt = extra["decode_kernels_event_timed"]
+        for name, nbytes in (("decode_gateup", gateup_bytes(M, d, f)), ("decode_down", down_bytes(M, d, f))):
+            if name in kt:
+                gbs = nbytes / (kt[name]["avg_us"] * 1e-6) / 1e9
+                kt[name].update(GBps=round(gbs, 1), frac_of_read_ceiling=ratio(gbs, best),
+                                frac_of_hbm_peak=round(gbs / HBM_PEAK_GBS, 4))
 
     if "rmsnorm" in want:
         # ---------------------------------------------------------------- RMSNorm
@@ -311,87 +414,80 @@ def extras(torch, np, ffn, I, sets, x, g, b, ws, extra, clocks, want):
         xs += [xs[0].clone() for _ in range(ROTATE - 1)]
         ys = [torch.empty_like(xs[0]) for _ in range(ROTATE)]
         gd = to_dev(gr, torch)
-        for i in range(8):
+
+        def rstep(i):
             ffn.rmsnorm(xs[i % ROTATE], gd, eps, out=ys[i % ROTATE])
-        tr = time_calls(torch, lambda i: ffn.rmsnorm(xs[i % ROTATE], gd, eps, out=ys[i % ROTATE]), 40)
+        warm_up(rstep)
+        tr = time_calls(torch, rstep, 40)
         rbytes = 2 * RMS["rows"] * RMS["d"] * 2 + RMS["d"] * 2
         rgbs = rbytes / (tr * 1e-3) / 1e9
         extra["rmsnorm"] = {"us": round(tr * 1e3, 2), "GBps": round(rgbs, 1),
                             "frac_of_hbm_peak": round(rgbs / HBM_PEAK_GBS, 4),
                             "frac_of_read_ceiling": ratio(rgbs, best),
                             "frac_of_copy_ceiling": ratio(rgbs, copy_gbs)}
+        keep["C2 rmsnorm 16384x4096"] = dict(kind="rmsnorm", inputs=(xr, gr, eps), gpu=to_host(ys[0]),
+                                             work=rbytes, unit="GB/s")
         log("rmsnorm", extra["rmsnorm"])
         del xs, ys
         torch.cuda.empty_cache()
 
-    if "q8" in want:
-        # ------------------------------------------------------------------- Q8_0
-        log("generating q8 inputs", Q8)
-        q = I.make_q8_block(Q8["seed"], Q8["M"], Q8["d"], Q8["f"])
-        qx, qg = to_dev(q.x, torch), to_dev(q.g, torch)
+    def qdev(m):
+        return (torch.from_numpy(m.qs).to("cuda"), torch.from_numpy(m.scales.view(np.int16)).to("cuda"))
 
-        def qdev(m):
-            return (torch.from_numpy(m.qs).to("cuda"), torch.from_numpy(m.scales.view(np.int16)).to("cuda"))
+    for kind, cfg, make, mbytes in (("q8", Q8, I.make_q8_block, q8_matrix_bytes),
+                                    ("q4", Q4, I.make_q4_block, q4_matrix_bytes)):
+        if kind not in want:
+            continue
+        log(f"generating {kind} inputs", cfg)
+        Mq, dq, fq = cfg["M"], cfg["d"], cfg["f"]
+        q = make(cfg["seed"], Mq, dq, fq)
+        qx, qg = to_dev(q.x, torch), to_dev(q.g, torch)
         q0 = [qdev(m) for m in (q.w_gate, q.w_up, q.w_down)]
         qsets = [q0] + [[(a.clone(), s.clone()) for a, s in q0] for _ in range(ROTATE - 1)]
-        qws = ffn.alloc_workspace(ffn.lib().ffn_swiglu_block_q8_workspace_size(Q8["M"], Q8["d"], Q8["f"]))
+        qws = ffn.alloc_workspace(getattr(ffn.lib(), f"ffn_swiglu_block_{kind}_workspace_size")(Mq, dq, fq))
         qy = torch.empty_like(qx)
-
         # calls marshalled once per weight set: the per-call Python work of
         # building the weight structs is comparable to the block's GPU time
-        qcalls = [ffn.prepare_swiglu_block_quant("q8", qx, qg, *st, q.eps, qy, qws) for st in qsets]
+        qcalls = [ffn.prepare_swiglu_block_quant(kind, qx, qg, *st, q.eps, qy, qws) for st in qsets]
 
-        def qstep(i):
+        def qstep(i, qcalls=qcalls):
             qcalls[i % ROTATE]()
         warm_up(qstep)
         tq = time_calls(torch, qstep, 200)
-        qbytes = 3 * (Q8["f"] * Q8["d"] + Q8["f"] * Q8["d"] // 32 * 2) + 2 * Q8["M"] * Q8["d"] * 2 + Q8["d"] * 2
+        kq = kernel_times(ffn, qstep, 40)
+        mat = mbytes(fq, dq)
+        qbytes = 3 * mat + 2 * Mq * dq * 2 + dq * 2
         qgbs = qbytes / (tq * 1e-3) / 1e9
-        extra["q8_decode"] = {"us": round(tq * 1e3, 2), "GBps": round(qgbs, 1),
-                              "frac_of_read_ceiling": ratio(qgbs, best)}
-        log("q8", extra["q8_decode"])
+        res = {"us": round(tq * 1e3, 2), "GBps": round(qgbs, 1), "frac_of_read_ceiling": ratio(qgbs, best),
+               "kernels_us_event_timed": kq}
+        gu, dn = kq.get(f"{kind}_gateup"), kq.get(f"{kind}_down")
+        if gu:
+            gub = 2 * mat + Mq * dq * 2 + Mq * fq * 2
+            res["gateup_kernel_GBps"] = round(gub / (gu * 1e-6) / 1e9, 1)
+        if dn:
+            dnb = mat + Mq * fq * 2 + 2 * Mq * dq * 2
+            res["down_kernel_GBps"] = round(dnb / (dn * 1e-6) / 1e9, 1)
+        extra[f"{kind}_decode"] = res
+        keep[f"{'C5 ' if kind == 'q8' else ''}{kind} decode M={Mq}"] = dict(
+            kind=kind, inputs=q, gpu=to_host(qy), work=qbytes, unit="GB/s")
+        log(kind, res)
         del qcalls, qsets, q0
         torch.cuda.empty_cache()
 
-    if "q4" in want:
-        # ------------------------------------------------------------------- Q4_0
-        log("generating q4 inputs", Q4)
-        q4 = I.make_q4_block(Q4["seed"], Q4["M"], Q4["d"], Q4["f"])
-        q4x, q4g = to_dev(q4.x, torch), to_dev(q4.g, torch)
-        q40 = [qdev(m) for m in (q4.w_gate, q4.w_up, q4.w_down)]
-        q4sets = [q40] + [[(a.clone(), s.clone()) for a, s in q40] for _ in range(ROTATE - 1)]
-        q4ws = ffn.alloc_workspace(ffn.lib().ffn_swiglu_block_q4_workspace_size(Q4["M"], Q4["d"], Q4["f"]))
-        q4y = torch.empty_like(q4x)
-
-        q4calls = [ffn.prepare_swiglu_block_quant("q4", q4x, q4g, *st, q4.eps, q4y, q4ws) for st in q4sets]
-
-        def q4step(i):
-            q4calls[i % ROTATE]()
-        warm_up(q4step)
-        t4 = time_calls(torch, q4step, 200)
-        ffn.timing_reset()
-        ffn.timing_enable(True, 256)
-        for i in range(40):
-            q4step(i)
-        k4 = ffn.timing_collect()
-        ffn.timing_enable(False)
-        fd = Q4["f"] * Q4["d"]
-        q4_mat = fd // 2 + fd // 32 * 2          # nibbles + fp16 scales of one matrix
-        q4bytes = 3 * q4_mat + 2 * Q4["M"] * Q4["d"] * 2 + Q4["d"] * 2
-        q4gbs = q4bytes / (t4 * 1e-3) / 1e9
-        gu4 = k4["q4_gateup"][1] / k4["q4_gateup"][0] * 1e3     # us per launch
-        dn4 = k4["q4_down"][1] / k4["q4_down"][0] * 1e3
-        gu4_bytes = 2 * q4_mat + Q4["M"] * Q4["d"] * 2 + Q4["M"] * Q4["f"] * 2
-        dn4_bytes = q4_mat + Q4["M"] * Q4["f"] * 2 + 2 * Q4["M"] * Q4["d"] * 2
-        extra["q4_decode"] = {"us": round(t4 * 1e3, 2), "GBps": round(q4gbs, 1),
-                              "frac_of_read_ceiling": ratio(q4gbs, best),
-                              "gateup_kernel_us": round(gu4, 2),
-                              "gateup_kernel_GBps": round(gu4_bytes / (gu4 * 1e-6) / 1e9, 1),
-                              "down_kernel_us": round(dn4, 2),
-                              "down_kernel_GBps": round(dn4_bytes / (dn4 * 1e-6) / 1e9, 1)}
-        log("q4", extra["q4_decode"])
-        del q4calls, q4sets, q40
-        torch.cuda.empty_cache()
+    if "tiny" in want:
+        # ------------------------------------------------------- tiny fp32 block
+        tb = I.make_block(TINY["seed"], TINY["M"], TINY["d"], TINY["f"], "f32")
+        tdev = [to_dev(a, torch) for a in (tb.x, tb.g, tb.w_gate, tb.w_up, tb.w_down)]
+        ty = torch.empty_like(tdev[0])
+        tws = ffn.alloc_workspace(ffn.workspace_size(ffn.FFN_F32, TINY["M"], TINY["d"], TINY["f"], "auto"))
+        for i in range(20):
+            ffn.swiglu_block(*tdev, tb.eps, "auto", out=ty, workspace=tws)
+        tt = time_calls(torch, lambda i: ffn.swiglu_block(*tdev, tb.eps, "auto", out=ty, workspace=tws), 200)
+        tflop = 6 * TINY["M"] * TINY["d"] * TINY["f"]
+        extra["tiny_f32"] = {"us": round(tt * 1e3, 2), "GFLOPs": round(tflop / (tt * 1e-3) / 1e9, 2),
+                             "note": "launch-bound; parity case, no roofline bar"}
+        keep["C1 tiny f32 M=8"] = dict(kind="block", inputs=(tb, TINY["M"]), gpu=to_host(ty), work=tflop,
+                                       unit="GFLOP/s")
 
     if "prefill" in want:
         # ---------------------------------------------------------------- prefill
@@ -416,29 +512,41 @@ def extras(torch, np, ffn, I, sets, x, g, b, ws, extra, clocks, want):
             tf.append(time_calls(torch, lambda j: pstep(i, "fused"), 1))
             ts.append(time_calls(torch, lambda j: pstep(i, "split"), 1))
         mf = float(np.median(tf))
-        with clocks:  # the clock under MFMA load, in a separate ~0.3 s pass of the same calls
+        with clocks:  # the firmware clock under MFMA load, in a separate ~0.3 s pass of the same calls
             for i in range(max(1, int(0.3 / (mf * 1e-3)))):
                 pstep(i, "fused")
             torch.cuda.synchronize()
         extra["gpu_clock_during_prefill_calls"] = clocks.summary()
-        ffn.timing_reset()
-        ffn.timing_enable(True, 256)
-        for i in range(4):
-            pstep(i, "fused")
-            pstep(i, "split")
-        kp = ffn.timing_collect()
-        ffn.timing_enable(False)
+        kp_f = kernel_times(ffn, lambda i: pstep(i, "fused"), 4)
+        kp_s = kernel_times(ffn, lambda i: pstep(i, "split"), 4)
         mf, msp = float(np.median(tf)), float(np.median(ts))
+        tff = flops / (mf * 1e-3) / 1e12
         extra["prefill"] = {
             "fused_ms": round(mf, 3), "split_ms": round(msp, 3),
-            "fused_TFLOPs": round(flops / (mf * 1e-3) / 1e12, 1),
+            "fused_p10_p90_ms": [round(float(np.percentile(tf, 10)), 3), round(float(np.percentile(tf, 90)), 3)],
+            "fused_TFLOPs": round(tff, 1),
             "split_TFLOPs": round(flops / (msp * 1e-3) / 1e12, 1),
-            "fused_frac_of_bf16_peak": round(flops / (mf * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "fused_frac_of_bf16_peak": round(tff / BF16_PEAK_TFLOPS, 4),
+            "fused_frac_of_mfma_loop_peak": ratio(tff, mfma_peak),
             "split_over_fused_time": round(msp / mf, 3),
-            "kernels_avg_ms_event_timed": {k: round(t / n, 4) for k, (n, t) in kp.items()}}
-        gu_ms = kp["gemm_gateup_fused"][1] / kp["gemm_gateup_fused"][0]
-        extra["prefill"]["gateup_fused_kernel_TFLOPs"] = round(4.0 * Mp * dp * fp / (gu_ms * 1e-3) / 1e12, 1)
+            "fused_kernels_us_event_timed": kp_f, "split_kernels_us_event_timed": kp_s}
+        gu_us = kp_f.get("gemm_gateup_fused")
+        dn_us = kp_f.get("gemm_down_residual")
+        if gu_us:
+            t = 4.0 * Mp * dp * fp / (gu_us * 1e-6) / 1e12
+            extra["prefill"]["gateup_fused_kernel_TFLOPs"] = round(t, 1)
+            extra["prefill"]["gateup_fused_kernel_frac_of_mfma_loop_peak"] = ratio(t, mfma_peak)
+        if dn_us:
+            t = 2.0 * Mp * dp * fp / (dn_us * 1e-6) / 1e12
+            extra["prefill"]["down_kernel_TFLOPs"] = round(t, 1)
+            extra["prefill"]["down_kernel_frac_of_mfma_loop_peak"] = ratio(t, mfma_peak)
         log("prefill", extra["prefill"])
+        pstep(0, "fused")
+        yf = to_host(py)
+        pstep(0, "split")
+        ysp = to_host(py)
+        keep["C4 prefill fused"] = dict(kind="prefill", inputs=bp, gpu=yf, work=flops, unit="TFLOP/s")
+        keep["C4 prefill split"] = dict(kind="prefill", inputs=bp, gpu=ysp, work=flops, unit="TFLOP/s")
 
         # vendor-library context at the same shapes (torch matmul -> hipBLASLt)
         wgu = torch.cat([pw[0][0], pw[0][1]], 0)
@@ -480,8 +588,7 @@ def tp8_shards(torch, np, ffn, I, extra, read_ceiling):
     def dstep(i):
         wg, wu, wd = sets[i % nrot]
         ffn.swiglu_block(x, g, wg, wu, wd, bb.eps, "auto", out=y, workspace=ws)
-    for i in range(50):
-        dstep(i)
+    warm_up(dstep, 50)
     t = time_calls(torch, dstep, 500)
     gbs = decode_bytes(M, d, f) / (t * 1e-3) / 1e9
     out["decode_M16_f1376"] = {"us": round(t * 1e3, 2), "GBps": round(gbs, 1),
@@ -505,53 +612,130 @@ def tp8_shards(torch, np, ffn, I, extra, read_ceiling):
     del w, x, y, ws
     torch.cuda.empty_cache()
 
-    wl = I.WORKLOADS["q8_tp8_shard"]
-    M, d, f = wl["M"], wl["d"], wl["f"]
-    q = I.make_q8_block(wl["seed"], M, d, f)
-    qx, qg = to_dev(q.x, torch), to_dev(q.g, torch)
-    q0 = [(torch.from_numpy(m.qs).to("cuda"), torch.from_numpy(m.scales.view(np.int16)).to("cuda"))
-          for m in (q.w_gate, q.w_up, q.w_down)]
-    qsets = [q0] + [[(a.clone(), s.clone()) for a, s in q0] for _ in range(nrot - 1)]
-    qws = ffn.alloc_workspace(ffn.lib().ffn_swiglu_block_q8_workspace_size(M, d, f))
-    qy = torch.empty_like(qx)
+    for kind, mbytes in (("q8", q8_matrix_bytes), ("q4", q4_matrix_bytes)):
+        wl = I.WORKLOADS[f"{kind}_tp8_shard"]
+        M, d, f = wl["M"], wl["d"], wl["f"]
+        q = (I.make_q8_block if kind == "q8" else I.make_q4_block)(wl["seed"], M, d, f)
+        qx, qg = to_dev(q.x, torch), to_dev(q.g, torch)
+        q0 = [(torch.from_numpy(m.qs).to("cuda"), torch.from_numpy(m.scales.view(np.int16)).to("cuda"))
+              for m in (q.w_gate, q.w_up, q.w_down)]
+        n = nrot if kind == "q8" else 2 * nrot
+        qsets = [q0] + [[(a.clone(), s.clone()) for a, s in q0] for _ in range(n - 1)]
+        qws = ffn.alloc_workspace(getattr(ffn.lib(), f"ffn_swiglu_block_{kind}_workspace_size")(M, d, f))
+        qy = torch.empty_like(qx)
+        qcalls = [ffn.prepare_swiglu_block_quant(kind, qx, qg, *st, q.eps, qy, qws) for st in qsets]
 
-    qcalls = [ffn.prepare_swiglu_block_quant("q8", qx, qg, *st, q.eps, qy, qws) for st in qsets]
-
-    def qstep(i):
-        qcalls[i % nrot]()
-    warm_up(qstep, 50)
-    tq = time_calls(torch, qstep, 500)
-    qbytes = 3 * (f * d + f * d // 32 * 2) + 2 * M * d * 2 + d * 2
-    qgbs = qbytes / (tq * 1e-3) / 1e9
-    out["q8_M8_f2176"] = {"us": round(tq * 1e3, 2), "GBps": round(qgbs, 1),
-                          "frac_of_read_ceiling": ratio(qgbs, read_ceiling)}
-    del qcalls, qsets, q0
-    torch.cuda.empty_cache()
-
-    wl = I.WORKLOADS["q4_tp8_shard"]
-    M, d, f = wl["M"], wl["d"], wl["f"]
-    q4 = I.make_q4_block(wl["seed"], M, d, f)
-    qx, qg = to_dev(q4.x, torch), to_dev(q4.g, torch)
-    q0 = [(torch.from_numpy(m.qs).to("cuda"), torch.from_numpy(m.scales.view(np.int16)).to("cuda"))
-          for m in (q4.w_gate, q4.w_up, q4.w_down)]
-    qsets = [q0] + [[(a.clone(), s.clone()) for a, s in q0] for _ in range(2 * nrot - 1)]
-    qws = ffn.alloc_workspace(ffn.lib().ffn_swiglu_block_q4_workspace_size(M, d, f))
-    qy = torch.empty_like(qx)
-
-    q4calls = [ffn.prepare_swiglu_block_quant("q4", qx, qg, *st, q4.eps, qy, qws) for st in qsets]
-
-    def q4step(i):
-        q4calls[i % (2 * nrot)]()
-    warm_up(q4step, 50)
-    tq = time_calls(torch, q4step, 500)
-    qbytes = 3 * (f * d // 2 + f * d // 32 * 2) + 2 * M * d * 2 + d * 2
-    qgbs = qbytes / (tq * 1e-3) / 1e9
-    out["q4_M8_f2176"] = {"us": round(tq * 1e3, 2), "GBps": round(qgbs, 1),
-                          "frac_of_read_ceiling": ratio(qgbs, read_ceiling)}
-    del q4calls, qsets, q0
-    torch.cuda.empty_cache()
+        def qstep(i, qcalls=qcalls, n=n):
+            qcalls[i % n]()
+        warm_up(qstep, 50)
+        tq = time_calls(torch, qstep, 500)
+        qbytes = 3 * mbytes(f, d) + 2 * M * d * 2 + d * 2
+        qgbs = qbytes / (tq * 1e-3) / 1e9
+        out[f"{kind}_M8_f2176"] = {"us": round(tq * 1e3, 2), "GBps": round(qgbs, 1),
+                                   "frac_of_read_ceiling": ratio(qgbs, read_ceiling)}
+        del qcalls, qsets, q0
+        torch.cuda.empty_cache()
     extra["tp8_shard"] = out
     log("tp8 shard", out)
+
+
+# ----------------------------------------------------------------------------
+# CPU leg: the oracle as it stands, timed, and each workload's error
+# ----------------------------------------------------------------------------
+def cpu_oracle_leg(keep, budget_s=60.0):
+    """Time the fp64 oracle on every kept workload, with 1 thread and with the
+    BLAS library's default (all host threads), and compare this run's GPU
+    output with the oracle's.  The prefill block is timed on two sampled row
+    counts (rows are independent) and extrapolated linearly to all rows; its
+    error is taken over the larger sample.  Returns (per-workload timings,
+    per-workload errors)."""
+    import numpy as np
+    from threadpoolctl import threadpool_info, threadpool_limits
+    from oracle import ffn_oracle as O
+
+    def blas_threads():
+        return max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+
+    def run(entry, rows=None):
+        k, inp = entry["kind"], entry["inputs"]
+        if k == "block":
+            blk, m = inp
+            return O.block_from_stored(blk.dtype, blk.x[:m], blk.g, blk.w_gate, blk.w_up, blk.w_down, blk.eps)
+        if k == "rmsnorm":
+            xr, gr, eps = inp
+            return O.rmsnorm_from_stored("bf16", xr, gr, eps)
+        if k == "prefill":
+            return O.block_from_stored("bf16", inp.x[rows], inp.g, inp.w_gate, inp.w_up, inp.w_down, inp.eps)
+        fn = O.swiglu_block_q8 if k == "q8" else O.swiglu_block_q4
+        return fn(inp.x, inp.g, (inp.w_gate.qs, inp.w_gate.scales), (inp.w_up.qs, inp.w_up.scales),
+                  (inp.w_down.qs, inp.w_down.scales), inp.eps)
+
+    def timed(entry, threads, rows=None, min_s=0.5):
+        with threadpool_limits(limits=threads):
+            used = blas_threads()
+            reps, t0 = 0, time.perf_counter()
+            while True:
+                r = run(entry, rows)
+                reps += 1
+                if time.perf_counter() - t0 >= min_s:
+                    break
+        return (time.perf_counter() - t0) / reps, used, r, reps
+
+    def decode(a):
+        return O.as_f64(a, "bf16" if a.dtype == np.uint16 else "f32")
+
+    t_start = time.perf_counter()
+    timings, errors = {}, {}
+    prefill_rows = None
+    for name, e in keep.items():
+        if time.perf_counter() - t_start > budget_s:
+            timings[name] = {"skipped": f"CPU leg budget of {budget_s:.0f} s spent"}
+            continue
+        if e["kind"] == "prefill":
+            bp = e["inputs"]
+            if prefill_rows is None:
+                rng = np.random.default_rng(44)
+                prefill_rows = np.sort(np.concatenate(
+                    [[0, bp.M - 1], rng.choice(np.arange(1, bp.M - 1), 62, replace=False)]))
+            small = prefill_rows[::2]
+            row = {}
+            ref = None
+            for label, thr in (("1_thread", 1), ("all_threads", None)):
+                ts, used, _, _ = timed(e, thr, small, min_s=0.0)
+                tl, used, r, _ = timed(e, thr, prefill_rows, min_s=0.0)
+                ref = r
+                per_row = max((tl - ts) / (prefill_rows.size - small.size), 1e-9)
+                full = ts + per_row * (bp.M - small.size)
+                row[label] = {"value": round(e["work"] / full / 1e12, 6), "unit": e["unit"], "threads": used,
+                              "sample": f"{small.size} and {prefill_rows.size} sampled rows "
+                                        f"({ts:.2f} / {tl:.2f} s), extrapolated linearly to {bp.M} rows "
+                                        f"({full:.1f} s)"}
+            timings[name] = row
+            a = decode(e["gpu"])[prefill_rows]
+        else:
+            row = {}
+            ref = None
+            threads = (("1_thread", 1),) if e["kind"] == "rmsnorm" else (("1_thread", 1), ("all_threads", None))
+            for label, thr in threads:
+                t, used, r, reps = timed(e, thr)
+                ref = r
+                scale = 1e12 if e["unit"] == "TFLOP/s" else 1e9
+                row[label] = {"value": round(e["work"] / t / scale, 4), "unit": e["unit"], "threads": used,
+                              "sample": f"whole workload, {reps} call(s), {t:.3f} s per call"}
+            if e["kind"] == "rmsnorm":
+                row["note"] = "the oracle's norm is numpy elementwise work: one thread whatever BLAS has"
+            timings[name] = row
+            a = decode(e["gpu"])
+        dlt = np.abs(a - ref)
+        den = float(np.max(np.abs(ref))) or 1.0
+        err = {"max_norm": float(dlt.max()) / den,
+               "rel_l2": float(np.linalg.norm(a - ref) / max(np.linalg.norm(ref), 1e-300))}
+        if e["kind"] == "rmsnorm":
+            nz = ref != 0
+            err["elementwise_rel"] = float(np.max(dlt[nz] / np.abs(ref[nz])))
+        errors[name] = {k: float(f"{v:.4g}") for k, v in err.items()}
+        log("oracle", name, timings[name], errors[name])
+    return timings, errors
 
 
 def main() -> int:
@@ -560,7 +744,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-extra", action="store_true", help="skip the secondary workloads")
-    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--extras", default="all",
                     help="comma-separated subset of the secondary workloads: " + ",".join(EXTRAS))
     ap.add_argument("--min-warmup-s", type=float, default=1.0,
@@ -620,11 +804,13 @@ def main() -> int:
         half = COPY_BYTES
         buf = torch.empty(2 * half, dtype=torch.uint8, device="cuda")
         buf.fill_(1)
-        ffn.probe_copy(buf[:half], buf[half:])
+        ffn.probe_copy(buf[:half], buf[half:], 8, False)
         torch.cuda.synchronize()
         return 0
 
-    # per-kernel durations: the same steps again, each launch bracketed by events
+    keep = {"C3 decode M=16": dict(kind="block", inputs=(b, M), gpu=to_host(y), work=decode_bytes(M, d, f),
+                                   unit="GB/s")}
+    # per-kernel durations: the same steps again, each dispatch carrying its own event pair
     ffn.timing_reset()
     ffn.timing_enable(True, max_launches=4 * args.steps + 16)
     ms_instr = time_calls(torch, step, args.steps)
@@ -636,13 +822,15 @@ def main() -> int:
     roofline = {"bound": "hbm", "kernel": "decode_gateup (fused RMSNorm + gate/up + SwiGLU)",
                 "achieved": round(gu_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": read_traffic(),
-                "avg_launch_us": round(gu_us, 2), "bytes_per_launch": gateup_bytes(M, d, f)}
+                "avg_launch_us": round(gu_us, 2), "launches": n_gu, "bytes_per_launch": gateup_bytes(M, d, f),
+                "duration_source": "HIP events bound to each dispatch (hipExtLaunchKernel), "
+                                   "second pass over the timed steps"}
     kernels = {k: {"launches": n, "avg_us": round(t / n * 1e3, 2)} for k, (n, t) in kt.items()}
     log(f"kernels {kernels}; instrumented pass {ms_instr * 1e3:.2f} us/call")
 
     pct = per_call_us(torch, step, args.steps)
-    # the clock under this load, over ~0.3 s of the same calls (the driver's
-    # clock readout refreshes every few ms; a shorter window reads idle)
+    # the firmware clock under this load, over ~0.3 s of the same calls (the
+    # management library's readout refreshes every few ms; a shorter window reads idle)
     clocks = ClockSampler(torch)
     with clocks:
         for i in range(max(1, int(0.3 / (ms * 1e-3)))):
@@ -654,17 +842,22 @@ def main() -> int:
              "decode_kernels_event_timed": kernels,
              "decode_M16_instrumented_us": round(ms_instr * 1e3, 2),
              "decode_M16_call_us_percentiles": pct,
-             "gpu_clock_during_decode_calls": clocks.summary()}
+             "gpu_clock_during_decode_calls": clocks.summary(),
+             "software": software_versions(torch)}
     if not args.no_extra:
-        extras(torch, np, ffn, I, sets, x, g, b, ws, extra, clocks, want)
+        extras(torch, np, ffn, I, sets, x, g, b, ws, extra, clocks, want, keep)
+    clocks.close()
 
     cpu = None
     if not args.no_cpu:
-        log("timing the CPU oracle on the decode workload")
-        cpu = cpu_baseline(b)
-        log("cpu", cpu)
-        extra["cpu_oracle_all_cores"] = cpu_baseline(b, target_s=5.0, threads=None)
-        log("cpu (all cores)", extra["cpu_oracle_all_cores"])
+        log("CPU leg: the oracle on every workload")
+        timings, errors = cpu_oracle_leg(keep)
+        extra["cpu_oracle"] = timings
+        extra["parity_vs_oracle_this_run"] = errors
+        c3 = timings.get("C3 decode M=16", {}).get("1_thread")
+        if c3:
+            cpu = {"value": c3["value"], "unit": "GB/s", "cores": c3["threads"], "kind": "oracle",
+                   "sample": f"decode block M={M} d={d} f={f} (bf16 inputs decoded to fp64): {c3['sample']}"}
 
     line = {
         "metric": "FFN block: decode GB/s & prefill TFLOP/s on 1 GPU, % of HBM/MFMA peak",

@@ -262,19 +262,37 @@ ffn_status ffn_probe_read(const void *src, size_t bytes, void *sink, int waves_p
                           void *stream);
 int ffn_probe_read_groups(int waves_per_cu);
 
-/* Copies `bytes` (multiple of 16) from src to dst with 16-byte loads/stores. */
-ffn_status ffn_probe_copy(const void *src, void *dst, size_t bytes, void *stream);
+/* Copies `bytes` (multiple of 16) from src to dst with 16-byte streaming
+ * loads and 16-byte stores (streaming stores if `nontemporal`).
+ * groups_per_cu 1..64: a grid-stride loop over that many 256-thread
+ * workgroups per CU; 0: one workgroup per contiguous 16 KiB chunk (the
+ * pattern of a row-per-wave elementwise kernel).  Sweep both: the best is
+ * the read+write ceiling. */
+ffn_status ffn_probe_copy(const void *src, void *dst, size_t bytes, int groups_per_cu,
+                          int nontemporal, void *stream);
+
+/* The dense bf16 matrix-core ceiling at the clock the chip holds under that
+ * load: ffn_probe_mfma_groups(waves_per_cu) workgroups of 4 waves, each wave
+ * issuing 8 * iters independent v_mfma_f32_16x16x32_bf16 (16384 flop each)
+ * from registers.  sink: >= 4 * 256 * groups bytes, written only in the
+ * practically impossible case that the result equals a fixed value.
+ * Returns INVALID_ARGUMENT for iters < 1 or waves_per_cu outside 1..32. */
+ffn_status ffn_probe_mfma(int iters, int waves_per_cu, void *sink, void *stream);
+int ffn_probe_mfma_groups(int waves_per_cu);
 
 /* ---- per-kernel timing ----------------------------------------------------
- * When enabled, every kernel the library launches FROM THE CALLING THREAD is
- * bracketed by a pair of HIP events recorded on the same stream;
- * ffn_timing_collect() waits for them and accumulates per-kernel totals.
- * The state (switch, events, totals) is the calling thread's own: timing
- * enabled on one thread neither records nor changes anything on another,
- * so the library stays reentrant.  Off by default; costs two event records
- * per launch when on (events are created at a thread's first timed launch
- * and destroyed when that thread disables timing).  At most max_launches
- * launches are recorded between two collects; later ones run untimed. */
+ * When enabled, every kernel the library enqueues FROM THE CALLING THREAD
+ * gets a pair of HIP events bound to the dispatch itself
+ * (hipExtLaunchKernel), so a duration is the kernel's own begin-to-end
+ * time, as a profiler's kernel trace reports it; ffn_timing_collect()
+ * waits for them and accumulates per-kernel totals under the launch site's
+ * name ("decode_gateup", "q8_down", ...; a site's second and later kernels
+ * are "<name>/2", "<name>/3").  The state (switch, events, totals) is the
+ * calling thread's own: timing enabled on one thread neither records nor
+ * changes anything on another, so the library stays reentrant.  Off by
+ * default.  Events are created at a thread's first timed dispatch and
+ * destroyed when that thread disables timing.  At most max_launches
+ * dispatches are timed between two collects; later ones run untimed. */
 ffn_status ffn_timing_enable(int on, int max_launches);
 int ffn_timing_enabled(void);            /* 1 if on for the calling thread  */
 ffn_status ffn_timing_collect(void);     /* synchronises the recorded events */

@@ -274,7 +274,14 @@ def test_probe_and_timing_validation(L):
     INV = ffn.FFN_ERR_INVALID_ARGUMENT
     assert L.ffn_probe_read(A, 15, B, 4, None) == INV
     assert L.ffn_probe_read(A, 1 << 20, B, 0, None) == INV
-    assert L.ffn_probe_copy(A, A + 16, 64, None) == INV
+    assert L.ffn_probe_copy(A, A + 16, 64, 0, 0, None) == INV     # overlap
+    assert L.ffn_probe_copy(A, B, 64, 65, 0, None) == INV         # groups per CU 0..64
+    assert L.ffn_probe_copy(A, B, 24, 0, 0, None) == INV          # multiple of 16
+    assert L.ffn_probe_copy(A, B, 0, 0, 1, None) == ffn.FFN_OK    # nothing to copy
+    assert L.ffn_probe_mfma(0, 8, A, None) == INV
+    assert L.ffn_probe_mfma(10, 33, A, None) == INV
+    assert L.ffn_probe_mfma(10, 8, 0, None) == INV
+    assert L.ffn_probe_mfma_groups(0) == 0
     assert L.ffn_timing_enable(1, 0) == INV
     assert L.ffn_timing_enable(0, 0) == ffn.FFN_OK
     assert L.ffn_timing_count() == 0

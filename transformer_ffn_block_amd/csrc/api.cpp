@@ -36,18 +36,23 @@ ffn_status ok() {
 }
 
 // ---- per-kernel timing ---------------------------------------------------
-// Timing state belongs to the calling thread: only launches issued by the
-// thread that enabled timing are bracketed, and the totals are that
-// thread's.  Events are created on first use (so enabling touches no device)
-// and destroyed when the thread disables timing.  No HIP call is made from
-// a thread-exit destructor: a thread that ends with timing still enabled
+// Timing state belongs to the calling thread: only kernels enqueued by the
+// thread that enabled timing are timed, and the totals are that thread's.
+// Each dispatch gets its own event pair, bound to the kernel by
+// hipExtLaunchKernel (ffn::dispatch_events); a launcher's first kernel is
+// named after the launch site, its later ones "<name>/2", "<name>/3".
+// Events are created on first use (so enabling touches no device) and
+// destroyed when the thread disables timing.  No HIP call is made from a
+// thread-exit destructor: a thread that ends with timing still enabled
 // leaks its events.
 struct Timing {
   bool on = false;
   int cap = 0;
   int used = 0;
-  std::vector<hipEvent_t> ev;  // 2 per launch slot, created on demand
-  std::vector<const char*> name;
+  const char* site = nullptr;  // launch site being issued (set by timed())
+  int sub = 0;                 // dispatches issued so far by that site
+  std::vector<hipEvent_t> ev;  // 2 per dispatch slot, created on demand
+  std::vector<std::string> name;
   std::map<std::string, std::pair<int64_t, double>> total;
   std::vector<std::string> order;
 };
@@ -55,25 +60,14 @@ thread_local Timing t_timing;
 
 template <class F>
 hipError_t timed(const char* name, hipStream_t s, F&& f) {
+  (void)s;
   Timing& T = t_timing;
-  if (!T.on || T.used >= T.cap) return f();
-  const int i = T.used;
-  for (int k = 2 * i; k < 2 * i + 2; ++k) {
-    if (!T.ev[k]) {
-      const hipError_t e = hipEventCreate(&T.ev[k]);
-      if (e != hipSuccess) {
-        T.ev[k] = nullptr;
-        return e;
-      }
-    }
-  }
-  hipError_t e = hipEventRecord(T.ev[2 * i], s);
-  if (e != hipSuccess) return e;
-  e = f();
-  if (e != hipSuccess) return e;
-  T.name[i] = name;
-  T.used = i + 1;
-  return hipEventRecord(T.ev[2 * i + 1], s);
+  if (!T.on) return f();
+  T.site = name;
+  T.sub = 0;
+  const hipError_t e = f();
+  T.site = nullptr;
+  return e;
 }
 
 void release_events() {
@@ -529,14 +523,33 @@ ffn_status ffn_probe_read(const void* src, size_t bytes, void* sink, int waves_p
   return ok();
 }
 
-ffn_status ffn_probe_copy(const void* src, void* dst, size_t bytes, void* stream) {
+ffn_status ffn_probe_copy(const void* src, void* dst, size_t bytes, int groups_per_cu,
+                          int nontemporal, void* stream) {
   if (!src || !dst) return fail(FFN_ERR_INVALID_ARGUMENT, "null pointer");
   if (bytes % 16) return fail(FFN_ERR_INVALID_ARGUMENT, "bytes must be a multiple of 16");
+  if (groups_per_cu < 0 || groups_per_cu > 64)
+    return fail(FFN_ERR_INVALID_ARGUMENT, "groups_per_cu must be 0..64");
   if (!aligned(src, 16) || !aligned(dst, 16)) return fail(FFN_ERR_UNSUPPORTED, "alignment");
   if (overlap(src, bytes, dst, bytes)) return fail(FFN_ERR_INVALID_ARGUMENT, "overlap");
+  if (bytes / 16 / 1024 > 0x7FFFFFFFull) return fail(FFN_ERR_UNSUPPORTED, "too large");
   if (bytes == 0) return ok();
   hipStream_t s = (hipStream_t)stream;
-  FFN_LAUNCH("probe_copy", s, ffn::launch_probe_copy(src, dst, bytes, s));
+  FFN_LAUNCH("probe_copy", s,
+             ffn::launch_probe_copy(src, dst, bytes, groups_per_cu, nontemporal != 0, s));
+  return ok();
+}
+
+int ffn_probe_mfma_groups(int waves_per_cu) {
+  return waves_per_cu < 1 || waves_per_cu > 32 ? 0 : ffn::probe_mfma_groups(waves_per_cu);
+}
+
+ffn_status ffn_probe_mfma(int iters, int waves_per_cu, void* sink, void* stream) {
+  if (!sink) return fail(FFN_ERR_INVALID_ARGUMENT, "null pointer");
+  if (iters < 1 || waves_per_cu < 1 || waves_per_cu > 32)
+    return fail(FFN_ERR_INVALID_ARGUMENT, "iters >= 1, waves_per_cu 1..32");
+  if (!aligned(sink, 16)) return fail(FFN_ERR_UNSUPPORTED, "alignment");
+  hipStream_t s = (hipStream_t)stream;
+  FFN_LAUNCH("probe_mfma", s, ffn::launch_probe_mfma(iters, waves_per_cu, (float*)sink, s));
   return ok();
 }
 
@@ -553,7 +566,7 @@ ffn_status ffn_timing_enable(int on, int max_launches) {
   if (T.cap != max_launches) {
     release_events();
     T.ev.assign(2 * (size_t)max_launches, nullptr);
-    T.name.assign(max_launches, nullptr);
+    T.name.assign(max_launches, std::string());
     T.cap = max_launches;
   }
   T.used = 0;
@@ -571,7 +584,7 @@ ffn_status ffn_timing_collect(void) {
     float ms = 0.f;
     if (hipEventElapsedTime(&ms, T.ev[2 * i], T.ev[2 * i + 1]) != hipSuccess)
       return fail(FFN_ERR_LAUNCH, "event elapsed time failed");
-    const std::string nm = T.name[i] ? T.name[i] : "?";
+    const std::string& nm = T.name[i];
     auto it = T.total.find(nm);
     if (it == T.total.end()) {
       T.order.push_back(nm);
@@ -606,6 +619,28 @@ void ffn_timing_reset(void) {
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+namespace ffn {
+
+void dispatch_events(hipEvent_t* start, hipEvent_t* stop) {
+  *start = *stop = nullptr;
+  Timing& T = t_timing;
+  if (!T.on || !T.site || T.used >= T.cap) return;
+  const int i = T.used;
+  for (int k = 2 * i; k < 2 * i + 2; ++k)
+    if (!T.ev[k] && hipEventCreate(&T.ev[k]) != hipSuccess) {
+      T.ev[k] = nullptr;
+      return;  // this dispatch runs untimed
+    }
+  T.name[i] = T.sub == 0 ? std::string(T.site) : std::string(T.site) + "/" + std::to_string(T.sub + 1);
+  ++T.sub;
+  T.used = i + 1;
+  *start = T.ev[2 * i];
+  *stop = T.ev[2 * i + 1];
+}
+
+}  // namespace ffn
 
 // ---------------------------------------------------------------------------
 // The block for callers that cannot allocate: its workspace is `scratch`, a

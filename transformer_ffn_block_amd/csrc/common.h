@@ -25,6 +25,18 @@ __device__ __forceinline__ uint2 ld_nt(const uint2* p) {
   return make_uint2(v.x, v.y);
 }
 
+// 16-byte store; NT = streaming (non-temporal) store
+template <bool NT>
+__device__ __forceinline__ void st16(uint4* p, const uint4& v) {
+  if (NT) {
+    u32x4 w;
+    w.x = v.x; w.y = v.y; w.z = v.z; w.w = v.w;
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(p));
+  } else {
+    *p = v;
+  }
+}
+
 // v if keep else 0, component-wise (a ternary on the struct type would go
 // through private memory)
 __device__ __forceinline__ uint4 keep_or_zero(bool keep, const uint4& v) {

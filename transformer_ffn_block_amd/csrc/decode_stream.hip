@@ -434,11 +434,11 @@ static hipError_t launch_ds(const void* act, const void* gain, const void* w0, c
   const uint16_t* rr = (const uint16_t*)resid;
   uint16_t* o = (uint16_t*)out;
   if (M <= 8)
-    hipLaunchKernelGGL((decode_stream<NMAT, 1, WAVES, FOLD, false>), grid, block, 0, s, a, gg, p0, p1, rr, o, M, K, N, eps);
+    FFN_DISPATCH((decode_stream<NMAT, 1, WAVES, FOLD, false>), grid, block, 0, s, a, gg, p0, p1, rr, o, M, K, N, eps);
   else if (M <= 16)
-    hipLaunchKernelGGL((decode_stream<NMAT, 1, WAVES, FOLD, true>), grid, block, 0, s, a, gg, p0, p1, rr, o, M, K, N, eps);
+    FFN_DISPATCH((decode_stream<NMAT, 1, WAVES, FOLD, true>), grid, block, 0, s, a, gg, p0, p1, rr, o, M, K, N, eps);
   else
-    hipLaunchKernelGGL((decode_stream<NMAT, 2, WAVES, FOLD, true>), grid, block, 0, s, a, gg, p0, p1, rr, o, M, K, N, eps);
+    FFN_DISPATCH((decode_stream<NMAT, 2, WAVES, FOLD, true>), grid, block, 0, s, a, gg, p0, p1, rr, o, M, K, N, eps);
   return hipGetLastError();
 }
 
@@ -598,7 +598,7 @@ hipError_t launch_decode_persistent(const void* x, const void* g, const void* wg
                                     int M, int d, int f, float eps, hipStream_t s) {
   const int splits = decode_persistent_splits(d, f);
   const int nc = (int)decode_persistent_counters(d, splits);
-  hipLaunchKernelGGL(clear_u32, dim3((unsigned)((nc + 255) / 256)), dim3(256), 0, s, ctr, nc);
+  FFN_DISPATCH(clear_u32, dim3((unsigned)((nc + 255) / 256)), dim3(256), 0, s, ctr, nc);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   static int cus = 0;  // compute units of the device (gfx950 parts share one count)
@@ -612,7 +612,7 @@ hipError_t launch_decode_persistent(const void* x, const void* g, const void* wg
   }
   const int n_items = (f + 15) / 16 + ((d + 15) / 16) * splits;
   const int grid = n_items < FFN_DS_PERSIST_WPE * cus ? n_items : FFN_DS_PERSIST_WPE * cus;
-  hipLaunchKernelGGL(decode_persistent, dim3((unsigned)grid), dim3(kPersistWaves * 64), 0, s,
+  FFN_DISPATCH(decode_persistent, dim3((unsigned)grid), dim3(kPersistWaves * 64), 0, s,
                      (const uint16_t*)x, (const uint16_t*)g, (const uint16_t*)wg,
                      (const uint16_t*)wu, (const uint16_t*)wd, (uint16_t*)h, part, (uint16_t*)y,
                      ctr, M, d, f, eps, splits, 1u << 20);

@@ -75,11 +75,11 @@ hipError_t launch_gemm_f32(int epi, const float* a, const float* w0, const float
                            const float* resid, float* c, int M, int N, int K, hipStream_t s) {
   const dim3 grid((unsigned)((N + FT - 1) / FT), (unsigned)((M + FT - 1) / FT)), block(256);
   if (epi == F32_SWIGLU)
-    hipLaunchKernelGGL(gemm_f32<F32_SWIGLU>, grid, block, 0, s, a, w0, w1, resid, c, M, N, K);
+    FFN_DISPATCH(gemm_f32<F32_SWIGLU>, grid, block, 0, s, a, w0, w1, resid, c, M, N, K);
   else if (epi == F32_RESIDUAL)
-    hipLaunchKernelGGL(gemm_f32<F32_RESIDUAL>, grid, block, 0, s, a, w0, w1, resid, c, M, N, K);
+    FFN_DISPATCH(gemm_f32<F32_RESIDUAL>, grid, block, 0, s, a, w0, w1, resid, c, M, N, K);
   else
-    hipLaunchKernelGGL(gemm_f32<F32_STORE>, grid, block, 0, s, a, w0, w1, resid, c, M, N, K);
+    FFN_DISPATCH(gemm_f32<F32_STORE>, grid, block, 0, s, a, w0, w1, resid, c, M, N, K);
   return hipGetLastError();
 }
 
@@ -96,7 +96,7 @@ hipError_t launch_swiglu_f32(const float* G, const float* U, float* h, int64_t c
   int64_t blocks = (count + 255) / 256;
   if (blocks > 4096) blocks = 4096;
   if (blocks < 1) blocks = 1;
-  hipLaunchKernelGGL(swiglu_f32, dim3((unsigned)blocks), dim3(256), 0, s, G, U, h, count);
+  FFN_DISPATCH(swiglu_f32, dim3((unsigned)blocks), dim3(256), 0, s, G, U, h, count);
   return hipGetLastError();
 }
 

@@ -2,10 +2,18 @@
 // C ABI is include/ffn.h).  Each launcher assumes its arguments were already
 // validated by the API layer and only enqueues kernels on `s`.
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace ffn {
+
+// Per-dispatch timing.  While the API layer's per-kernel timing is on for
+// the calling thread, dispatch_events() hands out a fresh (start, stop)
+// event pair for the next kernel, which hipExtLaunchKernel binds to the
+// dispatch itself (the kernel's own begin and end timestamps, not event
+// records around it); otherwise both are null and the launch is plain.
+void dispatch_events(hipEvent_t* start, hipEvent_t* stop);
 
 // RMSNorm, one wavefront per row ("When to hand-write a GPU kernel on Apple
 // Silicon", Rung 2 / Rung 4).  elem_bytes 2 = bf16, 4 = fp32.
@@ -88,6 +96,22 @@ hipError_t launch_splitk_residual(const float* part, int splits, const void* x, 
 int probe_read_groups(int waves_per_cu);
 hipError_t launch_probe_read(const void* src, size_t bytes, void* sink, int waves_per_cu,
                              hipStream_t s);
-hipError_t launch_probe_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
+// groups_per_cu > 0: grid-stride copy with that many 256-thread workgroups
+// per CU; 0: one workgroup per contiguous 16 KiB chunk.
+int probe_copy_groups(size_t bytes, int groups_per_cu);
+hipError_t launch_probe_copy(const void* src, void* dst, size_t bytes, int groups_per_cu,
+                             bool nontemporal, hipStream_t s);
+// Matrix-core loop: probe_mfma_groups(waves_per_cu) workgroups of 4 waves,
+// each wave 8 * iters bf16 16x16x32 MFMAs (16384 flop each).
+int probe_mfma_groups(int waves_per_cu);
+hipError_t launch_probe_mfma(int iters, int waves_per_cu, float* sink, hipStream_t s);
 
 }  // namespace ffn
+
+// Every kernel of the library is enqueued through this macro.
+#define FFN_DISPATCH(kernel, grid, block, lds, stream, ...)                                     \
+  do {                                                                                          \
+    hipEvent_t ffn_e0_ = nullptr, ffn_e1_ = nullptr;                                            \
+    ::ffn::dispatch_events(&ffn_e0_, &ffn_e1_);                                                 \
+    hipExtLaunchKernelGGL(kernel, grid, block, lds, stream, ffn_e0_, ffn_e1_, 0u, __VA_ARGS__); \
+  } while (0)

@@ -693,11 +693,11 @@ static hipError_t launch_cfg(const void* act, const void* w0, const void* w1, co
   if (K % kDmaBK == 0 && (size_t)M * K * 2 < ((size_t)1 << 31) && (size_t)N * K * 2 < ((size_t)1 << 31)) {
     // whole tiles and an even number of K tiles: the ping-pong schedule
     if (kPingPong && M % kBM == 0 && N % BNO == 0 && K % (kPpS * kPpBK) == 0)
-      hipLaunchKernelGGL((gemm_dma<kBM, kBN, kWM, kWN, EPI, kPpBK, kPpS, true>), dim3((unsigned)tiles),
+      FFN_DISPATCH((gemm_dma<kBM, kBN, kWM, kWN, EPI, kPpBK, kPpS, true>), dim3((unsigned)tiles),
                          dim3(kWM * kWN * 64), 0, s, (const uint16_t*)act, (const uint16_t*)w0,
                          (const uint16_t*)w1, (const uint16_t*)resid, (uint16_t*)out, M, N, K);
     else
-      hipLaunchKernelGGL((gemm_dma<kBM, kBN, kWM, kWN, EPI, kDmaBK, kDmaS, false>), dim3((unsigned)tiles),
+      FFN_DISPATCH((gemm_dma<kBM, kBN, kWM, kWN, EPI, kDmaBK, kDmaS, false>), dim3((unsigned)tiles),
                          dim3(kWM * kWN * 64), 0, s, (const uint16_t*)act, (const uint16_t*)w0,
                          (const uint16_t*)w1, (const uint16_t*)resid, (uint16_t*)out, M, N, K);
     return hipGetLastError();
@@ -707,7 +707,7 @@ static hipError_t launch_cfg(const void* act, const void* w0, const void* w1, co
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      kLdsBytes);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(kWM * kWN * 64), kLdsBytes, s,
+  FFN_DISPATCH(kern, dim3((unsigned)tiles), dim3(kWM * kWN * 64), kLdsBytes, s,
                      (const uint16_t*)act, (const uint16_t*)w0, (const uint16_t*)w1,
                      (const uint16_t*)resid, (uint16_t*)out, M, N, K);
   return hipGetLastError();
@@ -747,7 +747,7 @@ hipError_t launch_swiglu_bf16(const void* G, const void* U, void* h, int64_t cou
   int64_t blocks = (nchunk + 255) / 256;
   if (blocks > 256 * 16) blocks = 256 * 16;  // grid-stride beyond 16 workgroups per CU
   if (blocks < 1) blocks = 1;
-  hipLaunchKernelGGL(swiglu_bf16, dim3((unsigned)blocks), dim3(256), 0, s, (const uint4*)G,
+  FFN_DISPATCH(swiglu_bf16, dim3((unsigned)blocks), dim3(256), 0, s, (const uint4*)G,
                      (const uint4*)U, (uint4*)h, nchunk);
   return hipGetLastError();
 }

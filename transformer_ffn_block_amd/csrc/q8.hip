@@ -476,14 +476,14 @@ static void launch_q8_mt(const uint16_t* a, const uint16_t* gn, float eps, const
                          int N, hipStream_t s) {
   const dim3 grid((unsigned)((N + 15) / 16), (unsigned)splits), block(WAVES * 64);
   if constexpr (FOLD) {
-    hipLaunchKernelGGL((q8_stream<NMAT, 1, WAVES, SALIGN, 8, PART, true>), grid, block, 0, s, a, gn, q0, s0, q1, s1, rr, o, part, M, K, N, eps);
+    FFN_DISPATCH((q8_stream<NMAT, 1, WAVES, SALIGN, 8, PART, true>), grid, block, 0, s, a, gn, q0, s0, q1, s1, rr, o, part, M, K, N, eps);
   } else {
     if (M <= 8)
-      hipLaunchKernelGGL((q8_stream<NMAT, 1, WAVES, SALIGN, 8, PART, false>), grid, block, 0, s, a, gn, q0, s0, q1, s1, rr, o, part, M, K, N, eps);
+      FFN_DISPATCH((q8_stream<NMAT, 1, WAVES, SALIGN, 8, PART, false>), grid, block, 0, s, a, gn, q0, s0, q1, s1, rr, o, part, M, K, N, eps);
     else if (M <= 16)
-      hipLaunchKernelGGL((q8_stream<NMAT, 1, WAVES, SALIGN, 16, PART, false>), grid, block, 0, s, a, gn, q0, s0, q1, s1, rr, o, part, M, K, N, eps);
+      FFN_DISPATCH((q8_stream<NMAT, 1, WAVES, SALIGN, 16, PART, false>), grid, block, 0, s, a, gn, q0, s0, q1, s1, rr, o, part, M, K, N, eps);
     else
-      hipLaunchKernelGGL((q8_stream<NMAT, 2, WAVES, SALIGN, 0, PART, false>), grid, block, 0, s, a, gn, q0, s0, q1, s1, rr, o, part, M, K, N, eps);
+      FFN_DISPATCH((q8_stream<NMAT, 2, WAVES, SALIGN, 0, PART, false>), grid, block, 0, s, a, gn, q0, s0, q1, s1, rr, o, part, M, K, N, eps);
   }
 }
 

@@ -126,9 +126,9 @@ static hipError_t launch_eb(const void* x, const void* g, void* y, int64_t rows,
   const bool few = rows <= FFN_RMS_PREG_ROWS;
 #define FFN_RMS_CACHED(C)                                                                              \
   if (few)                                                                                           \
-    hipLaunchKernelGGL((rmsnorm_cached<EB, C, true>), grid, block, 0, s, xx, gg, yy, rows, nchunk, inv_d, eps); \
+    FFN_DISPATCH((rmsnorm_cached<EB, C, true>), grid, block, 0, s, xx, gg, yy, rows, nchunk, inv_d, eps); \
   else                                                                                               \
-    hipLaunchKernelGGL((rmsnorm_cached<EB, C, false>), grid, block, 0, s, xx, gg, yy, rows, nchunk, inv_d, eps);
+    FFN_DISPATCH((rmsnorm_cached<EB, C, false>), grid, block, 0, s, xx, gg, yy, rows, nchunk, inv_d, eps);
   if (nchunk <= 64 * 2) {
     FFN_RMS_CACHED(2)
   } else if (nchunk <= 64 * 4) {
@@ -138,7 +138,7 @@ static hipError_t launch_eb(const void* x, const void* g, void* y, int64_t rows,
   } else if (nchunk <= 64 * 16) {
     FFN_RMS_CACHED(16)
   } else
-    hipLaunchKernelGGL((rmsnorm_stream<EB>), grid, block, 0, s, xx, gg, yy, rows, nchunk, inv_d, eps);
+    FFN_DISPATCH((rmsnorm_stream<EB>), grid, block, 0, s, xx, gg, yy, rows, nchunk, inv_d, eps);
   return hipGetLastError();
 }
 

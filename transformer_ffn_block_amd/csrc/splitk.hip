@@ -36,7 +36,7 @@ hipError_t launch_splitk_residual(const float* part, int splits, const void* x, 
                                   int N, hipStream_t s) {
   const int groups = M * (N / 8);
   const dim3 grid((unsigned)((groups + 255) / 256)), block(256);
-  hipLaunchKernelGGL(splitk_residual, grid, block, 0, s, (const float4*)part, splits,
+  FFN_DISPATCH(splitk_residual, grid, block, 0, s, (const float4*)part, splits,
                      (const uint4*)x, (uint4*)y, groups, (size_t)M * N / 4);
   return hipGetLastError();
 }

@@ -46,7 +46,9 @@ SIGNATURES = [
     ("ffn_last_error", ctypes.c_char_p, []),
     ("ffn_probe_read", _I, [_VP, _SZ, _VP, _I, _VP]),
     ("ffn_probe_read_groups", _I, [_I]),
-    ("ffn_probe_copy", _I, [_VP, _VP, _SZ, _VP]),
+    ("ffn_probe_copy", _I, [_VP, _VP, _SZ, _I, _I, _VP]),
+    ("ffn_probe_mfma", _I, [_I, _I, _VP, _VP]),
+    ("ffn_probe_mfma_groups", _I, [_I]),
     ("ffn_timing_enable", _I, [_I, _I]),
     ("ffn_timing_enabled", _I, []),
     ("ffn_timing_collect", _I, []),
@@ -352,9 +354,22 @@ def probe_read(src, sink, waves_per_cu: int, stream=None) -> None:
                                waves_per_cu, _stream_handle(stream)), "ffn_probe_read")
 
 
-def probe_copy(src, dst, stream=None) -> None:
+def probe_copy(src, dst, groups_per_cu: int = 0, nontemporal: bool = False, stream=None) -> None:
+    if src.numel() * src.element_size() != dst.numel() * dst.element_size():
+        raise ValueError("probe_copy: src and dst must have the same size in bytes")
     check(lib().ffn_probe_copy(src.data_ptr(), dst.data_ptr(), src.numel() * src.element_size(),
-                               _stream_handle(stream)), "ffn_probe_copy")
+                               groups_per_cu, 1 if nontemporal else 0, _stream_handle(stream)),
+          "ffn_probe_copy")
+
+
+def probe_mfma(iters: int, waves_per_cu: int, sink, stream=None) -> int:
+    """Run the matrix-core loop; returns the flop it executes."""
+    groups = lib().ffn_probe_mfma_groups(waves_per_cu)
+    if sink.numel() * sink.element_size() < 4 * 256 * groups:
+        raise ValueError("probe_mfma: sink too small")
+    check(lib().ffn_probe_mfma(iters, waves_per_cu, sink.data_ptr(), _stream_handle(stream)),
+          "ffn_probe_mfma")
+    return groups * 4 * 8 * iters * 16384
 
 
 def timing_enable(on: bool, max_launches: int = 4096) -> None:
