@@ -79,8 +79,10 @@ struct DsLds {
   static constexpr int ssq = WAVES * MT * 16;                   // partial sums of squares
 };
 
-// One 16-row output tile over stages [zs, ze) of the reduction axis (ze < 0:
-// all of it), split over the workgroup's WAVES waves.
+// Output rows [row0, row1) (at most 16: one MFMA tile) over stages [zs, ze)
+// of the reduction axis (ze < 0: all of it), split over the workgroup's WAVES
+// waves.  Tile rows past row1 are loaded with an out-of-range buffer offset
+// (zeros, no memory access) and never stored.
 // ASTAGE: activations fetched in 256-byte token segments and staged through
 // LDS (pays off from about 8 tokens); otherwise read straight from L2 in the
 // MFMA operand layout (for one token every lane reads the same 64 bytes).
@@ -95,7 +97,7 @@ __device__ __forceinline__ void ds_tile(
     const uint16_t* __restrict__ resid,  // [M, N] (DS_EPI_DOWN)
     uint16_t* __restrict__ out,          // [M, N] bf16 (GATEUP, DOWN)
     float* __restrict__ part,            // [M, N] fp32 (PARTIAL)
-    int M, int K, int N, float eps, int tile, int zs, int ze,
+    int M, int K, int N, float eps, int row0, int row1, int zs, int ze,
     uint4* __restrict__ wbs, uint4* __restrict__ abs_, float* __restrict__ ssqs) {
   constexpr int ST = 16;  // 16-byte chunks per row per stage (128 k)
   auto lds_w = [&](int w, int m, int i) -> uint4& { return wbs[(w * NMAT + m) * 256 + i]; };
@@ -111,7 +113,7 @@ __device__ __forceinline__ void ds_tile(
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int r = lane & 15, q = lane >> 4;
-  const int j0 = tile * 16;
+  const int j0 = row0;
   const int K8 = K >> 3;
   const int nst = (K8 + ST - 1) / ST;
   const int z0 = zs, z1 = ze < 0 ? nst : ze;
@@ -129,9 +131,10 @@ __device__ __forceinline__ void ds_tile(
   int cst[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
-    const int row = min(j0 + 4 * u + q, N - 1);  // rows past N: clamped, never stored
+    const int row = j0 + 4 * u + q;  // rows past row1 (<= N): nothing loaded, never stored
     cst[u] = (r - (4 * u + q)) & 15;
-    gw[u] = (unsigned)row * (unsigned)K * 2u;
+    // kOutOfRange plus any in-row offset (< 2^31) stays past the resource
+    gw[u] = row < row1 ? (unsigned)row * (unsigned)K * 2u : kOutOfRange;
   }
   const int rd_base = (r >> 2) * 64 + (r & 3) * 16;
 
@@ -360,16 +363,23 @@ __device__ __forceinline__ void ds_tile(
       v0[e] = s0;
       v1[e] = s1;
     }
-    if (tok < M && col < N) {
+    if (tok < M && col < row1) {
       const size_t off = (size_t)tok * N + col;
-      uint2 o;
+      // four columns inside the range and 4-element aligned: vector access;
+      // otherwise (the edge of an unaligned row range) element by element
+      const bool whole = col + 4 <= row1 && (off & 3) == 0;
+      const int nc = min(4, row1 - col);
       if (EPI == DS_EPI_PARTIAL) {
         float* pp = part + off;
         if (COH) {
           coh_st8(pp, __float_as_uint(v0[0]), __float_as_uint(v0[1]));
           coh_st8(pp + 2, __float_as_uint(v0[2]), __float_as_uint(v0[3]));
-        } else {
+        } else if (whole) {
           *reinterpret_cast<float4*>(pp) = make_float4(v0[0], v0[1], v0[2], v0[3]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (e < nc) pp[e] = v0[e];
         }
         continue;
       }
@@ -383,17 +393,32 @@ __device__ __forceinline__ void ds_tile(
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) v0[e] = silu_mul(v0[e] * rs, v1[e] * rs);
-        o.x = pack_bf16x2(v0[0], v0[1]);
-        o.y = pack_bf16x2(v0[2], v0[3]);
-      } else {
+      } else if (whole) {
         const uint2 xr = *reinterpret_cast<const uint2*>(resid + off);
-        o.x = pack_bf16x2(bf2f(xr.x & 0xFFFFu) + v0[0], bf2f(xr.x >> 16) + v0[1]);
-        o.y = pack_bf16x2(bf2f(xr.y & 0xFFFFu) + v0[2], bf2f(xr.y >> 16) + v0[3]);
+        v0[0] += bf2f(xr.x & 0xFFFFu);
+        v0[1] += bf2f(xr.x >> 16);
+        v0[2] += bf2f(xr.y & 0xFFFFu);
+        v0[3] += bf2f(xr.y >> 16);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (e < nc) v0[e] += bf2f(resid[off + e]);
       }
-      if (COH)
+      uint2 o;
+      o.x = pack_bf16x2(v0[0], v0[1]);
+      o.y = pack_bf16x2(v0[2], v0[3]);
+      if (COH) {
         coh_st8(out + off, o.x, o.y);
-      else
+      } else if (whole) {
         *reinterpret_cast<uint2*>(out + off) = o;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (e < nc) {
+            const uint32_t w = e < 2 ? o.x : o.y;
+            out[off + e] = (uint16_t)(e & 1 ? w >> 16 : w & 0xFFFFu);
+          }
+      }
     }
   }
 }
@@ -413,8 +438,12 @@ void decode_stream(
   __shared__ uint4 wb[L::wb];
   __shared__ uint4 ab[L::ab];
   __shared__ float ssq[L::ssq];
+  // workgroup b of G owns rows [b N / G, (b + 1) N / G): at most 16 rows
+  // (G >= N / 16), as even a share of the rows as the grid allows
+  const int row0 = (int)(((long)blockIdx.x * N) / gridDim.x);
+  const int row1 = (int)(((long)(blockIdx.x + 1) * N) / gridDim.x);
   ds_tile<NMAT, MT, WAVES, FOLD, ASTAGE, NMAT == 2 ? DS_EPI_GATEUP : DS_EPI_DOWN, false>(
-      act, gain, w0, w1, resid, out, nullptr, M, K, N, eps, blockIdx.x, 0, -1, wb, ab, ssq);
+      act, gain, w0, w1, resid, out, nullptr, M, K, N, eps, row0, row1, 0, -1, wb, ab, ssq);
 }
 
 // Tokens per launch (two 16-token tiles keep the LDS stages within budget);
@@ -422,11 +451,33 @@ void decode_stream(
 int decode_chunk_tokens() { return 32; }
 int decode_max_tokens() { return 64; }
 
+// Balanced gate/up grids.  A 16-row tile per workgroup leaves the compute
+// units unevenly loaded when the tile count is not a multiple of the
+// workgroups that fit at once (f = 11008: 688 tiles on 768 slots, three
+// tiles on 176 CUs and two on 80; the kernel lasts as long as the busiest
+// CU).  Instead the grid is sized to whole rounds of resident workgroups and
+// each takes an equal share (<= 16) of the rows.  FFN_DS_BALANCE 0 keeps
+// one workgroup per 16-row tile.
+#ifndef FFN_DS_BALANCE
+#define FFN_DS_BALANCE 1
+#endif
+
+template <int NMAT, int MT, int WAVES, bool FOLD, bool ASTAGE>
+static void launch_one(const uint16_t* a, const uint16_t* gg, const uint16_t* p0,
+                       const uint16_t* p1, const uint16_t* rr, uint16_t* o, int M, int K, int N,
+                       float eps, hipStream_t s) {
+  auto kern = decode_stream<NMAT, MT, WAVES, FOLD, ASTAGE>;
+  // the occupancy of a kernel is fixed: computed once (the library assumes
+  // every device it runs on is the same model)
+  static const int slots = NMAT == 2 ? resident_slots(kern, WAVES * 64) : 0;
+  const int groups = NMAT == 2 ? stream_groups(N, slots, FFN_DS_BALANCE) : (N + 15) / 16;
+  FFN_DISPATCH(kern, dim3((unsigned)groups), dim3(WAVES * 64), 0, s, a, gg, p0, p1, rr, o, M, K, N, eps);
+}
+
 template <int NMAT, int WAVES, bool FOLD>
 static hipError_t launch_ds(const void* act, const void* gain, const void* w0, const void* w1,
                             const void* resid, void* out, int M, int K, int N, float eps,
                             hipStream_t s) {
-  const dim3 grid((unsigned)((N + 15) / 16)), block(WAVES * 64);
   const uint16_t* a = (const uint16_t*)act;
   const uint16_t* gg = (const uint16_t*)gain;
   const uint16_t* p0 = (const uint16_t*)w0;
@@ -434,11 +485,11 @@ static hipError_t launch_ds(const void* act, const void* gain, const void* w0, c
   const uint16_t* rr = (const uint16_t*)resid;
   uint16_t* o = (uint16_t*)out;
   if (M <= 8)
-    FFN_DISPATCH((decode_stream<NMAT, 1, WAVES, FOLD, false>), grid, block, 0, s, a, gg, p0, p1, rr, o, M, K, N, eps);
+    launch_one<NMAT, 1, WAVES, FOLD, false>(a, gg, p0, p1, rr, o, M, K, N, eps, s);
   else if (M <= 16)
-    FFN_DISPATCH((decode_stream<NMAT, 1, WAVES, FOLD, true>), grid, block, 0, s, a, gg, p0, p1, rr, o, M, K, N, eps);
+    launch_one<NMAT, 1, WAVES, FOLD, true>(a, gg, p0, p1, rr, o, M, K, N, eps, s);
   else
-    FFN_DISPATCH((decode_stream<NMAT, 2, WAVES, FOLD, true>), grid, block, 0, s, a, gg, p0, p1, rr, o, M, K, N, eps);
+    launch_one<NMAT, 2, WAVES, FOLD, true>(a, gg, p0, p1, rr, o, M, K, N, eps, s);
   return hipGetLastError();
 }
 
@@ -521,7 +572,8 @@ void decode_persistent(const uint16_t* __restrict__ x, const uint16_t* __restric
     if (item >= n_items) break;
     if (item < n_gu) {
       ds_tile<2, 1, W, true, true, DS_EPI_GATEUP, true>(x, g, wg, wu, nullptr, h, nullptr, M, d, f,
-                                                         eps, item, 0, -1, wb, ab, ssq);
+                                                         eps, item * 16, min(item * 16 + 16, f), 0, -1,
+                                                         wb, ab, ssq);
       // h stores complete (written through) before the tile is counted
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
       __syncthreads();
@@ -552,7 +604,8 @@ void decode_persistent(const uint16_t* __restrict__ x, const uint16_t* __restric
       __syncthreads();
       ds_tile<1, 1, W, false, true, DS_EPI_PARTIAL, true>(h, nullptr, wd, nullptr, nullptr, nullptr,
                                                          part + (size_t)z * M * d, M, f, d, 0.f,
-                                                         tile, zs, ze, wb, ab, ssq);
+                                                         tile * 16, min(tile * 16 + 16, d), zs, ze,
+                                                         wb, ab, ssq);
       __builtin_amdgcn_s_waitcnt(0x0F70);  // partial stores complete before counting
       __syncthreads();
       if (threadIdx.x == 0) {

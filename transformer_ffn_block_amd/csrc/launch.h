@@ -15,6 +15,31 @@ namespace ffn {
 // records around it); otherwise both are null and the launch is plain.
 void dispatch_events(hipEvent_t* start, hipEvent_t* stop);
 
+// Compute units of the current device (256 if the runtime cannot tell).
+int device_cus();
+
+// Workgroups of `kern` (block threads, no dynamic LDS) resident at once on
+// the device; 0 if the runtime cannot tell.
+template <class Kern>
+inline int resident_slots(Kern kern, int block) {
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, block, 0) != hipSuccess || per_cu < 1)
+    return 0;
+  return per_cu * device_cus();
+}
+
+// Grid of a weight-streaming projection of N output rows whose workgroups
+// each own an equal share (at most 16: one MFMA tile) of the rows, given
+// `slots` resident workgroups.  policy 0: one workgroup per 16-row tile;
+// 1: if the tiles fit one round, fill that round (every compute unit gets an
+// equal number of rows); 2: also, past one round, whole rounds.
+inline int stream_groups(int N, int slots, int policy) {
+  const int t0 = (N + 15) / 16;
+  if (policy <= 0 || slots < 1) return t0;
+  if (t0 <= slots) return 2 * t0 > slots ? slots : t0;
+  return policy >= 2 ? (t0 + slots - 1) / slots * slots : t0;
+}
+
 // RMSNorm, one wavefront per row ("When to hand-write a GPU kernel on Apple
 // Silicon", Rung 2 / Rung 4).  elem_bytes 2 = bf16, 4 = fp32.
 hipError_t launch_rmsnorm(int elem_bytes, const void* x, const void* g, void* y,

@@ -104,7 +104,7 @@ __global__ __launch_bounds__(256) void probe_mfma(int iters, float* __restrict__
   if (v == 1234.5678f) sink[blockIdx.x * 256 + threadIdx.x] = v;
 }
 
-static int num_cus() {
+int device_cus() {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 256;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
@@ -113,7 +113,7 @@ static int num_cus() {
 }
 
 int probe_read_groups(int waves_per_cu) {
-  const int g = num_cus() * waves_per_cu / 4;
+  const int g = device_cus() * waves_per_cu / 4;
   return g > 0 ? g : 1;
 }
 
@@ -126,7 +126,7 @@ hipError_t launch_probe_read(const void* src, size_t bytes, void* sink, int wave
 
 int probe_copy_groups(size_t bytes, int groups_per_cu) {
   const int64_t n = (int64_t)(bytes / 16);
-  int64_t g = groups_per_cu > 0 ? (int64_t)num_cus() * groups_per_cu : (n + kCopyChunk - 1) / kCopyChunk;
+  int64_t g = groups_per_cu > 0 ? (int64_t)device_cus() * groups_per_cu : (n + kCopyChunk - 1) / kCopyChunk;
   if (groups_per_cu > 0 && g > (n + 255) / 256) g = (n + 255) / 256;
   return (int)(g < 1 ? 1 : g);
 }

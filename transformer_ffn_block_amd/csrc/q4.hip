@@ -138,7 +138,10 @@ void q4_stream(
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int r = lane & 15, q = lane >> 4;
-  const int j0 = blockIdx.x * 16;
+  // workgroup b of G (gridDim.x) owns output rows [b N / G, (b + 1) N / G),
+  // at most 16; tile rows past row1 load nothing and are never stored
+  const int j0 = (int)(((long)blockIdx.x * N) / gridDim.x);
+  const int row1 = (int)(((long)(blockIdx.x + 1) * N) / gridDim.x);
   const int nb = K >> 5;                // blocks per row
   const int K32 = K >> 5;               // 16-byte nibble chunks per row (one per block)
   const int K8 = K >> 3;                // 16-byte activation chunks per row
@@ -160,12 +163,13 @@ void q4_stream(
 #pragma unroll
   for (int u = 0; u < NU; ++u) {
     const int rr = 8 * u + (lane >> 3);
-    const int row = min(j0 + rr, N - 1);  // rows past N: clamped, never stored
+    const int row = j0 + rr;
     cst[u] = ((lane & 7) - (rr >> 1)) & 7;
-    gq[u] = (unsigned)row * (unsigned)(K / 2);
+    // kOutOfRange plus any in-row offset (< 2^31) stays past the resource
+    gq[u] = row < row1 ? (unsigned)row * (unsigned)(K / 2) : kOutOfRange;
   }
   // this lane's weight row (MFMA B operand) and its scales
-  const int jr = min(j0 + r, N - 1);
+  const int jr = min(j0 + r, row1 - 1);  // scale row (rows past row1: a valid row's, cached)
   const uint16_t* ps[NMAT];
   ps[0] = s0 + (size_t)jr * nb;
   if (NMAT == 2) ps[NMAT - 1] = s1 + (size_t)jr * nb;
@@ -465,7 +469,7 @@ void q4_stream(
         v0 += red[w][t][0][e][lane];
         if (NMAT == 2) v1 += red[w][t][NMAT - 1][e][lane];
       }
-      if (tok < M && col < N) {
+      if (tok < M && col < row1) {
         const size_t off = (size_t)tok * N + col;
         if (PART) {
           part[(size_t)blockIdx.y * M * N + off] = v0;
@@ -489,21 +493,52 @@ void q4_stream(
 // Tokens per launch; the API walks larger M in chunks of this size.
 int q4_max_tokens() { return 32; }
 
+// Gate/up grid policy (stream_groups): 1 = fill a single round evenly when
+// the tiles fit one.  Whole rounds past one (policy 2: 1536 workgroups of
+// 11-12 rows instead of 1088 tiles at f = 17408) measured slower in
+// interleaved A/B (Q8_0 block 73.1 -> 78.0 us, Q4_0 55.6 -> 56.9 us at 8
+// tokens): the extra workgroups cost more than the partial last round.
+#ifndef FFN_Q4_BALANCE
+#define FFN_Q4_BALANCE 1
+#endif
+
+template <class Kern>
+static void q4_go(Kern kern, bool gateup, int splits, int N, int threads, const uint16_t* a,
+                     const uint16_t* gn, const uint8_t* q0, const uint16_t* s0,
+                     const uint8_t* q1, const uint16_t* s1, const uint16_t* rr,
+                     uint16_t* o, float* part, int M, int K, float eps, int slots, hipStream_t s) {
+  const int groups = gateup ? stream_groups(N, slots, FFN_Q4_BALANCE) : (N + 15) / 16;
+  FFN_DISPATCH(kern, dim3((unsigned)groups, (unsigned)splits), dim3(threads), 0, s, a, gn, q0, s0, q1,
+               s1, rr, o, part, M, K, N, eps);
+}
+
 template <int NMAT, int WAVES, bool SALIGN, bool PART, bool FOLD = false>
 static void launch_q4_mt(const uint16_t* a, const uint16_t* gn, float eps, const uint8_t* q0,
                          const uint16_t* s0, const uint8_t* q1, const uint16_t* s1,
                          const uint16_t* rr, uint16_t* o, float* part, int splits, int M, int K,
                          int N, hipStream_t s) {
-  const dim3 grid((unsigned)((N + 15) / 16), (unsigned)splits), block(WAVES * 64);
+  constexpr int T = WAVES * 64;
+  constexpr bool GU = NMAT == 2;
+  // each kernel's occupancy is fixed: computed once (the library assumes
+  // every device it runs on is the same model)
   if constexpr (FOLD) {
-    FFN_DISPATCH((q4_stream<NMAT, 1, WAVES, SALIGN, 8, PART, true>), grid, block, 0, s, a, gn, q0, s0, q1, s1, rr, o, part, M, K, N, eps);
+    auto k = q4_stream<NMAT, 1, WAVES, SALIGN, 8, PART, true>;
+    static const int slots = GU ? resident_slots(k, T) : 0;
+    q4_go(k, GU, splits, N, T, a, gn, q0, s0, q1, s1, rr, o, part, M, K, eps, slots, s);
   } else {
-    if (M <= 8)
-      FFN_DISPATCH((q4_stream<NMAT, 1, WAVES, SALIGN, 8, PART, false>), grid, block, 0, s, a, gn, q0, s0, q1, s1, rr, o, part, M, K, N, eps);
-    else if (M <= 16)
-      FFN_DISPATCH((q4_stream<NMAT, 1, WAVES, SALIGN, 16, PART, false>), grid, block, 0, s, a, gn, q0, s0, q1, s1, rr, o, part, M, K, N, eps);
-    else
-      FFN_DISPATCH((q4_stream<NMAT, 2, WAVES, SALIGN, 0, PART, false>), grid, block, 0, s, a, gn, q0, s0, q1, s1, rr, o, part, M, K, N, eps);
+    if (M <= 8) {
+      auto k = q4_stream<NMAT, 1, WAVES, SALIGN, 8, PART, false>;
+      static const int slots = GU ? resident_slots(k, T) : 0;
+      q4_go(k, GU, splits, N, T, a, gn, q0, s0, q1, s1, rr, o, part, M, K, eps, slots, s);
+    } else if (M <= 16) {
+      auto k = q4_stream<NMAT, 1, WAVES, SALIGN, 16, PART, false>;
+      static const int slots = GU ? resident_slots(k, T) : 0;
+      q4_go(k, GU, splits, N, T, a, gn, q0, s0, q1, s1, rr, o, part, M, K, eps, slots, s);
+    } else {
+      auto k = q4_stream<NMAT, 2, WAVES, SALIGN, 0, PART, false>;
+      static const int slots = GU ? resident_slots(k, T) : 0;
+      q4_go(k, GU, splits, N, T, a, gn, q0, s0, q1, s1, rr, o, part, M, K, eps, slots, s);
+    }
   }
 }
 
