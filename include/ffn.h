@@ -57,7 +57,16 @@
 extern "C" {
 #endif
 
-typedef enum {
+/* The enums below cross the ABI as plain ints: a caller may pass any value
+ * (the library rejects unknown ones).  C++ gives them a fixed int
+ * representation so that such a value is well defined there too. */
+#ifdef __cplusplus
+#define FFN_ENUM_BASE : int
+#else
+#define FFN_ENUM_BASE
+#endif
+
+typedef enum FFN_ENUM_BASE {
   FFN_OK = 0,
   FFN_ERR_INVALID_ARGUMENT = 1, /* null pointer, negative size, bad enum, overlap */
   FFN_ERR_UNSUPPORTED = 2,      /* shape/alignment outside what the kernels take   */
@@ -65,7 +74,7 @@ typedef enum {
   FFN_ERR_LAUNCH = 4            /* a kernel launch was rejected by the runtime     */
 } ffn_status;
 
-typedef enum { FFN_F32 = 0, FFN_BF16 = 1 } ffn_dtype;
+typedef enum FFN_ENUM_BASE { FFN_F32 = 0, FFN_BF16 = 1 } ffn_dtype;
 
 /* Schedule of the block.  FUSED computes both gate/up projections in one
  * kernel whose epilogue applies silu(G)*U; SPLIT runs the gate GEMM, the up
@@ -78,7 +87,7 @@ typedef enum { FFN_F32 = 0, FFN_BF16 = 1 } ffn_dtype;
  * to 64 tokens (the norm folded into the gate/up kernel, FUSED's
  * schedule) and FUSED beyond (measured faster than SPLIT at the prefill
  * shapes on this device); for fp32 it is FUSED. */
-typedef enum {
+typedef enum FFN_ENUM_BASE {
   FFN_VARIANT_AUTO = 0,
   FFN_VARIANT_FUSED = 1,
   FFN_VARIANT_SPLIT = 2,

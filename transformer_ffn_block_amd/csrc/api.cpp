@@ -223,10 +223,14 @@ size_t ffn_swiglu_block_persistent_status_offset(int64_t M, int64_t d, int64_t f
   return ws_layout(2, M, d, f, false, true).ctr + 4;
 }
 
-ffn_status ffn_swiglu_block(ffn_dtype dt, const void* x, const void* g, const void* w_gate,
-                            const void* w_up, const void* w_down, void* y, int64_t M, int64_t d,
-                            int64_t f, float eps, ffn_variant variant, void* workspace,
-                            size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Every check of a block call that does not involve the workspace.
+ffn_status check_block_args(ffn_dtype dt, const void* x, const void* g, const void* w_gate,
+                            const void* w_up, const void* w_down, const void* y, int64_t M,
+                            int64_t d, int64_t f, float eps, ffn_variant variant) {
   FFN_TRY(check_dtype(dt));
   if (!x || !g || !w_gate || !w_up || !w_down || !y)
     return fail(FFN_ERR_INVALID_ARGUMENT, "null pointer");
@@ -236,14 +240,31 @@ ffn_status ffn_swiglu_block(ffn_dtype dt, const void* x, const void* g, const vo
   FFN_TRY(check_eps(eps));
   const size_t es = elem_size(dt);
   FFN_TRY(check_block_dims(M, d, f, 16 / (int64_t)es));
-  const bool persistent = use_persistent(variant);
-  if (persistent && (dt != FFN_BF16 || M > 16))
+  if (use_persistent(variant) && (dt != FFN_BF16 || M > 16))
     return fail(FFN_ERR_UNSUPPORTED, "the persistent schedule takes bf16 and at most 16 tokens");
   if (!aligned(x, 16) || !aligned(g, 16) || !aligned(w_gate, 16) || !aligned(w_up, 16) ||
       !aligned(w_down, 16) || !aligned(y, 16))
     return fail(FFN_ERR_UNSUPPORTED, "tensors must be 16-byte aligned");
   if ((size_t)f * d * es >= ((size_t)1 << 31))
     return fail(FFN_ERR_UNSUPPORTED, "weight matrices must be smaller than 2 GiB");
+  const size_t ny = (size_t)M * d * es, nw = (size_t)f * d * es;
+  if (overlap(y, ny, x, ny) || overlap(y, ny, g, (size_t)d * es) || overlap(y, ny, w_gate, nw) ||
+      overlap(y, ny, w_up, nw) || overlap(y, ny, w_down, nw))
+    return fail(FFN_ERR_INVALID_ARGUMENT, "y overlaps an input or the workspace");
+  return FFN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ffn_status ffn_swiglu_block(ffn_dtype dt, const void* x, const void* g, const void* w_gate,
+                            const void* w_up, const void* w_down, void* y, int64_t M, int64_t d,
+                            int64_t f, float eps, ffn_variant variant, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  FFN_TRY(check_block_args(dt, x, g, w_gate, w_up, w_down, y, M, d, f, eps, variant));
+  const size_t es = elem_size(dt);
+  const bool persistent = use_persistent(variant);
   const bool split = use_split(variant);
   const WsLayout L = ws_layout(es, M, d, f, split, persistent);
   if (M > 0 && (!workspace || workspace_bytes < L.total))
@@ -251,10 +272,8 @@ ffn_status ffn_swiglu_block(ffn_dtype dt, const void* x, const void* g, const vo
                 workspace ? workspace_bytes : (size_t)0);
   if (workspace && !aligned(workspace, 256))
     return fail(FFN_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
-  const size_t ny = (size_t)M * d * es, nw = (size_t)f * d * es;
-  if (overlap(y, ny, x, ny) || overlap(y, ny, g, (size_t)d * es) || overlap(y, ny, w_gate, nw) ||
-      overlap(y, ny, w_up, nw) || overlap(y, ny, w_down, nw) ||
-      overlap(y, ny, workspace, workspace ? L.total : 0))
+  const size_t ny = (size_t)M * d * es;
+  if (overlap(y, ny, workspace, workspace ? L.total : 0))
     return fail(FFN_ERR_INVALID_ARGUMENT, "y overlaps an input or the workspace");
   if (M == 0) return ok();
 
@@ -686,16 +705,15 @@ ffn_status ffn_swiglu_block_noalloc(ffn_dtype dt, const void* x, const void* g, 
                                     const void* w_up, const void* w_down, void* y, int64_t M,
                                     int64_t d, int64_t f, float eps, ffn_variant variant,
                                     void* stream) {
-  // a shape the block would reject gets the block's own error below
+  // every argument is checked before the device's array is looked up
+  FFN_TRY(check_block_args(dt, x, g, w_gate, w_up, w_down, y, M, d, f, eps, variant));
   const size_t need = ffn_swiglu_block_workspace_size(dt, M, d, f, variant);
   if (need > kNoAllocScratchBytes)
     return fail(FFN_ERR_UNSUPPORTED,
                 "this shape needs %zu bytes of workspace; the library's scratch array holds %zu "
                 "(use ffn_swiglu_block with a caller workspace)",
                 need, kNoAllocScratchBytes);
-  if (M == 0 || need == 0)  // nothing to launch, or an invalid call: no device lookup
-    return ffn_swiglu_block(dt, x, g, w_gate, w_up, w_down, y, M, d, f, eps, variant, nullptr, 0,
-                            stream);
+  if (M == 0) return ok();
   void* ws = nullptr;
   FFN_TRY(scratch_for_current_device(&ws));
   return ffn_swiglu_block(dt, x, g, w_gate, w_up, w_down, y, M, d, f, eps, variant, ws,
