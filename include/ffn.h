@@ -86,12 +86,20 @@ typedef enum FFN_ENUM_BASE { FFN_F32 = 0, FFN_BF16 = 1 } ffn_dtype;
  * counters.  AUTO takes, for bf16, the weight-streaming decode kernels up
  * to 64 tokens (the norm folded into the gate/up kernel, FUSED's
  * schedule) and FUSED beyond (measured faster than SPLIT at the prefill
- * shapes on this device); for fp32 it is FUSED. */
+ * shapes on this device); for fp32 it is FUSED.  FUSED_NORM (bf16) also
+ * folds the RMSNorm into the fused gate/up GEMM of the prefill regime
+ * (more than 64 tokens): the GEMM reads x, multiplies it by g on its way
+ * into shared memory, sums x^2 over the K loop and scales both projections
+ * by r_m in the epilogue, so no norm launch and no n round trip
+ * ("Megakernels on Mac", "Dependencies and synchronization": the scale is
+ * applied only after the whole row's sum); up to 64 tokens it is AUTO
+ * (whose decode kernels fold the norm already). */
 typedef enum FFN_ENUM_BASE {
   FFN_VARIANT_AUTO = 0,
   FFN_VARIANT_FUSED = 1,
   FFN_VARIANT_SPLIT = 2,
-  FFN_VARIANT_PERSISTENT = 3
+  FFN_VARIANT_PERSISTENT = 3,
+  FFN_VARIANT_FUSED_NORM = 4
 } ffn_variant;
 
 /* One Q8_0 weight matrix [N, K] in split (structure-of-arrays) form:

@@ -94,7 +94,7 @@ def test_persistent_variant_scope(L):
     P = ffn.VARIANTS["persistent"]
     assert _block(L, v=P, M=17) == UNS                       # at most 16 tokens
     assert _block(L, v=P, dt=ffn.FFN_F32, d=256, f=704) == UNS  # bf16 only
-    assert _block(L, v=4) == ffn.FFN_ERR_INVALID_ARGUMENT
+    assert _block(L, v=5) == ffn.FFN_ERR_INVALID_ARGUMENT
     assert _block(L, v=P, M=0, ws=0, wsb=0) == ffn.FFN_OK
 
 

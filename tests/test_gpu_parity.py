@@ -276,7 +276,7 @@ def test_block_persistent_deterministic_and_close_to_two_launch_path(gpu_lib):
 # prefill regime (MFMA GEMMs), fused and split gate/up
 # ----------------------------------------------------------------------------
 @pytest.mark.parametrize("M,d,f", [(65, 512, 704), (300, 520, 712), (513, 1024, 2048), (1000, 256, 136)])
-@pytest.mark.parametrize("variant", ["fused", "split"])
+@pytest.mark.parametrize("variant", ["fused", "split", "fused_norm"])
 def test_block_prefill_ragged(gpu_lib, M, d, f, variant):
     from transformer_ffn_block_amd import ffn
     _say("block prefill ragged", M, d, f, variant)
@@ -287,7 +287,7 @@ def test_block_prefill_ragged(gpu_lib, M, d, f, variant):
 
 
 @pytest.mark.parametrize("M,d,f", [(256, 256, 128), (512, 512, 768), (768, 1024, 1280)])
-@pytest.mark.parametrize("variant", ["fused", "split"])
+@pytest.mark.parametrize("variant", ["fused", "split", "fused_norm"])
 def test_block_prefill_whole_tiles(gpu_lib, M, d, f, variant):
     """Shapes made of whole 256-token tiles with an even number of 64-deep K
     tiles, the ones the two-group (ping-pong) GEMM schedule takes; K = 128
@@ -318,6 +318,7 @@ def test_block_prefill_full_size_sampled_rows(gpu_lib, prefill_inputs):
     x, g, wg, wu, wd = _block_dev(b)
     y_f = ffn.swiglu_block(x, g, wg, wu, wd, b.eps, variant="fused")
     y_s = ffn.swiglu_block(x, g, wg, wu, wd, b.eps, variant="split")
+    y_n = ffn.swiglu_block(x, g, wg, wu, wd, b.eps, variant="fused_norm")
     torch.cuda.synchronize()
     fixed = np.array([0, 1, 255, 256, 4095, 4096, b.M - 256, b.M - 1])
     rest = np.setdiff1d(np.arange(b.M), fixed)
@@ -332,6 +333,8 @@ def test_block_prefill_full_size_sampled_rows(gpu_lib, prefill_inputs):
     record("C4 prefill split (256 rows)", rel_l2(as_[rows], r), TOL_BF16, "rel_l2")
     assert record("C4 prefill fused (256 rows)", ef, TOL_BF16) <= TOL_BF16
     assert record("C4 prefill split (256 rows)", es, TOL_BF16) <= TOL_BF16
+    an = host_f64(y_n)
+    assert record("C4 prefill fused_norm (256 rows)", max_norm_err(an[rows], r), TOL_BF16) <= TOL_BF16
     # per row too: no row's error hides under another row's larger outputs
     per_row = max(max_norm_err(a[rows][i], r[i]) for a in (af, as_) for i in range(rows.size))
     assert record("C4 prefill worst row (row-normalised)", per_row, TOL_BF16, "max_norm_per_row") <= TOL_BF16

@@ -211,7 +211,7 @@ size_t ffn_swiglu_block_workspace_size(ffn_dtype dt, int64_t M, int64_t d, int64
   if (dt != FFN_F32 && dt != FFN_BF16) return 0;
   if (M < 0 || d <= 0 || f <= 0) return 0;
   if (variant != FFN_VARIANT_AUTO && variant != FFN_VARIANT_FUSED && variant != FFN_VARIANT_SPLIT &&
-      variant != FFN_VARIANT_PERSISTENT)
+      variant != FFN_VARIANT_PERSISTENT && variant != FFN_VARIANT_FUSED_NORM)
     return 0;
   if (use_persistent(variant) && (dt != FFN_BF16 || M > 16 || d > INT32_MAX || f > INT32_MAX))
     return 0;
@@ -235,7 +235,7 @@ ffn_status check_block_args(ffn_dtype dt, const void* x, const void* g, const vo
   if (!x || !g || !w_gate || !w_up || !w_down || !y)
     return fail(FFN_ERR_INVALID_ARGUMENT, "null pointer");
   if (variant != FFN_VARIANT_AUTO && variant != FFN_VARIANT_FUSED && variant != FFN_VARIANT_SPLIT &&
-      variant != FFN_VARIANT_PERSISTENT)
+      variant != FFN_VARIANT_PERSISTENT && variant != FFN_VARIANT_FUSED_NORM)
     return fail(FFN_ERR_INVALID_ARGUMENT, "unknown variant %d", (int)variant);
   FFN_TRY(check_eps(eps));
   const size_t es = elem_size(dt);
@@ -290,7 +290,9 @@ ffn_status ffn_swiglu_block(ffn_dtype dt, const void* x, const void* g, const vo
     return ok();
   }
   const bool decode = dt == FFN_BF16 && !split && Mi <= ffn::decode_max_tokens();
-  if (!decode) FFN_LAUNCH("rmsnorm", s, ffn::launch_rmsnorm((int)es, x, g, n, M, d, eps, s));
+  // prefill with the norm folded into the fused gate/up GEMM
+  const bool fold_prefill = dt == FFN_BF16 && variant == FFN_VARIANT_FUSED_NORM && !decode;
+  if (!decode && !fold_prefill) FFN_LAUNCH("rmsnorm", s, ffn::launch_rmsnorm((int)es, x, g, n, M, d, eps, s));
   if (dt == FFN_F32) {
     const float* nf = (const float*)n;
     float* hf = (float*)h;
@@ -313,6 +315,9 @@ ffn_status ffn_swiglu_block(ffn_dtype dt, const void* x, const void* g, const vo
     FFN_LAUNCH("gemm_gate", s, ffn::launch_gemm_store(n, w_gate, G, Mi, fi, di, s));
     FFN_LAUNCH("gemm_up", s, ffn::launch_gemm_store(n, w_up, U, Mi, fi, di, s));
     FFN_LAUNCH("swiglu", s, ffn::launch_swiglu_bf16(G, U, h, (int64_t)M * f, s));
+  } else if (fold_prefill) {
+    FFN_LAUNCH("gemm_gateup_fused_norm", s,
+               ffn::launch_gemm_gateup_fused_norm(x, g, w_gate, w_up, h, Mi, di, fi, eps, s));
   } else if (!decode) {
     FFN_LAUNCH("gemm_gateup_fused", s, ffn::launch_gemm_gateup_fused(n, w_gate, w_up, h, Mi, di, fi, s));
   }

@@ -66,6 +66,11 @@ hipError_t launch_decode_persistent(const void* x, const void* g, const void* wg
 // Prefill (many tokens) LDS-tiled bf16 MFMA GEMMs, C[m][n] = sum_k A[m][k] W[n][k].
 hipError_t launch_gemm_gateup_fused(const void* n, const void* wg, const void* wu, void* h,
                                     int M, int d, int f, hipStream_t s);
+// The same with the RMSNorm folded in: x (not n) and the gain g go in, and
+// r_m scales the accumulators in the epilogue (register-staged kernel).
+hipError_t launch_gemm_gateup_fused_norm(const void* x, const void* g, const void* wg,
+                                         const void* wu, void* h, int M, int d, int f, float eps,
+                                         hipStream_t s);
 hipError_t launch_gemm_store(const void* a, const void* w, void* c, int M, int N, int K,
                              hipStream_t s);
 hipError_t launch_gemm_residual(const void* a, const void* w, const void* resid, void* y,

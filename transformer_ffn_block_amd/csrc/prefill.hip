@@ -63,14 +63,20 @@ enum { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_RESIDUAL = 2 };
 
 __device__ __forceinline__ int swz(int row) { return row & 7; }
 
-template <int BM, int BN, int WM, int WN, int EPI>
+// FOLD (SWIGLU only): the RMSNorm is folded in.  act is x; every token
+// chunk is multiplied by the gain on its way from registers to LDS (the
+// operand is bf16(x * g), as in the decode kernels) while the thread sums
+// the squares of x; the epilogue scales G and U by r_m = 1/sqrt(sum/K + eps)
+// once the whole row's sum is known (W n = r_m W (x * g)).
+template <int BM, int BN, int WM, int WN, int EPI, bool FOLD = false>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16(
-    const uint16_t* __restrict__ act,    // [M, K]
+    const uint16_t* __restrict__ act,    // [M, K]: n, or x (FOLD)
     const uint16_t* __restrict__ w0,     // [N, K]  (gate for SWIGLU)
     const uint16_t* __restrict__ w1,     // [N, K]  (up for SWIGLU)
     const uint16_t* __restrict__ resid,  // [M, N]  (RESIDUAL)
     uint16_t* __restrict__ out,          // [M, N]
-    int M, int N, int K) {
+    int M, int N, int K, const uint16_t* __restrict__ gain = nullptr, float eps = 0.f) {
+  static_assert(!FOLD || EPI == EPI_SWIGLU, "the norm folds into the fused gate/up GEMM only");
   constexpr int NT = WM * WN * 64;
   constexpr int TM = BM / WM;  // tokens per wave
   constexpr int TN = BN / WN;  // weight rows per wave (half gate, half up for SWIGLU)
@@ -133,6 +139,11 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16(
   const uint4* W1 = reinterpret_cast<const uint4*>(EPI == EPI_SWIGLU ? w1 : w0);
 
   uint4 pre[CH];
+  uint4 gpre;                        // FOLD: the gain chunk of the prefetched tile
+  float ssq[FOLD ? CH - CW : 1];     // FOLD: sums of squares of this thread's token rows
+#pragma unroll
+  for (int i = 0; i < (FOLD ? CH - CW : 1); ++i) ssq[i] = 0.f;
+  const uint4* G4 = reinterpret_cast<const uint4*>(gain);
   auto load_tile = [&](int kt) {
     const int kc = min(kt * 8 + ccol, K8 - 1);
 #pragma unroll
@@ -140,6 +151,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16(
       const uint4* base = i < CW ? ((EPI == EPI_SWIGLU && i >= CW / 2) ? W1 : W0) : A4;
       pre[i] = base[off[i] + kc];
     }
+    if (FOLD) gpre = G4[kc];
   };
   auto store_tile = [&](int stage, int kt) {
     uint4* L0 = lds + stage * ROWS * 8 + crow * 8 + sw_st;
@@ -147,6 +159,22 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16(
       const bool kin = kt * 8 + ccol < K8;
 #pragma unroll
       for (int i = 0; i < CH; ++i) pre[i] = keep_or_zero(kin, pre[i]);
+    }
+    if (FOLD) {
+      // token chunks: x * g in fp32, rounded once to bf16; sum of x^2
+      float gf[8];
+      unpack8(gpre, gf);
+#pragma unroll
+      for (int i = CW; i < CH; ++i) {
+        float xf[8];
+        unpack8(pre[i], xf);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          ssq[FOLD ? i - CW : 0] = __builtin_fmaf(xf[e], xf[e], ssq[FOLD ? i - CW : 0]);
+          xf[e] *= gf[e];
+        }
+        pre[i] = pack8(xf);
+      }
     }
 #pragma unroll
     for (int i = 0; i < CH; ++i) L0[i * (NT / 8) * 8] = pre[i];
@@ -196,10 +224,13 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16(
   auto iter = [&](int kt, auto do_store, auto do_load) {
     const uint4* L0 = lds + (kt & 1) * ROWS * 8;
     uint4 af[FN], bfr[FM];
+    // FOLD: the gain multiply needs registers of its own, so its tile goes
+    // to LDS before the fragments are live rather than between the MFMAs
+    if (FOLD && decltype(do_store)::value) store_tile((kt + 1) & 1, kt + 1);
     compute_ks(L0, 0, af, bfr);
-    if (decltype(do_store)::value) store_tile((kt + 1) & 1, kt + 1);
+    if (!FOLD && decltype(do_store)::value) store_tile((kt + 1) & 1, kt + 1);
     mfmas(af, bfr);
-    if (decltype(do_store)::value) {
+    if (!FOLD && decltype(do_store)::value) {
       // 12 fragment reads, then 4 MFMAs per LDS write
       __builtin_amdgcn_sched_group_barrier(0x100, FN + FM, 0);
 #pragma unroll
@@ -224,6 +255,22 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16(
   if (kt + 1 < nkt) iter(kt++, T_{}, F_{});
   iter(kt, F_{}, F_{});
 
+  // ---- FOLD: r_m of the tile's token rows.  A row's chunks are held by the
+  // 8 consecutive threads with its crow (ccol = 0..7); the last K loop
+  // iteration ended with a barrier, so the stages are free for the r table.
+  float* rtab = reinterpret_cast<float*>(lds);
+  if (FOLD) {
+#pragma unroll
+    for (int i = 0; i < (FOLD ? CH - CW : 1); ++i) {
+      float v = ssq[i];
+      v += __shfl_xor(v, 1, 64);
+      v += __shfl_xor(v, 2, 64);
+      v += __shfl_xor(v, 4, 64);
+      if (ccol == 0) rtab[i * (NT / 8) + crow] = 1.0f / __builtin_sqrtf(v / (float)K + eps);
+    }
+    __syncthreads();
+  }
+
   // ---- epilogue: lane holds D[4*fq + e][fr] of every (a, b) sub-tile
   if (EPI == EPI_SWIGLU) {
 #pragma unroll
@@ -233,7 +280,12 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16(
       for (int b = 0; b < FM; ++b) {
         const int tok = m0 + wm * TM + b * 16 + fr;
         if (tok < M && col < N) {
-          const f32x4 gg = acc[a][b], uu = acc[a + FN / 2][b];
+          f32x4 gg = acc[a][b], uu = acc[a + FN / 2][b];
+          if (FOLD) {
+            const float rs = rtab[wm * TM + b * 16 + fr];
+            gg *= rs;
+            uu *= rs;
+          }
           uint2 o;
           o.x = pack_bf16x2(silu_mul(gg[0], uu[0]), silu_mul(gg[1], uu[1]));
           o.y = pack_bf16x2(silu_mul(gg[2], uu[2]), silu_mul(gg[3], uu[3]));
@@ -684,13 +736,37 @@ constexpr int kBM = 256, kBN = 256, kWM = 2, kWN = 4;
 constexpr int kLdsBytes = 2 * (kBM + kBN) * 128;
 
 
+// FFN_PF_FORCE_REG 1 routes every GEMM to the register-staged kernel (for
+// measurements that compare the schedules).
+#ifndef FFN_PF_FORCE_REG
+#define FFN_PF_FORCE_REG 0
+#endif
+
+template <int EPI, bool FOLD = false>
+static hipError_t launch_reg(const void* act, const void* w0, const void* w1, const void* resid,
+                             void* out, int M, int N, int K, const void* gain, float eps,
+                             hipStream_t s) {
+  constexpr int BNO = EPI == EPI_SWIGLU ? kBN / 2 : kBN;
+  const long tiles = (long)((M + kBM - 1) / kBM) * ((N + BNO - 1) / BNO);
+  auto kern = gemm_bf16<kBM, kBN, kWM, kWN, EPI, FOLD>;
+  // allow more than the default dynamic LDS (per device, so done per launch)
+  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     kLdsBytes);
+  if (e != hipSuccess) return e;
+  FFN_DISPATCH(kern, dim3((unsigned)tiles), dim3(kWM * kWN * 64), kLdsBytes, s,
+               (const uint16_t*)act, (const uint16_t*)w0, (const uint16_t*)w1,
+               (const uint16_t*)resid, (uint16_t*)out, M, N, K, (const uint16_t*)gain, eps);
+  return hipGetLastError();
+}
+
 template <int EPI>
 static hipError_t launch_cfg(const void* act, const void* w0, const void* w1, const void* resid,
                              void* out, int M, int N, int K, hipStream_t s) {
   constexpr int BNO = EPI == EPI_SWIGLU ? kBN / 2 : kBN;
   const long tiles = (long)((M + kBM - 1) / kBM) * ((N + BNO - 1) / BNO);
   // whole K tiles and every operand addressable by a buffer resource: LDS-fed kernel
-  if (K % kDmaBK == 0 && (size_t)M * K * 2 < ((size_t)1 << 31) && (size_t)N * K * 2 < ((size_t)1 << 31)) {
+  if (!FFN_PF_FORCE_REG && K % kDmaBK == 0 && (size_t)M * K * 2 < ((size_t)1 << 31) &&
+      (size_t)N * K * 2 < ((size_t)1 << 31)) {
     // whole tiles and an even number of K tiles: the ping-pong schedule
     if (kPingPong && M % kBM == 0 && N % BNO == 0 && K % (kPpS * kPpBK) == 0)
       FFN_DISPATCH((gemm_dma<kBM, kBN, kWM, kWN, EPI, kPpBK, kPpS, true>), dim3((unsigned)tiles),
@@ -702,20 +778,17 @@ static hipError_t launch_cfg(const void* act, const void* w0, const void* w1, co
                          (const uint16_t*)w1, (const uint16_t*)resid, (uint16_t*)out, M, N, K);
     return hipGetLastError();
   }
-  auto kern = gemm_bf16<kBM, kBN, kWM, kWN, EPI>;
-  // allow more than the default dynamic LDS (per device, so done per launch)
-  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     kLdsBytes);
-  if (e != hipSuccess) return e;
-  FFN_DISPATCH(kern, dim3((unsigned)tiles), dim3(kWM * kWN * 64), kLdsBytes, s,
-                     (const uint16_t*)act, (const uint16_t*)w0, (const uint16_t*)w1,
-                     (const uint16_t*)resid, (uint16_t*)out, M, N, K);
-  return hipGetLastError();
+  return launch_reg<EPI>(act, w0, w1, resid, out, M, N, K, nullptr, 0.f, s);
 }
 
 hipError_t launch_gemm_gateup_fused(const void* n, const void* wg, const void* wu, void* h,
                                     int M, int d, int f, hipStream_t s) {
   return launch_cfg<EPI_SWIGLU>(n, wg, wu, nullptr, h, M, f, d, s);
+}
+hipError_t launch_gemm_gateup_fused_norm(const void* x, const void* g, const void* wg,
+                                         const void* wu, void* h, int M, int d, int f, float eps,
+                                         hipStream_t s) {
+  return launch_reg<EPI_SWIGLU, true>(x, wg, wu, nullptr, h, M, f, d, g, eps, s);
 }
 hipError_t launch_gemm_store(const void* a, const void* w, void* c, int M, int N, int K,
                              hipStream_t s) {

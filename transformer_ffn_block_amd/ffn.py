@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(_HERE, "libffn.so")
 
 FFN_OK, FFN_ERR_INVALID_ARGUMENT, FFN_ERR_UNSUPPORTED, FFN_ERR_WORKSPACE, FFN_ERR_LAUNCH = range(5)
 FFN_F32, FFN_BF16 = 0, 1
-VARIANTS = {"auto": 0, "fused": 1, "split": 2, "persistent": 3}
+VARIANTS = {"auto": 0, "fused": 1, "split": 2, "persistent": 3, "fused_norm": 4}
 
 # (name, restype, argtypes) of every function include/ffn.h declares
 _VP, _I64, _F, _I, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int, ctypes.c_size_t
