@@ -68,12 +68,12 @@ def _pick(per, sub):
 
 
 def traffic(fetch_csv, write_csv, kernel, copy_bytes, source, bytes_per_launch, command,
-            grid=None) -> str:
+            grid=None, copy_kernel="probe_copy") -> str:
     f_per, w_per = _counter(fetch_csv, "FETCH_SIZE", grid), _counter(write_csv, "WRITE_SIZE", grid)
     kname, f_kib, nf = _pick(f_per, kernel)
     _, w_kib, nw = _pick(w_per, kernel)
-    _, cf_kib, _ = _pick(f_per, "probe_copy")
-    _, cw_kib, _ = _pick(w_per, "probe_copy")
+    _, cf_kib, _ = _pick(f_per, copy_kernel)
+    _, cw_kib, _ = _pick(w_per, copy_kernel)
     f_scale = copy_bytes / (cf_kib * 1024.0)  # true bytes per counted byte (reads)
     w_scale = copy_bytes / (cw_kib * 1024.0)  # (writes)
     rd = f_kib * 1024.0 * f_scale
@@ -82,7 +82,7 @@ def traffic(fetch_csv, write_csv, kernel, copy_bytes, source, bytes_per_launch, 
         sha = hashlib.sha256(fh.read()).hexdigest()
     lines = [
         "# HBM traffic per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE (KiB per dispatch),",
-        "# each scaled by the same counter's reading for probe_copy moving copy_bytes",
+        f"# each scaled by the same counter's reading for {copy_kernel} moving copy_bytes",
         f"# command (fetch pass): {command.replace('PMC', 'FETCH_SIZE')}",
         f"# command (write pass): {command.replace('PMC', 'WRITE_SIZE')}",
         f"kernel = {kname.split('(')[0]}",
@@ -153,6 +153,8 @@ def main(argv=None) -> int:
     t.add_argument("--bytes-per-launch", type=int, required=True)
     t.add_argument("--command", required=True)
     t.add_argument("--grid", type=int, default=None, help="only dispatches of this grid size")
+    t.add_argument("--copy-kernel", default="probe_copy",
+                   help="substring naming the calibration copy kernel")
     c = sub.add_parser("counters")
     c.add_argument("csv")
     c.add_argument("--kernel", action="append", required=True, help="substring; repeatable")
@@ -164,7 +166,7 @@ def main(argv=None) -> int:
         sys.stdout.write(counters(a.csv, a.kernel, a.command))
     else:
         sys.stdout.write(traffic(a.fetch_csv, a.write_csv, a.kernel, a.copy_bytes, a.source,
-                                 a.bytes_per_launch, a.command, a.grid))
+                                 a.bytes_per_launch, a.command, a.grid, a.copy_kernel))
     return 0
 
 
