@@ -88,7 +88,9 @@ struct DsLds {
 // MFMA operand layout (for one token every lane reads the same 64 bytes).
 // COH: the output is written through to the coherence point shared by all
 // XCDs (it is read by other workgroups of the same launch).
-template <int NMAT, int MT, int WAVES, bool FOLD, bool ASTAGE, int EPI, bool COH>
+// KFULL: K is a multiple of the 128-k stage, so every stage is whole and the
+// clamps and masks of a partial last stage compile away.
+template <int NMAT, int MT, int WAVES, bool FOLD, bool ASTAGE, int EPI, bool COH, bool KFULL = false>
 __device__ __forceinline__ void ds_tile(
     const uint16_t* __restrict__ act,    // [M, K]: x (FOLD) or h
     const uint16_t* __restrict__ gain,   // [K] (FOLD)
@@ -100,6 +102,7 @@ __device__ __forceinline__ void ds_tile(
     int M, int K, int N, float eps, int row0, int row1, int zs, int ze,
     uint4* __restrict__ wbs, uint4* __restrict__ abs_, float* __restrict__ ssqs) {
   constexpr int ST = 16;  // 16-byte chunks per row per stage (128 k)
+  auto cl = [](int v, int hi) { return KFULL ? v : min(v, hi); };
   auto lds_w = [&](int w, int m, int i) -> uint4& { return wbs[(w * NMAT + m) * 256 + i]; };
   auto lds_a = [&](int w, int mt, int i) -> uint4& { return abs_[ASTAGE ? (w * MT + mt) * 256 + i : 0]; };
   auto lds_ssq = [&](int w, int t, int i) -> float& { return ssqs[(w * MT + t) * 16 + i]; };
@@ -176,7 +179,7 @@ __device__ __forceinline__ void ds_tile(
     const int st = st_req < 0 ? se - 1 : st_req;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int c = min(st * ST + cst[u], K8 - 1);
+      const int c = cl(st * ST + cst[u], K8 - 1);
       const unsigned o = st_req < 0 ? kOutOfRange : gw[u] + (unsigned)c * 16u;
 #pragma unroll
       for (int m = 0; m < NMAT; ++m) B.w[m][u] = buf_ld_nt(rw[m], o);
@@ -187,7 +190,7 @@ __device__ __forceinline__ void ds_tile(
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       // staged: chunk cst[u] of token 4u+q; direct: chunk 4u+q of token r
-      const int c = min(st * ST + (ASTAGE ? cst[u] : 4 * u + q), K8 - 1);
+      const int c = cl(st * ST + (ASTAGE ? cst[u] : 4 * u + q), K8 - 1);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) B.a[mt][u] = pa[mt][u][c];
       if (FOLD) B.g[u] = G4[c];  // the gain of the same chunk
@@ -209,7 +212,7 @@ __device__ __forceinline__ void ds_tile(
   // the next prefetch before the MFMAs of this stage run; staged activations
   // go to LDS already multiplied by the gain
   auto stage = [&](const WB& B, const AB& A, int st) {
-    const bool ragged = (st + 1) * ST > K8;  // only the last stage of a row can be partial
+    const bool ragged = !KFULL && (st + 1) * ST > K8;  // only the last stage of a row can be partial
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
 #pragma unroll
@@ -230,7 +233,7 @@ __device__ __forceinline__ void ds_tile(
     }
   };
   auto compute = [&](const AB& A, int st) {
-    const bool ragged = (st + 1) * ST > K8;
+    const bool ragged = !KFULL && (st + 1) * ST > K8;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int slot = rd_base + ((4 * t + q + r) & 15);
@@ -423,7 +426,7 @@ __device__ __forceinline__ void ds_tile(
   }
 }
 
-template <int NMAT, int MT, int WAVES, bool FOLD, bool ASTAGE>
+template <int NMAT, int MT, int WAVES, bool FOLD, bool ASTAGE, bool KFULL>
 __global__ __launch_bounds__(WAVES * 64)
 __attribute__((amdgpu_waves_per_eu(NMAT == 2 && MT == 1 && ASTAGE ? FFN_DS_GU_STAGED_WPE : 1)))
 void decode_stream(
@@ -442,7 +445,7 @@ void decode_stream(
   // (G >= N / 16), as even a share of the rows as the grid allows
   const int row0 = (int)(((long)blockIdx.x * N) / gridDim.x);
   const int row1 = (int)(((long)(blockIdx.x + 1) * N) / gridDim.x);
-  ds_tile<NMAT, MT, WAVES, FOLD, ASTAGE, NMAT == 2 ? DS_EPI_GATEUP : DS_EPI_DOWN, false>(
+  ds_tile<NMAT, MT, WAVES, FOLD, ASTAGE, NMAT == 2 ? DS_EPI_GATEUP : DS_EPI_DOWN, false, KFULL>(
       act, gain, w0, w1, resid, out, nullptr, M, K, N, eps, row0, row1, 0, -1, wb, ab, ssq);
 }
 
@@ -462,11 +465,11 @@ int decode_max_tokens() { return 64; }
 #define FFN_DS_BALANCE 1
 #endif
 
-template <int NMAT, int MT, int WAVES, bool FOLD, bool ASTAGE>
+template <int NMAT, int MT, int WAVES, bool FOLD, bool ASTAGE, bool KFULL>
 static void launch_one(const uint16_t* a, const uint16_t* gg, const uint16_t* p0,
                        const uint16_t* p1, const uint16_t* rr, uint16_t* o, int M, int K, int N,
                        float eps, hipStream_t s) {
-  auto kern = decode_stream<NMAT, MT, WAVES, FOLD, ASTAGE>;
+  auto kern = decode_stream<NMAT, MT, WAVES, FOLD, ASTAGE, KFULL>;
   // the occupancy of a kernel is fixed: computed once (the library assumes
   // every device it runs on is the same model)
   static const int slots = NMAT == 2 ? resident_slots(kern, WAVES * 64) : 0;
@@ -484,12 +487,17 @@ static hipError_t launch_ds(const void* act, const void* gain, const void* w0, c
   const uint16_t* p1 = (const uint16_t*)w1;
   const uint16_t* rr = (const uint16_t*)resid;
   uint16_t* o = (uint16_t*)out;
-  if (M <= 8)
-    launch_one<NMAT, 1, WAVES, FOLD, false>(a, gg, p0, p1, rr, o, M, K, N, eps, s);
-  else if (M <= 16)
-    launch_one<NMAT, 1, WAVES, FOLD, true>(a, gg, p0, p1, rr, o, M, K, N, eps, s);
-  else
-    launch_one<NMAT, 2, WAVES, FOLD, true>(a, gg, p0, p1, rr, o, M, K, N, eps, s);
+  const bool kfull = K % 128 == 0;  // whole 128-k stages
+  if (M <= 8) {
+    if (kfull) launch_one<NMAT, 1, WAVES, FOLD, false, true>(a, gg, p0, p1, rr, o, M, K, N, eps, s);
+    else launch_one<NMAT, 1, WAVES, FOLD, false, false>(a, gg, p0, p1, rr, o, M, K, N, eps, s);
+  } else if (M <= 16) {
+    if (kfull) launch_one<NMAT, 1, WAVES, FOLD, true, true>(a, gg, p0, p1, rr, o, M, K, N, eps, s);
+    else launch_one<NMAT, 1, WAVES, FOLD, true, false>(a, gg, p0, p1, rr, o, M, K, N, eps, s);
+  } else {
+    if (kfull) launch_one<NMAT, 2, WAVES, FOLD, true, true>(a, gg, p0, p1, rr, o, M, K, N, eps, s);
+    else launch_one<NMAT, 2, WAVES, FOLD, true, false>(a, gg, p0, p1, rr, o, M, K, N, eps, s);
+  }
   return hipGetLastError();
 }
 

@@ -112,6 +112,13 @@ void q8_stream(
     float* __restrict__ part,             // [gridDim.y, M, N] (PART)
     int M, int K, int N, float eps) {
   static_assert(!FOLD || (NMAT == 2 && !PART && ASTAGE == 8), "the norm folds into the 8-token gate/up kernel only");
+  // SALIGN is only chosen when K % 256 == 0: every stage is then whole, so
+  // the clamps and masks of a partial last stage compile away (10% fewer
+  // VALU instructions in the folded gate/up kernel; interleaved A/B,
+  // bitwise identical: block 73.8 -> 72.7 us at 8 tokens, 84.1 -> 82.2 at
+  // 16, 165 -> 156 at 32)
+  constexpr bool KFULL = SALIGN;
+  auto cl = [](int v, int hi) { return KFULL ? v : min(v, hi); };
   constexpr int SB = 8;  // 32-quant blocks per stage (256 k, 256 B per row)
   __shared__ uint4 wb[WAVES][NMAT][256];           // per-wave quant stage (4 KiB per matrix)
   __shared__ uint4 abuf[WAVES][ASTAGE ? ASTAGE * 32 : 1];  // per-wave activation stage [rows][32]
@@ -227,7 +234,7 @@ void q8_stream(
     const int st = st_req < 0 ? se - 1 : st_req;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int c = min(st * 16 + cst[u], K16 - 1);
+      const int c = cl(st * 16 + cst[u], K16 - 1);
       const unsigned o = st_req < 0 ? kOutOfRange : gq[u] + (unsigned)c * 16u;
 #pragma unroll
       for (int m = 0; m < NMAT; ++m) B.w[m][u] = buf_ld_nt(rq[m], o);
@@ -236,11 +243,11 @@ void q8_stream(
   auto load_s = [&](Batch& B, int st_req) {
     const int st = st_req < 0 ? se - 1 : st_req;
     if (SALIGN) {
-      const int c = min(st, (nb >> 3) - 1);
+      const int c = cl(st, (nb >> 3) - 1);
 #pragma unroll
       for (int m = 0; m < NMAT; ++m) B.s[m] = buf_ld16(rs[m], srow + (unsigned)c * 16u);
     } else {
-      const int b0 = min(st * SB + 2 * q, nb - 1), b1 = min(st * SB + 2 * q + 1, nb - 1);
+      const int b0 = cl(st * SB + 2 * q, nb - 1), b1 = cl(st * SB + 2 * q + 1, nb - 1);
 #pragma unroll
       for (int m = 0; m < NMAT; ++m)
         B.s[m].x = (uint32_t)ps[m][b0] | ((uint32_t)ps[m][b1] << 16);
@@ -254,13 +261,13 @@ void q8_stream(
         // row 2v + (lane>>5): chunk (lane&31 - row) & 31 of its stage
         // segment, or chunk lane & 31 when folding
         const int c = FOLD ? (lane & 31) : ((lane & 31) - (2 * v + (lane >> 5))) & 31;
-        B.a[v] = buf_ld16(ra, aro[ASTAGE ? v : 0] + (unsigned)min(st * 32 + c, K8 - 1) * 16u);
+        B.a[v] = buf_ld16(ra, aro[ASTAGE ? v : 0] + (unsigned)cl(st * 32 + c, K8 - 1) * 16u);
       }
-      if (FOLD) B.g = G4[min(st * 32 + (lane & 31), K8 - 1)];
+      if (FOLD) B.g = G4[cl(st * 32 + (lane & 31), K8 - 1)];
     } else {
 #pragma unroll
       for (int b = 0; b < SB; ++b) {
-        const int c = min(st * SB + b, nb - 1) * 4 + q;
+        const int c = cl(st * SB + b, nb - 1) * 4 + q;
 #pragma unroll
         for (int t = 0; t < MT; ++t) B.a[b * MT + t] = pa[t][c];
       }
@@ -273,7 +280,7 @@ void q8_stream(
   };
   // the quants (W) and the staged activations (A) of a stage go to LDS
   auto stage = [&](const Batch& W, const Batch& B, int st) {
-    const bool ragged = (st + 1) * SB > nb;  // only a row's last stage can be partial
+    const bool ragged = !KFULL && (st + 1) * SB > nb;  // only a row's last stage can be partial
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
 #pragma unroll
@@ -304,7 +311,7 @@ void q8_stream(
   // the MFMAs and scale FMAs of a stage: W supplies the scales, B the direct
   // activations (ASTAGE == 0)
   auto compute = [&](const Batch& W, const Batch& B, int st) {
-    const bool ragged = (st + 1) * SB > nb;
+    const bool ragged = !KFULL && (st + 1) * SB > nb;
     // per block: the MFMAs of a group of blocks first, then their scale FMAs,
     // so the FMAs do not wait on each MFMA in turn
     constexpr int GB = NMAT == 2 && ASTAGE == 8 && !FOLD ? FFN_Q8_GU8_GB : 4;
