@@ -168,11 +168,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16(
       for (int i = CW; i < CH; ++i) {
         float xf[8];
         unpack8(pre[i], xf);
+        ssq[FOLD ? i - CW : 0] = sumsq8(pre[i], ssq[FOLD ? i - CW : 0]);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          ssq[FOLD ? i - CW : 0] = __builtin_fmaf(xf[e], xf[e], ssq[FOLD ? i - CW : 0]);
-          xf[e] *= gf[e];
-        }
+        for (int e = 0; e < 8; ++e) xf[e] *= gf[e];
         pre[i] = pack8(xf);
       }
     }

@@ -214,11 +214,9 @@ void q8_stream(
     float xf[8], gf[8];
     unpack8(xa, xf);
     unpack8(gv, gf);
+    s2 = sumsq8(xa, s2);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      s2 = __builtin_fmaf(xf[e], xf[e], s2);
-      xf[e] *= gf[e];
-    }
+    for (int e = 0; e < 8; ++e) xf[e] *= gf[e];
     return pack8(xf);
   };
 
