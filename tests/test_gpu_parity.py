@@ -709,3 +709,48 @@ def test_prepared_quant_call_matches_wrapper(gpu_lib, kind):
     call()
     torch.cuda.synchronize()
     assert torch.equal(y, ref)
+
+
+# ----------------------------------------------------------------------------
+# balanced row ranges: gate/up grids that fill one round of resident
+# workgroups give each workgroup an equal share (< 16) of the rows, so row
+# ranges start at arbitrary rows and the epilogues store element by element
+# at unaligned edges.  On MI355X (256 CUs) these shapes take that path: the
+# bf16 16-token kernel holds 3 workgroups per CU (768 slots; f = 8192 is 512
+# tiles), the Q8_0 / Q4_0 8-token kernels 2 (512 slots; f = 6144 is 384).
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("M,d,f", [(16, 512, 8192), (12, 264, 8200), (3, 520, 12296)])
+def test_block_decode_balanced_row_ranges(gpu_lib, M, d, f):
+    from transformer_ffn_block_amd import ffn
+    _say("decode balanced", M, d, f)
+    b = I.make_block(3200 + M, M, d, f, "bf16")
+    r = O.block_from_stored("bf16", b.x, b.g, b.w_gate, b.w_up, b.w_down, b.eps)
+    err = max_norm_err(host_f64(_run_block(ffn, b, "auto")), r)
+    assert record(f"decode balanced rows {M}x{d}x{f}", err, TOL_BF16) <= TOL_BF16
+
+
+@pytest.mark.parametrize("kind", ["q8", "q4"])
+@pytest.mark.parametrize("M,d,f", [(8, 512, 6144), (5, 256, 7680), (16, 256, 6144)])
+def test_quant_balanced_row_ranges(gpu_lib, kind, M, d, f):
+    from transformer_ffn_block_amd import ffn
+    _say("quant balanced", kind, M, d, f)
+    if kind == "q8":
+        q = I.make_q8_block(3300 + M, M, d, f)
+        err, tol = max_norm_err(_run_q8(ffn, q), _q8_ref(q)), TOL_Q8
+    else:
+        q = I.make_q4_block(3400 + M, M, d, f)
+        err, tol = max_norm_err(_run_q4(ffn, q), _q4_ref(q)), TOL_Q4
+    assert record(f"{kind} balanced rows {M}x{d}x{f}", err, tol) <= tol
+
+
+def test_fused_norm_at_decode_sizes_is_auto(gpu_lib):
+    """Up to 64 tokens FUSED_NORM takes the decode kernels, which fold the
+    norm already: the same bits as AUTO."""
+    from transformer_ffn_block_amd import ffn
+    import torch
+    b = I.make_block(3500, 40, 512, 704, "bf16")
+    x, g, wg, wu, wd = _block_dev(b)
+    ya = ffn.swiglu_block(x, g, wg, wu, wd, b.eps, variant="auto")
+    yn = ffn.swiglu_block(x, g, wg, wu, wd, b.eps, variant="fused_norm")
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(ya), host_bits(yn))
