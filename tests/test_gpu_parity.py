@@ -754,3 +754,88 @@ def test_fused_norm_at_decode_sizes_is_auto(gpu_lib):
     yn = ffn.swiglu_block(x, g, wg, wu, wd, b.eps, variant="fused_norm")
     torch.cuda.synchronize()
     assert np.array_equal(host_bits(ya), host_bits(yn))
+
+
+# ----------------------------------------------------------------------------
+# maximum sizes: weight matrices just under the 2 GiB the ABI takes (32-bit
+# buffer offsets).  The oracle cannot run these whole, so the checks use
+# properties that fix the result at any size: W_down = 0 returns x bit for
+# bit, and a one-hot W_down picks one column j of h, which the oracle
+# computes from two weight rows (y[:, i] = x[:, i] + h[:, j], every other
+# column y = x).  Weights are drawn on the device from a seeded generator
+# (N(0, 0.02) as elsewhere); the rows the oracle needs are copied back.
+# ----------------------------------------------------------------------------
+def _big_normal(shape, seed, std=0.02):
+    import torch
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(seed)
+    return (torch.randn(shape, generator=gen, device="cuda", dtype=torch.float32) * std).to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("M,variant", [(4, "auto"), (300, "fused")])
+def test_block_max_size_one_hot_down(gpu_lib, M, variant):
+    from transformer_ffn_block_amd import ffn
+    import torch
+    d, f = 16384, 65528            # f * d * 2 = 2147221504 < 2^31 bytes
+    assert f * d * 2 < 2 ** 31 and (f + 8) * d * 2 >= 2 ** 31
+    _say("max size", M, d, f, variant)
+    b = I.make_block(3600 + M, M, d, 8, "bf16")   # x, g drawn as elsewhere (weights below)
+    x, g = dev(b.x), dev(b.g)
+    wg = _big_normal((f, d), 3601)
+    wu = _big_normal((f, d), 3602)
+    wd = torch.zeros((d, f), dtype=torch.bfloat16, device="cuda")
+    y0 = ffn.swiglu_block(x, g, wg, wu, wd, b.eps, variant=variant)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(y0), b.x)          # W_down = 0: y = x exactly
+    i, j = 12345, f - 3                                 # output column i reads h column j
+    wd[i, j] = 1.0
+    y1 = ffn.swiglu_block(x, g, wg, wu, wd, b.eps, variant=variant)
+    torch.cuda.synchronize()
+    a = host_f64(y1)
+    others = np.ones(d, bool)
+    others[i] = False
+    assert np.array_equal(host_bits(y1)[:, others], b.x[:, others])
+    rows = [host_bits(t[j:j + 1].contiguous()) for t in (wg, wu)]
+    n = O.rmsnorm_from_stored("bf16", b.x, b.g, b.eps)
+    G = n @ O.bf16_to_f64(rows[0][0])
+    U = n @ O.bf16_to_f64(rows[1][0])
+    want = O.bf16_to_f64(b.x[:, i]) + O.silu(G) * U
+    err = float(np.max(np.abs(a[:, i] - want)) / np.max(np.abs(want)))
+    assert record(f"max size {M}x{d}x{f} {variant} (one-hot down column)", err, TOL_BF16) <= TOL_BF16
+
+
+def test_q8_max_size_zero_down_and_one_hot(gpu_lib):
+    from transformer_ffn_block_amd import ffn
+    import torch
+    M, d, f = 8, 16384, 131040     # f * d = 2147155968 < 2^31 quant bytes
+    assert f * d < 2 ** 31 and (f + 32) * d >= 2 ** 31
+    _say("q8 max size", M, d, f)
+    q = I.make_q8_block(3700, M, d, 32)             # x, g (small weights unused)
+    x, g = dev(q.x), dev(q.g)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(3701)
+
+    def qmat(N, K):
+        qs = torch.randint(-127, 128, (N, K), generator=gen, device="cuda", dtype=torch.int8)
+        sc = (torch.randn((N, K // 32), generator=gen, device="cuda").abs() * (0.02 / 127 * 4)).half()
+        return qs, sc.view(torch.int16)
+    wg, wu = qmat(f, d), qmat(f, d)
+    wd = (torch.zeros((d, f), dtype=torch.int8, device="cuda"),
+          torch.zeros((d, f // 32), dtype=torch.int16, device="cuda"))
+    y0 = ffn.swiglu_block_q8(x, g, wg, wu, wd, q.eps)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(y0), q.x)
+    i, j = 777, 100003
+    wd[0][i, j] = 1
+    wd[1][i, j // 32] = 0x3C00                          # fp16 1.0: weight (i, j) = 1
+    y1 = ffn.swiglu_block_q8(x, g, wg, wu, wd, q.eps)
+    torch.cuda.synchronize()
+    a = host_f64(y1)
+    others = np.ones(d, bool)
+    others[i] = False
+    assert np.array_equal(host_bits(y1)[:, others], q.x[:, others])
+    row = lambda m: O.q8_dequant(m[0][j:j + 1].cpu().numpy(), m[1][j:j + 1].cpu().numpy().view(np.uint16))[0]
+    n = O.rmsnorm_from_stored("bf16", q.x, q.g, q.eps)
+    want = O.bf16_to_f64(q.x[:, i]) + O.silu(n @ row(wg)) * (n @ row(wu))
+    err = float(np.max(np.abs(a[:, i] - want)) / np.max(np.abs(want)))
+    assert record(f"q8 max size {M}x{d}x{f} (one-hot down column)", err, TOL_Q8) <= TOL_Q8
