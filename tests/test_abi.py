@@ -111,6 +111,14 @@ def test_workspace_sizes(L):
     split = L.ffn_swiglu_block_workspace_size(ffn.FFN_BF16, M, d, f, 2)
     assert fused == r256(M * d * 2) + r256(M * f * 2)
     assert split == fused + 2 * r256(M * f * 2)
+    # bf16 decode regime (M <= 64, fused schedule): h in the decode kernels'
+    # blocked layout, whole 16-token tiles of ceil(f / 128) 128-k stages;
+    # SPLIT and prefill keep h row-major [M, f]
+    for m, ff in ((1, 11008), (20, 704), (64, 1000)):
+        blk = ((m + 15) // 16 * 16) * ((ff + 127) // 128 * 128) * 2
+        assert L.ffn_swiglu_block_workspace_size(ffn.FFN_BF16, m, d, ff, 0) == r256(m * d * 2) + r256(blk)
+        assert L.ffn_swiglu_block_workspace_size(ffn.FFN_BF16, m, d, ff, 2) == r256(m * d * 2) + 3 * r256(m * ff * 2)
+    assert L.ffn_swiglu_block_workspace_size(ffn.FFN_BF16, 65, d, 704, 0) == r256(65 * d * 2) + r256(65 * 704 * 2)
     assert L.ffn_swiglu_block_workspace_size(ffn.FFN_F32, 8, 256, 704, 0) == r256(8 * 256 * 4) + r256(8 * 704 * 4)
     assert L.ffn_swiglu_block_workspace_size(5, M, d, f, 0) == 0
     # persistent: plus [S, M, d] fp32 partials and 2 + S + d/16 counter words

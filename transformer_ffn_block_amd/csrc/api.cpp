@@ -125,13 +125,26 @@ struct WsLayout {
   size_t n = 0, h = 0, G = 0, U = 0, part = 0, ctr = 0, total = 0;
 };
 
+// The decode regime (bf16, fused schedule, M <= decode_max_tokens()) keeps h
+// in the decode kernels' blocked layout: whole 16-token tiles of ceil(f/128)
+// 128-k stages each.
+bool decode_regime(size_t es, int64_t M, bool split, bool persistent) {
+  return es == 2 && !split && !persistent && M <= ffn::decode_max_tokens();
+}
+size_t decode_h_row_elems(int64_t f) {  // elements per token of blocked h
+  return ffn::decode_h_blocked() ? (size_t)((f + 127) / 128) * 128 : (size_t)f;
+}
+
 WsLayout ws_layout(size_t es, int64_t M, int64_t d, int64_t f, bool split, bool persistent = false) {
   WsLayout w;
   size_t at = 0;
   w.n = at;
   at += round256((size_t)M * d * es);
   w.h = at;
-  at += round256((size_t)M * f * es);
+  if (decode_regime(es, M, split, persistent) && ffn::decode_h_blocked())
+    at += round256((size_t)((M + 15) / 16) * 16 * decode_h_row_elems(f) * es);
+  else
+    at += round256((size_t)M * f * es);
   if (split) {
     w.G = at;
     at += round256((size_t)M * f * es);
@@ -289,7 +302,7 @@ ffn_status ffn_swiglu_block(ffn_dtype dt, const void* x, const void* g, const vo
                                              (unsigned*)(ws + L.ctr), y, Mi, di, fi, eps, s));
     return ok();
   }
-  const bool decode = dt == FFN_BF16 && !split && Mi <= ffn::decode_max_tokens();
+  const bool decode = decode_regime(es, M, split, false);
   // prefill with the norm folded into the fused gate/up GEMM
   const bool fold_prefill = dt == FFN_BF16 && variant == FFN_VARIANT_FUSED_NORM && !decode;
   if (!decode && !fold_prefill) FFN_LAUNCH("rmsnorm", s, ffn::launch_rmsnorm((int)es, x, g, n, M, d, eps, s));
@@ -327,14 +340,16 @@ ffn_status ffn_swiglu_block(ffn_dtype dt, const void* x, const void* g, const vo
   }
   // decode regime: launches of at most decode_chunk_tokens() tokens; the norm
   // is folded into the gate/up kernel, so n is never materialised
+  // (every chunk but the last is a whole number of 16-token tiles)
   const int step = ffn::decode_chunk_tokens();
+  const bool hblk = decode && ffn::decode_h_blocked();
   for (int m0 = 0; m0 < Mi; m0 += step) {
     const int mc = Mi - m0 < step ? Mi - m0 : step;
     const char* xc = (const char*)x + (size_t)m0 * d * es;
-    char* hc = (char*)h + (size_t)m0 * f * es;
+    char* hc = (char*)h + (size_t)m0 * (hblk ? decode_h_row_elems(f) : (size_t)f) * es;
     if (decode)
       FFN_LAUNCH("decode_gateup", s, ffn::launch_decode_gateup_norm(xc, g, w_gate, w_up, hc, mc, di, fi, eps, s));
-    FFN_LAUNCH("decode_down", s, ffn::launch_decode_down(hc, w_down, xc, (char*)y + (size_t)m0 * d * es, mc, di, fi, s));
+    FFN_LAUNCH("decode_down", s, ffn::launch_decode_down(hc, w_down, xc, (char*)y + (size_t)m0 * d * es, mc, di, fi, hblk, s));
   }
   return ok();
 }

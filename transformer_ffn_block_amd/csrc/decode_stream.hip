@@ -41,7 +41,13 @@
 //    counts): past the slice end the weight loads get an out-of-range buffer
 //    offset, which returns zeros without touching memory;
 //  * the W partial tiles (and partial sums of squares) are reduced in a fixed
-//    order through LDS: deterministic, no atomics.
+//    order through LDS: deterministic, no atomics;
+//  * h, which only these two kernels see, is kept in the down projection's
+//    MFMA operand order (blocked layout below): the gate/up epilogue scatters
+//    its 8-byte groups there, and the down kernel reads each 32-k operand of
+//    16 tokens as one contiguous 1 KiB wave load straight into registers, with
+//    no LDS stage for the activations (down projection at 16 tokens 19.2 ->
+//    18.6 us, bitwise identical to the row-major form).
 #include "common.h"
 #include "launch.h"
 
@@ -67,6 +73,19 @@ __device__ __forceinline__ void coh_st8(void* p, uint32_t lo, uint32_t hi) {
                      __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Blocked layout of h for the decode kernels: token tile T (16 tokens), 128-k
+// stage S, 32-k step t, 8-k group q, token r of the tile, 8 values, i.e.
+// element ((((T * nst + S) * 4 + t) * 64 + q * 16 + r) * 8 + e) holds
+// h[16 T + r, 128 S + 32 t + 8 q + e], nst = ceil(f / 128).  The 64 lanes
+// (r, q) of a wave then read the 16-byte MFMA B-operand fragments of one
+// 32-k step as one contiguous 1 KiB.  A buffer of T token tiles takes
+// T * 16 * nst * 128 elements; slots of tokens past M or columns past f are
+// never written and never used unmasked.
+__device__ __forceinline__ size_t hblk_index(int tok, int col, int nst) {
+  return ((((size_t)(tok >> 4) * nst + (col >> 7)) * 4 + ((col >> 5) & 3)) * 64 + ((col >> 3) & 3) * 16 +
+          (tok & 15)) * 8 + (col & 7);
+}
+
 // Epilogue of a tile: gate/up (h = silu(G) * U, with the folded norm),
 // down (y = x + acc) or an fp32 partial tile of a split reduction axis.
 enum { DS_EPI_GATEUP = 0, DS_EPI_DOWN = 1, DS_EPI_PARTIAL = 2 };
@@ -90,7 +109,10 @@ struct DsLds {
 // XCDs (it is read by other workgroups of the same launch).
 // KFULL: K is a multiple of the 128-k stage, so every stage is whole and the
 // clamps and masks of a partial last stage compile away.
-template <int NMAT, int MT, int WAVES, bool FOLD, bool ASTAGE, int EPI, bool COH, bool KFULL = false>
+// HBLK: h is in the blocked layout (hblk_index): the gate/up epilogue writes
+// it so, and a down tile reads it directly (requires !ASTAGE).
+template <int NMAT, int MT, int WAVES, bool FOLD, bool ASTAGE, int EPI, bool COH, bool KFULL = false,
+          bool HBLK = false>
 __device__ __forceinline__ void ds_tile(
     const uint16_t* __restrict__ act,    // [M, K]: x (FOLD) or h
     const uint16_t* __restrict__ gain,   // [K] (FOLD)
@@ -153,6 +175,15 @@ __device__ __forceinline__ void ds_tile(
       pa[t][u] = reinterpret_cast<const uint4*>(act) + (size_t)min(tok, M - 1) * K8;
     }
   const uint4* G4 = reinterpret_cast<const uint4*>(gain);
+  // blocked h: this lane's fragment of token tile mt (tokens past M repeat
+  // token M-1, as above), in 16-byte units, before the stage and step terms
+  static_assert(!HBLK || (!COH && (EPI == DS_EPI_GATEUP || (EPI == DS_EPI_DOWN && !ASTAGE))),
+                "blocked h: written by a gate/up tile, read directly by a down tile");
+  const uint4* H4 = reinterpret_cast<const uint4*>(act);
+  size_t hb[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t)
+    hb[t] = (size_t)t * nst * 256 + q * 16 + (min(t * 16 + r, M - 1) & 15);
 
   f32x4 acc[NMAT][MT];
   // sums of squares of x: direct layout, token r of tile t (ss[t][0]);
@@ -191,8 +222,13 @@ __device__ __forceinline__ void ds_tile(
     for (int u = 0; u < 4; ++u) {
       // staged: chunk cst[u] of token 4u+q; direct: chunk 4u+q of token r
       const int c = cl(st * ST + (ASTAGE ? cst[u] : 4 * u + q), K8 - 1);
+      if (HBLK && EPI == DS_EPI_DOWN) {
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) B.a[mt][u] = pa[mt][u][c];
+        for (int mt = 0; mt < MT; ++mt) B.a[mt][u] = H4[hb[mt] + (size_t)(st * 4 + u) * 64];
+      } else {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) B.a[mt][u] = pa[mt][u][c];
+      }
       if (FOLD) B.g[u] = G4[c];  // the gain of the same chunk
     }
   };
@@ -408,7 +444,21 @@ __device__ __forceinline__ void ds_tile(
       uint2 o;
       o.x = pack_bf16x2(v0[0], v0[1]);
       o.y = pack_bf16x2(v0[2], v0[3]);
-      if (COH) {
+      if (HBLK && NMAT == 2) {
+        // blocked h: four columns starting at a multiple of 4 share one
+        // 8-byte group; otherwise element by element
+        const int nstN = (N + 127) >> 7;
+        if (col + 4 <= row1 && (col & 3) == 0) {
+          *reinterpret_cast<uint2*>(out + hblk_index(tok, col, nstN)) = o;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (e < nc) {
+              const uint32_t w = e < 2 ? o.x : o.y;
+              out[hblk_index(tok, col + e, nstN)] = (uint16_t)(e & 1 ? w >> 16 : w & 0xFFFFu);
+            }
+        }
+      } else if (COH) {
         coh_st8(out + off, o.x, o.y);
       } else if (whole) {
         *reinterpret_cast<uint2*>(out + off) = o;
@@ -424,7 +474,7 @@ __device__ __forceinline__ void ds_tile(
   }
 }
 
-template <int NMAT, int MT, int WAVES, bool FOLD, bool ASTAGE, bool KFULL>
+template <int NMAT, int MT, int WAVES, bool FOLD, bool ASTAGE, bool KFULL, bool HBLK>
 __global__ __launch_bounds__(WAVES * 64)
 __attribute__((amdgpu_waves_per_eu(NMAT == 2 && MT == 1 && ASTAGE ? FFN_DS_GU_STAGED_WPE : 1)))
 void decode_stream(
@@ -443,7 +493,7 @@ void decode_stream(
   // (G >= N / 16), as even a share of the rows as the grid allows
   const int row0 = (int)(((long)blockIdx.x * N) / gridDim.x);
   const int row1 = (int)(((long)(blockIdx.x + 1) * N) / gridDim.x);
-  ds_tile<NMAT, MT, WAVES, FOLD, ASTAGE, NMAT == 2 ? DS_EPI_GATEUP : DS_EPI_DOWN, false, KFULL>(
+  ds_tile<NMAT, MT, WAVES, FOLD, ASTAGE, NMAT == 2 ? DS_EPI_GATEUP : DS_EPI_DOWN, false, KFULL, HBLK>(
       act, gain, w0, w1, resid, out, nullptr, M, K, N, eps, row0, row1, 0, -1, wb, ab, ssq);
 }
 
@@ -463,11 +513,11 @@ int decode_max_tokens() { return 64; }
 #define FFN_DS_BALANCE 1
 #endif
 
-template <int NMAT, int MT, int WAVES, bool FOLD, bool ASTAGE, bool KFULL>
+template <int NMAT, int MT, int WAVES, bool FOLD, bool ASTAGE, bool KFULL, bool HBLK>
 static void launch_one(const uint16_t* a, const uint16_t* gg, const uint16_t* p0,
                        const uint16_t* p1, const uint16_t* rr, uint16_t* o, int M, int K, int N,
                        float eps, hipStream_t s) {
-  auto kern = decode_stream<NMAT, MT, WAVES, FOLD, ASTAGE, KFULL>;
+  auto kern = decode_stream<NMAT, MT, WAVES, FOLD, ASTAGE, KFULL, HBLK>;
   // the occupancy of a kernel is fixed: computed once (the library assumes
   // every device it runs on is the same model)
   static const int slots = NMAT == 2 ? resident_slots(kern, WAVES * 64) : 0;
@@ -475,9 +525,39 @@ static void launch_one(const uint16_t* a, const uint16_t* gg, const uint16_t* p0
   FFN_DISPATCH(kern, dim3((unsigned)groups), dim3(WAVES * 64), 0, s, a, gg, p0, p1, rr, o, M, K, N, eps);
 }
 
+// Blocked h (see hblk_index) between the decode gate/up and down kernels;
+// FFN_DS_HBLK 0 keeps h row-major (the down kernel then stages 9..32-token
+// activations through LDS).
+#ifndef FFN_DS_HBLK
+#define FFN_DS_HBLK 1
+#endif
+
+int decode_h_blocked() { return FFN_DS_HBLK; }
+
+template <int NMAT, int MT, int WAVES, bool FOLD, bool ASTAGE, bool HBLK>
+static void launch_k(const uint16_t* a, const uint16_t* gg, const uint16_t* p0, const uint16_t* p1,
+                     const uint16_t* rr, uint16_t* o, int M, int K, int N, float eps, hipStream_t s) {
+  if (K % 128 == 0)  // whole 128-k stages
+    launch_one<NMAT, MT, WAVES, FOLD, ASTAGE, true, HBLK>(a, gg, p0, p1, rr, o, M, K, N, eps, s);
+  else
+    launch_one<NMAT, MT, WAVES, FOLD, ASTAGE, false, HBLK>(a, gg, p0, p1, rr, o, M, K, N, eps, s);
+}
+
+// Token-count dispatch: activations read directly for up to 8 tokens and
+// staged through LDS for 9..16 (one token tile) and 17..32 (two).
+template <int NMAT, int WAVES, bool FOLD, bool HBLK>
+static void launch_by_m(const uint16_t* a, const uint16_t* gg, const uint16_t* p0, const uint16_t* p1,
+                        const uint16_t* rr, uint16_t* o, int M, int K, int N, float eps, hipStream_t s) {
+  if (M <= 8) launch_k<NMAT, 1, WAVES, FOLD, false, HBLK>(a, gg, p0, p1, rr, o, M, K, N, eps, s);
+  else if (M <= 16) launch_k<NMAT, 1, WAVES, FOLD, true, HBLK>(a, gg, p0, p1, rr, o, M, K, N, eps, s);
+  else launch_k<NMAT, 2, WAVES, FOLD, true, HBLK>(a, gg, p0, p1, rr, o, M, K, N, eps, s);
+}
+
+// hblk: a gate/up kernel writes h blocked; a down kernel reads blocked h,
+// directly at every token count.
 template <int NMAT, int WAVES, bool FOLD>
 static hipError_t launch_ds(const void* act, const void* gain, const void* w0, const void* w1,
-                            const void* resid, void* out, int M, int K, int N, float eps,
+                            const void* resid, void* out, int M, int K, int N, float eps, bool hblk,
                             hipStream_t s) {
   const uint16_t* a = (const uint16_t*)act;
   const uint16_t* gg = (const uint16_t*)gain;
@@ -485,28 +565,25 @@ static hipError_t launch_ds(const void* act, const void* gain, const void* w0, c
   const uint16_t* p1 = (const uint16_t*)w1;
   const uint16_t* rr = (const uint16_t*)resid;
   uint16_t* o = (uint16_t*)out;
-  const bool kfull = K % 128 == 0;  // whole 128-k stages
-  if (M <= 8) {
-    if (kfull) launch_one<NMAT, 1, WAVES, FOLD, false, true>(a, gg, p0, p1, rr, o, M, K, N, eps, s);
-    else launch_one<NMAT, 1, WAVES, FOLD, false, false>(a, gg, p0, p1, rr, o, M, K, N, eps, s);
-  } else if (M <= 16) {
-    if (kfull) launch_one<NMAT, 1, WAVES, FOLD, true, true>(a, gg, p0, p1, rr, o, M, K, N, eps, s);
-    else launch_one<NMAT, 1, WAVES, FOLD, true, false>(a, gg, p0, p1, rr, o, M, K, N, eps, s);
+  if constexpr (NMAT == 1) {
+    if (!hblk) launch_by_m<NMAT, WAVES, FOLD, false>(a, gg, p0, p1, rr, o, M, K, N, eps, s);
+    else if (M <= 16) launch_k<NMAT, 1, WAVES, FOLD, false, true>(a, gg, p0, p1, rr, o, M, K, N, eps, s);
+    else launch_k<NMAT, 2, WAVES, FOLD, false, true>(a, gg, p0, p1, rr, o, M, K, N, eps, s);
   } else {
-    if (kfull) launch_one<NMAT, 2, WAVES, FOLD, true, true>(a, gg, p0, p1, rr, o, M, K, N, eps, s);
-    else launch_one<NMAT, 2, WAVES, FOLD, true, false>(a, gg, p0, p1, rr, o, M, K, N, eps, s);
+    if (hblk) launch_by_m<NMAT, WAVES, FOLD, true>(a, gg, p0, p1, rr, o, M, K, N, eps, s);
+    else launch_by_m<NMAT, WAVES, FOLD, false>(a, gg, p0, p1, rr, o, M, K, N, eps, s);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_decode_gateup_norm(const void* x, const void* g, const void* wg, const void* wu,
                                      void* h, int M, int d, int f, float eps, hipStream_t s) {
-  return launch_ds<2, FFN_DS_GU_WAVES, true>(x, g, wg, wu, nullptr, h, M, d, f, eps, s);
+  return launch_ds<2, FFN_DS_GU_WAVES, true>(x, g, wg, wu, nullptr, h, M, d, f, eps, FFN_DS_HBLK != 0, s);
 }
 
 hipError_t launch_decode_down(const void* h, const void* wd, const void* x, void* y, int M,
-                              int d, int f, hipStream_t s) {
-  return launch_ds<1, FFN_DS_DN_WAVES, false>(h, nullptr, wd, nullptr, x, y, M, f, d, 0.f, s);
+                              int d, int f, bool h_blocked, hipStream_t s) {
+  return launch_ds<1, FFN_DS_DN_WAVES, false>(h, nullptr, wd, nullptr, x, y, M, f, d, 0.f, h_blocked, s);
 }
 
 // ---------------------------------------------------------------------------

@@ -52,8 +52,13 @@ int decode_max_tokens();    // largest M routed to the decode kernels
 int decode_chunk_tokens();  // tokens per decode launch
 hipError_t launch_decode_gateup_norm(const void* x, const void* g, const void* wg, const void* wu,
                                      void* h, int M, int d, int f, float eps, hipStream_t s);
+// 1 if the decode gate/up kernel writes h in the blocked layout (token tile,
+// 128-k stage, MFMA operand order; T token tiles take T * 16 * ceil(f/128) *
+// 128 elements), which the down kernel then reads with h_blocked = true;
+// h from any other producer is row-major [M, f] (h_blocked = false).
+int decode_h_blocked();
 hipError_t launch_decode_down(const void* h, const void* wd, const void* x, void* y,
-                              int M, int d, int f, hipStream_t s);
+                              int M, int d, int f, bool h_blocked, hipStream_t s);
 // Single-dispatch block for 1..16 tokens: gate/up tiles, then (tile, K range)
 // down items in one launch ordered by completion counters (ctr: caller's
 // workspace, cleared by a preceding launch; part: [splits, M, d] fp32).
