@@ -346,6 +346,37 @@ def ceilings(torch, ffn, extra, clocks):
     return best, copy_best, mbest
 
 
+def same_size_reads(torch, ffn, sizes):
+    """The read probe over exactly as many bytes as a kernel streams, kernel
+    duration from the dispatch events (as for the decode kernels), best over
+    waves per CU; four rotated buffers, so the memory-side cache cannot serve
+    them.  A launch this short pays its start-up and drain, which the 4 GiB
+    read ceiling amortises: this is what one launch reading that many bytes
+    achieves, the context for a kernel's fraction of the ceiling."""
+    out = {}
+    sink = torch.empty(16 * ffn.lib().ffn_probe_read_groups(32), dtype=torch.uint8, device="cuda")
+    for name, n in sizes.items():
+        n16 = n // 16 * 16
+        bufs = [torch.empty(n16, dtype=torch.uint8, device="cuda") for _ in range(ROTATE)]
+        for bb in bufs:
+            bb.fill_(1)
+        best = None
+        for wpc in (4, 8, 12, 16, 32):
+            def fn(i, wpc=wpc):
+                ffn.probe_read(bufs[i % ROTATE], sink, wpc)
+            for i in range(8):
+                fn(i)
+            us = kernel_times(ffn, fn, 40)["probe_read"]
+            if best is None or us < best[0]:
+                best = (us, wpc)
+        out[name] = {"bytes": n16, "us": best[0], "GBps": round(n16 / (best[0] * 1e-6) / 1e9, 1),
+                     "waves_per_cu": best[1]}
+        del bufs
+    del sink
+    torch.cuda.empty_cache()
+    return out
+
+
 def extras(torch, np, ffn, I, sets, x, g, b, ws, extra, clocks, want, keep):
     best = copy_gbs = mfma_peak = None  # ceilings, measured when "ceilings" is selected
     M, d, f = b.M, b.d, b.f
@@ -400,11 +431,16 @@ def extras(torch, np, ffn, I, sets, x, g, b, ws, extra, clocks, want, keep):
             if f"decode_M{m}" in extra:
                 extra[f"decode_M{m}"]["frac_of_read_ceiling"] = ratio(extra[f"decode_M{m}"]["GBps"], best)
         kt = extra["decode_kernels_event_timed"]
-        for name, nbytes in (("decode_gateup", gateup_bytes(M, d, f)), ("decode_down", down_bytes(M, d, f))):
+        sizes = {"decode_gateup": gateup_bytes(M, d, f), "decode_down": down_bytes(M, d, f)}
+        same = same_size_reads(torch, ffn, sizes)
+        extra["hbm_read_same_size_as_decode_kernels"] = same
+        log("read probe at the decode kernels' sizes", same)
+        for name, nbytes in sizes.items():
             if name in kt:
                 gbs = nbytes / (kt[name]["avg_us"] * 1e-6) / 1e9
                 kt[name].update(GBps=round(gbs, 1), frac_of_read_ceiling=ratio(gbs, best),
-                                frac_of_hbm_peak=round(gbs / HBM_PEAK_GBS, 4))
+                                frac_of_hbm_peak=round(gbs / HBM_PEAK_GBS, 4),
+                                frac_of_same_size_read=round(same[name]["us"] / kt[name]["avg_us"], 4))
 
     if "rmsnorm" in want:
         # ---------------------------------------------------------------- RMSNorm
