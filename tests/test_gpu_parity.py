@@ -300,6 +300,24 @@ def test_block_prefill_whole_tiles(gpu_lib, M, d, f, variant):
     assert record(f"prefill whole tiles {M}x{d}x{f} {variant}", err, TOL_BF16) <= TOL_BF16
 
 
+@pytest.mark.parametrize("M,d,f", [(512, 256, 16640), (4352, 4096, 128)])
+def test_block_prefill_persistent_tile_walk(gpu_lib, M, d, f):
+    """More whole tiles than resident workgroups: the ping-pong GEMM walks
+    them persistently (one workgroup per slot, tiles b, b + grid, ...), so
+    some workgroups take one tile more than others.  (512, 256, 16640): 260
+    fused gate/up tiles; (4352, 4096, 128): 272 down tiles with the
+    shortest K loop.  Every output against the oracle."""
+    from transformer_ffn_block_amd import ffn
+    _say("block prefill persistent walk", M, d, f)
+    b = I.make_block(900 + M, M, d, f, "bf16")
+    r = O.block_from_stored("bf16", b.x, b.g, b.w_gate, b.w_up, b.w_down, b.eps)
+    a = host_f64(_run_block(ffn, b, "fused"))
+    assert record(f"prefill persistent walk {M}x{d}x{f}", max_norm_err(a, r), TOL_BF16) <= TOL_BF16
+    per_row = max(max_norm_err(a[i], r[i]) for i in range(M))
+    assert record(f"prefill persistent walk {M}x{d}x{f} worst row", per_row, TOL_BF16,
+                  "max_norm_per_row") <= TOL_BF16
+
+
 @pytest.fixture(scope="module")
 def prefill_inputs():
     wl = I.WORKLOADS["prefill"]

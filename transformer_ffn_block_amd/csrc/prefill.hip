@@ -49,8 +49,8 @@
 //    first add, one wait per tile instead of one per 16x16 sub-tile.
 //  * workgroups are dispatched round-robin over the 8 XCDs; tile ids are
 //    remapped so each XCD works on a contiguous range of tiles, grouped 8
-//    token tiles deep, so concurrently running tiles share operands in the
-//    XCD's own L2.
+//    token tiles deep (2 for the down projection), so concurrently running
+//    tiles share operands in the XCD's own L2.
 #include "common.h"
 #include "launch.h"
 
@@ -360,6 +360,26 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16(
 #define FFN_PF_PP 1
 #endif
 constexpr int kDmaBK = FFN_PF_BK, kDmaS = FFN_PF_S;
+// Token tiles per tile group (see the tile coordinates in gemm_dma).  With
+// XCD-contiguous ranges and one workgroup per CU, a round of the whole chip
+// covers every token tile and a few weight tiles when groups are 8 deep:
+// right when the activations fit the 256 MB memory-side cache and the
+// weights are streamed once (fused gate/up: n is 64 MB at M = 8192; 4 / 8
+// deep measured alike, 2 and 16 slower).  The down projection's activations
+// (h, 235 MB at M = 8192, f = 14336) do not fit: with 2-deep groups a round
+// covers half the token tiles and every weight tile, so h is read once and
+// the 117 MB of W_down is what repeats (down GEMM 0.772 -> 0.753 ms,
+// bitwise identical; a mapping that also kept 4 x 8 tile blocks per XCD
+// round measured the same as 2-deep groups).
+#ifndef FFN_PF_GM
+#define FFN_PF_GM 8
+#endif
+#ifndef FFN_PF_PERSIST
+#define FFN_PF_PERSIST 1
+#endif
+#ifndef FFN_PF_GM_RES
+#define FFN_PF_GM_RES 2
+#endif
 #ifndef FFN_PF_PP_BK
 #define FFN_PF_PP_BK 64
 #endif
@@ -386,7 +406,77 @@ __device__ __forceinline__ int dswz(int row) {
   return BK == 64 ? (row & 7) : ((row >> 2) & 3);
 }
 
-template <int BM, int BN, int WM, int WN, int EPI, int BK, int S, bool PP>
+// Epilogue of a gemm_dma tile at (m0, n0): the lane holds D[4*fq + e][fr] of
+// every (a, b) MFMA sub-tile of its wave's (wm, wn) block.
+template <int EPI, int FN, int FM, int TM, int TN>
+__device__ __forceinline__ void dma_epilogue(const f32x4 (&acc)[FN][FM],
+                                             const uint16_t* __restrict__ resid,
+                                             uint16_t* __restrict__ out, int M, int N, int m0,
+                                             int n0, int wm, int wn, int fr, int fq) {
+  if (EPI == EPI_SWIGLU) {
+#pragma unroll
+    for (int a = 0; a < FN / 2; ++a) {
+      const int col = n0 + wn * (TN / 2) + a * 16 + 4 * fq;
+#pragma unroll
+      for (int b = 0; b < FM; ++b) {
+        const int tok = m0 + wm * TM + b * 16 + fr;
+        if (tok < M && col < N) {
+          const f32x4 gg = acc[a][b], uu = acc[a + FN / 2][b];
+          uint2 o;
+          o.x = pack_bf16x2(silu_mul(gg[0], uu[0]), silu_mul(gg[1], uu[1]));
+          o.y = pack_bf16x2(silu_mul(gg[2], uu[2]), silu_mul(gg[3], uu[3]));
+          *reinterpret_cast<uint2*>(out + (size_t)tok * N + col) = o;
+        }
+      }
+    }
+  } else {
+    // residual: every load is issued before the first add (an address
+    // outside the output reads element 0 and is never stored), so the
+    // tile waits for memory once rather than once per sub-tile
+    uint2 xr[FN][FM];
+    if (EPI == EPI_RESIDUAL) {
+#pragma unroll
+      for (int a = 0; a < FN; ++a) {
+        const int col = n0 + wn * TN + a * 16 + 4 * fq;
+#pragma unroll
+        for (int b = 0; b < FM; ++b) {
+          const int tok = m0 + wm * TM + b * 16 + fr;
+          const size_t off = (tok < M && col < N) ? (size_t)tok * N + col : 0;
+          xr[a][b] = *reinterpret_cast<const uint2*>(resid + off);
+        }
+      }
+    }
+#pragma unroll
+    for (int a = 0; a < FN; ++a) {
+      const int col = n0 + wn * TN + a * 16 + 4 * fq;
+#pragma unroll
+      for (int b = 0; b < FM; ++b) {
+        const int tok = m0 + wm * TM + b * 16 + fr;
+        if (tok < M && col < N) {
+          const size_t off = (size_t)tok * N + col;
+          f32x4 v = acc[a][b];
+          if (EPI == EPI_RESIDUAL) {
+            v[0] += bf2f(xr[a][b].x & 0xFFFFu);
+            v[1] += bf2f(xr[a][b].x >> 16);
+            v[2] += bf2f(xr[a][b].y & 0xFFFFu);
+            v[3] += bf2f(xr[a][b].y >> 16);
+          }
+          uint2 o;
+          o.x = pack_bf16x2(v[0], v[1]);
+          o.y = pack_bf16x2(v[2], v[3]);
+          *reinterpret_cast<uint2*>(out + off) = o;
+        }
+      }
+    }
+  }
+}
+
+// PERSIST (ping-pong schedule only): the grid is at most one workgroup per
+// resident slot and each workgroup walks tiles blockIdx.x, + gridDim.x, ...;
+// as soon as a tile's K loop has read its last stage, the first S K tiles
+// of the workgroup's next tile go out, so their latency overlaps the
+// epilogue instead of opening the next tile.
+template <int BM, int BN, int WM, int WN, int EPI, int BK, int S, bool PP, bool PERSIST = false>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_dma(
     const uint16_t* __restrict__ act,    // [M, K]
     const uint16_t* __restrict__ w0,     // [N, K]  (gate for SWIGLU)
@@ -421,19 +511,26 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_dma(
   const int K8 = K >> 3;
   const int nkt = K / BK;
 
-  // ---- tile coordinates: XCD-contiguous, then grouped 8 token tiles deep
+  // ---- tile coordinates: XCD-contiguous, then grouped GM token tiles deep
+  // (a persistent grid is a multiple of 8 workgroups or one per tile, so a
+  // workgroup's tiles stay on its XCD)
+  static_assert(!PERSIST || PP, "the persistent walk uses the ping-pong schedule");
   const int ntm = (M + BM - 1) / BM, ntn = (N + BNO - 1) / BNO;
   const int T = ntm * ntn;
-  int L = blockIdx.x;
-  if ((T & 7) == 0) L = (L & 7) * (T >> 3) + (L >> 3);
-  constexpr int GM = 8;
-  const int group = L / (GM * ntn);
-  const int first_m = group * GM;
-  const int gm = min(ntm - first_m, GM);
-  const int inner = L - group * GM * ntn;
-  const int tm = first_m + inner % gm;
-  const int tn = inner / gm;
-  const int m0 = tm * BM, n0 = tn * BNO;
+  auto coords = [&](int tile, int& m0_, int& n0_) {
+    int L = tile;
+    if ((T & 7) == 0) L = (L & 7) * (T >> 3) + (L >> 3);
+    constexpr int GM = EPI == EPI_RESIDUAL ? FFN_PF_GM_RES : FFN_PF_GM;
+    const int group = L / (GM * ntn);
+    const int first_m = group * GM;
+    const int gm = min(ntm - first_m, GM);
+    const int inner = L - group * GM * ntn;
+    m0_ = (first_m + inner % gm) * BM;
+    n0_ = (inner / gm) * BNO;
+  };
+  int m0i, n0i;
+  coords(blockIdx.x, m0i, n0i);
+  const int m0 = m0i, n0 = n0i;
 
   // ---- load sources: instruction j of this thread fills LDS position
   // p = j*NT + tid = row p / CPR, stored chunk p % CPR, which holds global
@@ -591,10 +688,11 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_dma(
     const int wave_s = __builtin_amdgcn_readfirstlane(wave);
     const int rr = tid / CPR;
     const unsigned cgp = (unsigned)((tid % CPR) ^ dswz<BK>(rr)) * 16u;
-    const unsigned vw = (unsigned)(n0 + rr) * (unsigned)K * 2u + cgp;
-    const unsigned va = (unsigned)(m0 + rr) * (unsigned)K * 2u + cgp;
+    const unsigned vw0 = (unsigned)(n0 + rr) * (unsigned)K * 2u + cgp;
+    const unsigned va0 = (unsigned)(m0 + rr) * (unsigned)K * 2u + cgp;
     const int blk = RJ * K * 2;  // bytes of one load instruction's row block
-    auto issue_pp = [&](int i, int kt) {
+    // vw, va: this lane's weight-row and token-row source offsets of the tile
+    auto issue_pp = [&](int i, int kt, unsigned vw, unsigned va) {
       uint4* Ls = stage(i);
       const int ko = kt * BK * 2;
 #pragma unroll
@@ -609,20 +707,17 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_dma(
         }
       }
     };
-    static_for<S>([&](auto si) { issue_pp(decltype(si)::value, decltype(si)::value); });
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt(0x0F70 | (((S - 1) * J) & 15) | ((((S - 1) * J) >> 4) << 14));  // tile 0
-    bar();
+    static_for<S>([&](auto si) { issue_pp(decltype(si)::value, decltype(si)::value, vw0, va0); });
     // S tiles per iteration keep every stage index a compile-time constant,
     // and no path reaches a read of one stage with a DMA into that same
     // stage pending: the compiler then adds no wait for the DMA before the
     // reads.  body(i, ks, kt): k-step ks of tile kt, in stage i.  The group
     // is a compile-time constant in each copy of the loop.
-    auto run = [&](auto gi) {
+    auto run = [&](auto gi, unsigned vw, unsigned va) {
       constexpr int G = decltype(gi)::value;
       auto body = [&](auto si, auto ki, int kt) {
         constexpr int i = decltype(si)::value, ks = decltype(ki)::value;
-        if (ks == 0 && kt >= 1 && kt + S - 1 < nkt) issue_pp((i + S - 1) % S, kt + S - 1);
+        if (ks == 0 && kt >= 1 && kt + S - 1 < nkt) issue_pp((i + S - 1) % S, kt + S - 1, vw, va);
         readf(i, ks);
         wait_lds();
         if (ks == KS - 1 && G == 1) wait_next(kt);
@@ -638,8 +733,45 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_dma(
         });
       }
     };
-    if (__builtin_amdgcn_readfirstlane(wm) == 0) run(I0);
-    else run(I1);
+    if constexpr (!PERSIST) {
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      __builtin_amdgcn_s_waitcnt(0x0F70 | (((S - 1) * J) & 15) | ((((S - 1) * J) >> 4) << 14));  // tile 0
+      bar();
+      if (__builtin_amdgcn_readfirstlane(wm) == 0) run(I0, vw0, va0);
+      else run(I1, vw0, va0);
+    } else {
+    int pm0 = m0, pn0 = n0;
+    unsigned vw = vw0, va = va0;
+    for (int tile = blockIdx.x;;) {
+      // K tile 0 of this tile has landed (the S - 1 after it and the
+      // previous tile's output stores may still be in flight: loads
+      // complete in order, and at most (S - 1) J operations remain)
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      __builtin_amdgcn_s_waitcnt(0x0F70 | (((S - 1) * J) & 15) | ((((S - 1) * J) >> 4) << 14));
+      bar();
+      if (__builtin_amdgcn_readfirstlane(wm) == 0) run(I0, vw, va);
+      else run(I1, vw, va);
+      // every wave has passed the K loop's last barrier, after which no
+      // stage is read: the next tile's first S K tiles can go out
+      const int next = tile + (int)gridDim.x;
+      int m1 = 0, n1 = 0;
+      if (next < T) {
+        coords(next, m1, n1);
+        vw = (unsigned)(n1 + rr) * (unsigned)K * 2u + cgp;
+        va = (unsigned)(m1 + rr) * (unsigned)K * 2u + cgp;
+        static_for<S>([&](auto si) { issue_pp(decltype(si)::value, decltype(si)::value, vw, va); });
+      }
+      dma_epilogue<EPI, FN, FM, TM, TN>(acc, resid, out, M, N, pm0, pn0, wm, wn, fr, fq);
+      if (next >= T) return;
+#pragma unroll
+      for (int a = 0; a < FN; ++a)
+#pragma unroll
+        for (int b = 0; b < FM; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+      tile = next;
+      pm0 = m1;
+      pn0 = n1;
+    }
+    }
   } else {
 #pragma unroll
   for (int i = 0; i < S - 1; ++i) issue(i, i);
@@ -669,63 +801,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_dma(
   }
   }
 
-  // ---- epilogue: lane holds D[4*fq + e][fr] of every (a, b) sub-tile
-  if (EPI == EPI_SWIGLU) {
-#pragma unroll
-    for (int a = 0; a < FN / 2; ++a) {
-      const int col = n0 + wn * (TN / 2) + a * 16 + 4 * fq;
-#pragma unroll
-      for (int b = 0; b < FM; ++b) {
-        const int tok = m0 + wm * TM + b * 16 + fr;
-        if (tok < M && col < N) {
-          const f32x4 gg = acc[a][b], uu = acc[a + FN / 2][b];
-          uint2 o;
-          o.x = pack_bf16x2(silu_mul(gg[0], uu[0]), silu_mul(gg[1], uu[1]));
-          o.y = pack_bf16x2(silu_mul(gg[2], uu[2]), silu_mul(gg[3], uu[3]));
-          *reinterpret_cast<uint2*>(out + (size_t)tok * N + col) = o;
-        }
-      }
-    }
-  } else {
-    // residual: every load is issued before the first add (an address
-    // outside the output reads element 0 and is never stored), so the
-    // tile waits for memory once rather than once per sub-tile
-    uint2 xr[FN][FM];
-    if (EPI == EPI_RESIDUAL) {
-#pragma unroll
-      for (int a = 0; a < FN; ++a) {
-        const int col = n0 + wn * TN + a * 16 + 4 * fq;
-#pragma unroll
-        for (int b = 0; b < FM; ++b) {
-          const int tok = m0 + wm * TM + b * 16 + fr;
-          const size_t off = (tok < M && col < N) ? (size_t)tok * N + col : 0;
-          xr[a][b] = *reinterpret_cast<const uint2*>(resid + off);
-        }
-      }
-    }
-#pragma unroll
-    for (int a = 0; a < FN; ++a) {
-      const int col = n0 + wn * TN + a * 16 + 4 * fq;
-#pragma unroll
-      for (int b = 0; b < FM; ++b) {
-        const int tok = m0 + wm * TM + b * 16 + fr;
-        if (tok < M && col < N) {
-          const size_t off = (size_t)tok * N + col;
-          f32x4 v = acc[a][b];
-          if (EPI == EPI_RESIDUAL) {
-            v[0] += bf2f(xr[a][b].x & 0xFFFFu);
-            v[1] += bf2f(xr[a][b].x >> 16);
-            v[2] += bf2f(xr[a][b].y & 0xFFFFu);
-            v[3] += bf2f(xr[a][b].y >> 16);
-          }
-          uint2 o;
-          o.x = pack_bf16x2(v[0], v[1]);
-          o.y = pack_bf16x2(v[2], v[3]);
-          *reinterpret_cast<uint2*>(out + off) = o;
-        }
-      }
-    }
-  }
+  dma_epilogue<EPI, FN, FM, TM, TN>(acc, resid, out, M, N, m0, n0, wm, wn, fr, fq);
 }
 
 // Tile configuration: 256 tokens x 256 weight rows, 8 waves as 2 x 4, each
@@ -765,12 +841,20 @@ static hipError_t launch_cfg(const void* act, const void* w0, const void* w1, co
   // whole K tiles and every operand addressable by a buffer resource: LDS-fed kernel
   if (!FFN_PF_FORCE_REG && K % kDmaBK == 0 && (size_t)M * K * 2 < ((size_t)1 << 31) &&
       (size_t)N * K * 2 < ((size_t)1 << 31)) {
-    // whole tiles and an even number of K tiles: the ping-pong schedule
-    if (kPingPong && M % kBM == 0 && N % BNO == 0 && K % (kPpS * kPpBK) == 0)
-      FFN_DISPATCH((gemm_dma<kBM, kBN, kWM, kWN, EPI, kPpBK, kPpS, true>), dim3((unsigned)tiles),
-                         dim3(kWM * kWN * 64), 0, s, (const uint16_t*)act, (const uint16_t*)w0,
-                         (const uint16_t*)w1, (const uint16_t*)resid, (uint16_t*)out, M, N, K);
-    else
+    // whole tiles and an even number of K tiles: the ping-pong schedule,
+    // walked persistently when the tiles take more than one round
+    if (kPingPong && M % kBM == 0 && N % BNO == 0 && K % (kPpS * kPpBK) == 0) {
+      auto pers = gemm_dma<kBM, kBN, kWM, kWN, EPI, kPpBK, kPpS, true, true>;
+      static const int slots = resident_slots(pers, kWM * kWN * 64) / 8 * 8;
+      if (FFN_PF_PERSIST && slots >= 8 && tiles > slots)
+        FFN_DISPATCH(pers, dim3((unsigned)slots), dim3(kWM * kWN * 64), 0, s, (const uint16_t*)act,
+                     (const uint16_t*)w0, (const uint16_t*)w1, (const uint16_t*)resid, (uint16_t*)out, M,
+                     N, K);
+      else
+        FFN_DISPATCH((gemm_dma<kBM, kBN, kWM, kWN, EPI, kPpBK, kPpS, true>), dim3((unsigned)tiles),
+                     dim3(kWM * kWN * 64), 0, s, (const uint16_t*)act, (const uint16_t*)w0,
+                     (const uint16_t*)w1, (const uint16_t*)resid, (uint16_t*)out, M, N, K);
+    } else
       FFN_DISPATCH((gemm_dma<kBM, kBN, kWM, kWN, EPI, kDmaBK, kDmaS, false>), dim3((unsigned)tiles),
                          dim3(kWM * kWN * 64), 0, s, (const uint16_t*)act, (const uint16_t*)w0,
                          (const uint16_t*)w1, (const uint16_t*)resid, (uint16_t*)out, M, N, K);
