@@ -118,10 +118,14 @@ __device__ __forceinline__ float sumsq8(const uint4& v, float acc) {
   return acc;
 }
 
-// silu(v) * u in fp32: v / (1 + e^-v) * u.  For v -> -inf, e^-v overflows to
-// +inf and the quotient is -0, the correct limit.
+// silu(v) * u in fp32: v * (1 / (1 + e^-v)) * u, the reciprocal from
+// v_rcp_f32 (within 1 ulp; the result is rounded to bf16 afterwards) rather
+// than an IEEE division, whose correction sequence made the SwiGLU epilogue
+// of the fused prefill GEMM ~2% of its time (1.400 -> 1.374 ms).  For
+// v -> -inf (finite), e^-v overflows to +inf, its reciprocal is 0 and the
+// product is -0, the correct limit.
 __device__ __forceinline__ float silu_mul(float v, float u) {
-  return v / (1.0f + __expf(-v)) * u;
+  return v * __builtin_amdgcn_rcpf(1.0f + __expf(-v)) * u;
 }
 
 // Sum over the 64 lanes of a wavefront (butterfly, every lane gets the total).
