@@ -57,6 +57,14 @@ struct Chunk<4> {
 };
 
 constexpr int kRowsPerBlock = 4;  // 4 wavefronts, one row each
+// Launches of many rows stream x in and y out with non-temporal (streaming)
+// loads and stores: 16384 x 4096 bf16 50.3 -> 46.9 us (interleaved A/B,
+// bitwise identical; the prefill block, whose GEMM then reads n, unchanged).
+// Launches of a few rows keep plain accesses: their output is read at once
+// by the next kernel.
+#ifndef FFN_RMS_NT
+#define FFN_RMS_NT 1
+#endif
 #ifndef FFN_RMS_PREG_ROWS
 #define FFN_RMS_PREG_ROWS 64
 #endif
@@ -70,6 +78,7 @@ __global__ __launch_bounds__(256) void rmsnorm_cached(const uint4* __restrict__ 
                                                       const uint4* __restrict__ g,
                                                       uint4* __restrict__ y, int64_t rows,
                                                       int nchunk, float inv_d, float eps) {
+  constexpr bool NT = !PREG && FFN_RMS_NT;
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
   if (row >= rows) return;
@@ -78,7 +87,7 @@ __global__ __launch_bounds__(256) void rmsnorm_cached(const uint4* __restrict__ 
 #pragma unroll
   for (int i = 0; i < CACHE; ++i) {
     const int c = lane + 64 * i;
-    v[i] = c < nchunk ? xr[c] : make_uint4(0, 0, 0, 0);
+    v[i] = c < nchunk ? (NT ? ld_nt(xr + c) : xr[c]) : make_uint4(0, 0, 0, 0);
     if (PREG) gv[PREG ? i : 0] = c < nchunk ? g[c] : make_uint4(0, 0, 0, 0);
   }
   float acc = 0.f;
@@ -90,7 +99,7 @@ __global__ __launch_bounds__(256) void rmsnorm_cached(const uint4* __restrict__ 
 #pragma unroll
   for (int i = 0; i < CACHE; ++i) {
     const int c = lane + 64 * i;
-    if (c < nchunk) yr[c] = Chunk<EB>::scale(v[i], PREG ? gv[PREG ? i : 0] : g[c], r);
+    if (c < nchunk) st16<NT>(yr + c, Chunk<EB>::scale(v[i], PREG ? gv[PREG ? i : 0] : g[c], r));
   }
 }
 
