@@ -144,7 +144,12 @@ ffn_status ffn_rmsnorm(ffn_dtype dt, const void *x, const void *g, void *y,
  * shape it would reject).  It holds n [M,d] and h [M,f] (plus G, U [M,f]
  * for SPLIT; for PERSISTENT, fp32 partial sums [S, M, d] and
  * 4 * (2 + S + ceil(d/16)) bytes of counters, S = the schedule's number of
- * K ranges of the down projection, 1 to 8), each 256-byte aligned. */
+ * K ranges of the down projection, 1 to 8), each 256-byte aligned.  For
+ * bf16 with AUTO, FUSED or FUSED_NORM and M <= 64 (the decode kernels) h
+ * takes ceil(M/16) * 16 rows of ceil(f/128) * 128 elements: it is kept in
+ * the down projection's operand order, not row-major.  The workspace's
+ * contents are the library's own between calls; the sizes are what a
+ * caller relies on. */
 size_t ffn_swiglu_block_workspace_size(ffn_dtype dt, int64_t M, int64_t d, int64_t f,
                                        ffn_variant variant);
 
