@@ -740,37 +740,37 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_dma(
       if (__builtin_amdgcn_readfirstlane(wm) == 0) run(I0, vw0, va0);
       else run(I1, vw0, va0);
     } else {
-    int pm0 = m0, pn0 = n0;
-    unsigned vw = vw0, va = va0;
-    for (int tile = blockIdx.x;;) {
-      // K tile 0 of this tile has landed (the S - 1 after it and the
-      // previous tile's output stores may still be in flight: loads
-      // complete in order, and at most (S - 1) J operations remain)
-      __atomic_signal_fence(__ATOMIC_SEQ_CST);
-      __builtin_amdgcn_s_waitcnt(0x0F70 | (((S - 1) * J) & 15) | ((((S - 1) * J) >> 4) << 14));
-      bar();
-      if (__builtin_amdgcn_readfirstlane(wm) == 0) run(I0, vw, va);
-      else run(I1, vw, va);
-      // every wave has passed the K loop's last barrier, after which no
-      // stage is read: the next tile's first S K tiles can go out
-      const int next = tile + (int)gridDim.x;
-      int m1 = 0, n1 = 0;
-      if (next < T) {
-        coords(next, m1, n1);
-        vw = (unsigned)(n1 + rr) * (unsigned)K * 2u + cgp;
-        va = (unsigned)(m1 + rr) * (unsigned)K * 2u + cgp;
-        static_for<S>([&](auto si) { issue_pp(decltype(si)::value, decltype(si)::value, vw, va); });
+      int pm0 = m0, pn0 = n0;
+      unsigned vw = vw0, va = va0;
+      for (int tile = blockIdx.x;;) {
+        // K tile 0 of this tile has landed (the S - 1 after it and the
+        // previous tile's output stores may still be in flight: loads
+        // complete in order, and at most (S - 1) J operations remain)
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_waitcnt(0x0F70 | (((S - 1) * J) & 15) | ((((S - 1) * J) >> 4) << 14));
+        bar();
+        if (__builtin_amdgcn_readfirstlane(wm) == 0) run(I0, vw, va);
+        else run(I1, vw, va);
+        // every wave has passed the K loop's last barrier, after which no
+        // stage is read: the next tile's first S K tiles can go out
+        const int next = tile + (int)gridDim.x;
+        int m1 = 0, n1 = 0;
+        if (next < T) {
+          coords(next, m1, n1);
+          vw = (unsigned)(n1 + rr) * (unsigned)K * 2u + cgp;
+          va = (unsigned)(m1 + rr) * (unsigned)K * 2u + cgp;
+          static_for<S>([&](auto si) { issue_pp(decltype(si)::value, decltype(si)::value, vw, va); });
+        }
+        dma_epilogue<EPI, FN, FM, TM, TN>(acc, resid, out, M, N, pm0, pn0, wm, wn, fr, fq);
+        if (next >= T) return;
+#pragma unroll
+        for (int a = 0; a < FN; ++a)
+#pragma unroll
+          for (int b = 0; b < FM; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+        tile = next;
+        pm0 = m1;
+        pn0 = n1;
       }
-      dma_epilogue<EPI, FN, FM, TM, TN>(acc, resid, out, M, N, pm0, pn0, wm, wn, fr, fq);
-      if (next >= T) return;
-#pragma unroll
-      for (int a = 0; a < FN; ++a)
-#pragma unroll
-        for (int b = 0; b < FM; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-      tile = next;
-      pm0 = m1;
-      pn0 = n1;
-    }
     }
   } else {
 #pragma unroll
