@@ -497,18 +497,24 @@ def extras(torch, np, ffn, I, sets, x, g, b, ws, extra, clocks, want, keep):
         res = {"us": round(tq * 1e3, 2), "GBps": round(qgbs, 1), "frac_of_read_ceiling": ratio(qgbs, best),
                "kernels_us_event_timed": kq}
         gu, dn = kq.get(f"{kind}_gateup"), kq.get(f"{kind}_down")
+        gub = 2 * mat + Mq * dq * 2 + Mq * fq * 2
+        dnb = mat + Mq * fq * 2 + 2 * Mq * dq * 2
         if gu:
-            gub = 2 * mat + Mq * dq * 2 + Mq * fq * 2
             res["gateup_kernel_GBps"] = round(gub / (gu * 1e-6) / 1e9, 1)
         if dn:
-            dnb = mat + Mq * fq * 2 + 2 * Mq * dq * 2
             res["down_kernel_GBps"] = round(dnb / (dn * 1e-6) / 1e9, 1)
         extra[f"{kind}_decode"] = res
+        del qcalls, qsets, q0
+        torch.cuda.empty_cache()
+        if best and gu and dn:
+            # the read probe over each kernel's byte count, as for bf16 decode
+            same = same_size_reads(torch, ffn, {"gateup": gub, "down": dnb})
+            res["read_probe_same_size_us"] = {k: v["us"] for k, v in same.items()}
+            res["gateup_frac_of_same_size_read"] = round(same["gateup"]["us"] / gu, 4)
+            res["down_frac_of_same_size_read"] = round(same["down"]["us"] / dn, 4)
         keep[f"{'C5 ' if kind == 'q8' else ''}{kind} decode M={Mq}"] = dict(
             kind=kind, inputs=q, gpu=to_host(qy), work=qbytes, unit="GB/s")
         log(kind, res)
-        del qcalls, qsets, q0
-        torch.cuda.empty_cache()
 
     if "tiny" in want:
         # ------------------------------------------------------- tiny fp32 block
