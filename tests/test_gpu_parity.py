@@ -161,9 +161,12 @@ def test_block_decode_full_size(gpu_lib, decode_inputs, M):
 
 
 @pytest.mark.parametrize("M,d,f", [(2, 512, 704), (3, 520, 712), (5, 64, 8), (9, 520, 712),
-                                   (12, 1032, 136), (17, 256, 384), (33, 1032, 520), (63, 512, 1024),
-                                   (64, 264, 136)])
+                                   (12, 1032, 136), (17, 256, 384), (24, 520, 712), (33, 1032, 520),
+                                   (40, 1032, 200), (63, 512, 1024), (64, 264, 136)])
 def test_block_decode_ragged(gpu_lib, M, d, f):
+    """Decode kernels (norm folded, h kept in the down projection's operand
+    order) at token counts across the one- and two-tile kernels and chunked
+    launches, with d and f off the 128-k stage (partial last stages)."""
     from transformer_ffn_block_amd import ffn
     _say("block decode ragged", M, d, f)
     b = I.make_block(400 + M, M, d, f, "bf16")
