@@ -338,9 +338,12 @@ ffn_status ffn_swiglu_block(ffn_dtype dt, const void* x, const void* g, const vo
     FFN_LAUNCH("gemm_down_residual", s, ffn::launch_gemm_residual(h, w_down, x, y, Mi, di, fi, s));
     return ok();
   }
-  // decode regime: launches of at most decode_chunk_tokens() tokens; the norm
-  // is folded into the gate/up kernel, so n is never materialised
-  // (every chunk but the last is a whole number of 16-token tiles)
+  // decode regime: gate/up launches of at most decode_chunk_tokens() tokens
+  // (the norm is folded in, so n is never materialised; every chunk but the
+  // last is a whole number of 16-token tiles).  With h blocked, one down
+  // launch takes every token (it reads h straight into registers, so up to
+  // four token tiles fit): W_down is streamed once per call.  Row-major h
+  // (SPLIT) is read in chunks like the gate/up side.
   const int step = ffn::decode_chunk_tokens();
   const bool hblk = decode && ffn::decode_h_blocked();
   for (int m0 = 0; m0 < Mi; m0 += step) {
@@ -349,8 +352,10 @@ ffn_status ffn_swiglu_block(ffn_dtype dt, const void* x, const void* g, const vo
     char* hc = (char*)h + (size_t)m0 * (hblk ? decode_h_row_elems(f) : (size_t)f) * es;
     if (decode)
       FFN_LAUNCH("decode_gateup", s, ffn::launch_decode_gateup_norm(xc, g, w_gate, w_up, hc, mc, di, fi, eps, s));
-    FFN_LAUNCH("decode_down", s, ffn::launch_decode_down(hc, w_down, xc, (char*)y + (size_t)m0 * d * es, mc, di, fi, hblk, s));
+    if (!hblk)
+      FFN_LAUNCH("decode_down", s, ffn::launch_decode_down(hc, w_down, xc, (char*)y + (size_t)m0 * d * es, mc, di, fi, false, s));
   }
+  if (hblk) FFN_LAUNCH("decode_down", s, ffn::launch_decode_down(h, w_down, x, y, Mi, di, fi, true, s));
   return ok();
 }
 

@@ -554,7 +554,8 @@ static void launch_by_m(const uint16_t* a, const uint16_t* gg, const uint16_t* p
 }
 
 // hblk: a gate/up kernel writes h blocked; a down kernel reads blocked h,
-// directly at every token count.
+// directly at every token count, up to four token tiles (64 tokens) per
+// launch.
 template <int NMAT, int WAVES, bool FOLD>
 static hipError_t launch_ds(const void* act, const void* gain, const void* w0, const void* w1,
                             const void* resid, void* out, int M, int K, int N, float eps, bool hblk,
@@ -568,7 +569,9 @@ static hipError_t launch_ds(const void* act, const void* gain, const void* w0, c
   if constexpr (NMAT == 1) {
     if (!hblk) launch_by_m<NMAT, WAVES, FOLD, false>(a, gg, p0, p1, rr, o, M, K, N, eps, s);
     else if (M <= 16) launch_k<NMAT, 1, WAVES, FOLD, false, true>(a, gg, p0, p1, rr, o, M, K, N, eps, s);
-    else launch_k<NMAT, 2, WAVES, FOLD, false, true>(a, gg, p0, p1, rr, o, M, K, N, eps, s);
+    else if (M <= 32) launch_k<NMAT, 2, WAVES, FOLD, false, true>(a, gg, p0, p1, rr, o, M, K, N, eps, s);
+    else if (M <= 48) launch_k<NMAT, 3, WAVES, FOLD, false, true>(a, gg, p0, p1, rr, o, M, K, N, eps, s);
+    else launch_k<NMAT, 4, WAVES, FOLD, false, true>(a, gg, p0, p1, rr, o, M, K, N, eps, s);
   } else {
     if (hblk) launch_by_m<NMAT, WAVES, FOLD, true>(a, gg, p0, p1, rr, o, M, K, N, eps, s);
     else launch_by_m<NMAT, WAVES, FOLD, false>(a, gg, p0, p1, rr, o, M, K, N, eps, s);
