@@ -175,6 +175,22 @@ def test_block_decode_ragged(gpu_lib, M, d, f):
     assert record(f"decode ragged {M}x{d}x{f}", err, TOL_BF16) <= TOL_BF16
 
 
+@pytest.mark.parametrize("M,d,f", [(33, 520, 4104), (64, 1032, 4200), (36, 264, 10248),
+                                   (57, 520, 10312), (48, 136, 16400)])
+def test_block_decode_wide_gateup(gpu_lib, M, d, f):
+    """33..64 tokens with enough 16-row tiles for one gate/up launch over
+    every token tile: on a 256-CU device f = 4104 and 4200 take two-wave
+    workgroups, f >= 10248 one wave per workgroup (the narrower f of the
+    ragged cases take two 32-token launches).  d and f are off the 128-k
+    stage."""
+    from transformer_ffn_block_amd import ffn
+    _say("block decode wide gate/up", M, d, f)
+    b = I.make_block(500 + M, M, d, f, "bf16")
+    r = O.block_from_stored("bf16", b.x, b.g, b.w_gate, b.w_up, b.w_down, b.eps)
+    err = max_norm_err(host_f64(_run_block(ffn, b, "auto")), r)
+    assert record(f"decode wide gate/up {M}x{d}x{f}", err, TOL_BF16) <= TOL_BF16
+
+
 # ----------------------------------------------------------------------------
 # bf16 SPLIT with few tokens: norm kernel, the prefill GEMMs on partial
 # token tiles, the activation pass, then the decode down projection

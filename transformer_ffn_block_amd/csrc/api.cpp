@@ -338,14 +338,14 @@ ffn_status ffn_swiglu_block(ffn_dtype dt, const void* x, const void* g, const vo
     FFN_LAUNCH("gemm_down_residual", s, ffn::launch_gemm_residual(h, w_down, x, y, Mi, di, fi, s));
     return ok();
   }
-  // decode regime: gate/up launches of at most decode_chunk_tokens() tokens
-  // (the norm is folded in, so n is never materialised; every chunk but the
-  // last is a whole number of 16-token tiles).  With h blocked, one down
-  // launch takes every token (it reads h straight into registers, so up to
-  // four token tiles fit): W_down is streamed once per call.  Row-major h
-  // (SPLIT) is read in chunks like the gate/up side.
-  const int step = ffn::decode_chunk_tokens();
+  // decode regime: gate/up launches of at most decode_gateup_tokens() tokens
+  // with h blocked, decode_chunk_tokens() otherwise (the norm is folded in,
+  // so n is never materialised; every chunk but the last is a whole number
+  // of 16-token tiles).  With h blocked, one down launch takes every token
+  // (it reads h straight into registers, so up to four token tiles fit).
+  // Row-major h (SPLIT) is read in chunks like the gate/up side.
   const bool hblk = decode && ffn::decode_h_blocked();
+  const int step = hblk ? ffn::decode_gateup_tokens() : ffn::decode_chunk_tokens();
   for (int m0 = 0; m0 < Mi; m0 += step) {
     const int mc = Mi - m0 < step ? Mi - m0 : step;
     const char* xc = (const char*)x + (size_t)m0 * d * es;

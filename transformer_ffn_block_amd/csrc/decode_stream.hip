@@ -534,6 +534,14 @@ static void launch_one(const uint16_t* a, const uint16_t* gg, const uint16_t* p0
 
 int decode_h_blocked() { return FFN_DS_HBLK; }
 
+// With blocked h the gate/up kernel also takes 33..64 tokens (three or four
+// 16-token tiles) in one launch, so the weights stream once per call.
+// FFN_DS_GU64 0 keeps 32-token launches.
+#ifndef FFN_DS_GU64
+#define FFN_DS_GU64 1
+#endif
+int decode_gateup_tokens() { return FFN_DS_HBLK && FFN_DS_GU64 ? 64 : 32; }
+
 template <int NMAT, int MT, int WAVES, bool FOLD, bool ASTAGE, bool HBLK>
 static void launch_k(const uint16_t* a, const uint16_t* gg, const uint16_t* p0, const uint16_t* p1,
                      const uint16_t* rr, uint16_t* o, int M, int K, int N, float eps, hipStream_t s) {
@@ -573,8 +581,31 @@ static hipError_t launch_ds(const void* act, const void* gain, const void* w0, c
     else if (M <= 48) launch_k<NMAT, 3, WAVES, FOLD, false, true>(a, gg, p0, p1, rr, o, M, K, N, eps, s);
     else launch_k<NMAT, 4, WAVES, FOLD, false, true>(a, gg, p0, p1, rr, o, M, K, N, eps, s);
   } else {
-    if (hblk) launch_by_m<NMAT, WAVES, FOLD, true>(a, gg, p0, p1, rr, o, M, K, N, eps, s);
-    else launch_by_m<NMAT, WAVES, FOLD, false>(a, gg, p0, p1, rr, o, M, K, N, eps, s);
+    if (hblk && M > 32) {
+      // 33..64 tokens in one launch.  Every workgroup stages all the tokens'
+      // activations (M/32 bytes per weight byte it streams), so the choice
+      // rests on how many 16-row tiles there are per compute unit (measured
+      // at d = 2048..8192, f = 1376..14336): below one, two 32-token
+      // launches keep more waves in flight; up to 2.5, two-wave workgroups
+      // (the K range split over both); past that, one wave per workgroup.
+      const int tiles = (N + 15) / 16, cus = device_cus();
+      if (tiles < cus) {
+        // tokens 32.. start at token tile 2 of blocked h
+        const size_t h2 = (size_t)32 * ((N + 127) / 128) * 128;
+        launch_by_m<NMAT, WAVES, FOLD, true>(a, gg, p0, p1, rr, o, 32, K, N, eps, s);
+        launch_by_m<NMAT, WAVES, FOLD, true>(a + (size_t)32 * K, gg, p0, p1, rr, o + h2, M - 32, K, N, eps, s);
+      } else if (2 * tiles < 5 * cus) {
+        if (M > 48) launch_k<NMAT, 4, 2, FOLD, true, true>(a, gg, p0, p1, rr, o, M, K, N, eps, s);
+        else launch_k<NMAT, 3, 2, FOLD, true, true>(a, gg, p0, p1, rr, o, M, K, N, eps, s);
+      } else {
+        if (M > 48) launch_k<NMAT, 4, 1, FOLD, true, true>(a, gg, p0, p1, rr, o, M, K, N, eps, s);
+        else launch_k<NMAT, 3, 1, FOLD, true, true>(a, gg, p0, p1, rr, o, M, K, N, eps, s);
+      }
+    } else if (hblk) {
+      launch_by_m<NMAT, WAVES, FOLD, true>(a, gg, p0, p1, rr, o, M, K, N, eps, s);
+    } else {
+      launch_by_m<NMAT, WAVES, FOLD, false>(a, gg, p0, p1, rr, o, M, K, N, eps, s);
+    }
   }
   return hipGetLastError();
 }

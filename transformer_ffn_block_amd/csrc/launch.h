@@ -49,7 +49,8 @@ hipError_t launch_rmsnorm(int elem_bytes, const void* x, const void* g, void* y,
 //   gate/up: h[M,f] = silu(n Wg^T) * (n Wu^T) with n = rmsnorm(x) * g folded in
 //   down   : y[M,d] = x + h Wd^T
 int decode_max_tokens();    // largest M routed to the decode kernels
-int decode_chunk_tokens();  // tokens per decode launch
+int decode_chunk_tokens();  // tokens per decode launch (row-major h)
+int decode_gateup_tokens(); // tokens per decode gate/up launch writing blocked h
 hipError_t launch_decode_gateup_norm(const void* x, const void* g, const void* wg, const void* wu,
                                      void* h, int M, int d, int f, float eps, hipStream_t s);
 // 1 if the decode gate/up kernel writes h in the blocked layout (token tile,
