@@ -766,6 +766,24 @@ def test_block_decode_balanced_row_ranges(gpu_lib, M, d, f):
     assert record(f"decode balanced rows {M}x{d}x{f}", err, TOL_BF16) <= TOL_BF16
 
 
+@pytest.mark.parametrize("M,d,f", [(16, 5120, 1032), (1, 5128, 520), (8, 4104, 264),
+                                   (24, 3080, 136), (40, 3080, 200)])
+def test_block_decode_balanced_down_rows(gpu_lib, M, d, f):
+    """Balanced row ranges in the down projection: on a 256-CU device the
+    1..16-token down kernel holds two workgroups per CU (512 slots), so d =
+    5120 / 5128 / 4104 (320 / 321 / 257 row tiles) spread as 8-10 rows per
+    workgroup; the 17..64-token kernels hold one (256 slots), so d = 3080
+    (193 tiles) gives 12-13 rows.  Row ranges start at unaligned rows, so
+    the residual loads and output stores go element by element at the
+    edges; f is off the 128-k stage in all but one case."""
+    from transformer_ffn_block_amd import ffn
+    _say("decode balanced down", M, d, f)
+    b = I.make_block(3250 + M, M, d, f, "bf16")
+    r = O.block_from_stored("bf16", b.x, b.g, b.w_gate, b.w_up, b.w_down, b.eps)
+    err = max_norm_err(host_f64(_run_block(ffn, b, "auto")), r)
+    assert record(f"decode balanced down rows {M}x{d}x{f}", err, TOL_BF16) <= TOL_BF16
+
+
 @pytest.mark.parametrize("kind", ["q8", "q4"])
 @pytest.mark.parametrize("M,d,f", [(8, 512, 6144), (5, 256, 7680), (16, 256, 6144)])
 def test_quant_balanced_row_ranges(gpu_lib, kind, M, d, f):

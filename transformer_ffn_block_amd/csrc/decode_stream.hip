@@ -502,7 +502,7 @@ void decode_stream(
 int decode_chunk_tokens() { return 32; }
 int decode_max_tokens() { return 64; }
 
-// Balanced gate/up grids.  A 16-row tile per workgroup leaves the compute
+// Balanced grids.  A 16-row tile per workgroup leaves the compute
 // units unevenly loaded when the tile count is not a multiple of the
 // workgroups that fit at once (f = 11008: 688 tiles on 768 slots, three
 // tiles on 176 CUs and two on 80; the kernel lasts as long as the busiest
@@ -512,6 +512,13 @@ int decode_max_tokens() { return 64; }
 #ifndef FFN_DS_BALANCE
 #define FFN_DS_BALANCE 1
 #endif
+// The down projections too: at d = 5120 its 320 row tiles on 512 slots
+// (two 8-wave workgroups per CU) left 64 CUs with two tiles; balanced, every
+// CU takes 20 rows (block 93.4 -> 88.8 us at 16 tokens, d = 6144 120.9 ->
+// 116.1 us; bitwise identical, other shapes unchanged).
+#ifndef FFN_DS_DN_BALANCE
+#define FFN_DS_DN_BALANCE 1
+#endif
 
 template <int NMAT, int MT, int WAVES, bool FOLD, bool ASTAGE, bool KFULL, bool HBLK>
 static void launch_one(const uint16_t* a, const uint16_t* gg, const uint16_t* p0,
@@ -520,8 +527,8 @@ static void launch_one(const uint16_t* a, const uint16_t* gg, const uint16_t* p0
   auto kern = decode_stream<NMAT, MT, WAVES, FOLD, ASTAGE, KFULL, HBLK>;
   // the occupancy of a kernel is fixed: computed once (the library assumes
   // every device it runs on is the same model)
-  static const int slots = NMAT == 2 ? resident_slots(kern, WAVES * 64) : 0;
-  const int groups = NMAT == 2 ? stream_groups(N, slots, FFN_DS_BALANCE) : (N + 15) / 16;
+  static const int slots = NMAT == 2 || FFN_DS_DN_BALANCE ? resident_slots(kern, WAVES * 64) : 0;
+  const int groups = NMAT == 2 || FFN_DS_DN_BALANCE ? stream_groups(N, slots, FFN_DS_BALANCE) : (N + 15) / 16;
   FFN_DISPATCH(kern, dim3((unsigned)groups), dim3(WAVES * 64), 0, s, a, gg, p0, p1, rr, o, M, K, N, eps);
 }
 
