@@ -507,10 +507,15 @@ int decode_max_tokens() { return 64; }
 // workgroups that fit at once (f = 11008: 688 tiles on 768 slots, three
 // tiles on 176 CUs and two on 80; the kernel lasts as long as the busiest
 // CU).  Instead the grid is sized to whole rounds of resident workgroups and
-// each takes an equal share (<= 16) of the rows.  FFN_DS_BALANCE 0 keeps
-// one workgroup per 16-row tile.
+// each takes an equal share (<= 16) of the rows.  Past one round, the grid
+// is a whole multiple of the compute units (policy 3 of stream_groups), so
+// every CU still gets the same number of rows: 1.5 rounds of 14-15 rows
+// instead of 1.34 rounds of 16 (M = 1 / 8 / 24 / 48 / 64 at f = 11008:
+// 0.4-1.7% faster; d = 5120, f = 13824 at 16 tokens 89.2 -> 85.6 us;
+// bitwise identical).  FFN_DS_BALANCE 0 keeps one workgroup per 16-row
+// tile, 1 balances single rounds only.
 #ifndef FFN_DS_BALANCE
-#define FFN_DS_BALANCE 1
+#define FFN_DS_BALANCE 3
 #endif
 // The down projections too: at d = 5120 its 320 row tiles on 512 slots
 // (two 8-wave workgroups per CU) left 64 CUs with two tiles; balanced, every
@@ -528,7 +533,8 @@ static void launch_one(const uint16_t* a, const uint16_t* gg, const uint16_t* p0
   // the occupancy of a kernel is fixed: computed once (the library assumes
   // every device it runs on is the same model)
   static const int slots = NMAT == 2 || FFN_DS_DN_BALANCE ? resident_slots(kern, WAVES * 64) : 0;
-  const int groups = NMAT == 2 || FFN_DS_DN_BALANCE ? stream_groups(N, slots, FFN_DS_BALANCE) : (N + 15) / 16;
+  static const int cus = device_cus();
+  const int groups = NMAT == 2 || FFN_DS_DN_BALANCE ? stream_groups(N, slots, FFN_DS_BALANCE, cus) : (N + 15) / 16;
   FFN_DISPATCH(kern, dim3((unsigned)groups), dim3(WAVES * 64), 0, s, a, gg, p0, p1, rr, o, M, K, N, eps);
 }
 

@@ -32,10 +32,14 @@ inline int resident_slots(Kern kern, int block) {
 // each own an equal share (at most 16: one MFMA tile) of the rows, given
 // `slots` resident workgroups.  policy 0: one workgroup per 16-row tile;
 // 1: if the tiles fit one round, fill that round (every compute unit gets an
-// equal number of rows); 2: also, past one round, whole rounds.
-inline int stream_groups(int N, int slots, int policy) {
+// equal number of rows); 2: also, past one round, whole rounds; 3: with at
+// least one tile per compute unit (`cus` of them), the same number of
+// workgroups on every compute unit, in as many rounds as that takes (fewer
+// tiles: as policy 1).
+inline int stream_groups(int N, int slots, int policy, int cus = 0) {
   const int t0 = (N + 15) / 16;
   if (policy <= 0 || slots < 1) return t0;
+  if (policy >= 3 && cus > 0 && t0 >= cus) return (t0 + cus - 1) / cus * cus;
   if (t0 <= slots) return 2 * t0 > slots ? slots : t0;
   return policy >= 2 ? (t0 + slots - 1) / slots * slots : t0;
 }

@@ -483,8 +483,12 @@ int q8_max_tokens() { return 32; }
 // 11-12 rows instead of 1088 tiles at f = 17408) measured slower in
 // interleaved A/B (Q8_0 block 73.1 -> 78.0 us, Q4_0 55.6 -> 56.9 us at 8
 // tokens): the extra workgroups cost more than the partial last round.
+// Policy 3 (a whole multiple of the compute units: 1280 workgroups of 13-14
+// rows at f = 17408, five per CU) measured slightly faster (Q8_0 71.9 ->
+// 71.6 us at 8 tokens, 64.5 -> 63.9 at 1; Q4_0 55.5 -> 55.0 and 48.1 ->
+// 47.6; bitwise identical).
 #ifndef FFN_Q8_BALANCE
-#define FFN_Q8_BALANCE 1
+#define FFN_Q8_BALANCE 3
 #endif
 
 template <class Kern>
@@ -492,7 +496,8 @@ static void q8_go(Kern kern, bool gateup, int splits, int N, int threads, const 
                      const uint16_t* gn, const int8_t* q0, const uint16_t* s0,
                      const int8_t* q1, const uint16_t* s1, const uint16_t* rr,
                      uint16_t* o, float* part, int M, int K, float eps, int slots, hipStream_t s) {
-  const int groups = gateup ? stream_groups(N, slots, FFN_Q8_BALANCE) : (N + 15) / 16;
+  static const int cus = device_cus();
+  const int groups = gateup ? stream_groups(N, slots, FFN_Q8_BALANCE, cus) : (N + 15) / 16;
   FFN_DISPATCH(kern, dim3((unsigned)groups, (unsigned)splits), dim3(threads), 0, s, a, gn, q0, s0, q1,
                s1, rr, o, part, M, K, N, eps);
 }
