@@ -20,7 +20,8 @@
 //
 // With M <= 64 tokens every weight is used M times, far below the flop:byte
 // ridge, so the kernels are bound by reading W from HBM once.  gfx950 design:
-//  * a workgroup owns 16 weight rows (per matrix); its W waves split K into
+//  * a workgroup owns at most 16 weight rows (per matrix; an equal share of
+//    the rows when the grid is balanced, below); its W waves split K into
 //    contiguous slices of 128-k stages;
 //  * weights are fetched in 256-byte row segments (4 rows x 256 B per wave
 //    instruction), which streams markedly faster on this chip than the
@@ -47,7 +48,9 @@
 //    its 8-byte groups there, and the down kernel reads each 32-k operand of
 //    16 tokens as one contiguous 1 KiB wave load straight into registers, with
 //    no LDS stage for the activations (down projection at 16 tokens 19.2 ->
-//    18.6 us, bitwise identical to the row-major form).
+//    18.6 us, bitwise identical to the row-major form);
+//  * up to 64 tokens (four 16-token tiles) go through each projection in one
+//    launch, so every weight is streamed once per call.
 #include "common.h"
 #include "launch.h"
 
@@ -497,8 +500,10 @@ void decode_stream(
       act, gain, w0, w1, resid, out, nullptr, M, K, N, eps, row0, row1, 0, -1, wb, ab, ssq);
 }
 
-// Tokens per launch (two 16-token tiles keep the LDS stages within budget);
-// the API walks larger decode batches in chunks of this size.
+// Tokens per launch with row-major h (two 16-token tiles keep the LDS
+// stages within budget): the API walks larger decode batches in chunks of
+// this size.  With blocked h the gate/up kernel takes up to
+// decode_gateup_tokens() and the down kernel every token.
 int decode_chunk_tokens() { return 32; }
 int decode_max_tokens() { return 64; }
 
