@@ -118,7 +118,17 @@ def test_workspace_sizes(L):
         blk = ((m + 15) // 16 * 16) * ((ff + 127) // 128 * 128) * 2
         assert L.ffn_swiglu_block_workspace_size(ffn.FFN_BF16, m, d, ff, 0) == r256(m * d * 2) + r256(blk)
         assert L.ffn_swiglu_block_workspace_size(ffn.FFN_BF16, m, d, ff, 2) == r256(m * d * 2) + 3 * r256(m * ff * 2)
-    assert L.ffn_swiglu_block_workspace_size(ffn.FFN_BF16, 65, d, 704, 0) == r256(65 * d * 2) + r256(65 * 704 * 2)
+    # prefill (M > 64) GEMMs whose tiles leave compute units idle split K and
+    # add fp32 partial planes: at M = 65, d = 4096, f = 704 on 256 CUs (the
+    # count assumed without a device) the fused gate/up GEMM has 6 tiles ->
+    # 16 ranges (2 x 16 planes of [65, 704]), the down GEMM 16 tiles -> 11
+    # ranges (its K = 704 holds 11 K tiles of 64): one region for the larger
+    base = r256(65 * d * 2) + r256(65 * 704 * 2)
+    part = max(2 * 16 * 65 * 704 * 4, 11 * 65 * d * 4)
+    assert L.ffn_swiglu_block_workspace_size(ffn.FFN_BF16, 65, d, 704, 0) == base + r256(part)
+    # SPLIT: only the down GEMM splits; 8192 tokens fill the chip: no partials
+    assert L.ffn_swiglu_block_workspace_size(ffn.FFN_BF16, 65, d, 704, 2) == base + 2 * r256(65 * 704 * 2) + r256(11 * 65 * d * 4)
+    assert L.ffn_swiglu_block_workspace_size(ffn.FFN_BF16, 8192, d, 14336, 0) == r256(8192 * d * 2) + r256(8192 * 14336 * 2)
     assert L.ffn_swiglu_block_workspace_size(ffn.FFN_F32, 8, 256, 704, 0) == r256(8 * 256 * 4) + r256(8 * 704 * 4)
     assert L.ffn_swiglu_block_workspace_size(5, M, d, f, 0) == 0
     # persistent: plus [S, M, d] fp32 partials and 2 + S + d/16 counter words

@@ -379,6 +379,53 @@ def test_block_prefill_full_size_sampled_rows(gpu_lib, prefill_inputs):
 
 
 # ----------------------------------------------------------------------------
+# prefill GEMMs split over K (fewer tiles than compute units): fp32 partials
+# plus a second pass (SwiGLU for the fused gate/up GEMM, residual for the
+# down GEMM).  On a 256-CU device: (256, 1024, 2048) takes the two-group
+# schedule with 8 / 16 ranges; (65, 512, 704) and (300, 4096, 1024) the
+# one-group schedule (ragged token tiles; f = 704 also a ragged weight tile,
+# and 11 K tiles, an odd count, for the down GEMM) with 4 / 11 and 16 / 8
+# ranges; d = 1032 is off the K tile, so its gate/up GEMM stays unsplit
+# (register-staged) while its down GEMM (K = 576) splits 9 ways.
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("variant", ["fused", "split", "fused_norm"])
+@pytest.mark.parametrize("M,d,f", [(256, 1024, 2048), (65, 512, 704), (300, 4096, 1024),
+                                   (100, 1032, 576)])
+def test_block_prefill_split_k(gpu_lib, M, d, f, variant):
+    from transformer_ffn_block_amd import ffn
+    _say("block prefill split-K", M, d, f, variant)
+    b = I.make_block(5600 + M, M, d, f, "bf16")
+    r = O.block_from_stored("bf16", b.x, b.g, b.w_gate, b.w_up, b.w_down, b.eps)
+    a = host_f64(_run_block(ffn, b, variant))
+    assert record(f"prefill split-K {M}x{d}x{f} {variant}", max_norm_err(a, r), TOL_BF16) <= TOL_BF16
+    per_row = max(max_norm_err(a[i], r[i]) for i in range(M))
+    assert record(f"prefill split-K {M}x{d}x{f} {variant} worst row", per_row, TOL_BF16,
+                  "max_norm_per_row") <= TOL_BF16
+
+
+def test_block_prefill_split_k_decode_shape_sampled_rows(gpu_lib):
+    """128 tokens at the decode shape d = 4096, f = 11008 (86 gate/up and 16
+    down tiles: 2 and 16 K ranges on 256 CUs) against the oracle on 24 rows
+    (rows are independent, so the oracle computes just these), and the same
+    bits on a second call."""
+    from transformer_ffn_block_amd import ffn
+    import torch
+    M, d, f = 128, 4096, 11008
+    _say("block prefill split-K decode shape", M, d, f)
+    b = I.make_block(5700, M, d, f, "bf16")
+    x, g, wg, wu, wd = _block_dev(b)
+    y1 = ffn.swiglu_block(x, g, wg, wu, wd, b.eps, variant="auto")
+    y2 = ffn.swiglu_block(x, g, wg, wu, wd, b.eps, variant="auto")
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(y1), host_bits(y2))
+    rows = np.sort(np.concatenate([[0, 1, 63, 64, 126, 127],
+                                   np.random.default_rng(45).choice(np.arange(2, 126), 18, replace=False)]))
+    r = O.block_from_stored("bf16", b.x[rows], b.g, b.w_gate, b.w_up, b.w_down, b.eps)
+    a = host_f64(y1)[rows]
+    assert record("prefill split-K 128x4096x11008 (24 rows)", max_norm_err(a, r), TOL_BF16) <= TOL_BF16
+
+
+# ----------------------------------------------------------------------------
 # properties
 # ----------------------------------------------------------------------------
 @pytest.mark.parametrize("M", [16, 300])
@@ -476,11 +523,13 @@ def _tail_pair(kind, a, b, d, f):
     return host_bits(ya), host_bits(yb)[:a]
 
 
-# Rows are independent and each kernel's summation order does not depend on
-# M, so rows shared by two calls that take the same kernels are bitwise equal:
-# decode 17 vs 32 tokens (the two-tile kernels), prefill 300 vs 512 tokens
-# (ragged tiles in the one-group schedule vs whole tiles in the two-group
-# one), Q8/Q4 5 vs 8 and 17 vs 32 tokens.
+# Rows are independent and each kernel's summation order depends on M only
+# through the kernel choice and, for prefill GEMMs split over K, the number of
+# token tiles (which sets the K ranges), so rows shared by two calls that take
+# the same kernels are bitwise equal: decode 17 vs 32 tokens (the two-tile
+# kernels), prefill 300 vs 512 tokens (two token tiles each: ragged tiles in
+# the one-group schedule vs whole tiles in the two-group one, both split over
+# K at the same places), Q8/Q4 5 vs 8 and 17 vs 32 tokens.
 @pytest.mark.parametrize("kind,a,b,d,f", [("bf16", 17, 32, 1024, 2816), ("bf16", 300, 512, 512, 768),
                                           ("q8", 5, 8, 512, 1024), ("q8", 17, 32, 512, 704),
                                           ("q4", 5, 8, 512, 1024), ("q4", 17, 32, 512, 704)])

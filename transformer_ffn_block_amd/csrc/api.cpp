@@ -135,6 +135,23 @@ size_t decode_h_row_elems(int64_t f) {  // elements per token of blocked h
   return ffn::decode_h_blocked() ? (size_t)((f + 127) / 128) * 128 : (size_t)f;
 }
 
+// K ranges of the prefill GEMMs (bf16, more than decode_max_tokens()
+// tokens) when their tiles leave compute units idle; 1 = unsplit.  The gate/up
+// split applies to the fused GEMM (not SPLIT, not the register-staged
+// FUSED_NORM kernel, which never splits).
+struct PrefillSplits {
+  int gu = 1, dn = 1;
+};
+PrefillSplits prefill_splits(size_t es, int64_t M, int64_t d, int64_t f, bool split, bool persistent) {
+  PrefillSplits p;
+  if (es != 2 || persistent || M <= ffn::decode_max_tokens() || M > INT32_MAX || d > INT32_MAX ||
+      f > INT32_MAX)
+    return p;
+  if (!split) p.gu = ffn::prefill_gateup_splits((int)M, (int)d, (int)f);
+  p.dn = ffn::prefill_down_splits((int)M, (int)d, (int)f);
+  return p;
+}
+
 WsLayout ws_layout(size_t es, int64_t M, int64_t d, int64_t f, bool split, bool persistent = false) {
   WsLayout w;
   size_t at = 0;
@@ -157,6 +174,15 @@ WsLayout ws_layout(size_t es, int64_t M, int64_t d, int64_t f, bool split, bool 
     at += round256((size_t)sp * M * d * 4);
     w.ctr = at;
     at += round256(ffn::decode_persistent_counters((int)d, sp) * 4);
+  }
+  // fp32 partial sums of split-K prefill GEMMs (gate/up planes, then reused
+  // for the down projection's)
+  const PrefillSplits ps = prefill_splits(es, M, d, f, split, persistent);
+  const size_t pgu = ps.gu > 1 ? (size_t)2 * ps.gu * M * f * 4 : 0;
+  const size_t pdn = ps.dn > 1 ? (size_t)ps.dn * M * d * 4 : 0;
+  if (pgu || pdn) {
+    w.part = at;
+    at += round256(pgu > pdn ? pgu : pdn);
   }
   w.total = at;
   return w;
@@ -294,6 +320,8 @@ ffn_status ffn_swiglu_block(ffn_dtype dt, const void* x, const void* g, const vo
   char* ws = (char*)workspace;
   void* n = ws + L.n;
   void* h = ws + L.h;
+  float* part = (float*)(ws + L.part);
+  const PrefillSplits sp = prefill_splits(es, M, d, f, split, persistent);
   const int Mi = (int)M, di = (int)d, fi = (int)f;
 
   if (persistent) {
@@ -332,10 +360,21 @@ ffn_status ffn_swiglu_block(ffn_dtype dt, const void* x, const void* g, const vo
     FFN_LAUNCH("gemm_gateup_fused_norm", s,
                ffn::launch_gemm_gateup_fused_norm(x, g, w_gate, w_up, h, Mi, di, fi, eps, s));
   } else if (!decode) {
-    FFN_LAUNCH("gemm_gateup_fused", s, ffn::launch_gemm_gateup_fused(n, w_gate, w_up, h, Mi, di, fi, s));
+    if (sp.gu > 1) {
+      FFN_LAUNCH("gemm_gateup_fused_splitk", s,
+                 ffn::launch_gemm_gateup_fused_part(n, w_gate, w_up, part, sp.gu, Mi, di, fi, s));
+      FFN_LAUNCH("splitk_swiglu", s, ffn::launch_splitk_swiglu(part, sp.gu, h, Mi, fi, s));
+    } else {
+      FFN_LAUNCH("gemm_gateup_fused", s, ffn::launch_gemm_gateup_fused(n, w_gate, w_up, h, Mi, di, fi, s));
+    }
   }
   if (Mi > ffn::decode_max_tokens()) {
-    FFN_LAUNCH("gemm_down_residual", s, ffn::launch_gemm_residual(h, w_down, x, y, Mi, di, fi, s));
+    if (sp.dn > 1) {
+      FFN_LAUNCH("gemm_down_splitk", s, ffn::launch_gemm_down_part(h, w_down, part, sp.dn, Mi, di, fi, s));
+      FFN_LAUNCH("splitk_residual", s, ffn::launch_splitk_residual(part, sp.dn, x, y, Mi, di, s));
+    } else {
+      FFN_LAUNCH("gemm_down_residual", s, ffn::launch_gemm_residual(h, w_down, x, y, Mi, di, fi, s));
+    }
     return ok();
   }
   // decode regime: gate/up launches of at most decode_gateup_tokens() tokens

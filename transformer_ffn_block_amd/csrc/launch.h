@@ -85,6 +85,22 @@ hipError_t launch_gemm_store(const void* a, const void* w, void* c, int M, int N
                              hipStream_t s);
 hipError_t launch_gemm_residual(const void* a, const void* w, const void* resid, void* y,
                                 int M, int N, int K, hipStream_t s);
+// Split K for prefill GEMMs whose tiles leave compute units idle: the
+// number of K ranges (1: no split, use the launchers above), and the GEMMs
+// that write fp32 partial sums instead of their epilogue -- fused gate/up:
+// gate sums in part[z][M][f], up sums in part[Z + z][M][f]; down:
+// part[z][M][d] -- for launch_splitk_swiglu / launch_splitk_residual.
+constexpr int kPrefillMaxSplits = 16;
+int prefill_gateup_splits(int M, int d, int f);
+int prefill_down_splits(int M, int d, int f);
+hipError_t launch_gemm_gateup_fused_part(const void* n, const void* wg, const void* wu, float* part,
+                                         int Z, int M, int d, int f, hipStream_t s);
+hipError_t launch_gemm_down_part(const void* h, const void* wd, float* part, int Z, int M, int d,
+                                 int f, hipStream_t s);
+// h[m,j] = bf16(silu(sum_z G_z[m,j]) * sum_z U_z[m,j]), ranges added in z
+// order, from the partial planes above (f % 8 == 0).
+hipError_t launch_splitk_swiglu(const float* part, int splits, void* h, int M, int f,
+                                hipStream_t s);
 // h = silu(G) * U elementwise over `count` bf16 values (count % 8 == 0).
 hipError_t launch_swiglu_bf16(const void* G, const void* U, void* h, int64_t count,
                               hipStream_t s);
@@ -128,7 +144,7 @@ hipError_t launch_q4_down(const void* h, const uint8_t* qd, const uint16_t* sd, 
 int q4_max_tokens();
 
 // y[m,i] = bf16(x[m,i] + sum_{z < splits} part[z][m][i]), summed in z order
-// (N % 8 == 0).
+// (N % 8 == 0; splits <= kPrefillMaxSplits).
 hipError_t launch_splitk_residual(const float* part, int splits, const void* x, void* y, int M,
                                   int N, hipStream_t s);
 

@@ -538,14 +538,20 @@ __device__ __forceinline__ void dma_epilogue(const f32x4 (&acc)[FN][FM],
 // as soon as a tile's K loop has read its last stage, the first S K tiles
 // of the workgroup's next tile go out, so their latency overlaps the
 // epilogue instead of opening the next tile.
-template <int BM, int BN, int WM, int WN, int EPI, int BK, int S, bool PP, bool PERSIST = false>
+// PART (split K): workgroup (tile, z) covers the z-th of gridDim.y contiguous
+// ranges of K tiles (whole groups of S tiles on the ping-pong schedule) and
+// writes its fp32 partial sums instead of the epilogue: plane z of part
+// ([planes][M][N]; SWIGLU: the gate sums in plane z, the up sums in plane
+// gridDim.y + z), which a second pass adds up in range order.
+template <int BM, int BN, int WM, int WN, int EPI, int BK, int S, bool PP, bool PERSIST = false,
+          bool PART = false>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_dma(
     const uint16_t* __restrict__ act,    // [M, K]
     const uint16_t* __restrict__ w0,     // [N, K]  (gate for SWIGLU)
     const uint16_t* __restrict__ w1,     // [N, K]  (up for SWIGLU)
     const uint16_t* __restrict__ resid,  // [M, N]  (RESIDUAL)
     uint16_t* __restrict__ out,          // [M, N]
-    int M, int N, int K) {
+    int M, int N, int K, float* __restrict__ part) {
   constexpr int NT = WM * WN * 64;
   constexpr int TM = BM / WM, TN = BN / WN;
   constexpr int FM = TM / 16, FN = TN / 16;
@@ -571,7 +577,18 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_dma(
   const int wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
   const int K8 = K >> 3;
-  const int nkt = K / BK;
+  static_assert(!(PART && PERSIST), "split-K grids hold one tile per workgroup");
+  // this workgroup's K tiles [kt0, kt0 + nkt): ranges in whole groups of S
+  // K tiles whenever the tile count allows (always on the ping-pong
+  // schedule), so both schedules cut K at the same places
+  const int unit = (K / BK) % S == 0 ? S : 1;
+  const int units = (K / BK) / unit;
+  const int zr = PART ? (int)blockIdx.y : 0, Zr = PART ? (int)gridDim.y : 1;
+  const int u0 = (int)(((long)units * zr) / Zr), u1 = (int)(((long)units * (zr + 1)) / Zr);
+  const int kt0 = PART ? u0 * unit : 0;
+  const int nkt = PART ? (u1 - u0) * unit : K / BK;
+  const unsigned kbyte0 = (unsigned)kt0 * (unsigned)BK * 2u;  // byte offset of the range in a row
+  (void)K8;
 
   // ---- tile coordinates: XCD-contiguous, then grouped GM token tiles deep
   // (a persistent grid is a multiple of 8 workgroups or one per tile, so a
@@ -618,7 +635,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_dma(
     } else {
       src_row = min(m0 + row - BN, M - 1);
     }
-    soff[j] = (unsigned)src_row * (unsigned)K * 2u + (unsigned)cg * 16u;
+    soff[j] = (unsigned)src_row * (unsigned)K * 2u + (unsigned)cg * 16u + kbyte0;
   }
   // tile kt into stage i; tiles past the end read nothing (out-of-range
   // offset, or-ed in: a branch here would cost the exact load waits)
@@ -750,8 +767,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_dma(
     const int wave_s = __builtin_amdgcn_readfirstlane(wave);
     const int rr = tid / CPR;
     const unsigned cgp = (unsigned)((tid % CPR) ^ dswz<BK>(rr)) * 16u;
-    const unsigned vw0 = (unsigned)(n0 + rr) * (unsigned)K * 2u + cgp;
-    const unsigned va0 = (unsigned)(m0 + rr) * (unsigned)K * 2u + cgp;
+    const unsigned vw0 = (unsigned)(n0 + rr) * (unsigned)K * 2u + cgp + kbyte0;
+    const unsigned va0 = (unsigned)(m0 + rr) * (unsigned)K * 2u + cgp + kbyte0;
     const int blk = RJ * K * 2;  // bytes of one load instruction's row block
     // vw, va: this lane's weight-row and token-row source offsets of the tile
     auto issue_pp = [&](int i, int kt, unsigned vw, unsigned va) {
@@ -863,6 +880,24 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_dma(
   }
   }
 
+  if constexpr (PART) {
+    // fp32 partial sums: lane (fr, fq) holds 4 consecutive columns of token
+    // row fr of every sub-tile
+    constexpr int NA = EPI == EPI_SWIGLU ? FN / 2 : FN;
+#pragma unroll
+    for (int a = 0; a < FN; ++a) {
+      const int col = n0 + wn * (EPI == EPI_SWIGLU ? TN / 2 : TN) + (a % NA) * 16 + 4 * fq;
+      const int plane = a < NA ? zr : Zr + zr;  // SWIGLU: gate, then up
+#pragma unroll
+      for (int b = 0; b < FM; ++b) {
+        const int tok = m0 + wm * TM + b * 16 + fr;
+        if (tok < M && col < N)
+          *reinterpret_cast<float4*>(part + ((size_t)plane * M + tok) * N + col) =
+              make_float4(acc[a][b][0], acc[a][b][1], acc[a][b][2], acc[a][b][3]);
+      }
+    }
+    return;
+  }
   // whole tiles (the ping-pong schedule) store 16 bytes per lane
   dma_epilogue<EPI, FN, FM, TM, TN, PP && FFN_PF_WIDE != 0>(acc, resid, out, M, N, m0, n0, wm, wn, fr, fq);
 }
@@ -912,18 +947,76 @@ static hipError_t launch_cfg(const void* act, const void* w0, const void* w1, co
       if (FFN_PF_PERSIST && slots >= 8 && tiles > slots)
         FFN_DISPATCH(pers, dim3((unsigned)slots), dim3(kWM * kWN * 64), 0, s, (const uint16_t*)act,
                      (const uint16_t*)w0, (const uint16_t*)w1, (const uint16_t*)resid, (uint16_t*)out, M,
-                     N, K);
+                     N, K, nullptr);
       else
         FFN_DISPATCH((gemm_dma<kBM, kBN, kWM, kWN, EPI, kPpBK, kPpS, true>), dim3((unsigned)tiles),
                      dim3(kWM * kWN * 64), 0, s, (const uint16_t*)act, (const uint16_t*)w0,
-                     (const uint16_t*)w1, (const uint16_t*)resid, (uint16_t*)out, M, N, K);
+                     (const uint16_t*)w1, (const uint16_t*)resid, (uint16_t*)out, M, N, K, nullptr);
     } else
       FFN_DISPATCH((gemm_dma<kBM, kBN, kWM, kWN, EPI, kDmaBK, kDmaS, false>), dim3((unsigned)tiles),
                          dim3(kWM * kWN * 64), 0, s, (const uint16_t*)act, (const uint16_t*)w0,
-                         (const uint16_t*)w1, (const uint16_t*)resid, (uint16_t*)out, M, N, K);
+                         (const uint16_t*)w1, (const uint16_t*)resid, (uint16_t*)out, M, N, K, nullptr);
     return hipGetLastError();
   }
   return launch_reg<EPI>(act, w0, w1, resid, out, M, N, K, nullptr, 0.f, s);
+}
+
+// Split K for GEMMs whose tiles leave compute units idle (fewer than one per
+// CU: a down projection below 4096 tokens at d = 4096 has 16 per 256 tokens,
+// the fused gate/up 86 at f = 11008).  floor(CUs / tiles) ranges, at most
+// kPrefillMaxSplits and at least one group of K tiles each; 1 = no split.
+// Only the LDS-fed kernels split (K a multiple of the K tile).
+#ifndef FFN_PF_SPLITK
+#define FFN_PF_SPLITK 1
+#endif
+static bool dma_ok(int M, int N, int K) {
+  return !FFN_PF_FORCE_REG && K % kDmaBK == 0 && (size_t)M * K * 2 < ((size_t)1 << 31) &&
+         (size_t)N * K * 2 < ((size_t)1 << 31);
+}
+static bool pp_ok(int M, int N, int K, int bno) {
+  return kPingPong && M % kBM == 0 && N % bno == 0 && K % (kPpS * kPpBK) == 0;
+}
+static int splits_for(int M, int N, int K, int bno) {
+  if (!FFN_PF_SPLITK || !dma_ok(M, N, K)) return 1;
+  const long tiles = (long)((M + kBM - 1) / kBM) * ((N + bno - 1) / bno);
+  const int cus = device_cus();
+  long z = tiles > 0 ? cus / tiles : 1;
+  // the kernels' range unit: whole groups of S K tiles when they divide K
+  const int nk = pp_ok(M, N, K, bno) ? K / kPpBK : K / kDmaBK;
+  const int sg = pp_ok(M, N, K, bno) ? kPpS : kDmaS;
+  const int units = nk % sg == 0 ? nk / sg : nk;
+  if (z > kPrefillMaxSplits) z = kPrefillMaxSplits;
+  if (z > units) z = units;
+  return z > 1 ? (int)z : 1;
+}
+int prefill_gateup_splits(int M, int d, int f) { return splits_for(M, f, d, kBN / 2); }
+int prefill_down_splits(int M, int d, int f) { return splits_for(M, d, f, kBN); }
+
+template <int EPI>
+static hipError_t launch_part(const void* act, const void* w0, const void* w1, float* part, int Z,
+                              int M, int N, int K, hipStream_t s) {
+  constexpr int BNO = EPI == EPI_SWIGLU ? kBN / 2 : kBN;
+  const long tiles = (long)((M + kBM - 1) / kBM) * ((N + BNO - 1) / BNO);
+  if (Z < 1 || Z > kPrefillMaxSplits || !dma_ok(M, N, K)) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)tiles, (unsigned)Z), block(kWM * kWN * 64);
+  if (pp_ok(M, N, K, BNO))
+    FFN_DISPATCH((gemm_dma<kBM, kBN, kWM, kWN, EPI, kPpBK, kPpS, true, false, true>), grid, block, 0, s,
+                 (const uint16_t*)act, (const uint16_t*)w0, (const uint16_t*)w1, nullptr, nullptr, M,
+                 N, K, part);
+  else
+    FFN_DISPATCH((gemm_dma<kBM, kBN, kWM, kWN, EPI, kDmaBK, kDmaS, false, false, true>), grid, block,
+                 0, s, (const uint16_t*)act, (const uint16_t*)w0, (const uint16_t*)w1, nullptr,
+                 nullptr, M, N, K, part);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_gateup_fused_part(const void* n, const void* wg, const void* wu, float* part,
+                                         int Z, int M, int d, int f, hipStream_t s) {
+  return launch_part<EPI_SWIGLU>(n, wg, wu, part, Z, M, f, d, s);
+}
+hipError_t launch_gemm_down_part(const void* h, const void* wd, float* part, int Z, int M, int d,
+                                 int f, hipStream_t s) {
+  return launch_part<EPI_RESIDUAL>(h, wd, nullptr, part, Z, M, d, f, s);
 }
 
 hipError_t launch_gemm_gateup_fused(const void* n, const void* wg, const void* wu, void* h,

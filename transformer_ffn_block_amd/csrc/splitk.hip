@@ -1,5 +1,6 @@
-// Second pass of the split-K down projections: y = x + the fp32 partial sums
-// of the K ranges, added in range order (deterministic; no atomics).  The
+// Second passes of the split-K projections: y = x + the fp32 partial sums
+// of the K ranges of a down projection, or h = silu(G) * U from those of a
+// fused gate/up GEMM, added in range order (deterministic; no atomics).  The
 // deeper K split of the FFN-down projection is the experiment of "Megakernels
 // on Mac", "Projection shape changes the achieved rate"; here the split
 // spreads the few hundred 16-row output tiles of a decode down projection
@@ -51,22 +52,93 @@ static void splitk_go(const float* part, const void* x, void* y, int groups, siz
                (uint4*)y, groups, stride);
 }
 
+// h = silu(sum_z G_z) * sum_z U_z for the split-K fused gate/up GEMM: gate
+// planes 0..S-1, up planes S..2S-1 of [M, f] each; one thread per 8 outputs.
+template <int S>
+__global__ __launch_bounds__(256) void splitk_swiglu(const float4* __restrict__ part,
+                                                     uint4* __restrict__ h, int groups,
+                                                     size_t plane) {
+  const int i = blockIdx.x * 256 + threadIdx.x;  // 8-output group
+  if (i >= groups) return;
+  float4 ga[S], gb[S], ua[S], ub[S];
+#pragma unroll
+  for (int z = 0; z < S; ++z) {
+    const float4* pg = part + z * plane + 2 * (size_t)i;
+    const float4* pu = part + (S + z) * plane + 2 * (size_t)i;
+    ga[z] = pg[0];
+    gb[z] = pg[1];
+    ua[z] = pu[0];
+    ub[z] = pu[1];
+  }
+  float g[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, u[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int z = 0; z < S; ++z) {
+    g[0] += ga[z].x; g[1] += ga[z].y; g[2] += ga[z].z; g[3] += ga[z].w;
+    g[4] += gb[z].x; g[5] += gb[z].y; g[6] += gb[z].z; g[7] += gb[z].w;
+    u[0] += ua[z].x; u[1] += ua[z].y; u[2] += ua[z].z; u[3] += ua[z].w;
+    u[4] += ub[z].x; u[5] += ub[z].y; u[6] += ub[z].z; u[7] += ub[z].w;
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) g[e] = silu_mul(g[e], u[e]);
+  h[i] = pack8(g);
+}
+
+template <int S>
+static void swiglu_go(const float* part, void* h, int groups, size_t plane, hipStream_t s) {
+  const dim3 grid((unsigned)((groups + 255) / 256)), block(256);
+  FFN_DISPATCH(splitk_swiglu<S>, grid, block, 0, s, (const float4*)part, (uint4*)h, groups, plane);
+}
+
+// one instantiation per range count, 1..kPrefillMaxSplits
+template <template <int> class F, class... A>
+static bool by_splits(int splits, A... args) {
+  static_assert(kPrefillMaxSplits == 16 && kQuantMaxSplits <= kPrefillMaxSplits, "");
+  switch (splits) {
+    case 1: F<1>::go(args...); return true;
+    case 2: F<2>::go(args...); return true;
+    case 3: F<3>::go(args...); return true;
+    case 4: F<4>::go(args...); return true;
+    case 5: F<5>::go(args...); return true;
+    case 6: F<6>::go(args...); return true;
+    case 7: F<7>::go(args...); return true;
+    case 8: F<8>::go(args...); return true;
+    case 9: F<9>::go(args...); return true;
+    case 10: F<10>::go(args...); return true;
+    case 11: F<11>::go(args...); return true;
+    case 12: F<12>::go(args...); return true;
+    case 13: F<13>::go(args...); return true;
+    case 14: F<14>::go(args...); return true;
+    case 15: F<15>::go(args...); return true;
+    case 16: F<16>::go(args...); return true;
+  }
+  return false;
+}
+template <int S>
+struct ResidualGo {
+  static void go(const float* part, const void* x, void* y, int groups, size_t stride, hipStream_t s) {
+    splitk_go<S>(part, x, y, groups, stride, s);
+  }
+};
+template <int S>
+struct SwigluGo {
+  static void go(const float* part, void* h, int groups, size_t plane, hipStream_t s) {
+    swiglu_go<S>(part, h, groups, plane, s);
+  }
+};
+
 hipError_t launch_splitk_residual(const float* part, int splits, const void* x, void* y, int M,
                                   int N, hipStream_t s) {
-  static_assert(kQuantMaxSplits == 8, "one instantiation per range count");
   const int groups = M * (N / 8);
   const size_t stride = (size_t)M * N / 4;
-  switch (splits) {
-    case 1: splitk_go<1>(part, x, y, groups, stride, s); break;
-    case 2: splitk_go<2>(part, x, y, groups, stride, s); break;
-    case 3: splitk_go<3>(part, x, y, groups, stride, s); break;
-    case 4: splitk_go<4>(part, x, y, groups, stride, s); break;
-    case 5: splitk_go<5>(part, x, y, groups, stride, s); break;
-    case 6: splitk_go<6>(part, x, y, groups, stride, s); break;
-    case 7: splitk_go<7>(part, x, y, groups, stride, s); break;
-    case 8: splitk_go<8>(part, x, y, groups, stride, s); break;
-    default: return hipErrorInvalidValue;
-  }
+  if (!by_splits<ResidualGo>(splits, part, x, y, groups, stride, s)) return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_splitk_swiglu(const float* part, int splits, void* h, int M, int f,
+                                hipStream_t s) {
+  const int groups = M * (f / 8);
+  const size_t plane = (size_t)M * f / 4;
+  if (!by_splits<SwigluGo>(splits, part, h, groups, plane, s)) return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
