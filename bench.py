@@ -34,7 +34,7 @@ The same JSON line also carries:
                   each workload's error of this run's GPU output against it.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra] [--no-cpu]
-                       [--extras decode_m,persistent,ceilings,rmsnorm,q8,q4,prefill,tiny,tp8]
+                       [--extras decode_m,persistent,ceilings,rmsnorm,q8,q4,prefill,mid,tiny,tp8]
        (W untimed calls, continued until at least --min-warmup-s seconds, default 1,
         have passed; then K timed)
        python bench.py --profile-run   (decode steps plus one 512 MiB copy, for
@@ -153,7 +153,7 @@ def kernel_times(ffn, fn, n):
     return {k: round(t / c * 1e3, 2) for k, (c, t) in kt.items()}
 
 
-EXTRAS = ("decode_m", "persistent", "ceilings", "rmsnorm", "q8", "q4", "prefill", "tiny", "tp8")
+EXTRAS = ("decode_m", "persistent", "ceilings", "rmsnorm", "q8", "q4", "prefill", "mid", "tiny", "tp8")
 
 
 def per_call_us(torch, fn, n):
@@ -515,6 +515,40 @@ def extras(torch, np, ffn, I, sets, x, g, b, ws, extra, clocks, want, keep):
         keep[f"{'C5 ' if kind == 'q8' else ''}{kind} decode M={Mq}"] = dict(
             kind=kind, inputs=q, gpu=to_host(qy), work=qbytes, unit="GB/s")
         log(kind, res)
+
+    if "mid" in want:
+        # ------------------------------------------ batches between decode and prefill
+        wl = I.WORKLOADS["mid_batch"]
+        Ms, dm, fm = wl["M"], wl["d"], wl["f"]
+        log("generating mid-batch inputs", wl)
+        bm = I.make_block(wl["seed"], max(Ms), dm, fm, "bf16")
+        mx_all, mg = to_dev(bm.x, torch), to_dev(bm.g, torch)
+        mw = [[to_dev(a, torch) for a in (bm.w_gate, bm.w_up, bm.w_down)]]
+        nrot_m = max(2, int(600e6 // (3 * fm * dm * 2)) + 1)  # past the memory-side cache
+        mw += [[t.clone() for t in mw[0]] for _ in range(nrot_m - 1)]
+        res = {}
+        for Mm in Ms:
+            mx = mx_all[:Mm].contiguous()
+            my = torch.empty_like(mx)
+            mws = ffn.alloc_workspace(ffn.workspace_size(ffn.FFN_BF16, Mm, dm, fm, "auto"))
+
+            def mstep(i, mx=mx, my=my, mws=mws):
+                wg, wu, wd = mw[i % nrot_m]
+                ffn.swiglu_block(mx, mg, wg, wu, wd, bm.eps, "auto", out=my, workspace=mws)
+            warm_up(mstep)
+            t = time_calls(torch, mstep, 40)
+            km = kernel_times(ffn, mstep, 8)
+            res[f"M={Mm}"] = {"us": round(t * 1e3, 2),
+                              "weights_GBps": round(3 * fm * dm * 2 / (t * 1e-3) / 1e9, 1),
+                              "TFLOPs": round(6.0 * Mm * dm * fm / (t * 1e-3) / 1e12, 1),
+                              "kernels_us_event_timed": km}
+            del mws
+        res["note"] = ("AUTO at d=4096, f=11008 (the decode block's weights); GEMMs whose 256x256 "
+                       "tiles number fewer than the CUs are split over K")
+        extra["mid_batch"] = res
+        log("mid batch", res)
+        del mw, mx_all
+        torch.cuda.empty_cache()
 
     if "tiny" in want:
         # ------------------------------------------------------- tiny fp32 block

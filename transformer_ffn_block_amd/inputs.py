@@ -297,4 +297,7 @@ WORKLOADS = {
     "prefill_tp8_shard": dict(seed=8, M=8192, d=4096, f=14336 // 8, dtype="bf16"),
     "q8_tp8_shard":      dict(seed=9, M=8, d=5120, f=17408 // 8),
     "q4_tp8_shard":      dict(seed=10, M=8, d=5120, f=17408 // 8),
+    # between decode and prefill: the decode block's weights at batch sizes
+    # whose GEMM tiles do not fill the chip (the first M rows of x)
+    "mid_batch":         dict(seed=11, M=(128, 512, 2048), d=4096, f=11008, dtype="bf16"),
 }
