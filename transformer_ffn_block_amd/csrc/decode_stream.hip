@@ -789,15 +789,7 @@ hipError_t launch_decode_persistent(const void* x, const void* g, const void* wg
   FFN_DISPATCH(clear_u32, dim3((unsigned)((nc + 255) / 256)), dim3(256), 0, s, ctr, nc);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  static int cus = 0;  // compute units of the device (gfx950 parts share one count)
-  if (cus == 0) {
-    int dev = 0, v = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-      cus = v;
-    else
-      cus = 256;
-  }
+  const int cus = device_cus();
   const int n_items = (f + 15) / 16 + ((d + 15) / 16) * splits;
   const int grid = n_items < FFN_DS_PERSIST_WPE * cus ? n_items : FFN_DS_PERSIST_WPE * cus;
   FFN_DISPATCH(decode_persistent, dim3((unsigned)grid), dim3(kPersistWaves * 64), 0, s,

@@ -7,6 +7,8 @@
 // with four independent loads in flight per lane; the read probe's grid is a
 // parameter so callers can sweep occupancy ("Megakernels on Mac",
 // "Bandwidth and memory measurements": best of a sweep, not one geometry).
+#include <atomic>
+
 #include "common.h"
 #include "launch.h"
 
@@ -104,12 +106,16 @@ __global__ __launch_bounds__(256) void probe_mfma(int iters, float* __restrict__
   if (v == 1234.5678f) sink[blockIdx.x * 256 + threadIdx.x] = v;
 }
 
+// queried once per device (grid sizes read it on every launch)
 int device_cus() {
+  static std::atomic<int> cached[64];
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 256;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+  if (dev >= 0 && dev < 64 && (cus = cached[dev].load(std::memory_order_relaxed)) > 0) return cus;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
     return 256;
-  return cus > 0 ? cus : 256;
+  if (dev >= 0 && dev < 64) cached[dev].store(cus, std::memory_order_relaxed);
+  return cus;
 }
 
 int probe_read_groups(int waves_per_cu) {
