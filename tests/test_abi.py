@@ -103,6 +103,43 @@ def test_block_zero_tokens_is_a_noop(L):
     assert L.ffn_last_error().decode() == ""
 
 
+def _prefill_splits_rule(M, N, K, bno, cus=256):
+    """The documented split rule for a prefill GEMM (256-token tiles, bno
+    weight rows per tile, 64-deep K tiles in ranges of two when they pair up)."""
+    if K % 64:
+        return 1
+    tiles = -(-M // 256) * -(-N // bno)
+    nk = K // 64
+    pp = M % 256 == 0 and N % bno == 0 and K % 128 == 0
+    units = nk // 2 if (pp or nk % 2 == 0) else nk
+    z = min(cus // tiles, 16, units)
+    return max(z, 1)
+
+
+@pytest.mark.parametrize("M,d,f", [(65, 4096, 11008), (128, 4096, 11008), (256, 1024, 2048),
+                                   (300, 512, 768), (512, 4096, 14336), (1000, 4096, 11008),
+                                   (2048, 5120, 13824), (4096, 4096, 14336), (100, 1032, 576),
+                                   (777, 2048, 704)])
+def test_prefill_split_workspace(L, M, d, f):
+    """Above 64 tokens the bf16 workspace adds one fp32 region for split-K
+    partials: 2 Z_gu [M, f] planes (fused gate/up) or Z_dn [M, d] planes
+    (down), whichever is larger, with Z from the documented rule on 256 CUs
+    (the count assumed without a device); SPLIT splits only the down GEMM."""
+    def r256(n):
+        return (n + 255) // 256 * 256
+    zg = _prefill_splits_rule(M, f, d, 128)
+    zd = _prefill_splits_rule(M, d, f, 256)
+    pg = 2 * zg * M * f * 4 if zg > 1 else 0
+    pd = zd * M * d * 4 if zd > 1 else 0
+    base = r256(M * d * 2) + r256(M * f * 2)
+    part = r256(max(pg, pd)) if max(pg, pd) else 0
+    assert L.ffn_swiglu_block_workspace_size(ffn.FFN_BF16, M, d, f, 1) == base + part
+    assert L.ffn_swiglu_block_workspace_size(ffn.FFN_BF16, M, d, f, 2) == \
+        base + 2 * r256(M * f * 2) + (r256(pd) if pd else 0)
+    # fp32 blocks never split
+    assert L.ffn_swiglu_block_workspace_size(ffn.FFN_F32, M, d, f, 1) == r256(M * d * 4) + r256(M * f * 4)
+
+
 def test_workspace_sizes(L):
     def r256(n):
         return (n + 255) // 256 * 256
