@@ -396,6 +396,33 @@ def extras(torch, np, ffn, I, sets, x, g, b, ws, extra, clocks, want, keep):
             keep[f"C3 decode M={m}"] = dict(kind="block", inputs=(b, m), gpu=to_host(ym),
                                             work=decode_bytes(m, d, f), unit="GB/s")
             log(f"decode M={m}: {msm * 1e3:.2f} us/call")
+        # M = 16 calls replayed from a HIP graph (40 captured calls over the
+        # rotated weight sets): the same kernels without per-call host work
+        yg = torch.empty_like(x)
+
+        def stepg(i):
+            wg, wu, wd = sets[i % ROTATE]
+            ffn.swiglu_block(x, g, wg, wu, wd, b.eps, "auto", out=yg, workspace=ws)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for i in range(ROTATE):
+                stepg(i)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        ncap = 40
+        with torch.cuda.graph(graph):
+            for i in range(ncap):
+                stepg(i)
+        for _ in range(5):
+            graph.replay()
+        tg = time_calls(torch, lambda i: graph.replay(), 10) / ncap
+        extra["decode_M16_hip_graph"] = {"us": round(tg * 1e3, 2),
+                                         "GBps": round(decode_bytes(M, d, f) / (tg * 1e-3) / 1e9, 1),
+                                         "calls_per_graph": ncap}
+        log(f"decode M=16 from a HIP graph: {tg * 1e3:.2f} us/call")
+        del graph
     if "persistent" in want:
         # the single-dispatch (persistent) schedule at M = 16, interleaved with the
         # default two-launch schedule

@@ -943,3 +943,41 @@ def test_q8_max_size_zero_down_and_one_hot(gpu_lib):
     want = O.bf16_to_f64(q.x[:, i]) + O.silu(n @ row(wg)) * (n @ row(wu))
     err = float(np.max(np.abs(a[:, i] - want)) / np.max(np.abs(want)))
     assert record(f"q8 max size {M}x{d}x{f} (one-hot down column)", err, TOL_Q8) <= TOL_Q8
+
+
+# ----------------------------------------------------------------------------
+# HIP graphs: a block call captured on torch's capture stream and replayed
+# gives the eager call's bits on every replay (with eager work and
+# synchronisations between replays).  Decode kernels, and 128 tokens on the
+# split-K prefill GEMMs (their partial passes included).
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("M,d,f", [(16, 1024, 2816), (128, 1024, 2048)])
+def test_block_replayed_from_hip_graph(gpu_lib, M, d, f):
+    from transformer_ffn_block_amd import ffn
+    import torch
+    _say("block hip graph", M, d, f)
+    b = I.make_block(5800 + M, M, d, f, "bf16")
+    x, g, wg, wu, wd = _block_dev(b)
+    ws = ffn.alloc_workspace(ffn.workspace_size(ffn.FFN_BF16, M, d, f, "auto"))
+    y = torch.empty_like(x)
+    ref = host_bits(ffn.swiglu_block(x, g, wg, wu, wd, b.eps, variant="auto"))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up off the default stream, as capture requires
+        ffn.swiglu_block(x, g, wg, wu, wd, b.eps, variant="auto", out=y, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        ffn.swiglu_block(x, g, wg, wu, wd, b.eps, variant="auto", out=y, workspace=ws)
+    for rep in range(4):
+        y.fill_(float("nan"))
+        ws.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host_bits(y), ref), rep
+        # an eager call between replays leaves the captured one unaffected
+        ffn.swiglu_block(x, g, wg, wu, wd, b.eps, variant="auto", out=y, workspace=ws)
+        torch.cuda.synchronize()
+    del graph
