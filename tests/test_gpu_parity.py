@@ -981,3 +981,33 @@ def test_block_replayed_from_hip_graph(gpu_lib, M, d, f):
         ffn.swiglu_block(x, g, wg, wu, wd, b.eps, variant="auto", out=y, workspace=ws)
         torch.cuda.synchronize()
     del graph
+
+
+# ----------------------------------------------------------------------------
+# seeded random shapes across every regime (decode kernels, the 33..64-token
+# single launches, split-K and whole prefill GEMMs, balanced grids), each
+# against the oracle
+# ----------------------------------------------------------------------------
+def _random_shapes(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        M = int(rng.choice([rng.integers(1, 17), rng.integers(17, 65), rng.integers(65, 420)]))
+        # half the dimensions on the 64-deep K tile (LDS-fed and split-K
+        # GEMMs), half anywhere on the 8-element grid (register-staged GEMMs,
+        # ragged decode stages)
+        d = int(rng.integers(1, 17)) * 64 if rng.random() < 0.5 else int(rng.integers(1, 129)) * 8
+        f = int(rng.integers(1, 17)) * 64 if rng.random() < 0.5 else int(rng.integers(1, 129)) * 8
+        v = str(rng.choice(["auto", "fused", "split"]))
+        out.append((M, d, f, v))
+    return out
+
+
+@pytest.mark.parametrize("M,d,f,variant", _random_shapes(24, 2026))
+def test_block_random_shapes(gpu_lib, M, d, f, variant):
+    from transformer_ffn_block_amd import ffn
+    _say("block random shape", M, d, f, variant)
+    b = I.make_block(6000 + M + d + f, M, d, f, "bf16")
+    r = O.block_from_stored("bf16", b.x, b.g, b.w_gate, b.w_up, b.w_down, b.eps)
+    a = host_f64(_run_block(ffn, b, variant))
+    assert record(f"random {M}x{d}x{f} {variant}", max_norm_err(a, r), TOL_BF16) <= TOL_BF16
