@@ -616,9 +616,12 @@ def test_q8_full_size(gpu_lib):
 
 
 # d, f not multiples of 256 leave a partial last stage in the 8-token (1, 3,
-# 5), 16-token (12) and direct (17, 33) kernels and in the split-K down pass
+# 5), 16-token (12) and 32-row staged (17, 24, 32, 33, 48) kernels and in the
+# split-K down pass; d = 544 and 800 also take the scale loads of unaligned
+# rows in the 32-row gate/up kernel
 @pytest.mark.parametrize("M,d,f", [(1, 64, 32), (3, 160, 96), (12, 288, 352), (17, 512, 704),
-                                   (33, 256, 800), (64, 256, 256), (5, 128, 4224)])
+                                   (33, 256, 800), (64, 256, 256), (5, 128, 4224), (24, 544, 416),
+                                   (32, 1024, 2048), (48, 800, 288)])
 def test_q8_ragged_tokens(gpu_lib, M, d, f):
     from transformer_ffn_block_amd import ffn
     _say("q8 ragged", M, d, f)
@@ -717,12 +720,13 @@ def test_q4_full_size(gpu_lib):
     assert record("q4 decode M=8", err, TOL_Q4) <= TOL_Q4
 
 
-# M: 1..8 and 9..16 take the staged-activation kernels, 17..32 the two-tile
-# kernel, > 32 several launches; d, f not multiples of 256 leave a partial
-# last stage and use the per-block scale loads; the down projections split
-# K over 1..8 ranges (8 for d = 128, f = 4224)
+# M: 1..8 and 9..16 take the staged-activation kernels, 17..32 the 32-row
+# staged two-tile kernel, > 32 several launches; d, f not multiples of 256
+# leave a partial last stage and use the per-block scale loads; the down
+# projections split K over 1..8 ranges (8 for d = 128, f = 4224)
 @pytest.mark.parametrize("M,d,f", [(1, 64, 32), (3, 160, 96), (12, 288, 352), (17, 512, 704),
-                                   (33, 256, 800), (64, 256, 256), (5, 128, 4224)])
+                                   (33, 256, 800), (64, 256, 256), (5, 128, 4224), (24, 544, 416),
+                                   (32, 1024, 2048), (48, 800, 288)])
 def test_q4_ragged_tokens(gpu_lib, M, d, f):
     from transformer_ffn_block_amd import ffn
     _say("q4 ragged", M, d, f)

@@ -73,6 +73,20 @@
 #ifndef FFN_Q4_GU8_WPE
 #define FFN_Q4_GU8_WPE 3
 #endif
+// 17..32 tokens with both token tiles staged through LDS in two-wave
+// workgroups, as for Q8_0 (0: activations read straight from L2).
+// Interleaved A/B, d = 5120, f = 17408: block 106 / 122 / 139 -> 92 / 96 /
+// 100 us at 17 / 24 / 32 tokens, 197 / 270 -> 160 / 194 us at 48 / 64;
+// d = 4096, f = 11008 at 32 tokens 78 -> 52 us.
+#ifndef FFN_Q4_STAGE32
+#define FFN_Q4_STAGE32 1
+#endif
+#ifndef FFN_Q4_S32_WAVES
+#define FFN_Q4_S32_WAVES 2
+#endif
+#ifndef FFN_Q4_S32_GB
+#define FFN_Q4_S32_GB 1
+#endif
 #ifndef FFN_Q4_GU8_GB
 #define FFN_Q4_GU8_GB 4
 #endif
@@ -196,10 +210,12 @@ void q4_stream(
   // resources with 32-bit offsets (fewer VGPRs); the down kernels keep plain
   // pointers (the freed registers raised their occupancy and measured slower)
   constexpr bool kBuf = NMAT == 2;
-  const uint4* pa[ASTAGE && kBuf ? 1 : (ASTAGE ? NA : MT)];
+  // (32 staged rows: both kinds form the row offset at each load instead)
+  constexpr bool kRow = ASTAGE >= 32;
+  const uint4* pa[ASTAGE && (kBuf || kRow) ? 1 : (ASTAGE ? NA : MT)];
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(act, (long)M * K * 2);
-  unsigned aro[ASTAGE && kBuf ? NA : 1];
-  if (ASTAGE) {
+  unsigned aro[ASTAGE && kBuf && !kRow ? NA : 1];
+  if (ASTAGE && !kRow) {
 #pragma unroll
     for (int v = 0; v < NA; ++v) {
       const int row = min(2 * v + (lane >> 5), M - 1);
@@ -208,7 +224,7 @@ void q4_stream(
       else
         pa[kBuf ? 0 : v] = reinterpret_cast<const uint4*>(act) + (size_t)row * K8;
     }
-  } else {
+  } else if (!ASTAGE) {
 #pragma unroll
     for (int t = 0; t < MT; ++t)
       pa[t] = reinterpret_cast<const uint4*>(act) + (size_t)min(t * 16 + r, M - 1) * K8;
@@ -280,7 +296,12 @@ void q4_stream(
       for (int v = 0; v < NA; ++v) {
         const int c = FOLD ? (lane & 31) : ((lane & 31) - (2 * v + (lane >> 5))) & 31;
         const int cc = cl(st * 32 + c, K8 - 1);
-        B.a[v] = kBuf ? buf_ld16(ra, aro[kBuf ? v : 0] + (unsigned)cc * 16u) : pa[kBuf ? 0 : v][cc];
+        if (kRow) {
+          const unsigned ro = (unsigned)min(2 * v + (lane >> 5), M - 1) * (unsigned)K8 * 16u;
+          B.a[v] = buf_ld16(ra, ro + (unsigned)cc * 16u);
+        } else {
+          B.a[v] = kBuf ? buf_ld16(ra, aro[kBuf && !kRow ? v : 0] + (unsigned)cc * 16u) : pa[kBuf ? 0 : v][cc];
+        }
       }
       if (FOLD) B.g = G4[cl(st * 32 + (lane & 31), K8 - 1)];
     } else {
@@ -332,7 +353,7 @@ void q4_stream(
   auto compute = [&](const Batch& W, const Batch& B, int st) {
     const bool ragged = !KFULL && (st + 1) * SB > nb;
     // the MFMAs of a group of blocks first, then their scale FMAs
-    constexpr int GB = NMAT == 2 && ASTAGE == 8 && !FOLD ? FFN_Q4_GU8_GB : 4;
+    constexpr int GB = ASTAGE == 32 ? FFN_Q4_S32_GB : NMAT == 2 && ASTAGE == 8 && !FOLD ? FFN_Q4_GU8_GB : 4;
 #pragma unroll
     for (int b0 = 0; b0 < SB; b0 += GB) {
       f32x4 p[GB][NMAT][MT];
@@ -346,7 +367,7 @@ void q4_stream(
           if (ASTAGE) {
             // token r, chunk 4b + q of the stage; with 8 staged rows, lanes of
             // rows 8..15 re-read rows 0..7 (those outputs are never stored)
-            const int ar = r & (ASTAGE ? ASTAGE - 1 : 0);
+            const int ar = ASTAGE >= 32 ? t * 16 + r : r & (ASTAGE ? ASTAGE - 1 : 0);
             aa[t] = abuf[wave][ASTAGE ? ar * 32 + ((4 * b + q + ar) & 31) : 0];
           } else {
             aa[t] = B.a[b * MT + t];
@@ -545,6 +566,12 @@ static void launch_q4_mt(const uint16_t* a, const uint16_t* gn, float eps, const
       auto k = q4_stream<NMAT, 1, WAVES, SALIGN, 16, PART, false>;
       static const int slots = GU ? resident_slots(k, T) : 0;
       q4_go(k, GU, splits, N, T, a, gn, q0, s0, q1, s1, rr, o, part, M, K, eps, slots, s);
+    } else if (FFN_Q4_STAGE32) {
+      // 17..32 tokens: both token tiles staged through LDS (as for Q8_0)
+      constexpr int W2 = FFN_Q4_S32_WAVES;
+      auto k = q4_stream<NMAT, 2, W2, SALIGN, 32, PART, false>;
+      static const int slots = GU ? resident_slots(k, W2 * 64) : 0;
+      q4_go(k, GU, splits, N, W2 * 64, a, gn, q0, s0, q1, s1, rr, o, part, M, K, eps, slots, s);
     } else {
       auto k = q4_stream<NMAT, 2, WAVES, SALIGN, 0, PART, false>;
       static const int slots = GU ? resident_slots(k, T) : 0;

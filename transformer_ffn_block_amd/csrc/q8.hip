@@ -67,6 +67,22 @@
 #ifndef FFN_Q8_GU8_WPE
 #define FFN_Q8_GU8_WPE 3
 #endif
+// 17..32 tokens with both token tiles staged through LDS in two-wave
+// workgroups (0: activations read straight from L2 in the MFMA operand
+// layout, 256 VGPRs at four waves).  Interleaved A/B, d = 5120, f = 17408:
+// block 121 / 137 / 154 -> 107 / 111 / 116 us at 17 / 24 / 32 tokens, 230 /
+// 303 -> 191 / 226 us at 48 / 64 (two chunks); d = 4096, f = 11008 at 32
+// tokens 85 -> 59 us.  Then the waves per workgroup (four: 4-8% slower) and
+// the blocks per MFMA group of that kernel (two spills into AGPRs).
+#ifndef FFN_Q8_STAGE32
+#define FFN_Q8_STAGE32 1
+#endif
+#ifndef FFN_Q8_S32_WAVES
+#define FFN_Q8_S32_WAVES 2
+#endif
+#ifndef FFN_Q8_S32_GB
+#define FFN_Q8_S32_GB 1
+#endif
 #ifndef FFN_Q8_GU8_GB
 #define FFN_Q8_GU8_GB 1
 #endif
@@ -186,11 +202,11 @@ void q8_stream(
   const uint4* pa[ASTAGE ? 1 : MT];
   // staged rows through a buffer resource: 32-bit byte offsets per row
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(act, (long)M * K * 2);
-  unsigned aro[ASTAGE ? NA : 1];
+  unsigned aro[ASTAGE && ASTAGE < 32 ? NA : 1];
   if (ASTAGE) {
 #pragma unroll
     for (int v = 0; v < NA; ++v)
-      aro[ASTAGE ? v : 0] = (unsigned)min(2 * v + (lane >> 5), M - 1) * (unsigned)K8 * 16u;
+      if (ASTAGE < 32) aro[ASTAGE && ASTAGE < 32 ? v : 0] = (unsigned)min(2 * v + (lane >> 5), M - 1) * (unsigned)K8 * 16u;
   } else {
 #pragma unroll
     for (int t = 0; t < MT; ++t)
@@ -259,7 +275,11 @@ void q8_stream(
         // row 2v + (lane>>5): chunk (lane&31 - row) & 31 of its stage
         // segment, or chunk lane & 31 when folding
         const int c = FOLD ? (lane & 31) : ((lane & 31) - (2 * v + (lane >> 5))) & 31;
-        B.a[v] = buf_ld16(ra, aro[ASTAGE ? v : 0] + (unsigned)cl(st * 32 + c, K8 - 1) * 16u);
+        // 32 staged rows: the row offset is formed here (16 offsets held for
+        // the whole K loop would cost 16 VGPRs)
+        const unsigned ro = ASTAGE >= 32 ? (unsigned)min(2 * v + (lane >> 5), M - 1) * (unsigned)K8 * 16u
+                                         : aro[ASTAGE ? v : 0];
+        B.a[v] = buf_ld16(ra, ro + (unsigned)cl(st * 32 + c, K8 - 1) * 16u);
       }
       if (FOLD) B.g = G4[cl(st * 32 + (lane & 31), K8 - 1)];
     } else {
@@ -312,7 +332,7 @@ void q8_stream(
     const bool ragged = !KFULL && (st + 1) * SB > nb;
     // per block: the MFMAs of a group of blocks first, then their scale FMAs,
     // so the FMAs do not wait on each MFMA in turn
-    constexpr int GB = NMAT == 2 && ASTAGE == 8 && !FOLD ? FFN_Q8_GU8_GB : 4;
+    constexpr int GB = ASTAGE == 32 ? FFN_Q8_S32_GB : NMAT == 2 && ASTAGE == 8 && !FOLD ? FFN_Q8_GU8_GB : 4;
 #pragma unroll
     for (int b0 = 0; b0 < SB; b0 += GB) {
       f32x4 p[GB][NMAT][MT];
@@ -324,9 +344,10 @@ void q8_stream(
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
           if (ASTAGE) {
-            // token r, chunk 4b + q of the stage; with 8 staged rows, lanes of
-            // rows 8..15 re-read rows 0..7 (those outputs are never stored)
-            const int ar = r & (ASTAGE ? ASTAGE - 1 : 0);
+            // token r of tile t, chunk 4b + q of the stage; with 8 staged
+            // rows, lanes of rows 8..15 re-read rows 0..7 (those outputs are
+            // never stored); 32 staged rows hold both token tiles
+            const int ar = ASTAGE >= 32 ? t * 16 + r : r & (ASTAGE ? ASTAGE - 1 : 0);
             aa[t] = abuf[wave][ASTAGE ? ar * 32 + ((4 * b + q + ar) & 31) : 0];
           } else {
             aa[t] = B.a[b * MT + t];
@@ -524,6 +545,13 @@ static void launch_q8_mt(const uint16_t* a, const uint16_t* gn, float eps, const
       auto k = q8_stream<NMAT, 1, WAVES, SALIGN, 16, PART, false>;
       static const int slots = GU ? resident_slots(k, T) : 0;
       q8_go(k, GU, splits, N, T, a, gn, q0, s0, q1, s1, rr, o, part, M, K, eps, slots, s);
+    } else if (FFN_Q8_STAGE32) {
+      // 17..32 tokens: both token tiles staged through LDS, in workgroups of
+      // FFN_Q8_S32_WAVES waves (32 staged rows take 16 KiB per wave)
+      constexpr int W2 = FFN_Q8_S32_WAVES;
+      auto k = q8_stream<NMAT, 2, W2, SALIGN, 32, PART, false>;
+      static const int slots = GU ? resident_slots(k, W2 * 64) : 0;
+      q8_go(k, GU, splits, N, W2 * 64, a, gn, q0, s0, q1, s1, rr, o, part, M, K, eps, slots, s);
     } else {
       auto k = q8_stream<NMAT, 2, WAVES, SALIGN, 0, PART, false>;
       static const int slots = GU ? resident_slots(k, T) : 0;
