@@ -155,8 +155,14 @@ ffn_status ffn_rmsnorm(ffn_dtype dt, const void *x, const void *g, void *y,
  * (Z_dn [M, d] planes), Z = floor(compute units / tiles), at most 16, at
  * least one 64-deep K tile per range (at d = 4096, f = 11008 on 256 CUs:
  * Z_gu = 2 up to 256 tokens; Z_dn = 16 / 8 / 4 / 2 up to 256 / 512 / 1024 /
- * 2048 tokens).  The size therefore depends on the current device's
- * compute-unit count (256 is assumed where no device can be queried).  The
+ * 2048 tokens).  A GEMM of whole tiles needing more than one round of
+ * resident tiles whose last round holds at most half a round splits only
+ * its last output columns (those beyond the ones filling the earlier
+ * rounds): its planes are then [M, columns split] (at 768 tokens and
+ * f = 11008, 16 planes of the last 128 gate and up columns).  The size
+ * therefore depends on the current device's compute-unit count and
+ * occupancy (256 CUs, one tile each, are assumed where no device can be
+ * queried).  The
  * workspace's contents are the library's own between calls; the sizes are
  * what a caller relies on. */
 size_t ffn_swiglu_block_workspace_size(ffn_dtype dt, int64_t M, int64_t d, int64_t f,

@@ -116,21 +116,44 @@ def _prefill_splits_rule(M, N, K, bno, cus=256):
     return max(z, 1)
 
 
+def _prefill_plan_rule(M, N, K, bno, slots=256):
+    """(main, z): output columns [0, main) unsplit, the rest over z K ranges.
+    A GEMM with fewer tiles than compute units splits whole; past one round
+    of `slots` resident tiles (whole tiles, K in pairs of 64-deep tiles), the
+    columns filling the earlier rounds run unsplit and the rest -- at most
+    half a round -- split into as many ranges as fill one round."""
+    z = _prefill_splits_rule(M, N, K, bno)
+    if z > 1:
+        return 0, z
+    if not (M % 256 == 0 and N % bno == 0 and K % 128 == 0):
+        return N, 1
+    mt, nt = M // 256, N // bno
+    if mt * nt <= slots:
+        return N, 1
+    nm = (-(-mt * nt // slots) - 1) * slots // mt
+    if nm < 1 or nm >= nt:
+        return N, 1
+    zt = min(slots // (mt * (nt - nm)), 16, K // 128)
+    return (nm * bno, zt) if zt >= 2 else (N, 1)
+
+
 @pytest.mark.parametrize("M,d,f", [(65, 4096, 11008), (128, 4096, 11008), (256, 1024, 2048),
                                    (300, 512, 768), (512, 4096, 14336), (1000, 4096, 11008),
                                    (2048, 5120, 13824), (4096, 4096, 14336), (100, 1032, 576),
-                                   (777, 2048, 704)])
+                                   (777, 2048, 704), (768, 4096, 11008), (1024, 4096, 11008),
+                                   (4352, 4096, 1024), (1536, 4096, 11008)])
 def test_prefill_split_workspace(L, M, d, f):
     """Above 64 tokens the bf16 workspace adds one fp32 region for split-K
-    partials: 2 Z_gu [M, f] planes (fused gate/up) or Z_dn [M, d] planes
-    (down), whichever is larger, with Z from the documented rule on 256 CUs
-    (the count assumed without a device); SPLIT splits only the down GEMM."""
+    partials: 2 Z_gu [M, f - main] planes (fused gate/up) or Z_dn
+    [M, d - main] planes (down), whichever is larger, with the plans from the
+    documented rule on 256 CUs (the count assumed without a device); SPLIT
+    plans only the down GEMM."""
     def r256(n):
         return (n + 255) // 256 * 256
-    zg = _prefill_splits_rule(M, f, d, 128)
-    zd = _prefill_splits_rule(M, d, f, 256)
-    pg = 2 * zg * M * f * 4 if zg > 1 else 0
-    pd = zd * M * d * 4 if zd > 1 else 0
+    cg, zg = _prefill_plan_rule(M, f, d, 128)
+    cd, zd = _prefill_plan_rule(M, d, f, 256)
+    pg = 2 * zg * M * (f - cg) * 4 if zg > 1 else 0
+    pd = zd * M * (d - cd) * 4 if zd > 1 else 0
     base = r256(M * d * 2) + r256(M * f * 2)
     part = r256(max(pg, pd)) if max(pg, pd) else 0
     assert L.ffn_swiglu_block_workspace_size(ffn.FFN_BF16, M, d, f, 1) == base + part
@@ -138,6 +161,20 @@ def test_prefill_split_workspace(L, M, d, f):
         base + 2 * r256(M * f * 2) + (r256(pd) if pd else 0)
     # fp32 blocks never split
     assert L.ffn_swiglu_block_workspace_size(ffn.FFN_F32, M, d, f, 1) == r256(M * d * 4) + r256(M * f * 4)
+
+
+def test_prefill_tail_plans():
+    """The plans the rule gives for shapes just past whole rounds: 768 tokens
+    at f = 11008 have 258 gate/up tiles, so 85 column tiles (255 tiles) run
+    unsplit and the last 3 split 16 ways; 4352 tokens at d = 4096 have 272
+    down tiles, the last column's 17 split over all 8 K ranges of f = 1024."""
+    assert _prefill_plan_rule(768, 11008, 4096, 128) == (85 * 128, 16)
+    assert _prefill_plan_rule(1024, 11008, 4096, 128) == (64 * 128, 2)
+    assert _prefill_plan_rule(4352, 4096, 1024, 256) == (15 * 256, 8)
+    assert _prefill_plan_rule(768, 4096, 11008, 256) == (0, 5)
+    # whole rounds: no split
+    assert _prefill_plan_rule(8192, 14336, 4096, 128) == (14336, 1)
+    assert _prefill_plan_rule(8192, 4096, 14336, 256) == (4096, 1)
 
 
 def test_workspace_sizes(L):

@@ -425,6 +425,56 @@ def test_block_prefill_split_k_decode_shape_sampled_rows(gpu_lib):
     assert record("prefill split-K 128x4096x11008 (24 rows)", max_norm_err(a, r), TOL_BF16) <= TOL_BF16
 
 
+# Tile counts just past a whole round: the columns filling the earlier rounds
+# run unsplit (row stride of the full output) and the last columns split over
+# K.  On a 256-CU device, one 256 x 256 tile resident per CU: (2304, 512,
+# 3712) has 9 x 29 = 261 gate/up tiles -> 28 column tiles unsplit, the last
+# one's 9 tiles over 4 K ranges (its down GEMM splits whole, 14 ways);
+# (4352, 4096, 256) has 17 x 16 = 272 down tiles -> 15 columns unsplit, the
+# last one's 17 over 2 ranges (K = 256).  The workspace size shows the plan.
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("M,d,f,part_bytes", [(2304, 512, 3712, max(2 * 4 * 2304 * 128 * 4, 14 * 2304 * 512 * 4)),
+                                              (4352, 4096, 256, max(2 * 7 * 4352 * 256 * 4, 2 * 4352 * 256 * 4))])
+def test_block_prefill_split_tail(gpu_lib, M, d, f, part_bytes):
+    from transformer_ffn_block_amd import ffn
+    import torch
+    _say("block prefill split tail", M, d, f)
+    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("plan sizes stated for 256 compute units")
+    r256 = lambda n: (n + 255) // 256 * 256
+    assert ffn.workspace_size(ffn.FFN_BF16, M, d, f) == r256(M * d * 2) + r256(M * f * 2) + r256(part_bytes)
+    b = I.make_block(5800 + M, M, d, f, "bf16")
+    r = O.block_from_stored("bf16", b.x, b.g, b.w_gate, b.w_up, b.w_down, b.eps)
+    a = host_f64(_run_block(ffn, b, "fused"))
+    assert record(f"prefill split tail {M}x{d}x{f}", max_norm_err(a, r), TOL_BF16) <= TOL_BF16
+    per_row = max(max_norm_err(a[i], r[i]) for i in range(M))
+    assert record(f"prefill split tail {M}x{d}x{f} worst row", per_row, TOL_BF16,
+                  "max_norm_per_row") <= TOL_BF16
+
+
+def test_block_prefill_split_tail_mid_batch_sampled_rows(gpu_lib):
+    """768 tokens at d = 4096, f = 11008 (258 gate/up tiles: 85 column tiles
+    unsplit, the last 3 tiles over 16 K ranges; 48 down tiles split whole)
+    against the oracle on 24 rows, spanning the unsplit and the split columns
+    of every row, and the same bits on a second call."""
+    from transformer_ffn_block_amd import ffn
+    import torch
+    M, d, f = 768, 4096, 11008
+    _say("block prefill split tail mid batch", M, d, f)
+    b = I.make_block(5900, M, d, f, "bf16")
+    x, g, wg, wu, wd = _block_dev(b)
+    y1 = ffn.swiglu_block(x, g, wg, wu, wd, b.eps, variant="auto")
+    y2 = ffn.swiglu_block(x, g, wg, wu, wd, b.eps, variant="auto")
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(y1), host_bits(y2))
+    rows = np.sort(np.concatenate([[0, 255, 256, 511, 512, 767],
+                                   np.random.default_rng(46).choice(np.arange(1, 767), 18, replace=False)]))
+    rows = np.unique(rows)
+    r = O.block_from_stored("bf16", b.x[rows], b.g, b.w_gate, b.w_up, b.w_down, b.eps)
+    a = host_f64(y1)[rows]
+    assert record("prefill split tail 768x4096x11008 (24 rows)", max_norm_err(a, r), TOL_BF16) <= TOL_BF16
+
+
 # ----------------------------------------------------------------------------
 # properties
 # ----------------------------------------------------------------------------

@@ -4,6 +4,7 @@
 // prints.
 #include <hip/hip_runtime_api.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -135,20 +136,22 @@ size_t decode_h_row_elems(int64_t f) {  // elements per token of blocked h
   return ffn::decode_h_blocked() ? (size_t)((f + 127) / 128) * 128 : (size_t)f;
 }
 
-// K ranges of the prefill GEMMs (bf16, more than decode_max_tokens()
-// tokens) when their tiles leave compute units idle; 1 = unsplit.  The gate/up
-// split applies to the fused GEMM (not SPLIT, not the register-staged
+// Split-K plans of the prefill GEMMs (bf16, more than decode_max_tokens()
+// tokens): columns [0, main) unsplit, the rest over z K ranges.  The gate/up
+// plan applies to the fused GEMM (not SPLIT, not the register-staged
 // FUSED_NORM kernel, which never splits).
 struct PrefillSplits {
-  int gu = 1, dn = 1;
+  ffn::PrefillPlan gu, dn;
 };
 PrefillSplits prefill_splits(size_t es, int64_t M, int64_t d, int64_t f, bool split, bool persistent) {
   PrefillSplits p;
+  p.gu.main = (int)std::min<int64_t>(f, INT32_MAX);
+  p.dn.main = (int)std::min<int64_t>(d, INT32_MAX);
   if (es != 2 || persistent || M <= ffn::decode_max_tokens() || M > INT32_MAX || d > INT32_MAX ||
       f > INT32_MAX)
     return p;
-  if (!split) p.gu = ffn::prefill_gateup_splits((int)M, (int)d, (int)f);
-  p.dn = ffn::prefill_down_splits((int)M, (int)d, (int)f);
+  if (!split) p.gu = ffn::prefill_gateup_plan((int)M, (int)d, (int)f);
+  p.dn = ffn::prefill_down_plan((int)M, (int)d, (int)f);
   return p;
 }
 
@@ -178,8 +181,8 @@ WsLayout ws_layout(size_t es, int64_t M, int64_t d, int64_t f, bool split, bool 
   // fp32 partial sums of split-K prefill GEMMs (gate/up planes, then reused
   // for the down projection's)
   const PrefillSplits ps = prefill_splits(es, M, d, f, split, persistent);
-  const size_t pgu = ps.gu > 1 ? (size_t)2 * ps.gu * M * f * 4 : 0;
-  const size_t pdn = ps.dn > 1 ? (size_t)ps.dn * M * d * 4 : 0;
+  const size_t pgu = ps.gu.z > 1 ? (size_t)2 * ps.gu.z * M * (f - ps.gu.main) * 4 : 0;
+  const size_t pdn = ps.dn.z > 1 ? (size_t)ps.dn.z * M * (d - ps.dn.main) * 4 : 0;
   if (pgu || pdn) {
     w.part = at;
     at += round256(pgu > pdn ? pgu : pdn);
@@ -360,20 +363,32 @@ ffn_status ffn_swiglu_block(ffn_dtype dt, const void* x, const void* g, const vo
     FFN_LAUNCH("gemm_gateup_fused_norm", s,
                ffn::launch_gemm_gateup_fused_norm(x, g, w_gate, w_up, h, Mi, di, fi, eps, s));
   } else if (!decode) {
-    if (sp.gu > 1) {
+    // columns [0, c) unsplit, [c, f) split over K (row stride f throughout)
+    const int c = sp.gu.main;
+    if (c > 0)
+      FFN_LAUNCH("gemm_gateup_fused", s,
+                 ffn::launch_gemm_gateup_fused(n, w_gate, w_up, h, Mi, di, c, s, fi));
+    if (sp.gu.z > 1) {
+      const size_t wo = (size_t)c * d * 2;
+      char* hc = (char*)h + (size_t)c * 2;
       FFN_LAUNCH("gemm_gateup_fused_splitk", s,
-                 ffn::launch_gemm_gateup_fused_part(n, w_gate, w_up, part, sp.gu, Mi, di, fi, s));
-      FFN_LAUNCH("splitk_swiglu", s, ffn::launch_splitk_swiglu(part, sp.gu, h, Mi, fi, s));
-    } else {
-      FFN_LAUNCH("gemm_gateup_fused", s, ffn::launch_gemm_gateup_fused(n, w_gate, w_up, h, Mi, di, fi, s));
+                 ffn::launch_gemm_gateup_fused_part(n, (const char*)w_gate + wo, (const char*)w_up + wo,
+                                                    part, sp.gu.z, Mi, di, fi - c, s));
+      FFN_LAUNCH("splitk_swiglu", s, ffn::launch_splitk_swiglu(part, sp.gu.z, hc, Mi, fi - c, s, fi));
     }
   }
   if (Mi > ffn::decode_max_tokens()) {
-    if (sp.dn > 1) {
-      FFN_LAUNCH("gemm_down_splitk", s, ffn::launch_gemm_down_part(h, w_down, part, sp.dn, Mi, di, fi, s));
-      FFN_LAUNCH("splitk_residual", s, ffn::launch_splitk_residual(part, sp.dn, x, y, Mi, di, s));
-    } else {
-      FFN_LAUNCH("gemm_down_residual", s, ffn::launch_gemm_residual(h, w_down, x, y, Mi, di, fi, s));
+    const int c = sp.dn.main;
+    if (c > 0)
+      FFN_LAUNCH("gemm_down_residual", s, ffn::launch_gemm_residual(h, w_down, x, y, Mi, c, fi, s, di));
+    if (sp.dn.z > 1) {
+      const size_t co = (size_t)c * 2;
+      FFN_LAUNCH("gemm_down_splitk", s,
+                 ffn::launch_gemm_down_part(h, (const char*)w_down + (size_t)c * f * 2, part, sp.dn.z,
+                                            Mi, di - c, fi, s));
+      FFN_LAUNCH("splitk_residual", s,
+                 ffn::launch_splitk_residual(part, sp.dn.z, (const char*)x + co, (char*)y + co, Mi,
+                                             di - c, s, di));
     }
     return ok();
   }

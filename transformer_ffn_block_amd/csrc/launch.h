@@ -74,8 +74,10 @@ hipError_t launch_decode_persistent(const void* x, const void* g, const void* wg
                                     int M, int d, int f, float eps, hipStream_t s);
 
 // Prefill (many tokens) LDS-tiled bf16 MFMA GEMMs, C[m][n] = sum_k A[m][k] W[n][k].
+// ldo (0: the output width): row stride of h / y and the residual, for a
+// GEMM over a column block of a wider output (pointers at the block).
 hipError_t launch_gemm_gateup_fused(const void* n, const void* wg, const void* wu, void* h,
-                                    int M, int d, int f, hipStream_t s);
+                                    int M, int d, int f, hipStream_t s, int ldo = 0);
 // The same with the RMSNorm folded in: x (not n) and the gain g go in, and
 // r_m scales the accumulators in the epilogue (register-staged kernel).
 hipError_t launch_gemm_gateup_fused_norm(const void* x, const void* g, const void* wg,
@@ -84,15 +86,21 @@ hipError_t launch_gemm_gateup_fused_norm(const void* x, const void* g, const voi
 hipError_t launch_gemm_store(const void* a, const void* w, void* c, int M, int N, int K,
                              hipStream_t s);
 hipError_t launch_gemm_residual(const void* a, const void* w, const void* resid, void* y,
-                                int M, int N, int K, hipStream_t s);
-// Split K for prefill GEMMs whose tiles leave compute units idle: the
-// number of K ranges (1: no split, use the launchers above), and the GEMMs
-// that write fp32 partial sums instead of their epilogue -- fused gate/up:
-// gate sums in part[z][M][f], up sums in part[Z + z][M][f]; down:
-// part[z][M][d] -- for launch_splitk_swiglu / launch_splitk_residual.
+                                int M, int N, int K, hipStream_t s, int ldo = 0);
+// Split K for prefill GEMMs whose tiles leave compute units idle.  A plan
+// runs output columns [0, main) with the launchers above and splits the
+// columns [main, N) over K into z ranges (z = 1: no split, main = N; main =
+// 0: the whole GEMM splits), with the GEMMs below that write fp32 partial
+// sums instead of their epilogue -- fused gate/up: gate sums in
+// part[z][M][f], up sums in part[Z + z][M][f]; down: part[z][M][d], f and d
+// being the split block's width -- for launch_splitk_swiglu /
+// launch_splitk_residual.
 constexpr int kPrefillMaxSplits = 16;
-int prefill_gateup_splits(int M, int d, int f);
-int prefill_down_splits(int M, int d, int f);
+struct PrefillPlan {
+  int main = 0, z = 1;
+};
+PrefillPlan prefill_gateup_plan(int M, int d, int f);
+PrefillPlan prefill_down_plan(int M, int d, int f);
 hipError_t launch_gemm_gateup_fused_part(const void* n, const void* wg, const void* wu, float* part,
                                          int Z, int M, int d, int f, hipStream_t s);
 hipError_t launch_gemm_down_part(const void* h, const void* wd, float* part, int Z, int M, int d,
@@ -100,7 +108,7 @@ hipError_t launch_gemm_down_part(const void* h, const void* wd, float* part, int
 // h[m,j] = bf16(silu(sum_z G_z[m,j]) * sum_z U_z[m,j]), ranges added in z
 // order, from the partial planes above (f % 8 == 0).
 hipError_t launch_splitk_swiglu(const float* part, int splits, void* h, int M, int f,
-                                hipStream_t s);
+                                hipStream_t s, int ldo = 0);
 // h = silu(G) * U elementwise over `count` bf16 values (count % 8 == 0).
 hipError_t launch_swiglu_bf16(const void* G, const void* U, void* h, int64_t count,
                               hipStream_t s);
@@ -144,9 +152,11 @@ hipError_t launch_q4_down(const void* h, const uint8_t* qd, const uint16_t* sd, 
 int q4_max_tokens();
 
 // y[m,i] = bf16(x[m,i] + sum_{z < splits} part[z][m][i]), summed in z order
-// (N % 8 == 0; splits <= kPrefillMaxSplits).
+// (N % 8 == 0; splits <= kPrefillMaxSplits).  ldo (0: N): row stride of x, y
+// and h in elements, a multiple of 8, when the partials cover a column block
+// of a wider output (the pointers then point at the block's first column).
 hipError_t launch_splitk_residual(const float* part, int splits, const void* x, void* y, int M,
-                                  int N, hipStream_t s);
+                                  int N, hipStream_t s, int ldo = 0);
 
 // Bandwidth probes.
 int probe_read_groups(int waves_per_cu);

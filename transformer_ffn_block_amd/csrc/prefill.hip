@@ -419,8 +419,8 @@ __device__ __forceinline__ int dswz(int row) {
 template <int EPI, int FN, int FM, int TM, int TN, bool WIDE = false>
 __device__ __forceinline__ void dma_epilogue(const f32x4 (&acc)[FN][FM],
                                              const uint16_t* __restrict__ resid,
-                                             uint16_t* __restrict__ out, int M, int N, int m0,
-                                             int n0, int wm, int wn, int fr, int fq) {
+                                             uint16_t* __restrict__ out, int M, int N, int ldo,
+                                             int m0, int n0, int wm, int wn, int fr, int fq) {
   if constexpr (WIDE) {
     constexpr int NA = EPI == EPI_SWIGLU ? FN / 2 : FN;  // output sub-tiles across n
     static_assert(NA % 2 == 0, "sub-tiles pair up");
@@ -433,7 +433,7 @@ __device__ __forceinline__ void dma_epilogue(const f32x4 (&acc)[FN][FM],
       for (int a = 0; a < NA; ++a)
 #pragma unroll
         for (int b = 0; b < FM; ++b)
-          xr[a][b] = *reinterpret_cast<const uint2*>(resid + (size_t)(m0 + wm * TM + b * 16 + fr) * N +
+          xr[a][b] = *reinterpret_cast<const uint2*>(resid + (size_t)(m0 + wm * TM + b * 16 + fr) * ldo +
                                                      cw + a * 16 + 4 * fq);
     }
 #pragma unroll
@@ -470,7 +470,7 @@ __device__ __forceinline__ void dma_epilogue(const f32x4 (&acc)[FN][FM],
         const uint32_t ry = (uint32_t)__shfl_xor((int)send.y, 16, 64);
         const uint4 v = odd ? make_uint4(rx, ry, keep.x, keep.y) : make_uint4(keep.x, keep.y, rx, ry);
         const int col = cw + (2 * pr + (odd ? 1 : 0)) * 16 + 4 * (fq & 2);
-        *reinterpret_cast<uint4*>(out + (size_t)tok * N + col) = v;
+        *reinterpret_cast<uint4*>(out + (size_t)tok * ldo + col) = v;
       }
     }
     return;
@@ -487,7 +487,7 @@ __device__ __forceinline__ void dma_epilogue(const f32x4 (&acc)[FN][FM],
           uint2 o;
           o.x = pack_bf16x2(silu_mul(gg[0], uu[0]), silu_mul(gg[1], uu[1]));
           o.y = pack_bf16x2(silu_mul(gg[2], uu[2]), silu_mul(gg[3], uu[3]));
-          *reinterpret_cast<uint2*>(out + (size_t)tok * N + col) = o;
+          *reinterpret_cast<uint2*>(out + (size_t)tok * ldo + col) = o;
         }
       }
     }
@@ -503,7 +503,7 @@ __device__ __forceinline__ void dma_epilogue(const f32x4 (&acc)[FN][FM],
 #pragma unroll
         for (int b = 0; b < FM; ++b) {
           const int tok = m0 + wm * TM + b * 16 + fr;
-          const size_t off = (tok < M && col < N) ? (size_t)tok * N + col : 0;
+          const size_t off = (tok < M && col < N) ? (size_t)tok * ldo + col : 0;
           xr[a][b] = *reinterpret_cast<const uint2*>(resid + off);
         }
       }
@@ -515,7 +515,7 @@ __device__ __forceinline__ void dma_epilogue(const f32x4 (&acc)[FN][FM],
       for (int b = 0; b < FM; ++b) {
         const int tok = m0 + wm * TM + b * 16 + fr;
         if (tok < M && col < N) {
-          const size_t off = (size_t)tok * N + col;
+          const size_t off = (size_t)tok * ldo + col;
           f32x4 v = acc[a][b];
           if (EPI == EPI_RESIDUAL) {
             v[0] += bf2f(xr[a][b].x & 0xFFFFu);
@@ -551,7 +551,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_dma(
     const uint16_t* __restrict__ w1,     // [N, K]  (up for SWIGLU)
     const uint16_t* __restrict__ resid,  // [M, N]  (RESIDUAL)
     uint16_t* __restrict__ out,          // [M, N]
-    int M, int N, int K, float* __restrict__ part) {
+    int M, int N, int K, int ldo, float* __restrict__ part) {
   constexpr int NT = WM * WN * 64;
   constexpr int TM = BM / WM, TN = BN / WN;
   constexpr int FM = TM / 16, FN = TN / 16;
@@ -840,7 +840,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_dma(
           va = (unsigned)(m1 + rr) * (unsigned)K * 2u + cgp;
           static_for<S>([&](auto si) { issue_pp(decltype(si)::value, decltype(si)::value, vw, va); });
         }
-        dma_epilogue<EPI, FN, FM, TM, TN, FFN_PF_WIDE != 0>(acc, resid, out, M, N, pm0, pn0, wm, wn, fr, fq);
+        dma_epilogue<EPI, FN, FM, TM, TN, FFN_PF_WIDE != 0>(acc, resid, out, M, N, ldo, pm0, pn0, wm, wn, fr, fq);
         if (next >= T) return;
 #pragma unroll
         for (int a = 0; a < FN; ++a)
@@ -899,7 +899,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_dma(
     return;
   }
   // whole tiles (the ping-pong schedule) store 16 bytes per lane
-  dma_epilogue<EPI, FN, FM, TM, TN, PP && FFN_PF_WIDE != 0>(acc, resid, out, M, N, m0, n0, wm, wn, fr, fq);
+  dma_epilogue<EPI, FN, FM, TM, TN, PP && FFN_PF_WIDE != 0>(acc, resid, out, M, N, ldo, m0, n0, wm, wn, fr, fq);
 }
 
 // Tile configuration: 256 tokens x 256 weight rows, 8 waves as 2 x 4, each
@@ -931,9 +931,24 @@ static hipError_t launch_reg(const void* act, const void* w0, const void* w1, co
   return hipGetLastError();
 }
 
+// Workgroups of the persistent ping-pong kernel resident at once (a multiple
+// of 8, one per XCD slot; one per compute unit if the runtime cannot tell:
+// its LDS stages take 128 KB).
+template <int EPI>
+static int pp_slots() {
+  static const int slots = [] {
+    const int r = resident_slots(gemm_dma<kBM, kBN, kWM, kWN, EPI, kPpBK, kPpS, true, true>, kWM * kWN * 64);
+    return (r > 0 ? r : device_cus()) / 8 * 8;
+  }();
+  return slots;
+}
+
+// ldo: row stride of out and resid in elements (N unless the GEMM covers a
+// column block of a wider output)
 template <int EPI>
 static hipError_t launch_cfg(const void* act, const void* w0, const void* w1, const void* resid,
-                             void* out, int M, int N, int K, hipStream_t s) {
+                             void* out, int M, int N, int K, hipStream_t s, int ldo = 0) {
+  if (ldo <= 0) ldo = N;
   constexpr int BNO = EPI == EPI_SWIGLU ? kBN / 2 : kBN;
   const long tiles = (long)((M + kBM - 1) / kBM) * ((N + BNO - 1) / BNO);
   // whole K tiles and every operand addressable by a buffer resource: LDS-fed kernel
@@ -943,19 +958,19 @@ static hipError_t launch_cfg(const void* act, const void* w0, const void* w1, co
     // walked persistently when the tiles take more than one round
     if (kPingPong && M % kBM == 0 && N % BNO == 0 && K % (kPpS * kPpBK) == 0) {
       auto pers = gemm_dma<kBM, kBN, kWM, kWN, EPI, kPpBK, kPpS, true, true>;
-      static const int slots = resident_slots(pers, kWM * kWN * 64) / 8 * 8;
+      const int slots = pp_slots<EPI>();
       if (FFN_PF_PERSIST && slots >= 8 && tiles > slots)
         FFN_DISPATCH(pers, dim3((unsigned)slots), dim3(kWM * kWN * 64), 0, s, (const uint16_t*)act,
                      (const uint16_t*)w0, (const uint16_t*)w1, (const uint16_t*)resid, (uint16_t*)out, M,
-                     N, K, nullptr);
+                     N, K, ldo, nullptr);
       else
         FFN_DISPATCH((gemm_dma<kBM, kBN, kWM, kWN, EPI, kPpBK, kPpS, true>), dim3((unsigned)tiles),
                      dim3(kWM * kWN * 64), 0, s, (const uint16_t*)act, (const uint16_t*)w0,
-                     (const uint16_t*)w1, (const uint16_t*)resid, (uint16_t*)out, M, N, K, nullptr);
+                     (const uint16_t*)w1, (const uint16_t*)resid, (uint16_t*)out, M, N, K, ldo, nullptr);
     } else
       FFN_DISPATCH((gemm_dma<kBM, kBN, kWM, kWN, EPI, kDmaBK, kDmaS, false>), dim3((unsigned)tiles),
                          dim3(kWM * kWN * 64), 0, s, (const uint16_t*)act, (const uint16_t*)w0,
-                         (const uint16_t*)w1, (const uint16_t*)resid, (uint16_t*)out, M, N, K, nullptr);
+                         (const uint16_t*)w1, (const uint16_t*)resid, (uint16_t*)out, M, N, K, ldo, nullptr);
     return hipGetLastError();
   }
   return launch_reg<EPI>(act, w0, w1, resid, out, M, N, K, nullptr, 0.f, s);
@@ -989,8 +1004,45 @@ static int splits_for(int M, int N, int K, int bno) {
   if (z > units) z = units;
   return z > 1 ? (int)z : 1;
 }
-int prefill_gateup_splits(int M, int d, int f) { return splits_for(M, f, d, kBN / 2); }
-int prefill_down_splits(int M, int d, int f) { return splits_for(M, d, f, kBN); }
+
+// Past one round, a tile count just above a whole number of rounds leaves
+// the last round nearly empty (258 fused gate/up tiles at 768 tokens and
+// f = 11008 take two rounds of 256).  Then the columns that fill the rounds
+// before it run unsplit, and the rest -- at most half a round of tiles --
+// split over K into as many ranges as fill one round; FFN_PF_TAIL is the
+// least number of ranges worth the partial sums' extra traffic (0: off).
+#ifndef FFN_PF_TAIL
+#define FFN_PF_TAIL 2
+#endif
+template <int EPI>
+static PrefillPlan plan_for(int M, int N, int K) {
+  constexpr int BNO = EPI == EPI_SWIGLU ? kBN / 2 : kBN;
+  PrefillPlan p;
+  p.main = N;
+  const int z = splits_for(M, N, K, BNO);
+  if (z > 1) {
+    p.main = 0;
+    p.z = z;
+    return p;
+  }
+  if (!FFN_PF_SPLITK || FFN_PF_TAIL < 2 || !dma_ok(M, N, K) || !pp_ok(M, N, K, BNO)) return p;
+  const long mt = M / kBM, nt = N / BNO, tiles = mt * nt, slots = pp_slots<EPI>();
+  if (slots < 8 || tiles <= slots) return p;
+  const long rounds = (tiles + slots - 1) / slots;
+  const long nm = (rounds - 1) * slots / mt;  // column tiles filling the earlier rounds
+  if (nm < 1 || nm >= nt) return p;
+  const long tail = mt * (nt - nm);
+  const long units = K / kPpBK % kPpS == 0 ? K / kPpBK / kPpS : K / kPpBK;
+  long zt = slots / tail;
+  if (zt > kPrefillMaxSplits) zt = kPrefillMaxSplits;
+  if (zt > units) zt = units;
+  if (zt < FFN_PF_TAIL) return p;
+  p.main = (int)(nm * BNO);
+  p.z = (int)zt;
+  return p;
+}
+PrefillPlan prefill_gateup_plan(int M, int d, int f) { return plan_for<EPI_SWIGLU>(M, f, d); }
+PrefillPlan prefill_down_plan(int M, int d, int f) { return plan_for<EPI_RESIDUAL>(M, d, f); }
 
 template <int EPI>
 static hipError_t launch_part(const void* act, const void* w0, const void* w1, float* part, int Z,
@@ -1002,11 +1054,11 @@ static hipError_t launch_part(const void* act, const void* w0, const void* w1, f
   if (pp_ok(M, N, K, BNO))
     FFN_DISPATCH((gemm_dma<kBM, kBN, kWM, kWN, EPI, kPpBK, kPpS, true, false, true>), grid, block, 0, s,
                  (const uint16_t*)act, (const uint16_t*)w0, (const uint16_t*)w1, nullptr, nullptr, M,
-                 N, K, part);
+                 N, K, N, part);
   else
     FFN_DISPATCH((gemm_dma<kBM, kBN, kWM, kWN, EPI, kDmaBK, kDmaS, false, false, true>), grid, block,
                  0, s, (const uint16_t*)act, (const uint16_t*)w0, (const uint16_t*)w1, nullptr,
-                 nullptr, M, N, K, part);
+                 nullptr, M, N, K, N, part);
   return hipGetLastError();
 }
 
@@ -1020,8 +1072,8 @@ hipError_t launch_gemm_down_part(const void* h, const void* wd, float* part, int
 }
 
 hipError_t launch_gemm_gateup_fused(const void* n, const void* wg, const void* wu, void* h,
-                                    int M, int d, int f, hipStream_t s) {
-  return launch_cfg<EPI_SWIGLU>(n, wg, wu, nullptr, h, M, f, d, s);
+                                    int M, int d, int f, hipStream_t s, int ldo) {
+  return launch_cfg<EPI_SWIGLU>(n, wg, wu, nullptr, h, M, f, d, s, ldo);
 }
 hipError_t launch_gemm_gateup_fused_norm(const void* x, const void* g, const void* wg,
                                          const void* wu, void* h, int M, int d, int f, float eps,
@@ -1033,8 +1085,8 @@ hipError_t launch_gemm_store(const void* a, const void* w, void* c, int M, int N
   return launch_cfg<EPI_STORE>(a, w, nullptr, nullptr, c, M, N, K, s);
 }
 hipError_t launch_gemm_residual(const void* a, const void* w, const void* resid, void* y,
-                                int M, int N, int K, hipStream_t s) {
-  return launch_cfg<EPI_RESIDUAL>(a, w, nullptr, resid, y, M, N, K, s);
+                                int M, int N, int K, hipStream_t s, int ldo) {
+  return launch_cfg<EPI_RESIDUAL>(a, w, nullptr, resid, y, M, N, K, s, ldo);
 }
 
 // ---- split-variant activation: h = silu(G) * U, 8 bf16 per 16-byte chunk

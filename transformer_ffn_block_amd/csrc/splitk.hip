@@ -15,14 +15,17 @@
 
 namespace ffn {
 
+// x and y rows are ld8 groups of 8 elements apart (a column block of a wider
+// output when ld8 > n8, the block's width in groups)
 template <int S>
 __global__ __launch_bounds__(256) void splitk_residual(const float4* __restrict__ part,
                                                        const uint4* __restrict__ x,
                                                        uint4* __restrict__ y, int groups,
-                                                       size_t split_stride) {
+                                                       size_t split_stride, int n8, int ld8) {
   const int i = blockIdx.x * 256 + threadIdx.x;  // 8-output group
   if (i >= groups) return;
-  const uint4 xv = x[i];
+  const size_t io = ld8 == n8 ? (size_t)i : (size_t)(i / n8) * ld8 + i % n8;
+  const uint4 xv = x[io];
   float4 a[S], b[S];
 #pragma unroll
   for (int z = 0; z < S; ++z) {
@@ -41,15 +44,15 @@ __global__ __launch_bounds__(256) void splitk_residual(const float4* __restrict_
   unpack8(xv, xf);
 #pragma unroll
   for (int e = 0; e < 8; ++e) v[e] = xf[e] + v[e];
-  y[i] = pack8(v);
+  y[io] = pack8(v);
 }
 
 template <int S>
 static void splitk_go(const float* part, const void* x, void* y, int groups, size_t stride,
-                      hipStream_t s) {
+                      int n8, int ld8, hipStream_t s) {
   const dim3 grid((unsigned)((groups + 255) / 256)), block(256);
   FFN_DISPATCH(splitk_residual<S>, grid, block, 0, s, (const float4*)part, (const uint4*)x,
-               (uint4*)y, groups, stride);
+               (uint4*)y, groups, stride, n8, ld8);
 }
 
 // h = silu(sum_z G_z) * sum_z U_z for the split-K fused gate/up GEMM: gate
@@ -57,7 +60,7 @@ static void splitk_go(const float* part, const void* x, void* y, int groups, siz
 template <int S>
 __global__ __launch_bounds__(256) void splitk_swiglu(const float4* __restrict__ part,
                                                      uint4* __restrict__ h, int groups,
-                                                     size_t plane) {
+                                                     size_t plane, int n8, int ld8) {
   const int i = blockIdx.x * 256 + threadIdx.x;  // 8-output group
   if (i >= groups) return;
   float4 ga[S], gb[S], ua[S], ub[S];
@@ -80,13 +83,15 @@ __global__ __launch_bounds__(256) void splitk_swiglu(const float4* __restrict__ 
   }
 #pragma unroll
   for (int e = 0; e < 8; ++e) g[e] = silu_mul(g[e], u[e]);
-  h[i] = pack8(g);
+  h[ld8 == n8 ? (size_t)i : (size_t)(i / n8) * ld8 + i % n8] = pack8(g);
 }
 
 template <int S>
-static void swiglu_go(const float* part, void* h, int groups, size_t plane, hipStream_t s) {
+static void swiglu_go(const float* part, void* h, int groups, size_t plane, int n8, int ld8,
+                      hipStream_t s) {
   const dim3 grid((unsigned)((groups + 255) / 256)), block(256);
-  FFN_DISPATCH(splitk_swiglu<S>, grid, block, 0, s, (const float4*)part, (uint4*)h, groups, plane);
+  FFN_DISPATCH(splitk_swiglu<S>, grid, block, 0, s, (const float4*)part, (uint4*)h, groups, plane,
+               n8, ld8);
 }
 
 // one instantiation per range count, 1..kPrefillMaxSplits
@@ -115,30 +120,36 @@ static bool by_splits(int splits, A... args) {
 }
 template <int S>
 struct ResidualGo {
-  static void go(const float* part, const void* x, void* y, int groups, size_t stride, hipStream_t s) {
-    splitk_go<S>(part, x, y, groups, stride, s);
+  static void go(const float* part, const void* x, void* y, int groups, size_t stride, int n8,
+                 int ld8, hipStream_t s) {
+    splitk_go<S>(part, x, y, groups, stride, n8, ld8, s);
   }
 };
 template <int S>
 struct SwigluGo {
-  static void go(const float* part, void* h, int groups, size_t plane, hipStream_t s) {
-    swiglu_go<S>(part, h, groups, plane, s);
+  static void go(const float* part, void* h, int groups, size_t plane, int n8, int ld8,
+                 hipStream_t s) {
+    swiglu_go<S>(part, h, groups, plane, n8, ld8, s);
   }
 };
 
 hipError_t launch_splitk_residual(const float* part, int splits, const void* x, void* y, int M,
-                                  int N, hipStream_t s) {
+                                  int N, hipStream_t s, int ldo) {
+  if (ldo <= 0) ldo = N;
   const int groups = M * (N / 8);
   const size_t stride = (size_t)M * N / 4;
-  if (!by_splits<ResidualGo>(splits, part, x, y, groups, stride, s)) return hipErrorInvalidValue;
+  if (!by_splits<ResidualGo>(splits, part, x, y, groups, stride, N / 8, ldo / 8, s))
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
 hipError_t launch_splitk_swiglu(const float* part, int splits, void* h, int M, int f,
-                                hipStream_t s) {
+                                hipStream_t s, int ldo) {
+  if (ldo <= 0) ldo = f;
   const int groups = M * (f / 8);
   const size_t plane = (size_t)M * f / 4;
-  if (!by_splits<SwigluGo>(splits, part, h, groups, plane, s)) return hipErrorInvalidValue;
+  if (!by_splits<SwigluGo>(splits, part, h, groups, plane, f / 8, ldo / 8, s))
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
