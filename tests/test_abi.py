@@ -103,14 +103,21 @@ def test_block_zero_tokens_is_a_noop(L):
     assert L.ffn_last_error().decode() == ""
 
 
+def _tile_m(M):
+    """Token tile of the prefill GEMMs: 128 up to 128 tokens, else 256."""
+    return 128 if M <= 128 else 256
+
+
 def _prefill_splits_rule(M, N, K, bno, cus=256):
-    """The documented split rule for a prefill GEMM (256-token tiles, bno
-    weight rows per tile, 64-deep K tiles in ranges of two when they pair up)."""
+    """The documented split rule for a prefill GEMM (128- or 256-token tiles,
+    bno weight rows per tile, 64-deep K tiles in ranges of two when they pair
+    up)."""
     if K % 64:
         return 1
-    tiles = -(-M // 256) * -(-N // bno)
+    bm = _tile_m(M)
+    tiles = -(-M // bm) * -(-N // bno)
     nk = K // 64
-    pp = M % 256 == 0 and N % bno == 0 and K % 128 == 0
+    pp = M % bm == 0 and N % bno == 0 and K % 128 == 0
     units = nk // 2 if (pp or nk % 2 == 0) else nk
     z = min(cus // tiles, 16, units)
     return max(z, 1)
@@ -125,9 +132,10 @@ def _prefill_plan_rule(M, N, K, bno, slots=256):
     z = _prefill_splits_rule(M, N, K, bno)
     if z > 1:
         return 0, z
-    if not (M % 256 == 0 and N % bno == 0 and K % 128 == 0):
+    bm = _tile_m(M)
+    if not (M % bm == 0 and N % bno == 0 and K % 128 == 0):
         return N, 1
-    mt, nt = M // 256, N // bno
+    mt, nt = M // bm, N // bno
     if mt * nt <= slots:
         return N, 1
     nm = (-(-mt * nt // slots) - 1) * slots // mt
@@ -141,7 +149,8 @@ def _prefill_plan_rule(M, N, K, bno, slots=256):
                                    (300, 512, 768), (512, 4096, 14336), (1000, 4096, 11008),
                                    (2048, 5120, 13824), (4096, 4096, 14336), (100, 1032, 576),
                                    (777, 2048, 704), (768, 4096, 11008), (1024, 4096, 11008),
-                                   (4352, 4096, 1024), (1536, 4096, 11008)])
+                                   (4352, 4096, 1024), (1536, 4096, 11008), (128, 512, 38400),
+                                   (128, 512, 76800), (96, 4096, 11008)])
 def test_prefill_split_workspace(L, M, d, f):
     """Above 64 tokens the bf16 workspace adds one fp32 region for split-K
     partials: 2 Z_gu [M, f - main] planes (fused gate/up) or Z_dn
@@ -172,6 +181,9 @@ def test_prefill_tail_plans():
     assert _prefill_plan_rule(1024, 11008, 4096, 128) == (64 * 128, 2)
     assert _prefill_plan_rule(4352, 4096, 1024, 256) == (15 * 256, 8)
     assert _prefill_plan_rule(768, 4096, 11008, 256) == (0, 5)
+    # 128 tokens take 128-token tiles: 300 fused gate/up tiles at f = 38400
+    # are 44 past a round, split over the 4 K ranges of d = 512
+    assert _prefill_plan_rule(128, 38400, 512, 128) == (256 * 128, 4)
     # whole rounds: no split
     assert _prefill_plan_rule(8192, 14336, 4096, 128) == (14336, 1)
     assert _prefill_plan_rule(8192, 4096, 14336, 256) == (4096, 1)

@@ -475,6 +475,26 @@ def test_block_prefill_split_tail_mid_batch_sampled_rows(gpu_lib):
     assert record("prefill split tail 768x4096x11008 (24 rows)", max_norm_err(a, r), TOL_BF16) <= TOL_BF16
 
 
+# Up to 128 tokens the prefill GEMMs take 128-token tiles.  On a 256-CU
+# device: (128, 1024, 32768) has 256 fused gate/up tiles (one round,
+# unsplit) and a down GEMM of 4 tiles over 16 K ranges; (128, 512, 76800)
+# has 600 gate/up tiles -> 512 walked persistently and the last 88 over 2 K
+# ranges; (96, 512, 704) ragged tokens on the one-group schedule.
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("M,d,f", [(128, 1024, 32768), (128, 512, 76800), (96, 512, 704)])
+def test_block_prefill_128_token_tiles(gpu_lib, M, d, f):
+    from transformer_ffn_block_amd import ffn
+    _say("block prefill 128-token tiles", M, d, f)
+    b = I.make_block(6000 + M + f, M, d, f, "bf16")
+    r = O.block_from_stored("bf16", b.x, b.g, b.w_gate, b.w_up, b.w_down, b.eps)
+    for variant in ("fused", "split"):
+        a = host_f64(_run_block(ffn, b, variant))
+        assert record(f"prefill 128-token tiles {M}x{d}x{f} {variant}", max_norm_err(a, r), TOL_BF16) <= TOL_BF16
+        per_row = max(max_norm_err(a[i], r[i]) for i in range(M))
+        assert record(f"prefill 128-token tiles {M}x{d}x{f} {variant} worst row", per_row, TOL_BF16,
+                      "max_norm_per_row") <= TOL_BF16
+
+
 # ----------------------------------------------------------------------------
 # properties
 # ----------------------------------------------------------------------------

@@ -931,46 +931,71 @@ static hipError_t launch_reg(const void* act, const void* w0, const void* w1, co
   return hipGetLastError();
 }
 
+// Token tile of the LDS-fed kernels: 256, or 128 for batches of at most
+// FFN_PF_BM128 tokens (0 = off).  Up to 128 tokens the tile count is the same
+// either way and the 128-token tile skips the MFMA work and LDS traffic of
+// the padded rows (interleaved A/B, d = 4096, f = 11008: block 98.4 / 105.3 /
+// 112.5 -> 94.9 / 101.6 / 105.8 us at 65 / 100 / 128 tokens).  Above that it
+// multiplies the tiles, which costs whole rounds (300 tokens: 258 instead of
+// 172 gate/up tiles, 163 -> 213 us).
+#ifndef FFN_PF_BM128
+#define FFN_PF_BM128 128
+#endif
+static int tile_m(int M) { return M <= FFN_PF_BM128 ? kBM / 2 : kBM; }
+
 // Workgroups of the persistent ping-pong kernel resident at once (a multiple
 // of 8, one per XCD slot; one per compute unit if the runtime cannot tell:
-// its LDS stages take 128 KB).
-template <int EPI>
+// its LDS stages take 96-128 KB).
+template <int EPI, int BM>
 static int pp_slots() {
   static const int slots = [] {
-    const int r = resident_slots(gemm_dma<kBM, kBN, kWM, kWN, EPI, kPpBK, kPpS, true, true>, kWM * kWN * 64);
+    const int r = resident_slots(gemm_dma<BM, kBN, kWM, kWN, EPI, kPpBK, kPpS, true, true>, kWM * kWN * 64);
     return (r > 0 ? r : device_cus()) / 8 * 8;
   }();
   return slots;
 }
+template <int EPI>
+static int pp_slots(int bm) {
+  return bm == kBM ? pp_slots<EPI, kBM>() : pp_slots<EPI, kBM / 2>();
+}
 
 // ldo: row stride of out and resid in elements (N unless the GEMM covers a
 // column block of a wider output)
+template <int EPI, int BM>
+static void launch_dma(const void* act, const void* w0, const void* w1, const void* resid,
+                       void* out, int M, int N, int K, hipStream_t s, int ldo) {
+  constexpr int BNO = EPI == EPI_SWIGLU ? kBN / 2 : kBN;
+  const long tiles = (long)((M + BM - 1) / BM) * ((N + BNO - 1) / BNO);
+  // whole tiles and an even number of K tiles: the ping-pong schedule,
+  // walked persistently when the tiles take more than one round
+  if (kPingPong && M % BM == 0 && N % BNO == 0 && K % (kPpS * kPpBK) == 0) {
+    auto pers = gemm_dma<BM, kBN, kWM, kWN, EPI, kPpBK, kPpS, true, true>;
+    const int slots = pp_slots<EPI, BM>();
+    if (FFN_PF_PERSIST && slots >= 8 && tiles > slots)
+      FFN_DISPATCH(pers, dim3((unsigned)slots), dim3(kWM * kWN * 64), 0, s, (const uint16_t*)act,
+                   (const uint16_t*)w0, (const uint16_t*)w1, (const uint16_t*)resid, (uint16_t*)out, M,
+                   N, K, ldo, nullptr);
+    else
+      FFN_DISPATCH((gemm_dma<BM, kBN, kWM, kWN, EPI, kPpBK, kPpS, true>), dim3((unsigned)tiles),
+                   dim3(kWM * kWN * 64), 0, s, (const uint16_t*)act, (const uint16_t*)w0,
+                   (const uint16_t*)w1, (const uint16_t*)resid, (uint16_t*)out, M, N, K, ldo, nullptr);
+  } else
+    FFN_DISPATCH((gemm_dma<BM, kBN, kWM, kWN, EPI, kDmaBK, kDmaS, false>), dim3((unsigned)tiles),
+                 dim3(kWM * kWN * 64), 0, s, (const uint16_t*)act, (const uint16_t*)w0,
+                 (const uint16_t*)w1, (const uint16_t*)resid, (uint16_t*)out, M, N, K, ldo, nullptr);
+}
+
 template <int EPI>
 static hipError_t launch_cfg(const void* act, const void* w0, const void* w1, const void* resid,
                              void* out, int M, int N, int K, hipStream_t s, int ldo = 0) {
   if (ldo <= 0) ldo = N;
-  constexpr int BNO = EPI == EPI_SWIGLU ? kBN / 2 : kBN;
-  const long tiles = (long)((M + kBM - 1) / kBM) * ((N + BNO - 1) / BNO);
   // whole K tiles and every operand addressable by a buffer resource: LDS-fed kernel
   if (!FFN_PF_FORCE_REG && K % kDmaBK == 0 && (size_t)M * K * 2 < ((size_t)1 << 31) &&
       (size_t)N * K * 2 < ((size_t)1 << 31)) {
-    // whole tiles and an even number of K tiles: the ping-pong schedule,
-    // walked persistently when the tiles take more than one round
-    if (kPingPong && M % kBM == 0 && N % BNO == 0 && K % (kPpS * kPpBK) == 0) {
-      auto pers = gemm_dma<kBM, kBN, kWM, kWN, EPI, kPpBK, kPpS, true, true>;
-      const int slots = pp_slots<EPI>();
-      if (FFN_PF_PERSIST && slots >= 8 && tiles > slots)
-        FFN_DISPATCH(pers, dim3((unsigned)slots), dim3(kWM * kWN * 64), 0, s, (const uint16_t*)act,
-                     (const uint16_t*)w0, (const uint16_t*)w1, (const uint16_t*)resid, (uint16_t*)out, M,
-                     N, K, ldo, nullptr);
-      else
-        FFN_DISPATCH((gemm_dma<kBM, kBN, kWM, kWN, EPI, kPpBK, kPpS, true>), dim3((unsigned)tiles),
-                     dim3(kWM * kWN * 64), 0, s, (const uint16_t*)act, (const uint16_t*)w0,
-                     (const uint16_t*)w1, (const uint16_t*)resid, (uint16_t*)out, M, N, K, ldo, nullptr);
-    } else
-      FFN_DISPATCH((gemm_dma<kBM, kBN, kWM, kWN, EPI, kDmaBK, kDmaS, false>), dim3((unsigned)tiles),
-                         dim3(kWM * kWN * 64), 0, s, (const uint16_t*)act, (const uint16_t*)w0,
-                         (const uint16_t*)w1, (const uint16_t*)resid, (uint16_t*)out, M, N, K, ldo, nullptr);
+    if (tile_m(M) == kBM)
+      launch_dma<EPI, kBM>(act, w0, w1, resid, out, M, N, K, s, ldo);
+    else
+      launch_dma<EPI, kBM / 2>(act, w0, w1, resid, out, M, N, K, s, ldo);
     return hipGetLastError();
   }
   return launch_reg<EPI>(act, w0, w1, resid, out, M, N, K, nullptr, 0.f, s);
@@ -989,11 +1014,12 @@ static bool dma_ok(int M, int N, int K) {
          (size_t)N * K * 2 < ((size_t)1 << 31);
 }
 static bool pp_ok(int M, int N, int K, int bno) {
-  return kPingPong && M % kBM == 0 && N % bno == 0 && K % (kPpS * kPpBK) == 0;
+  return kPingPong && M % tile_m(M) == 0 && N % bno == 0 && K % (kPpS * kPpBK) == 0;
 }
 static int splits_for(int M, int N, int K, int bno) {
   if (!FFN_PF_SPLITK || !dma_ok(M, N, K)) return 1;
-  const long tiles = (long)((M + kBM - 1) / kBM) * ((N + bno - 1) / bno);
+  const int bm = tile_m(M);
+  const long tiles = (long)((M + bm - 1) / bm) * ((N + bno - 1) / bno);
   const int cus = device_cus();
   long z = tiles > 0 ? cus / tiles : 1;
   // the kernels' range unit: whole groups of S K tiles when they divide K
@@ -1026,7 +1052,8 @@ static PrefillPlan plan_for(int M, int N, int K) {
     return p;
   }
   if (!FFN_PF_SPLITK || FFN_PF_TAIL < 2 || !dma_ok(M, N, K) || !pp_ok(M, N, K, BNO)) return p;
-  const long mt = M / kBM, nt = N / BNO, tiles = mt * nt, slots = pp_slots<EPI>();
+  const int bm = tile_m(M);
+  const long mt = M / bm, nt = N / BNO, tiles = mt * nt, slots = pp_slots<EPI>(bm);
   if (slots < 8 || tiles <= slots) return p;
   const long rounds = (tiles + slots - 1) / slots;
   const long nm = (rounds - 1) * slots / mt;  // column tiles filling the earlier rounds
@@ -1044,21 +1071,30 @@ static PrefillPlan plan_for(int M, int N, int K) {
 PrefillPlan prefill_gateup_plan(int M, int d, int f) { return plan_for<EPI_SWIGLU>(M, f, d); }
 PrefillPlan prefill_down_plan(int M, int d, int f) { return plan_for<EPI_RESIDUAL>(M, d, f); }
 
-template <int EPI>
-static hipError_t launch_part(const void* act, const void* w0, const void* w1, float* part, int Z,
-                              int M, int N, int K, hipStream_t s) {
+template <int EPI, int BM>
+static void launch_part_bm(const void* act, const void* w0, const void* w1, float* part, int Z,
+                           int M, int N, int K, hipStream_t s) {
   constexpr int BNO = EPI == EPI_SWIGLU ? kBN / 2 : kBN;
-  const long tiles = (long)((M + kBM - 1) / kBM) * ((N + BNO - 1) / BNO);
-  if (Z < 1 || Z > kPrefillMaxSplits || !dma_ok(M, N, K)) return hipErrorInvalidValue;
+  const long tiles = (long)((M + BM - 1) / BM) * ((N + BNO - 1) / BNO);
   const dim3 grid((unsigned)tiles, (unsigned)Z), block(kWM * kWN * 64);
   if (pp_ok(M, N, K, BNO))
-    FFN_DISPATCH((gemm_dma<kBM, kBN, kWM, kWN, EPI, kPpBK, kPpS, true, false, true>), grid, block, 0, s,
+    FFN_DISPATCH((gemm_dma<BM, kBN, kWM, kWN, EPI, kPpBK, kPpS, true, false, true>), grid, block, 0, s,
                  (const uint16_t*)act, (const uint16_t*)w0, (const uint16_t*)w1, nullptr, nullptr, M,
                  N, K, N, part);
   else
-    FFN_DISPATCH((gemm_dma<kBM, kBN, kWM, kWN, EPI, kDmaBK, kDmaS, false, false, true>), grid, block,
+    FFN_DISPATCH((gemm_dma<BM, kBN, kWM, kWN, EPI, kDmaBK, kDmaS, false, false, true>), grid, block,
                  0, s, (const uint16_t*)act, (const uint16_t*)w0, (const uint16_t*)w1, nullptr,
                  nullptr, M, N, K, N, part);
+}
+
+template <int EPI>
+static hipError_t launch_part(const void* act, const void* w0, const void* w1, float* part, int Z,
+                              int M, int N, int K, hipStream_t s) {
+  if (Z < 1 || Z > kPrefillMaxSplits || !dma_ok(M, N, K)) return hipErrorInvalidValue;
+  if (tile_m(M) == kBM)
+    launch_part_bm<EPI, kBM>(act, w0, w1, part, Z, M, N, K, s);
+  else
+    launch_part_bm<EPI, kBM / 2>(act, w0, w1, part, Z, M, N, K, s);
   return hipGetLastError();
 }
 
