@@ -148,23 +148,22 @@ ffn_status ffn_rmsnorm(ffn_dtype dt, const void *x, const void *g, void *y,
  * bf16 with AUTO, FUSED or FUSED_NORM and M <= 64 (the decode kernels) h
  * takes ceil(M/16) * 16 rows of ceil(f/128) * 128 elements: it is kept in
  * the down projection's operand order, not row-major.  For bf16 with more
- * than 64 tokens, GEMMs whose 256 x 256 tiles number fewer than the
- * device's compute units are split over K: the workspace then also holds
- * their fp32 partial sums, one region sized for the larger of the fused
- * gate/up GEMM's (2 Z_gu [M, f] planes; not for SPLIT) and the down GEMM's
- * (Z_dn [M, d] planes), Z = floor(compute units / tiles), at most 16, at
- * least one 64-deep K tile per range (at d = 4096, f = 11008 on 256 CUs:
- * Z_gu = 2 up to 256 tokens; Z_dn = 16 / 8 / 4 / 2 up to 256 / 512 / 1024 /
- * 2048 tokens).  A GEMM of whole tiles needing more than one round of
- * resident tiles whose last round holds at most half a round splits only
- * its last output columns (those beyond the ones filling the earlier
- * rounds): its planes are then [M, columns split] (at 768 tokens and
- * f = 11008, 16 planes of the last 128 gate and up columns).  The size
- * therefore depends on the current device's compute-unit count and
- * occupancy (256 CUs, one tile each, are assumed where no device can be
- * queried).  The
- * workspace's contents are the library's own between calls; the sizes are
- * what a caller relies on. */
+ * than 64 tokens, GEMMs whose tiles (256 tokens x 256 weight rows; 128
+ * tokens up to 128 tokens) number fewer than the device's compute units
+ * are split over K: the workspace then also holds their fp32 partial sums,
+ * one region sized for the larger of the fused gate/up GEMM's (2 Z_gu
+ * [M, f] planes; not for SPLIT) and the down GEMM's (Z_dn [M, d] planes),
+ * Z = floor(compute units / tiles), at most 16, at least one 64-deep K tile
+ * per range (at d = 4096, f = 11008 on 256 CUs: Z_gu = 2 up to 256 tokens;
+ * Z_dn = 16 / 8 / 4 / 2 up to 256 / 512 / 1024 / 2048 tokens).  A GEMM of
+ * whole tiles needing more than one round of resident tiles, whose last
+ * round holds at most half a round, splits only its last output columns
+ * (those beyond the ones filling the earlier rounds): its planes are then
+ * [M, columns split] (at 768 tokens and f = 11008, 16 planes of the last
+ * 128 gate and up columns).  The size therefore depends on the current
+ * device's compute-unit count and occupancy (256 CUs, one tile each, are
+ * assumed where no device can be queried).  The workspace's contents are
+ * the library's own between calls; the sizes are what a caller relies on. */
 size_t ffn_swiglu_block_workspace_size(ffn_dtype dt, int64_t M, int64_t d, int64_t f,
                                        ffn_variant variant);
 
