@@ -106,7 +106,9 @@ hipError_t launch_gemm_gateup_fused_part(const void* n, const void* wg, const vo
 hipError_t launch_gemm_down_part(const void* h, const void* wd, float* part, int Z, int M, int d,
                                  int f, hipStream_t s);
 // h[m,j] = bf16(silu(sum_z G_z[m,j]) * sum_z U_z[m,j]), ranges added in z
-// order, from the partial planes above (f % 8 == 0).
+// order, from the partial planes above (f % 8 == 0).  ldo (0: f): row
+// stride of h in elements, a multiple of 8, when the planes cover a column
+// block of a wider h (h then points at the block's first column).
 hipError_t launch_splitk_swiglu(const float* part, int splits, void* h, int M, int f,
                                 hipStream_t s, int ldo = 0);
 // h = silu(G) * U elementwise over `count` bf16 values (count % 8 == 0).
@@ -152,8 +154,8 @@ hipError_t launch_q4_down(const void* h, const uint8_t* qd, const uint16_t* sd, 
 int q4_max_tokens();
 
 // y[m,i] = bf16(x[m,i] + sum_{z < splits} part[z][m][i]), summed in z order
-// (N % 8 == 0; splits <= kPrefillMaxSplits).  ldo (0: N): row stride of x, y
-// and h in elements, a multiple of 8, when the partials cover a column block
+// (N % 8 == 0; splits <= kPrefillMaxSplits).  ldo (0: N): row stride of x
+// and y in elements, a multiple of 8, when the partials cover a column block
 // of a wider output (the pointers then point at the block's first column).
 hipError_t launch_splitk_residual(const float* part, int splits, const void* x, void* y, int M,
                                   int N, hipStream_t s, int ldo = 0);
