@@ -235,6 +235,15 @@ def test_workspace_sizes(L):
     assert L.ffn_swiglu_block_q4_workspace_size(64, 5120, 17408) == \
         r256(64 * 5120 * 2) + r256(64 * 17408 * 2) + 4 * 32 * 5120 * 4
     assert L.ffn_swiglu_block_q4_workspace_size(-1, 5120, 17408) == 0
+    # d = 4096: 256 row tiles fill a round of 256 CUs, so up to 16 tokens the
+    # down projection runs unsplit (no partials); 32 tokens split 4 ways
+    assert L.ffn_swiglu_block_q8_workspace_size(8, 4096, 11008) == r256(8 * 11008 * 2)
+    assert L.ffn_swiglu_block_q8_workspace_size(16, 4096, 11008) == \
+        r256(16 * 4096 * 2) + r256(16 * 11008 * 2)
+    assert L.ffn_swiglu_block_q8_workspace_size(32, 4096, 11008) == \
+        r256(32 * 4096 * 2) + r256(32 * 11008 * 2) + r256(4 * 32 * 4096 * 4)
+    assert L.ffn_swiglu_block_q4_workspace_size(16, 4096, 11008) == \
+        r256(16 * 4096 * 2) + r256(16 * 11008 * 2)
     # beyond the weight-streaming regime the quantised blocks take no call
     assert L.ffn_swiglu_block_q4_workspace_size(65, 5120, 17408) == 0
     assert L.ffn_swiglu_block_q8_workspace_size(65, 5120, 17408) == 0

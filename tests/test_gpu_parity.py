@@ -700,6 +700,19 @@ def test_q8_ragged_tokens(gpu_lib, M, d, f):
     assert record(f"q8 ragged {M}x{d}x{f}", err, TOL_Q8) <= TOL_Q8
 
 
+# d = 4096: the down projection's 256 row tiles fill a round of 256 CUs, so
+# up to 16 tokens it runs unsplit in four-wave workgroups (no partials);
+# f = 800 leaves a partial last stage, 11008 is the decode shape
+@pytest.mark.parametrize("M,f", [(1, 800), (8, 11008), (13, 800), (16, 11008), (17, 800)])
+def test_q8_whole_round_down(gpu_lib, M, f):
+    from transformer_ffn_block_amd import ffn
+    d = 4096
+    _say("q8 whole-round down", M, d, f)
+    q = I.make_q8_block(900 + M, M, d, f)
+    err = max_norm_err(_run_q8(ffn, q), _q8_ref(q))
+    assert record(f"q8 whole-round down {M}x{d}x{f}", err, TOL_Q8) <= TOL_Q8
+
+
 @pytest.mark.parametrize("M", [8, 12, 33])
 def test_q8_quant_minus_128(gpu_lib, M):
     """The int8 range's extra value -128 (never drawn by the generator, but a
@@ -803,6 +816,17 @@ def test_q4_ragged_tokens(gpu_lib, M, d, f):
     q = I.make_q4_block(1800 + M, M, d, f)
     err = max_norm_err(_run_q4(ffn, q), _q4_ref(q))
     assert record(f"q4 ragged {M}x{d}x{f}", err, TOL_Q4) <= TOL_Q4
+
+
+# as for Q8_0: d = 4096 runs the down projection unsplit up to 16 tokens
+@pytest.mark.parametrize("M,f", [(1, 800), (8, 11008), (13, 800), (16, 11008), (17, 800)])
+def test_q4_whole_round_down(gpu_lib, M, f):
+    from transformer_ffn_block_amd import ffn
+    d = 4096
+    _say("q4 whole-round down", M, d, f)
+    q = I.make_q4_block(1900 + M, M, d, f)
+    err = max_norm_err(_run_q4(ffn, q), _q4_ref(q))
+    assert record(f"q4 whole-round down {M}x{d}x{f}", err, TOL_Q4) <= TOL_Q4
 
 
 def test_q4_folded_and_materialised_norm_agree(gpu_lib):

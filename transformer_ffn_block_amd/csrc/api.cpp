@@ -439,7 +439,7 @@ struct Q8Traits {
   static int max_tokens() { return ffn::q8_max_tokens(); }
   // fp32 partial sums of the split-K down projection for Mc tokens
   static size_t part_bytes(int64_t Mc, int64_t d, int64_t f) {
-    const int sp = ffn::q8_down_splits((int)d, (int)f);
+    const int sp = ffn::q8_down_splits((int)Mc, (int)d, (int)f);
     return sp > 1 ? (size_t)sp * (size_t)Mc * (size_t)d * 4 : 0;
   }
   // The norm folds into the gate/up kernel for every call of up to 8
@@ -471,7 +471,7 @@ struct Q4Traits {
   static int max_tokens() { return ffn::q4_max_tokens(); }
   // fp32 partial sums of the split-K down projection for Mc tokens
   static size_t part_bytes(int64_t Mc, int64_t d, int64_t f) {
-    const int sp = ffn::q4_down_splits((int)d, (int)f);
+    const int sp = ffn::q4_down_splits((int)Mc, (int)d, (int)f);
     return sp > 1 ? (size_t)sp * (size_t)Mc * (size_t)d * 4 : 0;
   }
   // the same bound as Q8_0 (measured: block 23.5 -> 21.0 us at f = 2176,

@@ -133,9 +133,9 @@ constexpr int kQuantMaxSplits = 8;
 hipError_t launch_q8_gateup(const void* act, const void* gain, float eps, const int8_t* qg,
                             const uint16_t* sg, const int8_t* qu, const uint16_t* su, void* h,
                             int M, int d, int f, hipStream_t s);
-// Down projection, split over K into q8_down_splits(d, f) ranges when that
+// Down projection, split over K into q8_down_splits(M, d, f) ranges when that
 // is above 1 (partials in part[splits][M][d], as for Q4_0 below).
-int q8_down_splits(int N, int K);
+int q8_down_splits(int M, int N, int K);
 hipError_t launch_q8_down(const void* h, const int8_t* qd, const uint16_t* sd, const void* x,
                           void* y, float* part, int M, int d, int f, hipStream_t s);
 int q8_max_tokens();
@@ -145,10 +145,10 @@ int q8_max_tokens();
 hipError_t launch_q4_gateup(const void* act, const void* gain, float eps, const uint8_t* qg,
                             const uint16_t* sg, const uint8_t* qu, const uint16_t* su, void* h,
                             int M, int d, int f, hipStream_t s);
-// Down projection, split over K into q4_down_splits(d, f) ranges when that
+// Down projection, split over K into q4_down_splits(M, d, f) ranges when that
 // is above 1: the fp32 partial sums go to part[splits][M][d] (caller's
 // workspace) and launch_splitk_residual adds them to x in range order.
-int q4_down_splits(int N, int K);
+int q4_down_splits(int M, int N, int K);
 hipError_t launch_q4_down(const void* h, const uint8_t* qd, const uint16_t* sd, const void* x,
                           void* y, float* part, int M, int d, int f, hipStream_t s);
 int q4_max_tokens();

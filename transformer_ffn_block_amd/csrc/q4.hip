@@ -96,6 +96,14 @@
 #ifndef FFN_Q4_DN_SPLIT_TARGET
 #define FFN_Q4_DN_SPLIT_TARGET 1024
 #endif
+// Down projections of up to FFN_Q4_DN_WHOLE tokens whose 16-row tiles fill
+// whole rounds of the compute units (d = 4096 on 256 CUs) run unsplit.
+// Interleaved A/B, d = 4096, f = 11008: block 29.5 / 33.6 / 39.8 -> 28.2 /
+// 31.1 / 37.9 us at 1 / 8 / 16 tokens; at 32 tokens the split stays faster
+// (50.6 -> 57.3 us unsplit).
+#ifndef FFN_Q4_DN_WHOLE
+#define FFN_Q4_DN_WHOLE 16
+#endif
 
 namespace ffn {
 
@@ -607,9 +615,10 @@ hipError_t launch_q4_gateup(const void* act, const void* gain, float eps, const 
 // Split-K factor of the down projection: enough (row tile, K range) workgroups
 // for about FFN_Q4_DN_SPLIT_TARGET of them in total (4 per compute unit on
 // 256 compute units), at most 8 ranges and no more than the 256-k stages.
-int q4_down_splits(int N, int K) {
+int q4_down_splits(int M, int N, int K) {
   const int target = FFN_Q4_DN_SPLIT_TARGET;
   const int tiles = (N + 15) / 16;
+  if (M <= FFN_Q4_DN_WHOLE && tiles % device_cus() == 0) return 1;
   const int nst = (K / 32 + 7) / 8;
   int sp = target > 0 ? (target + tiles - 1) / tiles : 1;
   sp = sp < 1 ? 1 : sp > kQuantMaxSplits ? kQuantMaxSplits : sp;
@@ -620,7 +629,7 @@ hipError_t launch_q4_down(const void* h, const uint8_t* qd, const uint16_t* sd, 
                           void* y, float* part, int M, int d, int f, hipStream_t s) {
   constexpr int W = FFN_Q4_DN_WAVES;
   const uint16_t* a = (const uint16_t*)h;
-  const int sp = q4_down_splits(d, f);
+  const int sp = q4_down_splits(M, d, f);
   const bool al = q4_scales_aligned(f, sd, nullptr);
   if (sp == 1) {
     if (al) launch_q4_mt<1, W, true, false>(a, nullptr, 0.f, qd, sd, nullptr, nullptr, (const uint16_t*)x, (uint16_t*)y, nullptr, 1, M, f, d, s);

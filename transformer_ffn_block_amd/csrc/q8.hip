@@ -55,6 +55,15 @@
 #ifndef FFN_Q8_DN_SPLIT_TARGET
 #define FFN_Q8_DN_SPLIT_TARGET 1024
 #endif
+// Down projections of up to FFN_Q8_DN_WHOLE tokens whose 16-row tiles fill
+// whole rounds of the compute units (d = 4096 on 256 CUs) run unsplit in
+// four-wave workgroups.  Interleaved A/B, d = 4096, f = 11008: block 38.7 /
+// 41.1 / 42.8 / 48.5 -> 36.9 / 39.0 / 39.9 / 46.4 us at 1 / 4 / 8 / 16
+// tokens; at 32 and 64 tokens the split stays faster (58.4 -> 62.3 and
+// 111.5 -> 120.2 us unsplit).
+#ifndef FFN_Q8_DN_WHOLE
+#define FFN_Q8_DN_WHOLE 16
+#endif
 
 // The 8-token gate/up kernel (two matrices, 8 staged token rows, norm not
 // folded): waves per SIMD it is register-allocated for, and the 32-quant
@@ -512,13 +521,17 @@ int q8_max_tokens() { return 32; }
 #define FFN_Q8_BALANCE 3
 #endif
 
+#ifndef FFN_Q8_DN_BALANCE
+#define FFN_Q8_DN_BALANCE 0
+#endif
 template <class Kern>
 static void q8_go(Kern kern, bool gateup, int splits, int N, int threads, const uint16_t* a,
                      const uint16_t* gn, const int8_t* q0, const uint16_t* s0,
                      const int8_t* q1, const uint16_t* s1, const uint16_t* rr,
                      uint16_t* o, float* part, int M, int K, float eps, int slots, hipStream_t s) {
   static const int cus = device_cus();
-  const int groups = gateup ? stream_groups(N, slots, FFN_Q8_BALANCE, cus) : (N + 15) / 16;
+  const int groups = gateup ? stream_groups(N, slots, FFN_Q8_BALANCE, cus)
+                     : FFN_Q8_DN_BALANCE ? stream_groups(N, 1, 3, cus) : (N + 15) / 16;
   FFN_DISPATCH(kern, dim3((unsigned)groups, (unsigned)splits), dim3(threads), 0, s, a, gn, q0, s0, q1,
                s1, rr, o, part, M, K, N, eps);
 }
@@ -587,9 +600,10 @@ hipError_t launch_q8_gateup(const void* act, const void* gain, float eps, const 
 // Split-K factor of the down projection, as for Q4_0: about
 // FFN_Q8_DN_SPLIT_TARGET workgroups in total, at most kQuantMaxSplits ranges
 // and no more than the 256-k stages.
-int q8_down_splits(int N, int K) {
+int q8_down_splits(int M, int N, int K) {
   const int target = FFN_Q8_DN_SPLIT_TARGET;
   const int tiles = (N + 15) / 16;
+  if (M <= FFN_Q8_DN_WHOLE && tiles % device_cus() == 0) return 1;
   const int nst = (K / 32 + 7) / 8;
   int sp = target > 0 ? (target + tiles - 1) / tiles : 1;
   sp = sp < 1 ? 1 : sp > kQuantMaxSplits ? kQuantMaxSplits : sp;
@@ -600,11 +614,12 @@ hipError_t launch_q8_down(const void* h, const int8_t* qd, const uint16_t* sd, c
                           void* y, float* part, int M, int d, int f, hipStream_t s) {
   constexpr int W = FFN_Q8_DN_WAVES;
   const uint16_t* a = (const uint16_t*)h;
-  const int sp = q8_down_splits(d, f);
+  const int sp = q8_down_splits(M, d, f);
   const bool al = q8_scales_aligned(f, sd, nullptr);
   if (sp == 1) {
-    if (al) launch_q8_mt<1, W, true, false>(a, nullptr, 0.f, qd, sd, nullptr, nullptr, (const uint16_t*)x, (uint16_t*)y, nullptr, 1, M, f, d, s);
-    else launch_q8_mt<1, W, false, false>(a, nullptr, 0.f, qd, sd, nullptr, nullptr, (const uint16_t*)x, (uint16_t*)y, nullptr, 1, M, f, d, s);
+    constexpr int W1 = FFN_Q8_DN_WHOLE > 0 ? 4 : W;
+    if (al) launch_q8_mt<1, W1, true, false>(a, nullptr, 0.f, qd, sd, nullptr, nullptr, (const uint16_t*)x, (uint16_t*)y, nullptr, 1, M, f, d, s);
+    else launch_q8_mt<1, W1, false, false>(a, nullptr, 0.f, qd, sd, nullptr, nullptr, (const uint16_t*)x, (uint16_t*)y, nullptr, 1, M, f, d, s);
     return hipGetLastError();
   }
   if (al) launch_q8_mt<1, W, true, true>(a, nullptr, 0.f, qd, sd, nullptr, nullptr, nullptr, nullptr, part, sp, M, f, d, s);
