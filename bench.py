@@ -570,8 +570,10 @@ def extras(torch, np, ffn, I, sets, x, g, b, ws, extra, clocks, want, keep):
                               "TFLOPs": round(6.0 * Mm * dm * fm / (t * 1e-3) / 1e12, 1),
                               "kernels_us_event_timed": km}
             del mws
-        res["note"] = ("AUTO at d=4096, f=11008 (the decode block's weights); GEMMs whose 256x256 "
-                       "tiles number fewer than the CUs are split over K")
+        res["note"] = ("AUTO at d=4096, f=11008 (the decode block's weights); GEMMs whose tiles "
+                       "number fewer than the CUs are split over K (128-token tiles up to 128 "
+                       "tokens), and past a whole round of tiles only the last columns split "
+                       "(768 tokens: 258 gate/up tiles)")
         extra["mid_batch"] = res
         log("mid batch", res)
         del mw, mx_all

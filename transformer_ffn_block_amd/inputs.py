@@ -299,5 +299,5 @@ WORKLOADS = {
     "q4_tp8_shard":      dict(seed=10, M=8, d=5120, f=17408 // 8),
     # between decode and prefill: the decode block's weights at batch sizes
     # whose GEMM tiles do not fill the chip (the first M rows of x)
-    "mid_batch":         dict(seed=11, M=(128, 512, 2048), d=4096, f=11008, dtype="bf16"),
+    "mid_batch":         dict(seed=11, M=(128, 512, 768, 2048), d=4096, f=11008, dtype="bf16"),
 }
